@@ -1,0 +1,212 @@
+"""Pins of the oracle's paged steps: metadata, page bound, top-k selection,
+token gathering and the sparse/full decode, against brute force, loops over
+the raw arrays, and the guarantees the EntmaxKV page states (bound >= best
+score in the page; support recovery; the 2 B delta error bound)."""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import entmax_oracle as O
+from sparse_long_context_page_amd import synth
+
+
+def small_inputs(kv_dtype="bf16", seq_lens=(100, 64, 37), H=4, Hkv=2, D=8, ps=16, seed=0,
+                 plant="none", n_planted=0):
+    w = synth.Workload("t", len(seq_lens), H, Hkv, D, ps, max(seq_lens), kv_dtype, (1.5,), (4,),
+                       1.0, plant=plant, n_planted=n_planted, seq_lens=tuple(seq_lens))
+    return synth.generate(w, seed)
+
+
+def raw_key(inp, b, g, t):
+    """Key of token t of sequence b, KV head g, read straight from the pool."""
+    w = inp["workload"]
+    phys = inp["block_table"][b, t // w.page_size]
+    x = inp["k_pool"][phys, g, t % w.page_size]
+    if w.kv_dtype == "bf16":
+        return synth.bf16_bits_to_f32(x).astype(np.float64)
+    return x.astype(np.float64)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_metadata_matches_token_loops(kv_dtype):
+    inp = small_inputs(kv_dtype)
+    w = inp["workload"]
+    kmin, kmax = O.page_metadata(inp["k_pool"], inp["block_table"], inp["seq_lens"],
+                                 w.page_size, kv_dtype)
+    for b, L in enumerate(inp["seq_lens"]):
+        for j in range((L + w.page_size - 1) // w.page_size):
+            phys = inp["block_table"][b, j]
+            for g in range(w.num_kv_heads):
+                toks = [raw_key(inp, b, g, t) for t in range(j * w.page_size, min(L, (j + 1) * w.page_size))]
+                lo = [min(k[d] for k in toks) for d in range(w.head_dim)]
+                hi = [max(k[d] for k in toks) for d in range(w.head_dim)]
+                assert list(kmin[phys, g]) == lo
+                assert list(kmax[phys, g]) == hi
+    # ragged tail rows (value 30) never leak into the box
+    assert np.nanmax(kmax) < synth.TAIL_FILL
+
+
+def test_bound_is_maximum_over_box_corners():
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        D = int(rng.integers(1, 9))
+        q = rng.normal(size=D).astype(np.float32).astype(np.float64)
+        lo = rng.normal(size=D)
+        hi = lo + rng.exponential(size=D)
+        best = max(float(np.dot(q, np.where(np.array(c), hi, lo)))
+                   for c in itertools.product([0, 1], repeat=D))
+        assert abs(O.page_bound(q, lo, hi) - best) <= 1e-12 * max(1.0, abs(best))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_bound_dominates_every_token_score(kv_dtype):
+    inp = small_inputs(kv_dtype, seq_lens=(300, 129), H=4, Hkv=2, D=16, ps=16, seed=5)
+    w = inp["workload"]
+    meta = O.page_metadata(inp["k_pool"], inp["block_table"], inp["seq_lens"], w.page_size, kv_dtype)
+    G = w.num_q_heads // w.num_kv_heads
+    for b in range(w.batch):
+        for h in range(w.num_q_heads):
+            ub, key, _ = O.select_for_head(inp, b, h, 3, meta=meta)
+            q = inp["q"][b, h].astype(np.float64)
+            L = inp["seq_lens"][b]
+            for j in range(len(ub)):
+                scores = [q @ raw_key(inp, b, h // G, t)
+                          for t in range(j * w.page_size, min(L, (j + 1) * w.page_size))]
+                assert ub[j] >= max(scores) - 1e-12
+
+
+def test_page_of_one_token_bound_is_exact_score():
+    inp = small_inputs("f32", seq_lens=(40,), H=2, Hkv=1, D=32, ps=16, seed=9)
+    # rebuild the same tokens as a 1-token-per-page cache
+    w = inp["workload"]
+    K, _ = O.gather_tokens(inp["k_pool"], 0, 0, inp["block_table"], inp["seq_lens"], 16, "f32")
+    q = inp["q"][0, 1].astype(np.float64)
+    for t in range(K.shape[0]):
+        assert O.page_bound(q, K[t], K[t]) == pytest.approx(float(q @ K[t]), rel=0, abs=1e-12)
+    # non-negative query: bound is q . kmax
+    qp = np.abs(q)
+    lo, hi = K.min(axis=0), K.max(axis=0)
+    assert O.page_bound(qp, lo, hi) == pytest.approx(float(qp @ hi), abs=1e-12)
+
+
+def rank_count_selection(key, budget):
+    """Independent formulation: page j is kept iff fewer than `budget` pages
+    beat it (a larger key, or an equal key at a lower index)."""
+    P = len(key)
+    keep = [j for j in range(P)
+            if sum(1 for i in range(P) if key[i] > key[j] or (key[i] == key[j] and i < j)) < budget]
+    return keep + [-1] * (budget - len(keep))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_selection_matches_rank_counting(seed):
+    rng = np.random.default_rng(seed)
+    P = int(rng.integers(1, 60))
+    # coarse values force many exact ties; include -0.0 and +0.0
+    key = (rng.integers(-4, 5, size=P) / 2.0).astype(np.float32)
+    key[rng.random(P) < 0.1] = np.float32(-0.0)
+    for budget in (1, 2, 5, P, P + 3):
+        sel = O.select_pages(key + np.float32(0.0), budget)
+        assert sel == rank_count_selection(key, budget)
+        kept = [j for j in sel if j >= 0]
+        assert kept == sorted(kept) and len(kept) == min(budget, P)
+
+
+def test_bound_key_rounds_once_to_float32():
+    ub = np.array([1.0 + 2.0 ** -30, -0.0, 3.0])
+    k = O.bound_key(ub)
+    assert k.dtype == np.float32
+    assert k[0] == np.float32(1.0) and np.signbit(k[1]) == False
+
+
+def test_near_tie_pages():
+    key = np.array([5.0, 4.0, 4.00001, 3.0, 4.0], dtype=np.float32)
+    nt = O.near_tie_pages(key, 2)
+    assert nt == {1, 2, 4}
+
+
+def test_gather_tokens_order_and_ragged_tail():
+    inp = small_inputs("bf16", seq_lens=(37,), H=2, Hkv=1, D=8, ps=16)
+    K, pos = O.gather_tokens(inp["k_pool"], 0, 0, inp["block_table"], inp["seq_lens"], 16, "bf16")
+    assert list(pos) == list(range(37))
+    for t in (0, 15, 16, 36):
+        np.testing.assert_array_equal(K[t], raw_key(inp, 0, 0, t))
+    Ks, ps_ = O.gather_tokens(inp["k_pool"], 0, 0, inp["block_table"], inp["seq_lens"], 16, "bf16",
+                              pages=[2, -1, 0])
+    assert list(ps_) == list(range(16)) + list(range(32, 37))
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+def test_full_decode_matches_dense_definition(alpha):
+    inp = small_inputs("bf16", seq_lens=(200,), H=2, Hkv=1, D=16, ps=16, seed=11)
+    r = O.decode_full(inp, 0, 1, alpha)
+    K = np.array([raw_key(inp, 0, 0, t) for t in range(200)])
+    phys = inp["block_table"][0]
+    V = np.array([synth.bf16_bits_to_f32(inp["v_pool"][phys[t // 16], 0, t % 16]).astype(np.float64)
+                  for t in range(200)])
+    z = K @ inp["q"][0, 1].astype(np.float64)
+    # check optimality of p directly (variational definition) and the output sum
+    a = (alpha - 1) * z
+    p = r.probs
+    assert abs(p.sum() - 1) < 1e-12 and (p >= 0).all()
+    m = 1 / (alpha - 1)
+    # KKT: for support tokens (a_i - tau) = p_i^(alpha-1); others a_i <= tau
+    sup = p > 0
+    np.testing.assert_allclose(a[sup] - r.tau, p[sup] ** (alpha - 1), atol=1e-12)
+    assert (a[~sup] <= r.tau + 1e-12).all()
+    np.testing.assert_allclose(r.out, (p[:, None] * V).sum(axis=0), atol=1e-12)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+@pytest.mark.parametrize("seed", range(3))
+def test_support_recovery_is_exact(alpha, seed):
+    inp = small_inputs("bf16", seq_lens=(700, 333), H=4, Hkv=2, D=16, ps=16, seed=20 + seed)
+    w = inp["workload"]
+    for b in range(w.batch):
+        P = (inp["seq_lens"][b] + 15) // 16
+        for h in range(w.num_q_heads):
+            full = O.decode_full(inp, b, h, alpha)
+            need = O.support_pages(full, 16)
+            sel = synth.constructed_selection(need, P, len(need) + 3, seed=seed)
+            sp = O.decode_sparse(inp, b, h, alpha, sel)
+            assert abs(sp.tau - full.tau) < 1e-12
+            np.testing.assert_allclose(sp.out, full.out, atol=1e-12)
+            assert sp.support == full.support
+            # every page selected -> identical decode
+            allp = O.decode_sparse(inp, b, h, alpha, list(range(P)))
+            np.testing.assert_allclose(allp.out, full.out, atol=0)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+def test_dropped_mass_identity_and_error_bound(alpha):
+    inp = small_inputs("f32", seq_lens=(640,), H=2, Hkv=1, D=16, ps=16, seed=33)
+    full = O.decode_full(inp, 0, 0, alpha)
+    rng = np.random.default_rng(0)
+    V, _ = O.gather_tokens(inp["v_pool"], 0, 0, inp["block_table"], inp["seq_lens"], 16, "f32")
+    B = np.linalg.norm(V, axis=1).max()
+    for _ in range(10):
+        keep_pages = sorted(rng.choice(40, size=int(rng.integers(1, 40)), replace=False).tolist())
+        sp = O.decode_sparse(inp, 0, 0, alpha, keep_pages)
+        kept = np.isin(full.positions, sp.positions)
+        delta = full.probs[~kept].sum()
+        # tau on a subset can only go down; kept probabilities only go up
+        assert sp.tau <= full.tau + 1e-12
+        p_tilde = np.zeros_like(full.probs)
+        p_tilde[kept] = sp.probs
+        assert (p_tilde[kept] >= full.probs[kept] - 1e-12).all()
+        # ||p - p~||_1 = 2 delta exactly, hence ||o - o~|| <= 2 B delta
+        assert abs(np.abs(full.probs - p_tilde).sum() - 2 * delta) < 1e-10
+        assert np.linalg.norm(full.out - sp.out) <= 2 * B * delta + 1e-10
+
+
+def test_empty_selection_and_planted_support():
+    inp = small_inputs("f32", seq_lens=(64,), H=1, Hkv=1, D=8, ps=16)
+    r = O.decode_sparse(inp, 0, 0, 1.5, [-1, -1])
+    assert r.support == 0 and np.all(r.out == 0)
+    # a planted key pointing at q dominates the scores and so the support
+    w = synth.Workload("p", 1, 1, 1, 64, 16, 4096, "f32", (1.5,), (32,), 0.5,
+                       plant="query", n_planted=8, plant_magnitude=40.0, block_table="contiguous")
+    inp = synth.generate(w, 1)
+    full = O.decode_full(inp, 0, 0, 1.5)
+    assert set(full.support_pos.tolist()) <= set(inp["planted"][(0, 0)].tolist())
