@@ -1,0 +1,181 @@
+/*
+ * entmaxkv.h - C ABI of a support-aware sparse alpha-entmax decode library
+ * for a paged KV cache, written for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes follows "Riepilogo Tecnico: EntmaxKV - Decodifica
+ * Consapevole del Supporto per l'Attention Entmax" (gist.science, paper
+ * 2605.21649), cited here as [EntmaxKV page]:
+ *   section 2.A  per-page key bounding boxes (k_min, k_max) and the
+ *                deterministic upper bound they give on a page's best score;
+ *   section 2.B  policy 1, a fixed budget of the top-k pages by that bound;
+ *   section 2.C  only the selected pages' K/V are read and alpha-entmax is
+ *                solved on that reduced set;
+ *   section 4    (efficiency) full-cache entmax decode as the baseline.
+ * The alpha-entmax definition is the standard Tsallis one (Peters, Niculae &
+ * Martins 2019): p_i = [(alpha-1) z_i - tau]_+^(1/(alpha-1)) with tau such
+ * that sum_i p_i = 1; z_i = q . k_i on the stored values (no scaling inside).
+ *
+ * Conventions shared by every entry point
+ *  - Array arguments are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or keeps a pointer after returning.
+ *  - `shape` is a HOST pointer, read during the call only.
+ *  - Work is enqueued on `stream` (0 = the null stream); calls return without
+ *    waiting for the GPU.
+ *  - `events` (nullable) is a host array of 2*k hipEvent_t handles created by
+ *    the caller; when given, events[2i] is recorded on `stream` right before
+ *    the call's i-th kernel and events[2i+1] right after it. k is stated per
+ *    entry point. Used for per-kernel timing.
+ *  - Every argument is validated on the host before any HIP call; on error
+ *    nothing is enqueued. Return codes are the ENTMAXKV_* values below.
+ *  - Device-side preconditions (not checked on the host, since they live in
+ *    device memory): 0 <= seq_lens[b] <= max_pages_per_seq * page_size;
+ *    block_table[b, j] in [0, num_phys_pages) for j < ceil(seq_lens[b] /
+ *    page_size). Kernels clamp seq_lens into that range and treat a block
+ *    table entry outside it as an empty page, so bad values give wrong
+ *    results, never out-of-bounds accesses.
+ *  - The library keeps no state between calls and is safe to call from
+ *    several host threads (each call uses only its own arguments).
+ *
+ * Layouts (row-major, all dense):
+ *   q            float32 [batch, num_q_heads, head_dim]
+ *   k_pool,
+ *   v_pool       kv_dtype [num_phys_pages, num_kv_heads, page_size, head_dim]
+ *                (one (page, KV head) is a contiguous page_size*head_dim block)
+ *   block_table  int32 [batch, max_pages_per_seq]: logical page j of sequence
+ *                b lives in physical page block_table[b, j]
+ *   seq_lens     int32 [batch]: tokens of sequence b are t < seq_lens[b];
+ *                token t is row t % page_size of logical page t / page_size
+ *   meta         kv_dtype [num_phys_pages, num_kv_heads, 2, head_dim]:
+ *                [..., 0, :] = k_min, [..., 1, :] = k_max of the page's
+ *                valid keys
+ *   sel          int32 [batch, num_q_heads, budget_pages]: selected logical
+ *                pages, strictly ascending, then -1 padding
+ *   out          float32 [batch, num_q_heads, head_dim]
+ *   tau          float32 [batch, num_q_heads] (nullable)
+ *   support      int32 [batch, num_q_heads] (nullable)
+ * Query head h uses KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Supported: head_dim in {64, 128}; page_size in {16, 32, 64};
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}; kv_dtype F32 or BF16;
+ * max_pages_per_seq <= 262144. Anything else returns ENTMAXKV_ERR_UNSUPPORTED.
+ */
+#ifndef ENTMAXKV_H
+#define ENTMAXKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ENTMAXKV_OK = 0,
+  ENTMAXKV_ERR_INVALID = -1,     /* null pointer, non-positive size, H % H_kv != 0,
+                                    budget <= 0, alpha <= 1 or not finite */
+  ENTMAXKV_ERR_UNSUPPORTED = -2, /* head_dim, page_size, group size, dtype or size
+                                    outside the supported set */
+  ENTMAXKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  ENTMAXKV_ERR_HIP = -4          /* a HIP launch or event record failed */
+};
+
+typedef enum { ENTMAXKV_F32 = 0, ENTMAXKV_BF16 = 1 } entmaxkv_dtype;
+
+typedef struct {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int32_t num_phys_pages;
+  int32_t kv_dtype; /* entmaxkv_dtype */
+} entmaxkv_shape;
+
+/* Which call a workspace is for (entmaxkv_workspace_bytes). */
+enum { ENTMAXKV_WS_SELECT = 0, ENTMAXKV_WS_SPARSE = 1, ENTMAXKV_WS_FULL = 2 };
+
+/*
+ * Page bounding boxes ([EntmaxKV page] section 2.A): for every logical page
+ * j < ceil(seq_lens[b]/page_size) of every sequence, writes the coordinate-
+ * wise min and max of its valid keys (rows t < seq_lens[b]) for each KV head
+ * to meta[block_table[b, j]]. min/max is exact, so meta holds stored key
+ * values (a zero may come out as -0 or +0). Pages not referenced are left
+ * untouched. Kernels launched: 1.
+ */
+int entmaxkv_build_page_meta(const entmaxkv_shape* shape, const void* k_pool,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             void* meta, hipStream_t stream, hipEvent_t* events);
+
+/*
+ * Page bounds and fixed-budget top-k ([EntmaxKV page] sections 2.A and 2.B
+ * policy 1). For each (b, h) and logical page j < P_b = ceil(seq_lens[b] /
+ * page_size):
+ *     ub[j] = fp32( sum_d max(q_d * kmin_d, q_d * kmax_d) )   (then -0 -> +0)
+ * the maximum of q.k over the page's box, summed in float64 from exact
+ * products and rounded once to float32. Selects the budget_pages pages with
+ * the largest ub, ties to the lower j, written ascending to sel[b, h, :]; if
+ * P_b <= budget_pages every page is kept. Unused slots are -1.
+ * sel_ub (nullable, float32 [batch, num_q_heads, budget_pages]) receives the
+ * ub of each kept page (-inf in unused slots).
+ * Workspace: entmaxkv_workspace_bytes(..., ENTMAXKV_WS_SELECT).
+ * Kernels launched: 2 (bounds, select).
+ */
+int entmaxkv_score_select(const entmaxkv_shape* shape, const float* q, const void* meta,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t budget_pages, int32_t* sel, float* sel_ub, void* ws,
+                          size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
+
+/*
+ * Sparse alpha-entmax decode ([EntmaxKV page] section 2.C). For each (b, h),
+ * gathers the valid tokens of the pages listed in sel[b, h, :] (entries < 0
+ * or >= P_b are ignored), computes z = q . k in float32 (float64 for F32
+ * caches), solves tau over those tokens only, and writes
+ *     out[b, h, :] = sum_i p_i v_i / sum_i p_i,  p_i = [(alpha-1) z_i - tau]_+^m
+ * (m = 1/(alpha-1); dividing by sum p, which is 1 up to rounding, keeps the
+ * output a convex combination). Only V rows with p_i > 0 are read. tau is in
+ * the (alpha-1) z units; support = #{p_i > 0}. A head with no tokens gets
+ * out = 0, tau = NaN, support = 0. The pages of the num_q_heads/num_kv_heads
+ * heads sharing a KV head are read once per call (their union).
+ * Workspace: entmaxkv_workspace_bytes(..., ENTMAXKV_WS_SPARSE) for the same
+ * budget_pages. Kernels launched: 2 (gather-score, threshold + P.V).
+ */
+int entmaxkv_decode_sparse(const entmaxkv_shape* shape, const float* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, const int32_t* sel, int32_t budget_pages,
+                           float alpha, float* out, float* tau, int32_t* support, void* ws,
+                           size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
+
+/*
+ * Full-cache alpha-entmax decode ([EntmaxKV page] section 4, the full-cache
+ * entmax baseline): as entmaxkv_decode_sparse with every page of every
+ * sequence selected. Workspace: entmaxkv_workspace_bytes(...,
+ * ENTMAXKV_WS_FULL). Kernels launched: 2 (score, threshold + P.V).
+ */
+int entmaxkv_decode_full(const entmaxkv_shape* shape, const float* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_table,
+                         const int32_t* seq_lens, float alpha, float* out, float* tau,
+                         int32_t* support, void* ws, size_t ws_bytes, hipStream_t stream,
+                         hipEvent_t* events);
+
+/*
+ * Workspace size in bytes for `which` (ENTMAXKV_WS_*) at this shape and
+ * budget (budget is ignored for ENTMAXKV_WS_FULL). Writes *bytes and returns
+ * ENTMAXKV_OK, or an error code for an invalid or unsupported shape.
+ */
+int entmaxkv_workspace_bytes(const entmaxkv_shape* shape, int32_t budget_pages, int32_t which,
+                             size_t* bytes);
+
+/* Static description of a return code; never NULL. */
+const char* entmaxkv_strerror(int code);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int entmaxkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTMAXKV_H */

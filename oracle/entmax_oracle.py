@@ -90,6 +90,23 @@ def page_metadata(k_pool, block_table, seq_lens, page_size: int, kv_dtype: str):
     return kmin, kmax
 
 
+def sequence_metadata(k_pool, block_table_row, seq_len: int, page_size: int, g: int,
+                      kv_dtype: str):
+    """The boxes of every logical page of one sequence for KV head g, in
+    logical page order: (kmin, kmax) float64 [P_b, D]. Same definition as
+    page_metadata, restricted to one sequence."""
+    P = num_pages(seq_len, page_size)
+    D = k_pool.shape[-1]
+    kmin = np.empty((P, D))
+    kmax = np.empty((P, D))
+    for j in range(P):
+        phys = int(block_table_row[j])
+        rows = kv_to_f64(k_pool[phys, g, :page_rows(j, seq_len, page_size), :], kv_dtype)
+        kmin[j] = rows.min(axis=0)
+        kmax[j] = rows.max(axis=0)
+    return kmin, kmax
+
+
 def page_bound(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> float:
     """Upper bound on q.k over the box [kmin, kmax] of one page (reading: the
     box maximum, sum_d max(q_d kmin_d, q_d kmax_d)).
@@ -353,17 +370,23 @@ def decode_sparse(inp: dict, b: int, h: int, alpha: float, sel) -> DecodeResult:
     return decode_tokens(inp["q"][b, h], K, V, pos, alpha)
 
 
-def select_for_head(inp: dict, b: int, h: int, budget: int, meta=None):
-    """Bounds and selection of one head: returns (ub float64 [P_b], key32, sel)."""
+def select_for_head(inp: dict, b: int, h: int, budget: int, meta=None, seq_meta=None):
+    """Bounds and selection of one head: returns (ub float64 [P_b], key32, sel).
+    `meta` is page_metadata's output; `seq_meta` is sequence_metadata's for
+    this (sequence, KV head); with neither, the boxes are computed here."""
     w = inp["workload"]
     G = w.num_q_heads // w.num_kv_heads
     g = h // G
-    if meta is None:
-        meta = page_metadata(inp["k_pool"], inp["block_table"], inp["seq_lens"],
-                             w.page_size, w.kv_dtype)
-    kmin, kmax = meta
     q = inp["q"][b, h].astype(np.float64)
-    ub = head_bounds(q, kmin, kmax, inp["block_table"][b], inp["seq_lens"][b], w.page_size, g)
+    if seq_meta is None and meta is None:
+        seq_meta = sequence_metadata(inp["k_pool"], inp["block_table"][b], inp["seq_lens"][b],
+                                     w.page_size, g, w.kv_dtype)
+    if seq_meta is not None:
+        kmin, kmax = seq_meta
+        ub = np.array([page_bound(q, kmin[j], kmax[j]) for j in range(kmin.shape[0])])
+    else:
+        kmin, kmax = meta
+        ub = head_bounds(q, kmin, kmax, inp["block_table"][b], inp["seq_lens"][b], w.page_size, g)
     key = bound_key(ub)
     return ub, key, select_pages(key, budget)
 

@@ -1,0 +1,283 @@
+// C ABI of the EntmaxKV-style decode library: host-side validation,
+// workspace planning and kernel dispatch. Every check runs before the first
+// HIP call, so a rejected call enqueues nothing.
+#include <math.h>
+
+#include "entmaxkv.h"
+#include "launch.hpp"
+
+using namespace ekv;
+
+namespace {
+
+constexpr int kMaxPagesPerSeq = 262144;
+constexpr size_t kMaxScoreLds = 150 * 1024;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_shape(const entmaxkv_shape* s, LaunchShape* out) {
+  if (!s) return ENTMAXKV_ERR_INVALID;
+  if (s->batch <= 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->head_dim <= 0 ||
+      s->page_size <= 0 || s->max_pages_per_seq <= 0 || s->num_phys_pages <= 0)
+    return ENTMAXKV_ERR_INVALID;
+  if (s->num_q_heads % s->num_kv_heads != 0) return ENTMAXKV_ERR_INVALID;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return ENTMAXKV_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return ENTMAXKV_ERR_UNSUPPORTED;
+  if (s->page_size != 16 && s->page_size != 32 && s->page_size != 64)
+    return ENTMAXKV_ERR_UNSUPPORTED;
+  if (s->kv_dtype != ENTMAXKV_F32 && s->kv_dtype != ENTMAXKV_BF16)
+    return ENTMAXKV_ERR_UNSUPPORTED;
+  if (s->max_pages_per_seq > kMaxPagesPerSeq) return ENTMAXKV_ERR_UNSUPPORTED;
+  // grid sizes stay far below 2^31 blocks and byte offsets fit 64 bits
+  if ((long long)s->batch * s->num_q_heads > (1LL << 24)) return ENTMAXKV_ERR_UNSUPPORTED;
+  if (out) {
+    out->batch = s->batch;
+    out->num_q_heads = s->num_q_heads;
+    out->num_kv_heads = s->num_kv_heads;
+    out->head_dim = s->head_dim;
+    out->page_size = s->page_size;
+    out->max_pages = s->max_pages_per_seq;
+    out->num_phys = s->num_phys_pages;
+    out->group = G;
+    out->bf16 = s->kv_dtype == ENTMAXKV_BF16;
+  }
+  return ENTMAXKV_OK;
+}
+
+int check_alpha(float alpha) {
+  if (!isfinite(alpha) || !(alpha > 1.0f)) return ENTMAXKV_ERR_INVALID;
+  return ENTMAXKV_OK;
+}
+
+int check_budget(int32_t budget) {
+  if (budget <= 0) return ENTMAXKV_ERR_INVALID;
+  if (budget > (1 << 22)) return ENTMAXKV_ERR_UNSUPPORTED;
+  return ENTMAXKV_OK;
+}
+
+// Width (in z units) of the window that holds every token of the support,
+// 1/(alpha-1), widened slightly so float32 rounding of z never drops one.
+float window_of(float alpha) {
+  const double w = 1.0 / ((double)alpha - 1.0);
+  return (float)(w * (1.0 + 1e-6) + 1e-3);
+}
+
+int score_lds_ok(const LaunchShape& s, const SplitPlan& p, bool sparse, int budget) {
+  const ScoreLds l = score_lds_layout(s.group, s.page_size, p.pages_per_split, sparse,
+                                      s.max_pages, budget, score_bytes(s.bf16));
+  return l.total <= kMaxScoreLds ? ENTMAXKV_OK : ENTMAXKV_ERR_UNSUPPORTED;
+}
+
+struct Events {
+  hipEvent_t* ev;
+  hipStream_t st;
+  bool before(int i) const { return !ev || hipEventRecord(ev[2 * i], st) == hipSuccess; }
+  bool after(int i) const { return !ev || hipEventRecord(ev[2 * i + 1], st) == hipSuccess; }
+};
+
+}  // namespace
+
+namespace ekv {
+
+SplitPlan plan_sparse(const LaunchShape& s, int budget) {
+  SplitPlan p;
+  const int keep = budget < s.max_pages ? budget : s.max_pages;
+  long long umax = (long long)s.group * keep;
+  if (umax > s.max_pages) umax = s.max_pages;
+  int pps = kSparseTokensPerSplit / s.page_size;
+  if (pps < 1) pps = 1;
+  const long long need = (umax + kMaxSplits - 1) / kMaxSplits;
+  if (pps < need) pps = (int)need;
+  p.pages_per_split = pps;
+  p.splits = (int)((umax + pps - 1) / pps);
+  p.cap = pps * s.page_size;
+  p.list_cap = keep * s.page_size;
+  return p;
+}
+
+SplitPlan plan_full(const LaunchShape& s) {
+  SplitPlan p;
+  int pps = kFullTokensPerSplit / s.page_size;
+  if (pps < 1) pps = 1;
+  const int need = (s.max_pages + kMaxSplits - 1) / kMaxSplits;
+  if (pps < need) pps = need;
+  p.pages_per_split = pps;
+  p.splits = (s.max_pages + pps - 1) / pps;
+  p.cap = pps * s.page_size;
+  p.list_cap = s.max_pages * s.page_size;
+  return p;
+}
+
+DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p) {
+  DecodeWs w;
+  const size_t bh = (size_t)s.batch * s.num_q_heads;
+  size_t o = 0;
+  const size_t zb = score_bytes(s.bf16);
+  w.cand = o;
+  o = align256(o + bh * p.splits * (size_t)p.cap * cand_bytes(s.bf16));
+  w.counts = o;
+  o = align256(o + bh * p.splits * 4);
+  w.maxima = o;
+  o = align256(o + bh * p.splits * zb);
+  w.list = o;
+  o = align256(o + bh * (size_t)p.list_cap * (zb + 4));
+  w.total = o;
+  return w;
+}
+
+}  // namespace ekv
+
+namespace {
+
+hipError_t launch_score(const LaunchShape& s, const SplitPlan& p, const float* q,
+                        const void* k_pool, const int32_t* bt, const int32_t* lens,
+                        const int32_t* sel, int budget, float window, void* ws,
+                        const DecodeWs& L, hipStream_t st) {
+  return s.bf16 ? launch_score_bf16(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st)
+                : launch_score_f32(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+}
+
+hipError_t launch_tau_pv(const LaunchShape& s, const SplitPlan& p, const void* v_pool,
+                         const int32_t* bt, const int32_t* lens, const int32_t* sel, int budget,
+                         float alpha, float window, float* out, float* tau, int32_t* support,
+                         void* ws, const DecodeWs& L, hipStream_t st) {
+  return s.bf16 ? launch_tau_pv_bf16(s, p, v_pool, bt, lens, sel, budget, alpha, window, out,
+                                     tau, support, ws, L, st)
+                : launch_tau_pv_f32(s, p, v_pool, bt, lens, sel, budget, alpha, window, out, tau,
+                                    support, ws, L, st);
+}
+
+int decode_common(const entmaxkv_shape* shape, const float* q, const void* k_pool,
+                  const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
+                  const int32_t* sel, int32_t budget, float alpha, float* out, float* tau,
+                  int32_t* support, void* ws, size_t ws_bytes, hipStream_t stream,
+                  hipEvent_t* events) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  const bool sparse = sel != nullptr;
+  if (sparse && (rc = check_budget(budget))) return rc;
+  if ((rc = check_alpha(alpha))) return rc;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return ENTMAXKV_ERR_INVALID;
+  const SplitPlan p = sparse ? plan_sparse(s, budget) : plan_full(s);
+  if ((rc = score_lds_ok(s, p, sparse, budget))) return rc;
+  const DecodeWs L = decode_ws_layout(s, p);
+  if (!ws || ws_bytes < L.total) return ENTMAXKV_ERR_WORKSPACE;
+  const float window = window_of(alpha);
+  const Events ev{events, stream};
+  if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
+  if (launch_score(s, p, q, k_pool, block_table, seq_lens, sel, budget, window, ws, L, stream) !=
+      hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
+  if (launch_tau_pv(s, p, v_pool, block_table, seq_lens, sel, budget, alpha, window, out, tau,
+                    support, ws, L, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
+  return ENTMAXKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int entmaxkv_version(void) { return 100; }
+
+const char* entmaxkv_strerror(int code) {
+  switch (code) {
+    case ENTMAXKV_OK: return "ok";
+    case ENTMAXKV_ERR_INVALID: return "invalid argument";
+    case ENTMAXKV_ERR_UNSUPPORTED: return "unsupported shape, dtype or size";
+    case ENTMAXKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case ENTMAXKV_ERR_HIP: return "HIP launch or event error";
+    default: return "unknown error code";
+  }
+}
+
+int entmaxkv_workspace_bytes(const entmaxkv_shape* shape, int32_t budget_pages, int32_t which,
+                             size_t* bytes) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  if (!bytes) return ENTMAXKV_ERR_INVALID;
+  switch (which) {
+    case ENTMAXKV_WS_SELECT:
+      if ((rc = check_budget(budget_pages))) return rc;
+      *bytes = align256(select_ws_bytes(s));
+      return ENTMAXKV_OK;
+    case ENTMAXKV_WS_SPARSE: {
+      if ((rc = check_budget(budget_pages))) return rc;
+      const SplitPlan p = plan_sparse(s, budget_pages);
+      if ((rc = score_lds_ok(s, p, true, budget_pages))) return rc;
+      *bytes = decode_ws_layout(s, p).total;
+      return ENTMAXKV_OK;
+    }
+    case ENTMAXKV_WS_FULL: {
+      const SplitPlan p = plan_full(s);
+      if ((rc = score_lds_ok(s, p, false, 0))) return rc;
+      *bytes = decode_ws_layout(s, p).total;
+      return ENTMAXKV_OK;
+    }
+    default:
+      return ENTMAXKV_ERR_INVALID;
+  }
+}
+
+int entmaxkv_build_page_meta(const entmaxkv_shape* shape, const void* k_pool,
+                             const int32_t* block_table, const int32_t* seq_lens, void* meta,
+                             hipStream_t stream, hipEvent_t* events) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  if (!k_pool || !block_table || !seq_lens || !meta) return ENTMAXKV_ERR_INVALID;
+  const Events ev{events, stream};
+  if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
+  if (launch_meta(s, k_pool, block_table, seq_lens, meta, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(0)) return ENTMAXKV_ERR_HIP;
+  return ENTMAXKV_OK;
+}
+
+int entmaxkv_score_select(const entmaxkv_shape* shape, const float* q, const void* meta,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t budget_pages, int32_t* sel, float* sel_ub, void* ws,
+                          size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  if ((rc = check_budget(budget_pages))) return rc;
+  if (!q || !meta || !block_table || !seq_lens || !sel) return ENTMAXKV_ERR_INVALID;
+  if (!ws || ws_bytes < select_ws_bytes(s)) return ENTMAXKV_ERR_WORKSPACE;
+  float* ub = static_cast<float*>(ws);
+  const Events ev{events, stream};
+  if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
+  if (launch_bounds(s, q, meta, block_table, seq_lens, ub, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
+  if (launch_select(s, ub, seq_lens, budget_pages, sel, sel_ub, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
+  return ENTMAXKV_OK;
+}
+
+int entmaxkv_decode_sparse(const entmaxkv_shape* shape, const float* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, const int32_t* sel, int32_t budget_pages,
+                           float alpha, float* out, float* tau, int32_t* support, void* ws,
+                           size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+  if (!sel) return ENTMAXKV_ERR_INVALID;
+  return decode_common(shape, q, k_pool, v_pool, block_table, seq_lens, sel, budget_pages, alpha,
+                       out, tau, support, ws, ws_bytes, stream, events);
+}
+
+int entmaxkv_decode_full(const entmaxkv_shape* shape, const float* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_table,
+                         const int32_t* seq_lens, float alpha, float* out, float* tau,
+                         int32_t* support, void* ws, size_t ws_bytes, hipStream_t stream,
+                         hipEvent_t* events) {
+  return decode_common(shape, q, k_pool, v_pool, block_table, seq_lens, nullptr, 0, alpha, out,
+                       tau, support, ws, ws_bytes, stream, events);
+}
+
+}  // extern "C"

@@ -1,0 +1,741 @@
+// Gather-score and threshold/P.V kernels of the alpha-entmax decode.
+// EntmaxKV summary page (gist.science paper 2605.21649), section 2.C: read
+// only the selected pages' K/V and solve alpha-entmax on that reduced set;
+// section 4 (efficiency): the full-cache entmax decode is the same with
+// every page. alpha-entmax: p_i = [(alpha-1) z_i - tau]_+^(1/(alpha-1)),
+// sum p = 1 (Peters, Niculae & Martins 2019).
+//
+// score_kernel (one workgroup per (page split, sequence, KV head)):
+//   Streams the split's K pages once for the G query heads of the KV head.
+//   A token row is spread over LT lanes, each holding two 16-byte chunks; the
+//   G partial dot products finish in a multi-value butterfly. Only tokens that
+//   can be in the support are kept: every token with p > 0 has
+//   z > max(z) - 1/(alpha-1) (at tau = (alpha-1) max z - 1 the top token alone
+//   has weight 1), and a running maximum can only underestimate max(z), so
+//   filtering against it keeps a superset. Survivors go to per-wave LDS lists,
+//   are filtered again against the workgroup maximum and written, in a fixed
+//   order, as this split's candidate region (z, token index) with its count
+//   and maximum. Sparse: the split is a slice of the union of the G heads'
+//   selected pages (each page read once), built from a bitmap in LDS.
+// tau_pv_kernel (one workgroup per (sequence, query head)):
+//   Takes the global maximum over the regions, gathers the candidates inside
+//   the window into a list, solves tau by a safeguarded Newton iteration on
+//   f(tau) = sum [a_i - tau]_+^m (bracketed by [a_max - 1, a_max], bisection
+//   when a Newton step leaves the bracket), then reads V rows only for the
+//   tokens with p > 0 and writes o = sum p v / sum p.
+#pragma once
+
+#include <float.h>
+
+#include "launch.hpp"
+
+namespace ekv {
+
+template <typename KV>
+struct KvTraits;
+template <>
+struct KvTraits<bf16_t> {
+  using Acc = float;
+  static constexpr int VPC = 8;
+};
+template <>
+struct KvTraits<float> {
+  using Acc = double;
+  static constexpr int VPC = 4;
+};
+
+template <typename KV>
+__device__ __forceinline__ void widen(const uint4& x, typename KvTraits<KV>::Acc (&f)[KvTraits<KV>::VPC]) {
+  if constexpr (sizeof(KV) == 2) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    f[0] = (double)__uint_as_float(x.x);
+    f[1] = (double)__uint_as_float(x.y);
+    f[2] = (double)__uint_as_float(x.z);
+    f[3] = (double)__uint_as_float(x.w);
+  }
+}
+
+// One candidate: a score in the accumulation precision and its token index
+// in the head's gathered list (slot * page_size + row).
+template <typename ZT>
+struct alignas(2 * sizeof(ZT)) Cand {
+  ZT z;
+  int idx;
+};
+
+template <typename T>
+__device__ __forceinline__ T neg_inf() {
+  return -__builtin_huge_val();
+}
+template <>
+__device__ __forceinline__ float neg_inf<float>() {
+  return -__builtin_inff();
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// First index in row[0..n) whose value (negatives read as +inf) is >= key; -1 if
+// row has no entry equal to key.
+__device__ __forceinline__ int find_slot(const int32_t* row, int n, int key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int v = row[mid];
+    const uint32_t kv = v < 0 ? 0xffffffffu : (uint32_t)v;
+    if (kv < (uint32_t)key) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo < n && row[lo] == key) ? lo : -1;
+}
+
+template <typename KV, int D, int G, int PS, bool SPARSE>
+__global__ void __launch_bounds__(kNT)
+score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
+             const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+             const int32_t* __restrict__ sel, int H, int Hkv, int U, int max_pages, int num_phys,
+             int budget, int pps, int splits, int cap, double window_d,
+             Cand<typename KvTraits<KV>::Acc>* __restrict__ cand, int* __restrict__ counts,
+             typename KvTraits<KV>::Acc* __restrict__ maxima) {
+  using Tr = KvTraits<KV>;
+  using Acc = typename Tr::Acc;  // also the score type
+  const Acc window = (Acc)window_d;
+  constexpr int VPC = Tr::VPC;
+  constexpr int LT = D / (2 * VPC);  // lanes per token row
+  constexpr int RW = kWave / LT;     // rows per wave step
+  static_assert(PS % RW == 0, "page must hold whole wave steps");
+  constexpr int STEPS = PS / RW;
+  using BF = Butterfly<G, LT>;
+  constexpr int CNT = BF::CNT;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc));
+  Acc* rz = reinterpret_cast<Acc*>(smem + lay.rz);
+  int* ri = reinterpret_cast<int*>(smem + lay.ri);
+  Acc* wmax = reinterpret_cast<Acc*>(smem + lay.wmax);
+  int* wcnt = reinterpret_cast<int*>(smem + lay.wcnt);
+  int* slice = reinterpret_cast<int*>(smem + lay.slice);
+  int* slots = reinterpret_cast<int*>(smem + lay.slots);
+  int* tmp = reinterpret_cast<int*>(smem + lay.tmp);
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int u = blockIdx.x % U;
+  const int split = blockIdx.x / U;
+  const int b = u / Hkv, g = u % Hkv;
+  const int L = clamp_len(seq_lens[b], max_pages * PS);
+  const int P = (L + PS - 1) / PS;
+  const int bh0 = b * H + g * G;
+
+  int n_slice;
+  if constexpr (SPARSE) {
+    unsigned* bm = reinterpret_cast<unsigned*>(smem + lay.bitmap);
+    const int32_t* selrow = sel + (size_t)bh0 * budget;
+    const bool staged = (size_t)G * budget <= (size_t)kSelCopy;
+    int32_t* ssel = reinterpret_cast<int32_t*>(smem + lay.ssel);
+    const int nwords = (P + 31) >> 5;
+    for (int i = tid; i < nwords; i += kNT) bm[i] = 0u;
+    if (staged)
+      for (int i = tid; i < G * budget; i += kNT) ssel[i] = selrow[i];
+    __syncthreads();
+    const int32_t* srow = staged ? ssel : selrow;
+    for (int i = tid; i < G * budget; i += kNT) {
+      const int jj = srow[i];
+      if (jj >= 0 && jj < P) atomicOr(&bm[jj >> 5], 1u << (jj & 31));
+    }
+    __syncthreads();
+    const int wpt = (nwords + kNT - 1) / kNT;
+    const int w0 = min(nwords, tid * wpt), w1 = min(nwords, w0 + wpt);
+    int local = 0;
+    for (int w = w0; w < w1; ++w) local += __popc(bm[w]);
+    int utot;
+    const int rbase = block_excl_scan<kNT>(local, tmp, &utot);
+    const int lo = split * pps;
+    const int hi = min(utot, lo + pps);
+    n_slice = max(0, hi - lo);
+    if (n_slice > 0) {
+      int r = rbase;
+      for (int w = w0; w < w1 && r < hi; ++w) {
+        unsigned bits = bm[w];
+        while (bits) {
+          const int bit = __ffs(bits) - 1;
+          bits &= bits - 1u;
+          if (r >= lo && r < hi) slice[r - lo] = w * 32 + bit;
+          ++r;
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < n_slice * G; i += kNT) {
+      const int p = i / G, h = i % G;
+      slots[i] = find_slot(srow + (size_t)h * budget, budget, slice[p]);
+    }
+    __syncthreads();
+  } else {
+    const int lo = split * pps;
+    n_slice = max(0, min(P, lo + pps) - lo);
+  }
+
+  if (n_slice == 0) {
+    if (tid < G) {
+      const size_t r = (size_t)(bh0 + tid) * splits + split;
+      counts[r] = 0;
+      maxima[r] = neg_inf<Acc>();
+    }
+    return;
+  }
+
+  const int c = lane % LT;
+  const int rsub = lane / LT;
+  Acc qv[G][2 * VPC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float* qh = q + (size_t)(bh0 + h) * D;
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) {
+      qv[h][e] = (Acc)qh[c * VPC + e];
+      qv[h][VPC + e] = (Acc)qh[D / 2 + c * VPC + e];
+    }
+  }
+  const int first = BF::first_index(lane);
+  const bool owner = BF::owner(lane);
+  uint64_t mymask[CNT];
+#pragma unroll
+  for (int i = 0; i < CNT; ++i) {
+    mymask[i] = 0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint64_t m = __ballot(owner && (first + i) == h);
+      if (first + i == h) mymask[i] = m;
+    }
+  }
+  const uint64_t ltm = lanemask_lt(lane);
+
+  Acc M[CNT];
+  int mycnt[CNT];
+#pragma unroll
+  for (int i = 0; i < CNT; ++i) {
+    M[i] = neg_inf<Acc>();
+    mycnt[i] = 0;
+  }
+
+  for (int p = wave; p < n_slice; p += kNW) {
+    const int j = SPARSE ? slice[p] : split * pps + p;
+    const int phys = block_table[(size_t)b * max_pages + j];
+    if (phys < 0 || phys >= num_phys) continue;
+    const int nvalid = min(PS, L - j * PS);
+    int myslot[CNT];
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      if constexpr (SPARSE) {
+        int v = -1;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          if (first + i == h) v = slots[p * G + h];
+        myslot[i] = v;
+      } else {
+        myslot[i] = j;
+      }
+    }
+    const KV* base = k_pool + ((size_t)phys * Hkv + g) * (size_t)PS * D;
+    uint4 xa[STEPS], xb[STEPS];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const KV* rp = base + (size_t)(s * RW + rsub) * D;
+      xa[s] = stream_load16(rp + c * VPC);
+      xb[s] = stream_load16(rp + D / 2 + c * VPC);
+    }
+    Acc zz[STEPS][CNT];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      Acc fa[VPC], fb[VPC];
+      widen<KV>(xa[s], fa);
+      widen<KV>(xb[s], fb);
+      Acc acc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        Acc a0 = 0, a1 = 0;
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) {
+          a0 = fma(qv[h][e], fa[e], a0);
+          a1 = fma(qv[h][VPC + e], fb[e], a1);
+        }
+        acc[h] = a0 + a1;
+      }
+      BF::reduce(acc, lane);
+#pragma unroll
+      for (int i = 0; i < CNT; ++i) zz[s][i] = acc[i];
+    }
+    // mask invalid rows and heads that did not select this page
+    Acc pm[CNT];
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      pm[i] = neg_inf<Acc>();
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        const bool ok = owner && (s * RW + rsub) < nvalid && myslot[i] >= 0;
+        if (!ok) zz[s][i] = neg_inf<Acc>();
+        pm[i] = max(pm[i], zz[s][i]);
+      }
+#pragma unroll
+      for (int w = LT; w < kWave; w <<= 1) pm[i] = max(pm[i], shfl_xor(pm[i], w));
+#pragma unroll
+      for (int w = 1; w < BF::DUP; w <<= 1) pm[i] = max(pm[i], shfl_xor(pm[i], w));
+      M[i] = max(M[i], pm[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const Acc thr = M[i] - window;
+      const int reg = (wave * G + first + i) * lay.wcap;
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        const Acc z = zz[s][i];
+        const bool f = z > neg_inf<Acc>() && z >= thr;
+        const uint64_t bal = __ballot(f);
+        if (f) {
+          const int pos = mycnt[i] + __popcll(bal & mymask[i] & ltm);
+          rz[reg + pos] = z;
+          ri[reg + pos] = myslot[i] * PS + s * RW + rsub;
+        }
+        mycnt[i] += __popcll(bal & mymask[i]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < CNT; ++i) {
+    if (owner && rsub == 0) {
+      wmax[wave * G + first + i] = M[i];
+      wcnt[wave * G + first + i] = mycnt[i];
+    }
+  }
+  __syncthreads();
+
+  for (int h = wave; h < G; h += kNW) {
+    Acc mg = neg_inf<Acc>();
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) mg = max(mg, wmax[w * G + h]);
+    const Acc thr = mg - window;
+    const size_t r = (size_t)(bh0 + h) * splits + split;
+    Cand<Acc>* dst = cand + r * (size_t)cap;
+    int o = 0;
+    for (int w = 0; w < kNW; ++w) {
+      const int n = wcnt[w * G + h];
+      const int reg = (w * G + h) * lay.wcap;
+      for (int e0 = 0; e0 < n; e0 += kWave) {
+        const int e = e0 + lane;
+        Acc z = neg_inf<Acc>();
+        int ix = 0;
+        if (e < n) {
+          z = rz[reg + e];
+          ix = ri[reg + e];
+        }
+        const bool f = e < n && z >= thr;
+        const uint64_t bal = __ballot(f);
+        if (f) {
+          Cand<Acc> cv;
+          cv.z = z;
+          cv.idx = ix;
+          dst[o + __popcll(bal & ltm)] = cv;
+        }
+        o += __popcll(bal);
+      }
+    }
+    if (lane == 0) {
+      counts[r] = o;
+      maxima[r] = mg;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// threshold and P.V
+
+// d^(m-1) for the common exponents, exp2/log2 otherwise (d > 0).
+__device__ __forceinline__ double pow_m1(double d, double m, int mcode) {
+  switch (mcode) {
+    case 1: return 1.0;
+    case 2: return d;
+    case 3: return d * d;
+    case 4: return d * d * d;
+    default: return exp2((m - 1.0) * log2(d));
+  }
+}
+
+template <int SNT>
+__device__ __forceinline__ void scope_sum2(double& a, double& c, double* red) {
+  a = wave_sum(a);
+  c = wave_sum(c);
+  if constexpr (SNT > kWave) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    if (lane == 0) {
+      red[2 * wid] = a;
+      red[2 * wid + 1] = c;
+    }
+    __syncthreads();
+    a = 0.0;
+    c = 0.0;
+#pragma unroll
+    for (int w = 0; w < SNT / kWave; ++w) {
+      a += red[2 * w];
+      c += red[2 * w + 1];
+    }
+    __syncthreads();
+  }
+}
+
+// Safeguarded Newton for sum_i [a_i - t]_+^m = 1 with a_i = am1 * z_i. The
+// root lies in [a_max - 1, a_max): f(a_max - 1) >= 1 (top term is 1) and
+// f(a_max) = 0. Called by the SNT threads t0 = 0..SNT-1 of the scope.
+template <int SNT, typename ZT>
+__device__ double solve_tau(const ZT* z, int n, double am1, double m, int mcode, double amax,
+                            int t0, double* red) {
+  double lo = amax - 1.0, hi = amax, t = lo;
+  for (int it = 0; it < 200; ++it) {
+    double f = 0.0, fp = 0.0;
+    for (int i = t0; i < n; i += SNT) {
+      const double d = am1 * (double)z[i] - t;
+      if (d > 0.0) {
+        const double pm1 = pow_m1(d, m, mcode);
+        fp += pm1;
+        f += pm1 * d;
+      }
+    }
+    scope_sum2<SNT>(f, fp, red);
+    fp *= m;
+    if (f >= 1.0) lo = t;
+    else hi = t;
+    if (f == 1.0) break;
+    const double scale = fmax(1.0, fabs(t));
+    double tn = fp > 0.0 ? t + (f - 1.0) / fp : 0.5 * (lo + hi);
+    if (fp > 0.0 && fabs(tn - t) <= 2.0 * DBL_EPSILON * scale) {
+      t = fmin(fmax(tn, lo), hi);
+      break;
+    }
+    if (!(tn > lo && tn < hi)) tn = 0.5 * (lo + hi);
+    if (hi - lo <= 4.0 * DBL_EPSILON * scale) {
+      t = 0.5 * (lo + hi);
+      break;
+    }
+    t = tn;
+  }
+  return t;
+}
+
+__device__ __forceinline__ double pow_m(double d, double m, int mcode) {
+  return d * pow_m1(d, m, mcode);
+}
+
+template <typename KV, int D, bool SPARSE>
+__global__ void __launch_bounds__(kNT)
+tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_table,
+              const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel, int H,
+              int Hkv, int G, int U, int PS, int max_pages, int num_phys, int budget, int splits,
+              int cap, int list_cap, float alpha, double window_d,
+              const Cand<typename KvTraits<KV>::Acc>* __restrict__ cand,
+              const int* __restrict__ counts, const typename KvTraits<KV>::Acc* __restrict__ maxima,
+              typename KvTraits<KV>::Acc* __restrict__ list_z, int* __restrict__ list_i,
+              float* __restrict__ out, float* __restrict__ tau_out, int32_t* __restrict__ sup_out) {
+  using ZT = typename KvTraits<KV>::Acc;
+  const ZT window = (ZT)window_d;
+  constexpr int VPC = 16 / sizeof(KV);
+  constexpr int LR = D / VPC;     // lanes per V row
+  constexpr int NG = kNT / LR;    // rows in flight per pass
+  __shared__ int roff[kMaxSplits];   // region offsets, later support token indices
+  __shared__ ZT lz[kListCap];
+  __shared__ int li[kListCap];
+  __shared__ float sp[kSupCap];
+  __shared__ float pvacc[NG][D];
+  __shared__ double red[2 * kNW];
+  __shared__ ZT fred[kNW];
+  __shared__ int tmp[kNW + 2];
+  __shared__ double tau_b;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int u = blockIdx.x % U, hh = blockIdx.x / U;
+  const int b = u / Hkv, g = u % Hkv;
+  const int h = g * G + hh;
+  const int bh = b * H + h;
+  const ZT* mx = maxima + (size_t)bh * splits;
+  const int* cn = counts + (size_t)bh * splits;
+
+  ZT M = neg_inf<ZT>();
+  for (int r = tid; r < splits; r += kNT) M = max(M, mx[r]);
+  M = block_reduce<kNT>(M, fred, [](ZT a, ZT c) { return max(a, c); });
+  if (M == neg_inf<ZT>()) {
+    for (int d = tid; d < D; d += kNT) out[(size_t)bh * D + d] = 0.0f;
+    if (tid == 0) {
+      if (tau_out) tau_out[bh] = __builtin_nanf("");
+      if (sup_out) sup_out[bh] = 0;
+    }
+    return;
+  }
+  const ZT thr = M - window;
+
+  // count window members per region (one wave per region, coalesced)
+  for (int r = wave; r < splits; r += kNW) {
+    const int n = cn[r];
+    const Cand<ZT>* src = cand + ((size_t)bh * splits + r) * cap;
+    int cnt = 0;
+    for (int e = lane; e < n; e += kWave) cnt += src[e].z >= thr;
+    cnt = wave_sum(cnt);
+    if (lane == 0) roff[r] = cnt;
+  }
+  __syncthreads();
+  int n_list;
+  {
+    const int cpt = (splits + kNT - 1) / kNT;
+    const int r0 = min(splits, tid * cpt), r1 = min(splits, r0 + cpt);
+    int s = 0;
+    for (int r = r0; r < r1; ++r) s += roff[r];
+    int base = block_excl_scan<kNT>(s, tmp, &n_list);
+    for (int r = r0; r < r1; ++r) {
+      const int v = roff[r];
+      roff[r] = base;
+      base += v;
+    }
+  }
+  __syncthreads();
+  const bool in_lds = n_list <= kListCap;
+  ZT* dz = in_lds ? lz : list_z + (size_t)bh * list_cap;
+  int* di = in_lds ? li : list_i + (size_t)bh * list_cap;
+  const uint64_t ltm = lanemask_lt(lane);
+  for (int r = wave; r < splits; r += kNW) {
+    const int n = cn[r];
+    const Cand<ZT>* src = cand + ((size_t)bh * splits + r) * cap;
+    int o = roff[r];
+    for (int e0 = 0; e0 < n; e0 += kWave) {
+      const int e = e0 + lane;
+      Cand<ZT> v;
+      v.z = neg_inf<ZT>();
+      v.idx = 0;
+      if (e < n) v = src[e];
+      const bool f = e < n && v.z >= thr;
+      const uint64_t bal = __ballot(f);
+      if (f) {
+        const int pos = o + __popcll(bal & ltm);
+        dz[pos] = v.z;
+        di[pos] = v.idx;
+      }
+      o += __popcll(bal);
+    }
+  }
+  __syncthreads();
+
+  const double am1 = (double)alpha - 1.0;
+  const double m = 1.0 / am1;
+  const int mcode = (m == 1.0) ? 1 : (m == 2.0) ? 2 : (m == 3.0) ? 3 : (m == 4.0) ? 4 : 0;
+  const double amax = am1 * (double)M;
+  if (n_list <= kWave * 4) {
+    if (wave == 0) {
+      const double t = solve_tau<kWave>(dz, n_list, am1, m, mcode, amax, lane, red);
+      if (lane == 0) tau_b = t;
+    }
+    __syncthreads();
+  } else {
+    const double t = solve_tau<kNT>(dz, n_list, am1, m, mcode, amax, tid, red);
+    if (tid == 0) tau_b = t;
+    __syncthreads();
+  }
+  const double tau = tau_b;
+
+  // support: tokens with a_i > tau, compacted in list order
+  const int cpt = (n_list + kNT - 1) / kNT;
+  const int i0 = min(n_list, tid * cpt), i1 = min(n_list, i0 + cpt);
+  int ns = 0;
+  double psum = 0.0;
+  for (int i = i0; i < i1; ++i) {
+    const double d = am1 * (double)dz[i] - tau;
+    if (d > 0.0) {
+      ++ns;
+      psum += pow_m(d, m, mcode);
+    }
+  }
+  int n_sup;
+  int sbase = block_excl_scan<kNT>(ns, tmp, &n_sup);
+  {
+    double dummy = 0.0;
+    scope_sum2<kNT>(psum, dummy, red);
+  }
+  const bool sup_lds = n_sup <= kSupCap;
+  if (sup_lds) {
+    for (int i = i0; i < i1; ++i) {
+      const double d = am1 * (double)dz[i] - tau;
+      if (d > 0.0) {
+        roff[sbase] = di[i];
+        sp[sbase] = (float)pow_m(d, m, mcode);
+        ++sbase;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int grp = tid / LR, c = tid % LR;
+  const int32_t* selrow = SPARSE ? sel + (size_t)bh * budget : nullptr;
+  auto row_ptr = [&](int idx) -> const KV* {
+    const int slot = idx / PS, r = idx - slot * PS;
+    const int j = SPARSE ? selrow[slot] : slot;
+    const int phys = block_table[(size_t)b * max_pages + j];
+    if (phys < 0 || phys >= num_phys) return nullptr;
+    return v_pool + (((size_t)phys * Hkv + g) * PS + r) * D + c * VPC;
+  };
+  float acc[VPC];
+#pragma unroll
+  for (int e = 0; e < VPC; ++e) acc[e] = 0.0f;
+  auto accumulate = [&](const KV* vp, float pk) {
+    if (!vp) return;
+    const uint4 x = *reinterpret_cast<const uint4*>(vp);
+    typename KvTraits<KV>::Acc f[VPC];
+    widen<KV>(x, f);
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) acc[e] = fmaf(pk, (float)f[e], acc[e]);
+  };
+  if (sup_lds) {
+    int k = grp;
+    for (; k + 3 * NG < n_sup; k += 4 * NG) {
+      const KV* p0 = row_ptr(roff[k]);
+      const KV* p1 = row_ptr(roff[k + NG]);
+      const KV* p2 = row_ptr(roff[k + 2 * NG]);
+      const KV* p3 = row_ptr(roff[k + 3 * NG]);
+      accumulate(p0, sp[k]);
+      accumulate(p1, sp[k + NG]);
+      accumulate(p2, sp[k + 2 * NG]);
+      accumulate(p3, sp[k + 3 * NG]);
+    }
+    for (; k < n_sup; k += NG) accumulate(row_ptr(roff[k]), sp[k]);
+  } else {
+    for (int i = grp; i < n_list; i += NG) {
+      const double d = am1 * (double)dz[i] - tau;
+      if (d > 0.0) accumulate(row_ptr(di[i]), (float)pow_m(d, m, mcode));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VPC; ++e) pvacc[grp][c * VPC + e] = acc[e];
+  __syncthreads();
+  const double inv = psum > 0.0 ? 1.0 / psum : 0.0;
+  for (int d = tid; d < D; d += kNT) {
+    float s = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) s += pvacc[gg][d];
+    out[(size_t)bh * D + d] = (float)((double)s * inv);
+  }
+  if (tid == 0) {
+    if (tau_out) tau_out[bh] = (float)tau;
+    if (sup_out) sup_out[bh] = n_sup;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers (instantiated per cache dtype in decode_*.hip)
+
+template <typename KV, int D, int G, int PS, bool SPARSE>
+hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float* q,
+                          const void* k_pool, const int32_t* bt, const int32_t* lens,
+                          const int32_t* sel, int budget, float window, void* ws,
+                          const DecodeWs& L, hipStream_t st) {
+  using ZT = typename KvTraits<KV>::Acc;
+  const int U = s.batch * s.num_kv_heads;
+  const ScoreLds lay =
+      score_lds_layout(G, PS, p.pages_per_split, SPARSE, s.max_pages, budget, sizeof(ZT));
+  auto kern = score_kernel<KV, D, G, PS, SPARSE>;
+  if (lay.total > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lay.total);
+    if (e != hipSuccess) return e;
+  }
+  char* w = static_cast<char*>(ws);
+  hipLaunchKernelGGL(kern, dim3(U * p.splits), dim3(kNT), lay.total, st, q,
+                     static_cast<const KV*>(k_pool), bt, lens, sel, s.num_q_heads,
+                     s.num_kv_heads, U, s.max_pages, s.num_phys, budget, p.pages_per_split,
+                     p.splits, p.cap, (double)window, reinterpret_cast<Cand<ZT>*>(w + L.cand),
+                     reinterpret_cast<int*>(w + L.counts), reinterpret_cast<ZT*>(w + L.maxima));
+  return hipGetLastError();
+}
+
+template <typename KV, int D, int G, bool SPARSE>
+hipError_t launch_score_ps(const LaunchShape& s, const SplitPlan& p, const float* q,
+                           const void* k_pool, const int32_t* bt, const int32_t* lens,
+                           const int32_t* sel, int budget, float window, void* ws,
+                           const DecodeWs& L, hipStream_t st) {
+  switch (s.page_size) {
+    case 16: return launch_score_t<KV, D, G, 16, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+    case 32: return launch_score_t<KV, D, G, 32, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+    default: return launch_score_t<KV, D, G, 64, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+  }
+}
+
+template <typename KV, int D, bool SPARSE>
+hipError_t launch_score_g(const LaunchShape& s, const SplitPlan& p, const float* q,
+                          const void* k_pool, const int32_t* bt, const int32_t* lens,
+                          const int32_t* sel, int budget, float window, void* ws,
+                          const DecodeWs& L, hipStream_t st) {
+  switch (s.group) {
+    case 1: return launch_score_ps<KV, D, 1, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+    case 2: return launch_score_ps<KV, D, 2, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+    case 4: return launch_score_ps<KV, D, 4, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+    default: return launch_score_ps<KV, D, 8, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+  }
+}
+
+template <typename KV>
+hipError_t launch_score_kv(const LaunchShape& s, const SplitPlan& p, const float* q,
+                           const void* k_pool, const int32_t* bt, const int32_t* lens,
+                           const int32_t* sel, int budget, float window, void* ws,
+                           const DecodeWs& L, hipStream_t st) {
+  if (sel) {
+    if (s.head_dim == 64) return launch_score_g<KV, 64, true>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+    return launch_score_g<KV, 128, true>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+  }
+  if (s.head_dim == 64) return launch_score_g<KV, 64, false>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+  return launch_score_g<KV, 128, false>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+}
+
+template <typename KV, int D, bool SPARSE>
+hipError_t launch_tau_pv_t(const LaunchShape& s, const SplitPlan& p, const void* v_pool,
+                           const int32_t* bt, const int32_t* lens, const int32_t* sel, int budget,
+                           float alpha, float window, float* out, float* tau, int32_t* support,
+                           void* ws, const DecodeWs& L, hipStream_t st) {
+  using ZT = typename KvTraits<KV>::Acc;
+  const int U = s.batch * s.num_kv_heads;
+  char* w = static_cast<char*>(ws);
+  ZT* list_z = reinterpret_cast<ZT*>(w + L.list);
+  int* list_i = reinterpret_cast<int*>(list_z + (size_t)s.batch * s.num_q_heads * p.list_cap);
+  hipLaunchKernelGGL((tau_pv_kernel<KV, D, SPARSE>), dim3(U * s.group), dim3(kNT), 0, st,
+                     static_cast<const KV*>(v_pool), bt, lens, sel, s.num_q_heads,
+                     s.num_kv_heads, s.group, U, s.page_size, s.max_pages, s.num_phys, budget,
+                     p.splits, p.cap, p.list_cap, alpha, (double)window,
+                     reinterpret_cast<const Cand<ZT>*>(w + L.cand),
+                     reinterpret_cast<const int*>(w + L.counts),
+                     reinterpret_cast<const ZT*>(w + L.maxima), list_z, list_i, out, tau,
+                     support);
+  return hipGetLastError();
+}
+
+template <typename KV>
+hipError_t launch_tau_pv_kv(const LaunchShape& s, const SplitPlan& p, const void* v_pool,
+                            const int32_t* bt, const int32_t* lens, const int32_t* sel,
+                            int budget, float alpha, float window, float* out, float* tau,
+                            int32_t* support, void* ws, const DecodeWs& L, hipStream_t st) {
+  if (sel) {
+    if (s.head_dim == 64) return launch_tau_pv_t<KV, 64, true>(s, p, v_pool, bt, lens, sel, budget, alpha, window, out, tau, support, ws, L, st);
+    return launch_tau_pv_t<KV, 128, true>(s, p, v_pool, bt, lens, sel, budget, alpha, window, out, tau, support, ws, L, st);
+  }
+  if (s.head_dim == 64) return launch_tau_pv_t<KV, 64, false>(s, p, v_pool, bt, lens, sel, budget, alpha, window, out, tau, support, ws, L, st);
+  return launch_tau_pv_t<KV, 128, false>(s, p, v_pool, bt, lens, sel, budget, alpha, window, out, tau, support, ws, L, st);
+}
+
+}  // namespace ekv

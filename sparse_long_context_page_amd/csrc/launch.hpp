@@ -1,0 +1,111 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace ekv {
+
+struct LaunchShape {
+  int batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages, num_phys;
+  int group;  // num_q_heads / num_kv_heads
+  bool bf16;
+};
+
+// Tokens handled by one workgroup of the gather-score kernels.
+constexpr int kSparseTokensPerSplit = 256;
+constexpr int kFullTokensPerSplit = 1024;
+constexpr int kMaxSplits = 4096;  // candidate regions per head (LDS-sized in the threshold kernel)
+
+constexpr int kNT = 256;
+constexpr int kNW = kNT / kWave;
+constexpr int kListCap = 4096;  // threshold list entries held in LDS
+constexpr int kSupCap = 4096;   // support entries held in LDS
+constexpr int kSelCopy = 8192;  // selection ints staged in LDS by the sparse score kernel
+
+
+// LDS layout of the score kernel (bytes), shared by host sizing and device carving.
+struct ScoreLds {
+  int wcap;  // candidate slots per (wave, head)
+  size_t rz, ri, wmax, wcnt, slice, slots, tmp, bitmap, ssel, total;
+};
+
+__host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// zbytes: bytes of one score (4 for bf16 caches, 8 for float32 caches).
+__host__ __device__ inline ScoreLds score_lds_layout(int G, int ps, int pps, bool sparse,
+                                                     int max_pages, int budget, int zbytes) {
+  ScoreLds l;
+  l.wcap = ((pps + kNW - 1) / kNW) * ps;
+  size_t o = 0;
+  const size_t nreg = (size_t)kNW * G * l.wcap;
+  l.rz = o; o = align16(o + nreg * zbytes);
+  l.ri = o; o = align16(o + nreg * 4);
+  l.wmax = o; o = align16(o + (size_t)kNW * G * zbytes);
+  l.wcnt = o; o = align16(o + (size_t)kNW * G * 4);
+  l.slice = o; o = align16(o + (size_t)pps * 4);
+  l.slots = o; o = align16(o + (size_t)pps * G * 4);
+  l.tmp = o; o = align16(o + (kNW + 2) * 4);
+  l.bitmap = o;
+  if (sparse) o = align16(o + (size_t)((max_pages + 31) / 32) * 4);
+  l.ssel = o;
+  if (sparse && (size_t)G * budget <= (size_t)kSelCopy) o = align16(o + (size_t)G * budget * 4);
+  l.total = o;
+  return l;
+}
+
+
+// Partition of one (sequence, KV head) unit's pages into workgroups.
+struct SplitPlan {
+  int pages_per_split;  // pages one workgroup streams
+  int splits;           // workgroups per unit
+  int cap;              // candidate slots per (head, split) = pages_per_split * page_size
+  int list_cap;         // threshold-list slots per head (worst case: every gathered token)
+};
+
+SplitPlan plan_sparse(const LaunchShape& s, int budget);
+SplitPlan plan_full(const LaunchShape& s);
+
+// Workspace carve-up of the decode calls (byte offsets, 256-aligned).
+struct DecodeWs {
+  size_t cand, counts, maxima, list, total;
+};
+// Scores are kept in the accumulation precision: float for bf16 caches,
+// double for float32 caches. A candidate is (score, token index).
+__host__ __device__ inline int score_bytes(bool bf16) { return bf16 ? 4 : 8; }
+__host__ __device__ inline int cand_bytes(bool bf16) { return bf16 ? 8 : 16; }
+DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p);
+size_t select_ws_bytes(const LaunchShape& s);
+
+hipError_t launch_meta(const LaunchShape& s, const void* k_pool, const int32_t* bt,
+                       const int32_t* lens, void* meta, hipStream_t st);
+
+hipError_t launch_bounds(const LaunchShape& s, const float* q, const void* meta,
+                         const int32_t* bt, const int32_t* lens, float* ub, hipStream_t st);
+
+hipError_t launch_select(const LaunchShape& s, const float* ub, const int32_t* lens,
+                         int budget, int32_t* sel, float* sel_ub, hipStream_t st);
+
+// Per-dtype instantiations (decode_bf16.hip, decode_f32.hip).
+hipError_t launch_score_bf16(const LaunchShape& s, const SplitPlan& p, const float* q,
+                             const void* k_pool, const int32_t* bt, const int32_t* lens,
+                             const int32_t* sel, int budget, float window, void* ws,
+                             const DecodeWs& L, hipStream_t st);
+hipError_t launch_score_f32(const LaunchShape& s, const SplitPlan& p, const float* q,
+                            const void* k_pool, const int32_t* bt, const int32_t* lens,
+                            const int32_t* sel, int budget, float window, void* ws,
+                            const DecodeWs& L, hipStream_t st);
+hipError_t launch_tau_pv_bf16(const LaunchShape& s, const SplitPlan& p, const void* v_pool,
+                              const int32_t* bt, const int32_t* lens, const int32_t* sel,
+                              int budget, float alpha, float window, float* out, float* tau,
+                              int32_t* support, void* ws, const DecodeWs& L, hipStream_t st);
+hipError_t launch_tau_pv_f32(const LaunchShape& s, const SplitPlan& p, const void* v_pool,
+                             const int32_t* bt, const int32_t* lens, const int32_t* sel,
+                             int budget, float alpha, float window, float* out, float* tau,
+                             int32_t* support, void* ws, const DecodeWs& L, hipStream_t st);
+
+
+}  // namespace ekv

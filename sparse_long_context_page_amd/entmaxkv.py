@@ -1,0 +1,255 @@
+"""Python binding of libentmaxkv.so (the C ABI in include/entmaxkv.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the decode runs in the library's HIP
+kernels. Importing this module loads the library and raises if it is not
+built (there is no fallback path).
+
+The function names match the C ABI:
+    entmaxkv_build_page_meta, entmaxkv_score_select, entmaxkv_decode_sparse,
+    entmaxkv_decode_full, entmaxkv_workspace_bytes, entmaxkv_strerror
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libentmaxkv.so")
+
+ENTMAXKV_OK = 0
+ENTMAXKV_ERR_INVALID = -1
+ENTMAXKV_ERR_UNSUPPORTED = -2
+ENTMAXKV_ERR_WORKSPACE = -3
+ENTMAXKV_ERR_HIP = -4
+
+ENTMAXKV_F32 = 0
+ENTMAXKV_BF16 = 1
+
+ENTMAXKV_WS_SELECT = 0
+ENTMAXKV_WS_SPARSE = 1
+ENTMAXKV_WS_FULL = 2
+
+# kernels each entry point launches (for per-kernel event timing)
+KERNELS = {"build_page_meta": 1, "score_select": 2, "decode_sparse": 2, "decode_full": 2}
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_phys_pages", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+    ]
+
+
+class EntmaxKVError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {entmaxkv_strerror(code)} (code {code})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m sparse_long_context_page_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    SP = ctypes.POINTER(Shape)
+    lib.entmaxkv_build_page_meta.argtypes = [SP, P, P, P, P, P, P]
+    lib.entmaxkv_score_select.argtypes = [SP, P, P, P, P, I32, P, P, P, SZ, P, P]
+    lib.entmaxkv_decode_sparse.argtypes = [SP, P, P, P, P, P, P, I32, F32, P, P, P, P, SZ, P, P]
+    lib.entmaxkv_decode_full.argtypes = [SP, P, P, P, P, P, F32, P, P, P, P, SZ, P, P]
+    lib.entmaxkv_workspace_bytes.argtypes = [SP, I32, I32, ctypes.POINTER(SZ)]
+    lib.entmaxkv_strerror.argtypes = [ctypes.c_int]
+    lib.entmaxkv_strerror.restype = ctypes.c_char_p
+    lib.entmaxkv_version.argtypes = []
+    for name in ("entmaxkv_build_page_meta", "entmaxkv_score_select", "entmaxkv_decode_sparse",
+                 "entmaxkv_decode_full", "entmaxkv_workspace_bytes", "entmaxkv_version"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def entmaxkv_strerror(code: int) -> str:
+    return lib.entmaxkv_strerror(int(code)).decode()
+
+
+def make_shape(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq,
+               num_phys_pages, kv_dtype) -> Shape:
+    if isinstance(kv_dtype, str):
+        kv_dtype = {"f32": ENTMAXKV_F32, "bf16": ENTMAXKV_BF16}[kv_dtype]
+    return Shape(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
+                 int(max_pages_per_seq), int(num_phys_pages), int(kv_dtype))
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+
+
+def _ptr(t, name, dtypes=None, nullable=False):
+    if t is None:
+        if nullable:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _kv_dtypes(shape: Shape):
+    return (torch.float32,) if shape.kv_dtype == ENTMAXKV_F32 else (torch.bfloat16, torch.int16)
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def _events(events):
+    if events is None:
+        return None
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(int(e)) for e in events])
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def _check(rc: int, where: str):
+    if rc != ENTMAXKV_OK:
+        raise EntmaxKVError(rc, where)
+
+
+def entmaxkv_workspace_bytes(shape: Shape, budget_pages: int, which: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.entmaxkv_workspace_bytes(ctypes.byref(shape), int(budget_pages), int(which),
+                                        ctypes.byref(out)), "entmaxkv_workspace_bytes")
+    return int(out.value)
+
+
+def workspace(shape: Shape, budget_pages: int, which: int, device) -> torch.Tensor:
+    """Allocate a workspace tensor of the size the library asks for."""
+    n = entmaxkv_workspace_bytes(shape, budget_pages, which)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+
+
+def entmaxkv_build_page_meta(shape: Shape, k_pool, block_table, seq_lens, meta, stream=None,
+                             events=None):
+    ev = _events(events)
+    rc = lib.entmaxkv_build_page_meta(
+        ctypes.byref(shape), _ptr(k_pool, "k_pool", _kv_dtypes(shape)),
+        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
+        _ptr(meta, "meta", _kv_dtypes(shape)), _stream(stream, k_pool.device),
+        ev[0] if ev else None)
+    _check(rc, "entmaxkv_build_page_meta")
+
+
+def entmaxkv_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_pages, sel,
+                          sel_ub=None, ws=None, stream=None, events=None):
+    if ws is None:
+        ws = workspace(shape, budget_pages, ENTMAXKV_WS_SELECT, q.device)
+    ev = _events(events)
+    rc = lib.entmaxkv_score_select(
+        ctypes.byref(shape), _ptr(q, "q", (torch.float32,)), _ptr(meta, "meta", _kv_dtypes(shape)),
+        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
+        int(budget_pages), _ptr(sel, "sel", (torch.int32,)),
+        _ptr(sel_ub, "sel_ub", (torch.float32,), nullable=True), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream, q.device), ev[0] if ev else None)
+    _check(rc, "entmaxkv_score_select")
+
+
+def entmaxkv_decode_sparse(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, sel,
+                           budget_pages, alpha, out, tau=None, support=None, ws=None,
+                           stream=None, events=None):
+    if ws is None:
+        ws = workspace(shape, budget_pages, ENTMAXKV_WS_SPARSE, q.device)
+    ev = _events(events)
+    rc = lib.entmaxkv_decode_sparse(
+        ctypes.byref(shape), _ptr(q, "q", (torch.float32,)),
+        _ptr(k_pool, "k_pool", _kv_dtypes(shape)), _ptr(v_pool, "v_pool", _kv_dtypes(shape)),
+        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
+        _ptr(sel, "sel", (torch.int32,)), int(budget_pages), float(alpha),
+        _ptr(out, "out", (torch.float32,)), _ptr(tau, "tau", (torch.float32,), nullable=True),
+        _ptr(support, "support", (torch.int32,), nullable=True), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream, q.device), ev[0] if ev else None)
+    _check(rc, "entmaxkv_decode_sparse")
+
+
+def entmaxkv_decode_full(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, alpha, out,
+                         tau=None, support=None, ws=None, stream=None, events=None):
+    if ws is None:
+        ws = workspace(shape, 0, ENTMAXKV_WS_FULL, q.device)
+    ev = _events(events)
+    rc = lib.entmaxkv_decode_full(
+        ctypes.byref(shape), _ptr(q, "q", (torch.float32,)),
+        _ptr(k_pool, "k_pool", _kv_dtypes(shape)), _ptr(v_pool, "v_pool", _kv_dtypes(shape)),
+        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
+        float(alpha), _ptr(out, "out", (torch.float32,)),
+        _ptr(tau, "tau", (torch.float32,), nullable=True),
+        _ptr(support, "support", (torch.int32,), nullable=True), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream, q.device), ev[0] if ev else None)
+    _check(rc, "entmaxkv_decode_full")
+
+
+# ---------------------------------------------------------------------------
+# HIP events for per-kernel timing (plumbing around hipEvent_t)
+
+
+class HipEvents:
+    """A set of timing-enabled hipEvent_t handles, passed as `events=`."""
+
+    _hip = None
+
+    def __init__(self, n: int):
+        if HipEvents._hip is None:
+            h = ctypes.CDLL("libamdhip64.so")
+            h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvents._hip = h
+        self.handles = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = HipEvents._hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.handles.append(e.value)
+
+    def __len__(self):
+        return len(self.handles)
+
+    def __iter__(self):
+        return iter(self.handles)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        out = ctypes.c_float()
+        HipEvents._hip.hipEventSynchronize(ctypes.c_void_p(self.handles[j]))
+        rc = HipEvents._hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.handles[i]),
+                                                ctypes.c_void_p(self.handles[j]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+    def close(self):
+        for e in self.handles:
+            HipEvents._hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.handles = []

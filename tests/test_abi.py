@@ -1,0 +1,134 @@
+"""The C ABI library on the host: it loads, exports every function the
+header declares, and rejects bad arguments with the documented codes
+before any HIP call (none of these calls reach a kernel)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "entmaxkv.h")
+LIB = os.path.join(ROOT, "sparse_long_context_page_amd", "libentmaxkv.so")
+
+
+@pytest.fixture(scope="module")
+def ek():
+    if not os.path.exists(LIB):
+        from sparse_long_context_page_amd import build
+        build.build(verbose=False)
+    from sparse_long_context_page_amd import entmaxkv
+    return entmaxkv
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(entmaxkv_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(ek):
+    names = declared_functions()
+    assert {"entmaxkv_build_page_meta", "entmaxkv_score_select", "entmaxkv_decode_sparse",
+            "entmaxkv_decode_full", "entmaxkv_workspace_bytes", "entmaxkv_strerror"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (entmaxkv_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(ek.lib, n)
+    # nothing else with C linkage leaks out under our prefix
+    assert exported == set(names)
+
+
+def test_strerror_and_version(ek):
+    for code in (0, -1, -2, -3, -4):
+        assert ek.entmaxkv_strerror(code)
+    assert "unknown" in ek.entmaxkv_strerror(7)
+    assert ek.lib.entmaxkv_version() >= 100
+
+
+def shape(ek, **kw):
+    base = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=32,
+                max_pages_per_seq=4096, num_phys_pages=16384, kv_dtype="bf16")
+    base.update(kw)
+    return ek.make_shape(**base)
+
+
+def ws_rc(ek, s, budget, which):
+    out = ctypes.c_size_t(0)
+    rc = ek.lib.entmaxkv_workspace_bytes(ctypes.byref(s), budget, which, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_workspace_sizes(ek):
+    s = shape(ek)
+    rc, sel_b = ws_rc(ek, s, 82, ek.ENTMAXKV_WS_SELECT)
+    assert rc == 0 and sel_b >= 4 * 32 * 4096 * 4
+    rc, sp = ws_rc(ek, s, 82, ek.ENTMAXKV_WS_SPARSE)
+    assert rc == 0 and sp > 0
+    rc, full = ws_rc(ek, s, 0, ek.ENTMAXKV_WS_FULL)
+    assert rc == 0 and full > sp
+    assert ws_rc(ek, s, 0, ek.ENTMAXKV_WS_SPARSE)[0] == ek.ENTMAXKV_ERR_INVALID
+    assert ws_rc(ek, s, 5, 9)[0] == ek.ENTMAXKV_ERR_INVALID
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), -1), (dict(num_q_heads=6, num_kv_heads=4), -1), (dict(head_dim=96), -2),
+    (dict(page_size=8), -2), (dict(num_q_heads=24, num_kv_heads=2), -2), (dict(kv_dtype=7), -2),
+    (dict(max_pages_per_seq=262145), -2), (dict(num_phys_pages=0), -1),
+])
+def test_shape_validation(ek, kw, code):
+    s = shape(ek, **kw)
+    assert ws_rc(ek, s, 8, ek.ENTMAXKV_WS_FULL)[0] == code
+    dummy = ctypes.c_void_p(256)
+    rc = ek.lib.entmaxkv_build_page_meta(ctypes.byref(s), dummy, dummy, dummy, dummy, None, None)
+    assert rc == code
+
+
+def test_null_shape_and_pointers(ek):
+    d = ctypes.c_void_p(256)
+    assert ek.lib.entmaxkv_build_page_meta(None, d, d, d, d, None, None) == -1
+    s = shape(ek)
+    assert ek.lib.entmaxkv_build_page_meta(ctypes.byref(s), None, d, d, d, None, None) == -1
+    assert ek.lib.entmaxkv_score_select(ctypes.byref(s), d, d, d, d, 8, None, None, d, 1 << 40,
+                                        None, None) == -1
+    assert ek.lib.entmaxkv_decode_full(ctypes.byref(s), d, d, d, d, d, 1.5, None, None, None, d,
+                                       1 << 40, None, None) == -1
+    assert ek.lib.entmaxkv_decode_sparse(ctypes.byref(s), d, d, d, d, d, None, 8, 1.5, d, None,
+                                         None, d, 1 << 40, None, None) == -1
+
+
+def test_budget_alpha_and_workspace_checks(ek):
+    s = shape(ek)
+    d = ctypes.c_void_p(256)
+    assert ek.lib.entmaxkv_score_select(ctypes.byref(s), d, d, d, d, 0, d, None, d, 1 << 40,
+                                        None, None) == -1
+    assert ek.lib.entmaxkv_score_select(ctypes.byref(s), d, d, d, d, 82, d, None, d, 16,
+                                        None, None) == -3
+    assert ek.lib.entmaxkv_score_select(ctypes.byref(s), d, d, d, d, 82, d, None, None, 1 << 40,
+                                        None, None) == -3
+    for alpha in (1.0, 0.5, -2.0, math.nan, math.inf):
+        assert ek.lib.entmaxkv_decode_full(ctypes.byref(s), d, d, d, d, d, alpha, d, None, None,
+                                           d, 1 << 40, None, None) == -1
+        assert ek.lib.entmaxkv_decode_sparse(ctypes.byref(s), d, d, d, d, d, d, 82, alpha, d,
+                                             None, None, d, 1 << 40, None, None) == -1
+    assert ek.lib.entmaxkv_decode_sparse(ctypes.byref(s), d, d, d, d, d, d, -3, 1.5, d, None,
+                                         None, d, 1 << 40, None, None) == -1
+    _, need = ws_rc(ek, s, 82, ek.ENTMAXKV_WS_SPARSE)
+    assert ek.lib.entmaxkv_decode_sparse(ctypes.byref(s), d, d, d, d, d, d, 82, 1.5, d, None,
+                                         None, d, need - 1, None, None) == -3
+    _, need = ws_rc(ek, s, 0, ek.ENTMAXKV_WS_FULL)
+    assert ek.lib.entmaxkv_decode_full(ctypes.byref(s), d, d, d, d, d, 1.5, d, None, None, d,
+                                       need - 1, None, None) == -3
+
+
+def test_binding_rejects_host_tensors(ek):
+    import torch
+    s = shape(ek, batch=1, num_q_heads=1, num_kv_heads=1, max_pages_per_seq=4, num_phys_pages=4)
+    with pytest.raises(ValueError):
+        ek.entmaxkv_build_page_meta(s, torch.zeros(4, 1, 32, 128, dtype=torch.bfloat16),
+                                    torch.zeros(1, 4, dtype=torch.int32),
+                                    torch.zeros(1, dtype=torch.int32),
+                                    torch.zeros(4, 1, 2, 128, dtype=torch.bfloat16))

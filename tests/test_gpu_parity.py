@@ -1,0 +1,223 @@
+"""GPU parity of the HIP path against the fp64 oracle on seeded inputs, at
+sizes the oracle finishes in seconds that still span several workgroup
+splits and ragged tails, plus the method's degenerate cases."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import entmax_oracle as O
+from sparse_long_context_page_amd import synth
+from parity_util import Dev, announce, check_decode, check_meta_sequence, check_selection, \
+    meta_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def full_compare(inp, budget, alpha, heads=None, check_full=True):
+    """Run every entry point and compare every (b, h) (or the listed ones)."""
+    w = inp["workload"]
+    dev = Dev(inp)
+    announce(f"{w.name}: meta/select/sparse/full budget={budget} alpha={alpha}")
+    meta = dev.build_meta()
+    sel, sel_ub = dev.select(budget)
+    out_s, tau_s, sup_s = dev.sparse(sel, budget, alpha)
+    if check_full:
+        out_f, tau_f, sup_f = dev.full(alpha)
+    torch.cuda.synchronize()
+    meta64 = meta_to_f64(meta, w.kv_dtype)
+    sel_np, ub_np = sel.cpu().numpy(), sel_ub.cpu().numpy()
+    o_s, t_s, s_s = out_s.cpu().numpy(), tau_s.cpu().numpy(), sup_s.cpu().numpy()
+    if check_full:
+        o_f, t_f, s_f = out_f.cpu().numpy(), tau_f.cpu().numpy(), sup_f.cpu().numpy()
+    G = w.num_q_heads // w.num_kv_heads
+    heads = heads or [(b, h) for b in range(w.batch) for h in range(w.num_q_heads)]
+    seq_meta = {}
+    near = 0
+    for b, h in heads:
+        g = h // G
+        if (b, g) not in seq_meta:
+            seq_meta[(b, g)] = check_meta_sequence(inp, meta64, b, g)
+        near += check_selection(inp, b, h, budget, sel_np[b, h], ub_np[b, h], seq_meta[(b, g)])
+        ref = O.decode_sparse(inp, b, h, alpha, sel_np[b, h])
+        check_decode(ref, o_s[b, h], t_s[b, h], s_s[b, h], w.kv_dtype, alpha, f"sparse b{b} h{h}")
+        if check_full:
+            ref = O.decode_full(inp, b, h, alpha)
+            check_decode(ref, o_f[b, h], t_f[b, h], s_f[b, h], w.kv_dtype, alpha, f"full b{b} h{h}")
+    return dev, near
+
+
+def test_tiny_f32_whole_workload():
+    w = synth.WORKLOADS["tiny_4k_f32"]
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS["tiny_4k_f32"])
+    full_compare(inp, 32, 1.5)
+
+
+@pytest.mark.parametrize("name,context,batch", [
+    ("gqa_32k", 3000, 2), ("long_128k", 5000, 2), ("alpha_sweep_64k", 4000, 2),
+    ("extreme_512k", 9000, 1)])
+def test_scaled_workloads(name, context, batch):
+    w = synth.shrink(synth.WORKLOADS[name], context=context, batch=batch,
+                     n_planted=min(synth.WORKLOADS[name].n_planted, 32))
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS[name])
+    P = (context + w.page_size - 1) // w.page_size
+    for alpha in w.alphas:
+        for budget in sorted(set(min(bud, P // 3) for bud in w.budgets)):
+            full_compare(inp, max(1, budget), alpha)
+
+
+@pytest.mark.parametrize("kv_dtype,D,ps,H,Hkv", [
+    ("bf16", 64, 16, 8, 1), ("bf16", 128, 64, 4, 2), ("f32", 128, 32, 2, 2), ("f32", 64, 16, 8, 4),
+    ("bf16", 64, 32, 16, 2), ("f32", 128, 64, 8, 1)])
+def test_shapes_and_ragged_lengths(kv_dtype, D, ps, H, Hkv):
+    lens = (1, ps, ps + 1, 7 * ps - 3, 1500)
+    w = synth.Workload("ragged", len(lens), H, Hkv, D, ps, max(lens), kv_dtype, (1.5,), (5,),
+                       4.0 / np.sqrt(D), plant="group_mean", n_planted=4, seq_lens=lens)
+    inp = synth.generate(w, 11)
+    for alpha in (1.25, 2.0, 3.0):
+        full_compare(inp, 5, alpha)
+
+
+def test_empty_and_short_sequences():
+    lens = (0, 3, 0, 40)
+    w = synth.Workload("empty", len(lens), 4, 2, 128, 16, 40, "bf16", (1.5,), (2,), 0.3,
+                       seq_lens=lens)
+    inp = synth.generate(w, 5)
+    dev, _ = full_compare(inp, 2, 1.5)
+    out, tau, sup = dev.full(1.5)
+    torch.cuda.synchronize()
+    assert (sup.cpu()[0] == 0).all() and torch.isnan(tau.cpu()[0]).all()
+    assert (out.cpu()[0] == 0).all()
+
+
+def test_budget_covering_every_page_matches_full():
+    w = synth.shrink(synth.WORKLOADS["long_128k"], context=3000, batch=2, n_planted=16)
+    inp = synth.generate(w, 3)
+    dev = Dev(inp)
+    P = (3000 + 31) // 32
+    announce("budget >= pages: sparse == full")
+    sel, _ = dev.select(P + 5)
+    s = dev.sparse(sel, P + 5, 1.5)
+    f = dev.full(1.5)
+    torch.cuda.synchronize()
+    assert (sel.cpu()[..., :P] == torch.arange(P, dtype=torch.int32)).all()
+    assert (sel.cpu()[..., P:] == -1).all()
+    np.testing.assert_allclose(s[0].cpu().numpy(), f[0].cpu().numpy(), atol=1e-6)
+    np.testing.assert_allclose(s[1].cpu().numpy(), f[1].cpu().numpy(), rtol=1e-6)
+    assert (s[2].cpu() == f[2].cpu()).all()
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+def test_support_recovery_on_gpu(alpha):
+    """A selection that holds the full-cache support gives the full output."""
+    w = synth.shrink(synth.WORKLOADS["gqa_32k"], context=4096, batch=2, n_planted=16)
+    inp = synth.generate(w, 2)
+    dev = Dev(inp)
+    announce(f"support recovery alpha={alpha}")
+    full = dev.full(alpha)
+    torch.cuda.synchronize()
+    P = 4096 // 16
+    budget = 40
+    sel = np.full((w.batch, w.num_q_heads, budget), -1, dtype=np.int32)
+    n_ok = 0
+    for b in range(w.batch):
+        for h in range(w.num_q_heads):
+            ref = O.decode_full(inp, b, h, alpha)
+            need = O.support_pages(ref, w.page_size)
+            if len(need) > budget:
+                continue
+            sel[b, h] = synth.constructed_selection(need, P, budget, seed=b * 100 + h)
+            n_ok += 1
+    assert n_ok >= w.batch * w.num_q_heads // 2
+    sel_t = torch.from_numpy(sel).cuda()
+    sp = dev.sparse(sel_t, budget, alpha)
+    torch.cuda.synchronize()
+    fo, ft, fs = (x.cpu().numpy() for x in full)
+    so, st, ss = (x.cpu().numpy() for x in sp)
+    for b in range(w.batch):
+        for h in range(w.num_q_heads):
+            if sel[b, h, 0] < 0:
+                continue
+            assert ss[b, h] == fs[b, h]
+            assert abs(st[b, h] - ft[b, h]) <= 1e-6 * max(1, abs(ft[b, h]))
+            np.testing.assert_allclose(so[b, h], fo[b, h], atol=1e-6 * np.linalg.norm(fo[b, h]) + 1e-7)
+
+
+def test_uniform_scores_use_global_lists():
+    """All keys equal: every token is in the support, so the candidate list and
+    the support overflow their LDS capacity and take the global-memory path."""
+    L = 16000
+    w = synth.Workload("uniform", 1, 2, 1, 128, 16, L, "bf16", (1.5,), (600,), 0.5,
+                       block_table="permuted")
+    inp = synth.generate(w, 9)
+    inp["k_pool"][:] = synth.f32_to_bf16_bits(np.full(1, 0.25, np.float32))[0]
+    dev = Dev(inp)
+    announce("uniform scores, global list path")
+    for alpha in (1.5, 2.0, 1.25):
+        out, tau, sup = dev.full(alpha)
+        sel, _ = dev.select(600)
+        so, st, ss = dev.sparse(sel, 600, alpha)
+        torch.cuda.synchronize()
+        assert (sup.cpu() == L).all() and (ss.cpu() == 600 * 16).all()
+        for h in range(2):
+            ref = O.decode_full(inp, 0, h, alpha)
+            check_decode(ref, out.cpu().numpy()[0, h], tau.cpu().numpy()[0, h],
+                         sup.cpu().numpy()[0, h], "bf16", alpha, "uniform full")
+            refs = O.decode_sparse(inp, 0, h, alpha, sel.cpu().numpy()[0, h])
+            check_decode(refs, so.cpu().numpy()[0, h], st.cpu().numpy()[0, h],
+                         ss.cpu().numpy()[0, h], "bf16", alpha, "uniform sparse")
+        # ties everywhere: the selection is the lowest page indices
+        assert (sel.cpu()[0, :, :600] == torch.arange(600, dtype=torch.int32)).all()
+
+
+def test_bitwise_determinism():
+    w = synth.shrink(synth.WORKLOADS["long_128k"], context=6000, batch=2, n_planted=16)
+    inp = synth.generate(w, 3)
+    dev = Dev(inp)
+    announce("determinism")
+    runs = []
+    for _ in range(2):
+        dev.build_meta()
+        sel, ub = dev.select(20)
+        s = dev.sparse(sel, 20, 1.5)
+        f = dev.full(1.5)
+        torch.cuda.synchronize()
+        runs.append([x.cpu().clone() for x in (dev.meta.view(torch.int16), sel, ub, *s, *f)])
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b)
+
+
+def test_invalid_selection_entries_are_ignored():
+    w = synth.shrink(synth.WORKLOADS["gqa_32k"], context=1000, batch=1, n_planted=8)
+    inp = synth.generate(w, 2)
+    dev = Dev(inp)
+    P = (1000 + 15) // 16
+    sel = np.full((1, w.num_q_heads, 6), -1, dtype=np.int32)
+    sel[0, :, 0] = 3
+    sel[0, :, 1] = 10
+    sel[0, :, 2] = P + 4  # beyond the sequence: ignored
+    sel[0, :, 3] = 1 << 20  # far beyond: ignored
+    announce("invalid selection entries")
+    out, tau, sup = dev.sparse(torch.from_numpy(sel).cuda(), 6, 1.5)
+    torch.cuda.synchronize()
+    for h in range(w.num_q_heads):
+        ref = O.decode_sparse(inp, 0, h, 1.5, [3, 10])
+        check_decode(ref, out.cpu().numpy()[0, h], tau.cpu().numpy()[0, h],
+                     sup.cpu().numpy()[0, h], "bf16", 1.5, "invalid entries")
+
+
+def test_kernel_events_are_recorded():
+    from sparse_long_context_page_amd import entmaxkv as E
+    w = synth.shrink(synth.WORKLOADS["long_128k"], context=4000, batch=1, n_planted=8)
+    inp = synth.generate(w, 3)
+    dev = Dev(inp)
+    dev.build_meta()
+    ev = E.HipEvents(4)
+    announce("events")
+    out, tau, sup = dev._outs()
+    E.entmaxkv_decode_full(dev.shape, dev.q, dev.k, dev.v, dev.bt, dev.lens, 1.5, out, tau, sup,
+                           events=list(ev))
+    torch.cuda.synchronize()
+    assert ev.elapsed_ms(0, 1) > 0 and ev.elapsed_ms(2, 3) > 0
+    assert ev.elapsed_ms(0, 3) >= ev.elapsed_ms(0, 1)
+    ev.close()

@@ -210,3 +210,21 @@ def test_empty_selection_and_planted_support():
     inp = synth.generate(w, 1)
     full = O.decode_full(inp, 0, 0, 1.5)
     assert set(full.support_pos.tolist()) <= set(inp["planted"][(0, 0)].tolist())
+
+
+def test_sequence_metadata_matches_pool_metadata():
+    inp = small_inputs("bf16", seq_lens=(100, 64, 37), seed=4)
+    w = inp["workload"]
+    kmin, kmax = O.page_metadata(inp["k_pool"], inp["block_table"], inp["seq_lens"], 16, "bf16")
+    for b in range(3):
+        for g in range(2):
+            smin, smax = O.sequence_metadata(inp["k_pool"], inp["block_table"][b],
+                                             inp["seq_lens"][b], 16, g, "bf16")
+            phys = inp["block_table"][b, :smin.shape[0]]
+            np.testing.assert_array_equal(smin, kmin[phys, g])
+            np.testing.assert_array_equal(smax, kmax[phys, g])
+            for h in (2 * g, 2 * g + 1):
+                a = O.select_for_head(inp, b, h, 3)
+                c = O.select_for_head(inp, b, h, 3, meta=(kmin, kmax))
+                np.testing.assert_array_equal(a[0], c[0])
+                assert a[2] == c[2]
