@@ -1,0 +1,392 @@
+"""Decode benchmark on one MI355X: sparse vs full-cache alpha-entmax decode.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_128k]
+
+One step is one pass of the decode hot path over the whole batch (every
+sequence, every query head): page bounds + top-k selection, sparse decode
+over the selected pages, and the full-cache decode on the same inputs. The
+page boxes are built once before timing (they are per-page state, written
+when a page is filled) and timed on their own.
+
+Inputs are generated on the host, uploaded, and resident in HBM before any
+timing. Each timed step is preceded by an untimed 1 GiB write that evicts the
+on-chip caches (L2 + MALL), so the step reads HBM, not a warm cache. HIP
+events bracket every step and every kernel (the library records them on the
+launch stream). Prints one JSON line.
+
+The CPU baseline is the float64 oracle run on this host's cores over a
+bounded sample of (sequence, query head) decodes of the same workload,
+scaled to steps/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import multiprocessing as mp
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from sparse_long_context_page_amd import synth  # noqa: E402
+
+METRIC = ("decode steps/s + achieved HBM GB/s (% of peak), sparse vs full entmax, "
+          "32K–512K")
+PEAK_HBM_GBPS = 8000.0
+KERNEL_NAMES = ["bounds", "select", "score_sparse", "tau_pv_sparse", "score_full", "tau_pv_full"]
+KERNEL_SOURCES = ["common.hpp", "launch.hpp", "select.hip", "decode_impl.hpp", "decode_bf16.hip",
+                  "decode_f32.hip", "meta.hip", "api.hip"]
+
+
+# ---------------------------------------------------------------------------
+# byte accounting (algorithmic bytes: what the method itself must move)
+
+
+def kv_elem_bytes(w) -> int:
+    return 2 if w.kv_dtype == "bf16" else 4
+
+
+def union_pages(sel: np.ndarray, G: int) -> np.ndarray:
+    """Distinct selected pages per (sequence, KV head): [B, H_kv]."""
+    B, H, _ = sel.shape
+    out = np.zeros((B, H // G), dtype=np.int64)
+    for b in range(B):
+        for g in range(H // G):
+            s = sel[b, g * G:(g + 1) * G].ravel()
+            out[b, g] = len(np.unique(s[s >= 0]))
+    return out
+
+
+def algorithmic_bytes(w, lens: np.ndarray, budget: int, sel: np.ndarray, sup_sparse: np.ndarray,
+                      sup_full: np.ndarray) -> dict:
+    """Per-kernel algorithmic bytes of one step. Workspace traffic (bounds,
+    candidate lists) is implementation overhead and is not counted."""
+    s = kv_elem_bytes(w)
+    B, H, Hkv, D, ps = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
+    G = H // Hkv
+    P = (lens + ps - 1) // ps
+    q_b = B * H * D * 4
+    out_b = B * H * D * 4
+    bt_b = int(P.sum()) * 4
+    meta_b = int(P.sum()) * Hkv * 2 * D * s
+    k_full_b = int(lens.sum()) * Hkv * D * s
+    up = union_pages(sel, G)
+    k_sel_b = int(up.sum()) * ps * D * s
+    v_sup_sparse = int(sup_sparse.sum()) * D * s
+    v_sup_full = int(sup_full.sum()) * D * s
+    sel_b = B * H * budget * 4
+    return {
+        "bounds": meta_b + q_b + bt_b,
+        "select": sel_b,
+        "score_sparse": k_sel_b + q_b + sel_b + bt_b,
+        "tau_pv_sparse": v_sup_sparse + out_b,
+        "score_full": k_full_b + q_b + bt_b,
+        "tau_pv_full": v_sup_full + out_b,
+        "_meta_build": int(lens.sum()) * Hkv * D * s + meta_b,
+        "_union_pages": int(up.sum()),
+        "_union_fraction": float(up.sum()) / float(B * H * min(budget, int(P.max()))),
+    }
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_long_context_page_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if there is none or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_hash:\s*(\w+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the host's cores over sampled heads
+
+_ORACLE_STATE = {}
+
+
+def _oracle_head(args):
+    from oracle import entmax_oracle as O
+    b, h, budget, alpha = args
+    inp = _ORACLE_STATE["inp"]
+    w = inp["workload"]
+    g = h // (w.num_q_heads // w.num_kv_heads)
+    seq_meta = _ORACLE_STATE["seq_meta"][(b, g)]
+    t0 = time.perf_counter()
+    _, _, sel = O.select_for_head(inp, b, h, budget, seq_meta=seq_meta)
+    sp = O.decode_sparse(inp, b, h, alpha, sel)
+    fu = O.decode_full(inp, b, h, alpha)
+    dt = time.perf_counter() - t0
+    return b, h, dt, sel, sp.out, fu.out
+
+
+def cpu_baseline(inp, budget, alpha, n_heads: int, seed: int = 0):
+    """Time the oracle's step (bounds+selection, sparse decode, full decode)
+    on a sample of (sequence, head) pairs; page boxes are built before timing,
+    as on the GPU."""
+    from oracle import entmax_oracle as O
+    w = inp["workload"]
+    rng = np.random.default_rng(seed)
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.batch, n_heads),
+                                               rng.integers(0, w.num_q_heads, n_heads))]
+    G = w.num_q_heads // w.num_kv_heads
+    seq_meta = {}
+    for b, h in pairs:
+        g = h // G
+        if (b, g) not in seq_meta:
+            seq_meta[(b, g)] = O.sequence_metadata(inp["k_pool"], inp["block_table"][b],
+                                                   inp["seq_lens"][b], w.page_size, g, w.kv_dtype)
+    _ORACLE_STATE["inp"] = inp
+    _ORACLE_STATE["seq_meta"] = seq_meta
+    cores = len(os.sched_getaffinity(0))
+    workers = min(cores, n_heads)
+    t0 = time.perf_counter()
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_pin_blas) as pool:
+        results = pool.map(_oracle_head, [(b, h, budget, alpha) for b, h in pairs])
+    wall = time.perf_counter() - t0
+    step_s = wall * (w.batch * w.num_q_heads) / n_heads
+    return {
+        "value": 1.0 / step_s,
+        "unit": "steps/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"{n_heads} random (sequence, head) pairs of {w.name}: bounds+top-{budget} "
+                   f"selection, sparse and full fp64 decode each; wall {wall:.2f} s on {workers} "
+                   f"processes, scaled by {w.batch * w.num_q_heads}/{n_heads} heads per step; "
+                   f"page boxes prebuilt"),
+        "_results": results,
+    }
+
+
+def _pin_blas():
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[k] = "1"
+
+
+# ---------------------------------------------------------------------------
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_128k", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--budget", type=int, default=None)
+    ap.add_argument("--oracle-heads", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="hot-cache timing (diagnostic)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(collectives and sharding are out of scope; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    w = synth.WORKLOADS[args.workload]
+    alpha = args.alpha if args.alpha is not None else w.alphas[0]
+    budget = args.budget if args.budget is not None else w.budgets[0]
+    t_gen = time.perf_counter()
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS[w.name])
+    t_gen = time.perf_counter() - t_gen
+    log = lambda m: (sys.stderr.write(f"[bench] {m}\n"), sys.stderr.flush())
+    log(f"generated {w.name} in {t_gen:.1f}s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, budget, alpha, args.oracle_heads)
+        log(f"cpu baseline {cpu['value']:.4g} steps/s on {cpu['cores']} cores")
+
+    import torch
+    from sparse_long_context_page_amd import entmaxkv as E
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kv_t = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+
+    def pool(a):
+        if w.kv_dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q = torch.from_numpy(inp["q"]).to(dev)
+    k = pool(inp["k_pool"])
+    v = pool(inp["v_pool"])
+    bt = torch.from_numpy(inp["block_table"]).to(dev)
+    lens = torch.from_numpy(inp["seq_lens"]).to(dev)
+    shape = E.make_shape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                         inp["max_pages"], inp["num_phys_pages"], w.kv_dtype)
+    meta = torch.empty((inp["num_phys_pages"], w.num_kv_heads, 2, w.head_dim), dtype=kv_t,
+                       device=dev)
+    B, H, D = w.batch, w.num_q_heads, w.head_dim
+    sel = torch.empty((B, H, budget), dtype=torch.int32, device=dev)
+    sel_ub = torch.empty((B, H, budget), dtype=torch.float32, device=dev)
+    out_s = torch.empty((B, H, D), device=dev)
+    out_f = torch.empty((B, H, D), device=dev)
+    tau_s = torch.empty((B, H), device=dev)
+    tau_f = torch.empty((B, H), device=dev)
+    sup_s = torch.empty((B, H), dtype=torch.int32, device=dev)
+    sup_f = torch.empty((B, H), dtype=torch.int32, device=dev)
+    ws_sel = E.workspace(shape, budget, E.ENTMAXKV_WS_SELECT, dev)
+    ws_sp = E.workspace(shape, budget, E.ENTMAXKV_WS_SPARSE, dev)
+    ws_fu = E.workspace(shape, budget, E.ENTMAXKV_WS_FULL, dev)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def flush(i):
+        if not args.no_flush:
+            flush_buf.fill_(i & 0xFF)
+
+    # page boxes (per-page state; timed separately)
+    n_meta = max(3, min(10, args.steps))
+    ev_meta = E.HipEvents(2 * n_meta)
+    E.entmaxkv_build_page_meta(shape, k, bt, lens, meta)
+    for i in range(n_meta):
+        flush(i)
+        E.entmaxkv_build_page_meta(shape, k, bt, lens, meta, events=list(ev_meta)[2 * i:2 * i + 2])
+    torch.cuda.synchronize()
+    meta_ms = float(np.mean([ev_meta.elapsed_ms(2 * i, 2 * i + 1) for i in range(n_meta)]))
+
+    call_sel = E.Prepared("score_select", shape, q, meta, bt, lens, budget, sel, sel_ub, ws=ws_sel,
+                          stream=stream)
+    call_sp = E.Prepared("decode_sparse", shape, q, k, v, bt, lens, sel, budget, alpha, out_s,
+                         tau_s, sup_s, ws=ws_sp, stream=stream)
+    call_fu = E.Prepared("decode_full", shape, q, k, v, bt, lens, alpha, out_f, tau_f, sup_f,
+                         ws=ws_fu, stream=stream)
+
+    def step(kev=None):
+        if kev is None:
+            call_sel()
+            call_sp()
+            call_fu()
+        else:
+            call_sel(kev[0:4])
+            call_sp(kev[4:8])
+            call_fu(kev[8:12])
+
+    for i in range(args.warmup):
+        flush(i)
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev_step = E.HipEvents(2 * K)
+    ev_kern = E.HipEvents(12 * K)
+    hk = list(ev_kern)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        flush(i)
+        ev_step.record(2 * i, stream)
+        step(hk[12 * i:12 * (i + 1)])
+        ev_step.record(2 * i + 1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_ms = np.array([ev_step.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)])
+    kern_ms = np.array([[ev_kern.elapsed_ms(12 * i + 2 * j, 12 * i + 2 * j + 1) for j in range(6)]
+                        for i in range(K)])
+    sparse_ms = np.array([ev_kern.elapsed_ms(12 * i, 12 * i + 7) for i in range(K)])
+    full_ms = np.array([ev_kern.elapsed_ms(12 * i + 8, 12 * i + 11) for i in range(K)])
+    ms_per_step = float(step_ms.mean())
+
+    sel_np = sel.cpu().numpy()
+    nbytes = algorithmic_bytes(w, inp["seq_lens"], budget, sel_np, sup_s.cpu().numpy(),
+                               sup_f.cpu().numpy())
+    kmean = kern_ms.mean(axis=0)
+    kernels = {}
+    for j, name in enumerate(KERNEL_NAMES):
+        gbps = nbytes[name] / (kmean[j] * 1e-3) / 1e9
+        kernels[name] = {"us": round(kmean[j] * 1e3, 2), "bytes": nbytes[name],
+                         "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    sparse_bytes = sum(nbytes[n] for n in KERNEL_NAMES[:4])
+    full_bytes = sum(nbytes[n] for n in KERNEL_NAMES[4:])
+    paths = {}
+    for name, ms, by in (("sparse", sparse_ms, sparse_bytes), ("full", full_ms, full_bytes)):
+        gbps = by / (ms.mean() * 1e-3) / 1e9
+        paths[name] = {"ms": round(float(ms.mean()), 4), "p10_ms": round(float(np.percentile(ms, 10)), 4),
+                       "p90_ms": round(float(np.percentile(ms, 90)), 4),
+                       "steps_per_s": round(1e3 / float(ms.mean()), 1), "bytes": by,
+                       "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    meta_gbps = nbytes["_meta_build"] / (meta_ms * 1e-3) / 1e9
+    paths["page_boxes"] = {"ms": round(meta_ms, 4), "bytes": nbytes["_meta_build"],
+                           "GBps": round(meta_gbps, 1), "frac": round(meta_gbps / PEAK_HBM_GBPS, 4),
+                           "note": "built once per page, outside the step"}
+    dom = int(np.argmax(kmean))
+    dname = KERNEL_NAMES[dom]
+    achieved = nbytes[dname] / (kmean[dom] * 1e-3) / 1e9
+    traffic = counter_traffic(dname, w.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                "kernel": dname, "bytes_per_launch": nbytes[dname],
+                "launch_us": round(kmean[dom] * 1e3, 2)}
+
+    parity = None
+    cpu_line = None
+    if cpu is not None:
+        errs_s, errs_f, sel_same = [], [], 0
+        o_s, o_f = out_s.cpu().numpy(), out_f.cpu().numpy()
+        for b, h, _, ref_sel, rs, rf in cpu["_results"]:
+            sel_same += int(list(sel_np[b, h]) == list(ref_sel))
+            errs_s.append(float(np.abs(o_s[b, h] - rs).max() / max(1e-30, np.linalg.norm(rs))))
+            errs_f.append(float(np.abs(o_f[b, h] - rf).max() / max(1e-30, np.linalg.norm(rf))))
+        parity = {"heads": len(cpu["_results"]), "selection_identical": sel_same,
+                  "max_rel_err_sparse": max(errs_s), "max_rel_err_full": max(errs_f),
+                  "tolerance_rel": 2e-3}
+        cpu_line = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
+
+    record = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_per_step, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": H, "kv_heads": w.num_kv_heads,
+                   "head_dim": D, "context": int(w.context), "page_size": w.page_size,
+                   "budget_pages": budget, "alpha": alpha, "kv_dtype": w.kv_dtype,
+                   "parallelism": "single GPU", "cache_flush": not args.no_flush,
+                   "step": "score_select + decode_sparse + decode_full"},
+        "paths": paths,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu_line,
+        "diagnostics": {"union_fraction": round(nbytes["_union_fraction"], 4),
+                        "mean_support_sparse": float(sup_s.float().mean()),
+                        "mean_support_full": float(sup_f.float().mean()),
+                        "wall_s_timed_region": round(wall, 3),
+                        "kernel_source_hash": kernel_source_hash()},
+        "parity_sample": parity,
+    }
+    print(json.dumps(record))
+
+
+if __name__ == "__main__":
+    main()

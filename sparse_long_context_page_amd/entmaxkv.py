@@ -150,62 +150,120 @@ def workspace(shape: Shape, budget_pages: int, which: int, device) -> torch.Tens
 # entry points
 
 
-def entmaxkv_build_page_meta(shape: Shape, k_pool, block_table, seq_lens, meta, stream=None,
-                             events=None):
-    ev = _events(events)
-    rc = lib.entmaxkv_build_page_meta(
+def _args_build_page_meta(shape: Shape, k_pool, block_table, seq_lens, meta, stream=None):
+    return lib.entmaxkv_build_page_meta, [
         ctypes.byref(shape), _ptr(k_pool, "k_pool", _kv_dtypes(shape)),
         _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
-        _ptr(meta, "meta", _kv_dtypes(shape)), _stream(stream, k_pool.device),
-        ev[0] if ev else None)
-    _check(rc, "entmaxkv_build_page_meta")
+        _ptr(meta, "meta", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
 
 
-def entmaxkv_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_pages, sel,
-                          sel_ub=None, ws=None, stream=None, events=None):
+def _args_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_pages, sel,
+                       sel_ub=None, ws=None, stream=None):
     if ws is None:
         ws = workspace(shape, budget_pages, ENTMAXKV_WS_SELECT, q.device)
-    ev = _events(events)
-    rc = lib.entmaxkv_score_select(
+    return lib.entmaxkv_score_select, [
         ctypes.byref(shape), _ptr(q, "q", (torch.float32,)), _ptr(meta, "meta", _kv_dtypes(shape)),
         _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
         int(budget_pages), _ptr(sel, "sel", (torch.int32,)),
         _ptr(sel_ub, "sel_ub", (torch.float32,), nullable=True), _ptr(ws, "ws"),
-        ws.numel() * ws.element_size(), _stream(stream, q.device), ev[0] if ev else None)
-    _check(rc, "entmaxkv_score_select")
+        ws.numel() * ws.element_size(), _stream(stream, q.device), None], ws
 
 
-def entmaxkv_decode_sparse(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, sel,
-                           budget_pages, alpha, out, tau=None, support=None, ws=None,
-                           stream=None, events=None):
+def _args_decode_sparse(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, sel,
+                        budget_pages, alpha, out, tau=None, support=None, ws=None, stream=None):
     if ws is None:
         ws = workspace(shape, budget_pages, ENTMAXKV_WS_SPARSE, q.device)
-    ev = _events(events)
-    rc = lib.entmaxkv_decode_sparse(
+    return lib.entmaxkv_decode_sparse, [
         ctypes.byref(shape), _ptr(q, "q", (torch.float32,)),
         _ptr(k_pool, "k_pool", _kv_dtypes(shape)), _ptr(v_pool, "v_pool", _kv_dtypes(shape)),
         _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
         _ptr(sel, "sel", (torch.int32,)), int(budget_pages), float(alpha),
         _ptr(out, "out", (torch.float32,)), _ptr(tau, "tau", (torch.float32,), nullable=True),
         _ptr(support, "support", (torch.int32,), nullable=True), _ptr(ws, "ws"),
-        ws.numel() * ws.element_size(), _stream(stream, q.device), ev[0] if ev else None)
-    _check(rc, "entmaxkv_decode_sparse")
+        ws.numel() * ws.element_size(), _stream(stream, q.device), None], ws
 
 
-def entmaxkv_decode_full(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, alpha, out,
-                         tau=None, support=None, ws=None, stream=None, events=None):
+def _args_decode_full(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, alpha, out,
+                      tau=None, support=None, ws=None, stream=None):
     if ws is None:
         ws = workspace(shape, 0, ENTMAXKV_WS_FULL, q.device)
-    ev = _events(events)
-    rc = lib.entmaxkv_decode_full(
+    return lib.entmaxkv_decode_full, [
         ctypes.byref(shape), _ptr(q, "q", (torch.float32,)),
         _ptr(k_pool, "k_pool", _kv_dtypes(shape)), _ptr(v_pool, "v_pool", _kv_dtypes(shape)),
         _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
         float(alpha), _ptr(out, "out", (torch.float32,)),
         _ptr(tau, "tau", (torch.float32,), nullable=True),
         _ptr(support, "support", (torch.int32,), nullable=True), _ptr(ws, "ws"),
-        ws.numel() * ws.element_size(), _stream(stream, q.device), ev[0] if ev else None)
-    _check(rc, "entmaxkv_decode_full")
+        ws.numel() * ws.element_size(), _stream(stream, q.device), None], ws
+
+
+def _run(name, fn, args, events):
+    if events is not None:
+        ev = _events(events)
+        args = list(args)
+        args[-1] = ev[0]
+    _check(fn(*args), name)
+
+
+def entmaxkv_build_page_meta(shape: Shape, k_pool, block_table, seq_lens, meta, stream=None,
+                             events=None):
+    fn, args = _args_build_page_meta(shape, k_pool, block_table, seq_lens, meta, stream)
+    _run("entmaxkv_build_page_meta", fn, args, events)
+
+
+def entmaxkv_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_pages, sel,
+                          sel_ub=None, ws=None, stream=None, events=None):
+    fn, args, _ = _args_score_select(shape, q, meta, block_table, seq_lens, budget_pages, sel,
+                                     sel_ub, ws, stream)
+    _run("entmaxkv_score_select", fn, args, events)
+
+
+def entmaxkv_decode_sparse(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, sel,
+                           budget_pages, alpha, out, tau=None, support=None, ws=None,
+                           stream=None, events=None):
+    fn, args, _ = _args_decode_sparse(shape, q, k_pool, v_pool, block_table, seq_lens, sel,
+                                      budget_pages, alpha, out, tau, support, ws, stream)
+    _run("entmaxkv_decode_sparse", fn, args, events)
+
+
+def entmaxkv_decode_full(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, alpha, out,
+                         tau=None, support=None, ws=None, stream=None, events=None):
+    fn, args, _ = _args_decode_full(shape, q, k_pool, v_pool, block_table, seq_lens, alpha, out,
+                                    tau, support, ws, stream)
+    _run("entmaxkv_decode_full", fn, args, events)
+
+
+class Prepared:
+    """An entry point with its arguments marshalled once, for tight loops.
+    The tensors must stay alive and unchanged in place while it is used.
+
+        call = Prepared("decode_full", shape, q, k, v, bt, lens, 1.5, out, ws=ws)
+        call()                 # or call(events=[e0, e1, e2, e3])
+    """
+
+    _makers = {"build_page_meta": _args_build_page_meta, "score_select": _args_score_select,
+               "decode_sparse": _args_decode_sparse, "decode_full": _args_decode_full}
+
+    def __init__(self, name: str, *args, **kwargs):
+        r = Prepared._makers[name](*args, **kwargs)
+        self.name = "entmaxkv_" + name
+        self.fn, self.args = r[0], r[1]
+        self.keep = (args, kwargs, r[2:] if len(r) > 2 else ())  # keep tensors alive
+        self._ev_cache = {}
+
+    def __call__(self, events=None):
+        if events is None:
+            rc = self.fn(*self.args)
+        else:
+            key = tuple(events)
+            ev = self._ev_cache.get(key)
+            if ev is None:
+                ev = self._ev_cache[key] = _events(events)
+            self.args[-1] = ev[0]
+            rc = self.fn(*self.args)
+            self.args[-1] = None
+        if rc != ENTMAXKV_OK:
+            raise EntmaxKVError(rc, self.name)
 
 
 # ---------------------------------------------------------------------------
@@ -225,6 +283,7 @@ class HipEvents:
                                               ctypes.c_void_p]
             h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
             h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             HipEvents._hip = h
         self.handles = []
         for _ in range(n):
@@ -233,6 +292,13 @@ class HipEvents:
             if rc != 0:
                 raise RuntimeError(f"hipEventCreate failed ({rc})")
             self.handles.append(e.value)
+
+    def record(self, i: int, stream) -> None:
+        """Record event i on `stream` (a torch stream or a raw handle)."""
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        rc = HipEvents._hip.hipEventRecord(ctypes.c_void_p(self.handles[i]), ctypes.c_void_p(handle))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def __len__(self):
         return len(self.handles)

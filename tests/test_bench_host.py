@@ -1,0 +1,42 @@
+"""Host-side logic of bench.py: byte accounting and the oracle CPU baseline."""
+import numpy as np
+
+import bench
+from sparse_long_context_page_amd import synth
+
+
+def test_union_pages_and_bytes():
+    w = synth.shrink(synth.WORKLOADS["long_128k"], context=4096, batch=2, n_planted=0, name="t")
+    sel = np.full((2, 32, 4), -1, dtype=np.int32)
+    sel[0, 0:4, :2] = [[1, 2], [2, 3], [1, 3], [7, 9]]  # group 0 of sequence 0: {1,2,3,7,9}
+    sel[1, 4:8, 0] = 5  # group 1 of sequence 1: {5}
+    up = bench.union_pages(sel, 4)
+    assert up[0, 0] == 5 and up[1, 1] == 1 and up.sum() == 6
+    lens = np.array([4096, 4096], dtype=np.int32)
+    sup_s = np.ones((2, 32), dtype=np.int32)
+    sup_f = np.full((2, 32), 3, dtype=np.int32)
+    nb = bench.algorithmic_bytes(w, lens, 4, sel, sup_s, sup_f)
+    P = 4096 // 32
+    assert nb["bounds"] == 2 * P * 8 * 2 * 128 * 2 + 2 * 32 * 128 * 4 + 2 * P * 4
+    assert nb["score_full"] == 2 * 4096 * 8 * 128 * 2 + 2 * 32 * 128 * 4 + 2 * P * 4
+    assert nb["score_sparse"] == 6 * 32 * 128 * 2 + 2 * 32 * 128 * 4 + 2 * 32 * 4 * 4 + 2 * P * 4
+    assert nb["tau_pv_full"] == 64 * 3 * 128 * 2 + 2 * 32 * 128 * 4
+
+
+def test_cpu_baseline_runs_and_matches_oracle_selection():
+    w = synth.shrink(synth.WORKLOADS["long_128k"], context=2048, batch=1, n_planted=8, name="t")
+    inp = synth.generate(w, 3)
+    cb = bench.cpu_baseline(inp, 8, 1.5, n_heads=4)
+    assert cb["value"] > 0 and cb["cores"] >= 1 and cb["kind"] == "oracle"
+    assert len(cb["_results"]) == 4
+    for b, h, dt, sel, rs, rf in cb["_results"]:
+        assert len(sel) == 8 and rs.shape == (128,) and rf.shape == (128,)
+
+
+def test_multi_gpu_request_exits(monkeypatch, capsys):
+    import pytest
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    assert "one GPU" in capsys.readouterr().err
