@@ -10,9 +10,11 @@ when a page is filled) and timed on their own.
 
 Inputs are generated on the host, uploaded, and resident in HBM before any
 timing. Each timed step is preceded by an untimed 1 GiB write that evicts the
-on-chip caches (L2 + MALL), so the step reads HBM, not a warm cache. HIP
-events bracket every step and every kernel (the library records them on the
-launch stream). Prints one JSON line.
+on-chip caches (L2 + MALL), so the step reads HBM, not a warm cache. In the
+timed pass HIP events mark only the call boundaries (step start, end of the
+sparse path, end of the full path); a second pass over the same steps has
+the library record events around every kernel, which gives the per-kernel
+durations behind the roofline figures. Prints one JSON line.
 
 The CPU baseline is the float64 oracle run on this host's cores over a
 bounded sample of (sequence, query head) decodes of the same workload,
@@ -197,6 +199,9 @@ def main():
     ap.add_argument("--oracle-heads", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="hot-cache timing (diagnostic)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the steps, run a plain 1 GiB device copy three times (a known-size "
+                         "reference for the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -290,26 +295,37 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # Timed pass: K steps; events only at call boundaries (start, after the
+    # sparse path, after the full path).
     K = args.steps
-    ev_step = E.HipEvents(2 * K)
-    ev_kern = E.HipEvents(12 * K)
-    hk = list(ev_kern)
+    ev_step = E.HipEvents(3 * K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         flush(i)
-        ev_step.record(2 * i, stream)
-        step(hk[12 * i:12 * (i + 1)])
-        ev_step.record(2 * i + 1, stream)
+        ev_step.record(3 * i, stream)
+        call_sel()
+        call_sp()
+        ev_step.record(3 * i + 1, stream)
+        call_fu()
+        ev_step.record(3 * i + 2, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_ms = np.array([ev_step.elapsed_ms(3 * i, 3 * i + 2) for i in range(K)])
+    sparse_ms = np.array([ev_step.elapsed_ms(3 * i, 3 * i + 1) for i in range(K)])
+    full_ms = np.array([ev_step.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(K)])
+    ms_per_step = float(step_ms.mean())
 
-    step_ms = np.array([ev_step.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)])
+    # Kernel pass: the same steps with events around every kernel (the library
+    # records them on the launch stream), for per-kernel durations.
+    ev_kern = E.HipEvents(12 * K)
+    hk = list(ev_kern)
+    for i in range(K):
+        flush(i)
+        step(hk[12 * i:12 * (i + 1)])
+    torch.cuda.synchronize()
     kern_ms = np.array([[ev_kern.elapsed_ms(12 * i + 2 * j, 12 * i + 2 * j + 1) for j in range(6)]
                         for i in range(K)])
-    sparse_ms = np.array([ev_kern.elapsed_ms(12 * i, 12 * i + 7) for i in range(K)])
-    full_ms = np.array([ev_kern.elapsed_ms(12 * i + 8, 12 * i + 11) for i in range(K)])
-    ms_per_step = float(step_ms.mean())
 
     sel_np = sel.cpu().numpy()
     nbytes = algorithmic_bytes(w, inp["seq_lens"], budget, sel_np, sup_s.cpu().numpy(),
@@ -386,6 +402,14 @@ def main():
         "parity_sample": parity,
     }
     print(json.dumps(record))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device-to-device copy done")
 
 
 if __name__ == "__main__":

@@ -159,6 +159,34 @@ struct Butterfly {
   __device__ __forceinline__ static bool owner(int lane) { return (lane & (DUP - 1)) == 0; }
 };
 
+// MFMA operand types (gfx950 v_mfma_f32_16x16x32_bf16). Lane l holds
+// A[l % 16][(l / 16) * 8 + j], B[(l / 16) * 8 + j][l % 16] for j < 8, and
+// D[(l / 16) * 4 + i][l % 16] for i < 4.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Part `part` (0, 1, 2) of the exact split x = p0 + p1 + p2 into bf16 values:
+// p0 = rne(x), p1 = rne(x - p0), p2 = x - p0 - p1. Each difference is exact
+// in float32 (the operands are within a factor of two), and the last
+// remainder has at most 8 significant bits, so it is a bf16 value.
+__device__ __forceinline__ uint32_t bf16_part(float x, int part) {
+  const uint32_t p0 = bf16_rne_bits(x);
+  const float r1 = x - __uint_as_float(p0 << 16);
+  const uint32_t p1 = bf16_rne_bits(r1);
+  const float r2 = r1 - __uint_as_float(p1 << 16);
+  const uint32_t p2 = bf16_rne_bits(r2);
+  return part == 0 ? p0 : (part == 1 ? p1 : (part == 2 ? p2 : 0u));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ __forceinline__ int clamp_len(int L, int max_tokens) {
   return L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
 }

@@ -198,6 +198,7 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
     return;
   }
 
+  const uint64_t ltm = lanemask_lt(lane);
   const int c = lane % LT;
   const int rsub = lane / LT;
   Acc qv[G][2 * VPC];
@@ -222,7 +223,6 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
       if (first + i == h) mymask[i] = m;
     }
   }
-  const uint64_t ltm = lanemask_lt(lane);
 
   Acc M[CNT];
   int mycnt[CNT];
@@ -314,7 +314,6 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
       }
     }
   }
-
 #pragma unroll
   for (int i = 0; i < CNT; ++i) {
     if (owner && rsub == 0) {
@@ -454,15 +453,16 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
   constexpr int VPC = 16 / sizeof(KV);
   constexpr int LR = D / VPC;     // lanes per V row
   constexpr int NG = kNT / LR;    // rows in flight per pass
-  __shared__ int roff[kMaxSplits];   // region offsets, later support token indices
+  __shared__ int roff[kMaxSplits + 1];  // region offsets
   __shared__ ZT lz[kListCap];
   __shared__ int li[kListCap];
-  __shared__ float sp[kSupCap];
+  __shared__ float sp[kListCap];
   __shared__ float pvacc[NG][D];
   __shared__ double red[2 * kNW];
   __shared__ ZT fred[kNW];
   __shared__ int tmp[kNW + 2];
   __shared__ double tau_b;
+  __shared__ int nb[2];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int u = blockIdx.x % U, hh = blockIdx.x / U;
@@ -471,10 +471,33 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
   const int bh = b * H + h;
   const ZT* mx = maxima + (size_t)bh * splits;
   const int* cn = counts + (size_t)bh * splits;
+  const Cand<ZT>* creg = cand + (size_t)bh * splits * cap;
+  const uint64_t ltm = lanemask_lt(lane);
 
-  ZT M = neg_inf<ZT>();
-  for (int r = tid; r < splits; r += kNT) M = max(M, mx[r]);
-  M = block_reduce<kNT>(M, fred, [](ZT a, ZT c) { return max(a, c); });
+  // Region counts and maxima: every thread loads its contiguous block of
+  // regions at once; one block scan turns counts into offsets.
+  const int cpt = (splits + kNT - 1) / kNT;
+  const int r0 = min(splits, tid * cpt), r1 = min(splits, r0 + cpt);
+  int s = 0;
+  ZT mloc = neg_inf<ZT>();
+  for (int r = r0; r < r1; ++r) {
+    const int c = cn[r];
+    roff[r] = c;
+    s += c;
+    mloc = max(mloc, mx[r]);
+  }
+  const ZT M = block_reduce<kNT>(mloc, fred, [](ZT a, ZT c) { return max(a, c); });
+  int n_cand;
+  {
+    int base = block_excl_scan<kNT>(s, tmp, &n_cand);
+    for (int r = r0; r < r1; ++r) {
+      const int v = roff[r];
+      roff[r] = base;
+      base += v;
+    }
+    if (tid == 0) roff[splits] = n_cand;
+  }
+  __syncthreads();
   if (M == neg_inf<ZT>()) {
     for (int d = tid; d < D; d += kNT) out[(size_t)bh * D + d] = 0.0f;
     if (tid == 0) {
@@ -485,55 +508,97 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
   }
   const ZT thr = M - window;
 
-  // count window members per region (one wave per region, coalesced)
-  for (int r = wave; r < splits; r += kNW) {
-    const int n = cn[r];
-    const Cand<ZT>* src = cand + ((size_t)bh * splits + r) * cap;
-    int cnt = 0;
-    for (int e = lane; e < n; e += kWave) cnt += src[e].z >= thr;
-    cnt = wave_sum(cnt);
-    if (lane == 0) roff[r] = cnt;
-  }
-  __syncthreads();
+  ZT* dz;
+  int* di;
   int n_list;
-  {
-    const int cpt = (splits + kNT - 1) / kNT;
-    const int r0 = min(splits, tid * cpt), r1 = min(splits, r0 + cpt);
-    int s = 0;
-    for (int r = r0; r < r1; ++r) s += roff[r];
-    int base = block_excl_scan<kNT>(s, tmp, &n_list);
+  if (n_cand <= kListCap) {
+    // Flat gather: entry i belongs to the last region whose offset is <= i.
+    // All loads are independent, so they are in flight together.
+    for (int i = tid; i < n_cand; i += kNT) {
+      int lo = 0, hi = splits;  // roff[lo] <= i < roff[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (roff[mid] <= i) lo = mid;
+        else hi = mid;
+      }
+      const Cand<ZT> v = creg[(size_t)lo * cap + (i - roff[lo])];
+      lz[i] = v.z;
+      li[i] = v.idx;
+    }
+    __syncthreads();
+    // Keep only the window, in place and in order (one wave; each chunk is
+    // read before any write, and writes never pass the read position).
+    if (wave == 0) {
+      int o = 0;
+      for (int e0 = 0; e0 < n_cand; e0 += kWave) {
+        const int e = e0 + lane;
+        ZT z = neg_inf<ZT>();
+        int ix = 0;
+        if (e < n_cand) {
+          z = lz[e];
+          ix = li[e];
+        }
+        const bool f = e < n_cand && z >= thr;
+        const uint64_t bal = __ballot(f);
+        if (f) {
+          lz[o + __popcll(bal & ltm)] = z;
+          li[o + __popcll(bal & ltm)] = ix;
+        }
+        o += __popcll(bal);
+      }
+      if (lane == 0) nb[0] = o;
+    }
+    __syncthreads();
+    n_list = nb[0];
+    dz = lz;
+    di = li;
+  } else {
+    // Large candidate sets: window members go to this head's global list
+    // (counted per region, then gathered, one wave per region).
+    for (int r = wave; r < splits; r += kNW) {
+      const int n = cn[r];
+      const Cand<ZT>* src = creg + (size_t)r * cap;
+      int cnt = 0;
+      for (int e = lane; e < n; e += kWave) cnt += src[e].z >= thr;
+      cnt = wave_sum(cnt);
+      if (lane == 0) roff[r] = cnt;  // only this wave touches roff[r] here
+    }
+    __syncthreads();
+    // roff now holds per-region window counts for r < splits; rebuild offsets
+    int s2 = 0;
+    for (int r = r0; r < r1; ++r) s2 += roff[r];
+    int base = block_excl_scan<kNT>(s2, tmp, &n_list);
+    __syncthreads();
     for (int r = r0; r < r1; ++r) {
       const int v = roff[r];
       roff[r] = base;
       base += v;
     }
-  }
-  __syncthreads();
-  const bool in_lds = n_list <= kListCap;
-  ZT* dz = in_lds ? lz : list_z + (size_t)bh * list_cap;
-  int* di = in_lds ? li : list_i + (size_t)bh * list_cap;
-  const uint64_t ltm = lanemask_lt(lane);
-  for (int r = wave; r < splits; r += kNW) {
-    const int n = cn[r];
-    const Cand<ZT>* src = cand + ((size_t)bh * splits + r) * cap;
-    int o = roff[r];
-    for (int e0 = 0; e0 < n; e0 += kWave) {
-      const int e = e0 + lane;
-      Cand<ZT> v;
-      v.z = neg_inf<ZT>();
-      v.idx = 0;
-      if (e < n) v = src[e];
-      const bool f = e < n && v.z >= thr;
-      const uint64_t bal = __ballot(f);
-      if (f) {
-        const int pos = o + __popcll(bal & ltm);
-        dz[pos] = v.z;
-        di[pos] = v.idx;
+    __syncthreads();
+    dz = list_z + (size_t)bh * list_cap;
+    di = list_i + (size_t)bh * list_cap;
+    for (int r = wave; r < splits; r += kNW) {
+      const int n = cn[r];
+      const Cand<ZT>* src = creg + (size_t)r * cap;
+      int o = roff[r];
+      for (int e0 = 0; e0 < n; e0 += kWave) {
+        const int e = e0 + lane;
+        Cand<ZT> v;
+        v.z = neg_inf<ZT>();
+        v.idx = 0;
+        if (e < n) v = src[e];
+        const bool f = e < n && v.z >= thr;
+        const uint64_t bal = __ballot(f);
+        if (f) {
+          const int pos = o + __popcll(bal & ltm);
+          dz[pos] = v.z;
+          di[pos] = v.idx;
+        }
+        o += __popcll(bal);
       }
-      o += __popcll(bal);
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   const double am1 = (double)alpha - 1.0;
   const double m = 1.0 / am1;
@@ -552,36 +617,54 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
   }
   const double tau = tau_b;
 
-  // support: tokens with a_i > tau, compacted in list order
-  const int cpt = (n_list + kNT - 1) / kNT;
-  const int i0 = min(n_list, tid * cpt), i1 = min(n_list, i0 + cpt);
-  int ns = 0;
-  double psum = 0.0;
-  for (int i = i0; i < i1; ++i) {
-    const double d = am1 * (double)dz[i] - tau;
-    if (d > 0.0) {
-      ++ns;
-      psum += pow_m(d, m, mcode);
-    }
-  }
+  // Support (a_i > tau) with p_i = (a_i - tau)^m; sum p in float64.
   int n_sup;
-  int sbase = block_excl_scan<kNT>(ns, tmp, &n_sup);
-  {
-    double dummy = 0.0;
-    scope_sum2<kNT>(psum, dummy, red);
-  }
-  const bool sup_lds = n_sup <= kSupCap;
-  if (sup_lds) {
-    for (int i = i0; i < i1; ++i) {
-      const double d = am1 * (double)dz[i] - tau;
-      if (d > 0.0) {
-        roff[sbase] = di[i];
-        sp[sbase] = (float)pow_m(d, m, mcode);
-        ++sbase;
+  double psum = 0.0;
+  const bool list_lds = dz == lz;
+  if (list_lds) {
+    // compact (idx, p) in place, in list order, by one wave
+    if (wave == 0) {
+      int o = 0;
+      for (int e0 = 0; e0 < n_list; e0 += kWave) {
+        const int e = e0 + lane;
+        double d = -1.0;
+        int ix = 0;
+        if (e < n_list) {
+          d = am1 * (double)lz[e] - tau;
+          ix = li[e];
+        }
+        const bool f = d > 0.0;
+        const uint64_t bal = __ballot(f);
+        if (f) {
+          const double pv = pow_m(d, m, mcode);
+          psum += pv;
+          li[o + __popcll(bal & ltm)] = ix;
+          sp[o + __popcll(bal & ltm)] = (float)pv;
+        }
+        o += __popcll(bal);
+      }
+      psum = wave_sum(psum);
+      if (lane == 0) {
+        nb[1] = o;
+        red[0] = psum;
       }
     }
+    __syncthreads();
+    n_sup = nb[1];
+    psum = red[0];
+  } else {
+    int ns = 0;
+    for (int i = tid; i < n_list; i += kNT) {
+      const double d = am1 * (double)dz[i] - tau;
+      if (d > 0.0) {
+        ++ns;
+        psum += pow_m(d, m, mcode);
+      }
+    }
+    double nsd = (double)ns;
+    scope_sum2<kNT>(psum, nsd, red);
+    n_sup = (int)nsd;
   }
-  __syncthreads();
 
   const int grp = tid / LR, c = tid % LR;
   const int32_t* selrow = SPARSE ? sel + (size_t)bh * budget : nullptr;
@@ -603,19 +686,19 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
 #pragma unroll
     for (int e = 0; e < VPC; ++e) acc[e] = fmaf(pk, (float)f[e], acc[e]);
   };
-  if (sup_lds) {
+  if (list_lds) {
     int k = grp;
     for (; k + 3 * NG < n_sup; k += 4 * NG) {
-      const KV* p0 = row_ptr(roff[k]);
-      const KV* p1 = row_ptr(roff[k + NG]);
-      const KV* p2 = row_ptr(roff[k + 2 * NG]);
-      const KV* p3 = row_ptr(roff[k + 3 * NG]);
+      const KV* p0 = row_ptr(li[k]);
+      const KV* p1 = row_ptr(li[k + NG]);
+      const KV* p2 = row_ptr(li[k + 2 * NG]);
+      const KV* p3 = row_ptr(li[k + 3 * NG]);
       accumulate(p0, sp[k]);
       accumulate(p1, sp[k + NG]);
       accumulate(p2, sp[k + 2 * NG]);
       accumulate(p3, sp[k + 3 * NG]);
     }
-    for (; k < n_sup; k += NG) accumulate(row_ptr(roff[k]), sp[k]);
+    for (; k < n_sup; k += NG) accumulate(row_ptr(li[k]), sp[k]);
   } else {
     for (int i = grp; i < n_list; i += NG) {
       const double d = am1 * (double)dz[i] - tau;
@@ -627,10 +710,10 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
   __syncthreads();
   const double inv = psum > 0.0 ? 1.0 / psum : 0.0;
   for (int d = tid; d < D; d += kNT) {
-    float s = 0.0f;
+    float sacc = 0.0f;
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) s += pvacc[gg][d];
-    out[(size_t)bh * D + d] = (float)((double)s * inv);
+    for (int gg = 0; gg < NG; ++gg) sacc += pvacc[gg][d];
+    out[(size_t)bh * D + d] = (float)((double)sacc * inv);
   }
   if (tid == 0) {
     if (tau_out) tau_out[bh] = (float)tau;

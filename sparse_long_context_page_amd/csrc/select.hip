@@ -111,17 +111,14 @@ __global__ void __launch_bounds__(kSelNT)
 select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens, int H, int G,
               int Hkv, int U, int ps, int max_pages, int budget, int32_t* __restrict__ sel,
               float* __restrict__ sel_ub) {
-  __shared__ float skeys[kSelLds];
+  constexpr int NW = kSelNT / kWave;
+  __shared__ uint32_t sord[kSelLds];
   __shared__ int hist[256];
-  __shared__ int tmp[kSelNT / kWave + 2];
-  __shared__ unsigned int ured[kSelNT / kWave];
+  __shared__ unsigned int ured[NW];
+  __shared__ int wcnt[NW][2];
   __shared__ int bc[2];
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  if (tid == 0) {
-    bc[0] = 0;
-    bc[1] = 0;
-  }
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int u = blockIdx.x % U, hh = blockIdx.x / U;
   const int b = u / Hkv, g = u % Hkv;
   const int bh = b * H + g * G + hh;
@@ -139,13 +136,13 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
     return;
   }
 
-  const float* keys = row;
-  if (P <= kSelLds) {
-    for (int i = tid; i < P; i += kSelNT) skeys[i] = row[i];
+  // Order-preserving 32-bit keys; staged in LDS when they fit.
+  const bool staged = P <= kSelLds;
+  if (staged) {
+    for (int i = tid; i < P; i += kSelNT) sord[i] = float_order(row[i] + 0.0f);
     __syncthreads();
-    keys = skeys;
   }
-  auto ord = [&](int i) -> uint32_t { return float_order(keys[i] + 0.0f); };
+  auto ord = [&](int i) -> uint32_t { return staged ? sord[i] : float_order(row[i] + 0.0f); };
 
   uint32_t mn = 0xffffffffu, mx = 0u;
   for (int i = tid; i < P; i += kSelNT) {
@@ -156,6 +153,8 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   mn = block_reduce<kSelNT>(mn, ured, [](uint32_t a, uint32_t c) { return min(a, c); });
   mx = block_reduce<kSelNT>(mx, ured, [](uint32_t a, uint32_t c) { return max(a, c); });
 
+  // Radix select of the budget-th largest key, 8 bits per pass from the
+  // highest bit where keys differ; stop once the boundary digit is taken whole.
   uint32_t prefix, pmask;
   int k = budget;  // rank still to place among keys matching the prefix
   if (mn == mx) {
@@ -163,21 +162,20 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
     pmask = 0xffffffffu;
   } else {
     int hb = 31 - __clz(mn ^ mx);
-    pmask = ~((2u << hb) - 1u);  // bits above hb (all keys agree there)
+    pmask = ~((2u << hb) - 1u);
     prefix = mx & pmask;
     while (true) {
       const int lo = hb >= 7 ? hb - 7 : 0;
       const int width = hb - lo + 1;
-      const uint32_t dmask = (width == 32) ? 0xffffffffu : ((1u << width) - 1u);
-      for (int i = tid; i < 256; i += kSelNT) hist[i] = 0;
+      const uint32_t dmask = (1u << width) - 1u;
+      hist[tid] = 0;  // kSelNT == 256 bins
       __syncthreads();
       for (int i = tid; i < P; i += kSelNT) {
         const uint32_t o = ord(i);
         if ((o & pmask) == prefix) atomicAdd(&hist[(o >> lo) & dmask], 1);
       }
       __syncthreads();
-      if (tid < kWave) {
-        // lane owns bins 4*lane .. 4*lane+3; suffix counts find the bin holding rank k
+      if (wave == 0) {
         int c4[4];
         int s = 0;
 #pragma unroll
@@ -185,13 +183,13 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
           c4[i] = hist[4 * lane + i];
           s += c4[i];
         }
-        int suf = s;
+        int suf = s;  // keys in this lane's bins and above
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
           const int o = __shfl_down(suf, d, kWave);
           if (lane + d < kWave) suf += o;
         }
-        int above = suf - s;  // keys in bins above this lane's bins
+        int above = suf - s;
         if (above < k && k <= suf) {
 #pragma unroll
           for (int i = 3; i >= 0; --i) {
@@ -209,54 +207,54 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
       k -= bc[1];
       prefix |= ((uint32_t)d) << lo;
       pmask |= dmask << lo;
-      __syncthreads();
       if (cnt_d == k || lo == 0) break;
       hb = lo - 1;
+      __syncthreads();
     }
   }
 
-  // Keep keys above the prefix, and the first k (by page index) equal to it.
-  const int cpt = (P + kSelNT - 1) / kSelNT;
-  const int i0 = min(P, tid * cpt), i1 = min(P, i0 + cpt);
-  int n_eq = 0;
-  for (int i = i0; i < i1; ++i) n_eq += ((ord(i) & pmask) == prefix);
-  int tot;
-  const int eq_base = block_excl_scan<kSelNT>(n_eq, tmp, &tot);
-  int n_sel = 0;
-  {
-    int e = eq_base;
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t m = ord(i) & pmask;
-      if (m > prefix) {
-        ++n_sel;
-      } else if (m == prefix) {
-        n_sel += (e < k);
-        ++e;
-      }
-    }
+  // Keep keys above the prefix and the first k (by page index) equal to it,
+  // written in ascending page order. Wave w owns a contiguous page range and
+  // walks it 64 pages at a time (consecutive LDS words, no bank conflicts).
+  const int span = ((P + NW * kWave - 1) / (NW * kWave)) * kWave;
+  const int j0 = min(P, wave * span), j1 = min(P, j0 + span);
+  const uint64_t ltm = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int n_eq = 0, n_gt = 0;
+  for (int base = j0; base < j1; base += kWave) {
+    const int j = base + lane;
+    uint32_t m = 0;
+    if (j < j1) m = ord(j) & pmask;
+    n_eq += __popcll(__ballot(j < j1 && m == prefix));
+    n_gt += __popcll(__ballot(j < j1 && m > prefix));
   }
-  const int out_base = block_excl_scan<kSelNT>(n_sel, tmp, &tot);
-  {
-    int e = eq_base, pos = out_base;
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t m = ord(i) & pmask;
-      bool take = false;
-      if (m > prefix) {
-        take = true;
-      } else if (m == prefix) {
-        take = e < k;
-        ++e;
-      }
-      if (take) {
-        out[pos] = i;
-        if (out_ub) out_ub[pos] = keys[i] + 0.0f;
-        ++pos;
-      }
-    }
+  if (lane == 0) {
+    wcnt[wave][0] = n_eq;
+    wcnt[wave][1] = n_gt;
   }
-  for (int i = tot + tid; i < budget; i += kSelNT) {
-    out[i] = -1;
-    if (out_ub) out_ub[i] = -__builtin_inff();
+  __syncthreads();
+  int eq_base = 0, sel_base = 0;
+  for (int w = 0; w < wave; ++w) {
+    const int e = wcnt[w][0];
+    sel_base += wcnt[w][1] + max(0, min(e, k - eq_base));
+    eq_base += e;
+  }
+  for (int base = j0; base < j1; base += kWave) {
+    const int j = base + lane;
+    uint32_t m = 0;
+    if (j < j1) m = ord(j) & pmask;
+    const bool eq = j < j1 && m == prefix;
+    const bool gt = j < j1 && m > prefix;
+    const uint64_t beq = __ballot(eq);
+    const int rank = eq_base + __popcll(beq & ltm);
+    const bool take = gt || (eq && rank < k);
+    const uint64_t bt = __ballot(take);
+    if (take) {
+      const int pos = sel_base + __popcll(bt & ltm);
+      out[pos] = j;
+      if (out_ub) out_ub[pos] = row[j] + 0.0f;
+    }
+    eq_base += __popcll(beq);
+    sel_base += __popcll(bt);
   }
 }
 
