@@ -1,0 +1,109 @@
+"""Parity at the workloads' full sizes (the configuration the benchmark
+times), on sampled (sequence, head) outputs the oracle computes one by one,
+plus properties that hold at any size for every head."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import entmax_oracle as O
+from sparse_long_context_page_amd import synth
+from parity_util import Dev, announce, check_decode, check_meta_sequence, check_selection, \
+    meta_to_f64
+
+pytestmark = pytest.mark.gpu
+
+N_SAMPLES = 6
+
+
+def sample_heads(w, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted({(int(rng.integers(0, w.batch)), int(rng.integers(0, w.num_q_heads)))
+                   for _ in range(n)})
+
+
+def whole_batch_properties(w, sel, sel_ub, out, tau, sup, budget, lens):
+    """Checks that hold for every head at any size: kept pages strictly
+    ascending and inside the sequence, -1 padding after them, a non-empty
+    support, finite outputs and thresholds."""
+    P = (lens + w.page_size - 1) // w.page_size
+    s = sel.cpu().numpy()
+    for b in range(w.batch):
+        keep = min(budget, int(P[b]))
+        rows = s[b]
+        assert (rows[:, keep:] == -1).all()
+        kept = rows[:, :keep]
+        assert (np.diff(kept, axis=1) > 0).all() and (kept >= 0).all() and (kept < P[b]).all()
+    o = out.cpu().numpy()
+    assert np.isfinite(o).all()
+    assert (sup.cpu().numpy() >= 1).all()
+    assert np.isfinite(tau.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("name", ["tiny_4k_f32", "gqa_32k", "long_128k", "extreme_512k"])
+def test_full_size_workload(name):
+    w = synth.WORKLOADS[name]
+    announce(f"full size {name}: generate")
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS[name])
+    dev = Dev(inp)
+    alpha, budget = w.alphas[0], w.budgets[0]
+    announce(f"full size {name}: meta/select/sparse/full")
+    meta = dev.build_meta()
+    sel, sel_ub = dev.select(budget)
+    sp = dev.sparse(sel, budget, alpha)
+    fu = dev.full(alpha)
+    torch.cuda.synchronize()
+    whole_batch_properties(w, sel, sel_ub, *sp, budget, inp["seq_lens"])
+    whole_batch_properties(w, sel, sel_ub, *fu, budget, inp["seq_lens"])
+    meta64 = meta_to_f64(meta, w.kv_dtype)
+    sel_np, ub_np = sel.cpu().numpy(), sel_ub.cpu().numpy()
+    so, st, ss = (x.cpu().numpy() for x in sp)
+    fo, ft, fs = (x.cpu().numpy() for x in fu)
+    G = w.num_q_heads // w.num_kv_heads
+    for b, h in sample_heads(w, N_SAMPLES, 7):
+        seq_meta = check_meta_sequence(inp, meta64, b, h // G)
+        check_selection(inp, b, h, budget, sel_np[b, h], ub_np[b, h], seq_meta)
+        check_decode(O.decode_sparse(inp, b, h, alpha, sel_np[b, h]), so[b, h], st[b, h],
+                     ss[b, h], w.kv_dtype, alpha, f"{name} sparse b{b} h{h}")
+        check_decode(O.decode_full(inp, b, h, alpha), fo[b, h], ft[b, h], fs[b, h],
+                     w.kv_dtype, alpha, f"{name} full b{b} h{h}")
+
+
+def test_full_size_alpha_sweep():
+    """Every (alpha, budget) cell of the 64K sweep at full size; the oracle
+    checks sampled heads of each cell."""
+    name = "alpha_sweep_64k"
+    w = synth.WORKLOADS[name]
+    announce(f"full size {name}: generate")
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS[name])
+    dev = Dev(inp)
+    meta = dev.build_meta()
+    meta64 = None
+    G = w.num_q_heads // w.num_kv_heads
+    heads = sample_heads(w, 4, 11)
+    seq_meta = {}
+    for budget in w.budgets:
+        announce(f"full size {name}: select budget={budget}")
+        sel, sel_ub = dev.select(budget)
+        torch.cuda.synchronize()
+        if meta64 is None:
+            meta64 = meta_to_f64(meta, w.kv_dtype)
+        sel_np, ub_np = sel.cpu().numpy(), sel_ub.cpu().numpy()
+        for b, h in heads:
+            if (b, h // G) not in seq_meta:
+                seq_meta[(b, h // G)] = check_meta_sequence(inp, meta64, b, h // G)
+            check_selection(inp, b, h, budget, sel_np[b, h], ub_np[b, h], seq_meta[(b, h // G)])
+        for alpha in w.alphas:
+            announce(f"full size {name}: decode budget={budget} alpha={alpha}")
+            sp = dev.sparse(sel, budget, alpha)
+            fu = dev.full(alpha) if budget == w.budgets[0] else None
+            torch.cuda.synchronize()
+            whole_batch_properties(w, sel, sel_ub, *sp, budget, inp["seq_lens"])
+            so, st, ss = (x.cpu().numpy() for x in sp)
+            for b, h in heads:
+                check_decode(O.decode_sparse(inp, b, h, alpha, sel_np[b, h]), so[b, h], st[b, h],
+                             ss[b, h], w.kv_dtype, alpha, f"sweep sparse a{alpha} B{budget} b{b} h{h}")
+            if fu is not None:
+                fo, ft, fs = (x.cpu().numpy() for x in fu)
+                for b, h in heads:
+                    check_decode(O.decode_full(inp, b, h, alpha), fo[b, h], ft[b, h], fs[b, h],
+                                 w.kv_dtype, alpha, f"sweep full a{alpha} b{b} h{h}")
