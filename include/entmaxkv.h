@@ -19,6 +19,9 @@
  *  - Array arguments are DEVICE pointers owned by the caller. The library
  *    never allocates, frees or keeps a pointer after returning.
  *  - `shape` is a HOST pointer, read during the call only.
+ *  - Alignment: q, k_pool, v_pool and meta must be 16-byte aligned and the
+ *    workspace 256-byte aligned (hipMalloc gives both); otherwise the call
+ *    returns ENTMAXKV_ERR_INVALID.
  *  - Work is enqueued on `stream` (0 = the null stream); calls return without
  *    waiting for the GPU.
  *  - `events` (nullable) is a host array of 2*k hipEvent_t handles created by
@@ -73,8 +76,9 @@ extern "C" {
 
 enum {
   ENTMAXKV_OK = 0,
-  ENTMAXKV_ERR_INVALID = -1,     /* null pointer, non-positive size, H % H_kv != 0,
-                                    budget <= 0, alpha <= 1 or not finite */
+  ENTMAXKV_ERR_INVALID = -1,     /* null or misaligned pointer, non-positive size,
+                                    H % H_kv != 0, budget <= 0, alpha <= 1 or not
+                                    finite */
   ENTMAXKV_ERR_UNSUPPORTED = -2, /* head_dim, page_size, group size, dtype or size
                                     outside the supported set */
   ENTMAXKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */

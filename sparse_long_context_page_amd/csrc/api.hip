@@ -15,6 +15,10 @@ constexpr size_t kMaxScoreLds = 150 * 1024;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Kernels use 16-byte vector loads of q, the pools and the box metadata, and
+// carve the workspace into 256-byte aligned pieces.
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
 int check_shape(const entmaxkv_shape* s, LaunchShape* out) {
   if (!s) return ENTMAXKV_ERR_INVALID;
   if (s->batch <= 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->head_dim <= 0 ||
@@ -64,9 +68,9 @@ float window_of(float alpha) {
 }
 
 int score_lds_ok(const LaunchShape& s, const SplitPlan& p, bool sparse, int budget) {
-  const ScoreLds l = score_lds_layout(s.group, s.page_size, p.pages_per_split, sparse,
-                                      s.max_pages, budget, score_bytes(s.bf16));
-  return l.total <= kMaxScoreLds ? ENTMAXKV_OK : ENTMAXKV_ERR_UNSUPPORTED;
+  const size_t total = score_lds_layout(s.group, s.page_size, p.pages_per_split, sparse,
+                                        s.max_pages, budget, score_bytes(s.bf16)).total;
+  return total <= kMaxScoreLds ? ENTMAXKV_OK : ENTMAXKV_ERR_UNSUPPORTED;
 }
 
 struct Events {
@@ -80,31 +84,48 @@ struct Events {
 
 namespace ekv {
 
-SplitPlan plan_sparse(const LaunchShape& s, int budget) {
+// Largest pages-per-workgroup, at most `pps`, whose score-kernel LDS (per-wave
+// candidate lists sized for every token of the split) fits; wide heads with
+// float32 caches and many heads per KV head need shorter splits.
+static int fit_pps(const LaunchShape& s, int pps, bool sparse, int budget) {
+  while (pps > 1 && score_lds_layout(s.group, s.page_size, pps, sparse, s.max_pages, budget,
+                                     score_bytes(s.bf16)).total > kMaxScoreLds)
+    pps /= 2;
+  return pps;
+}
+
+// One candidate region per (head, workgroup); their count per head is capped
+// by the threshold kernel's LDS.
+static SplitPlan finish_plan(const LaunchShape& s, long long pages, int pps) {
   SplitPlan p;
+  const long long need = (pages + kMaxSplits - 1) / kMaxSplits;
+  if (pps < need) pps = (int)need;
+  p.pages_per_split = pps;
+  p.splits = (int)((pages + pps - 1) / pps);
+  if (p.splits < 1) p.splits = 1;
+  p.cap = pps * s.page_size;
+  p.regions = p.splits;
+  p.rcap = p.cap;
+  return p;
+}
+
+SplitPlan plan_sparse(const LaunchShape& s, int budget) {
   const int keep = budget < s.max_pages ? budget : s.max_pages;
   long long umax = (long long)s.group * keep;
   if (umax > s.max_pages) umax = s.max_pages;
   int pps = kSparseTokensPerSplit / s.page_size;
   if (pps < 1) pps = 1;
-  const long long need = (umax + kMaxSplits - 1) / kMaxSplits;
-  if (pps < need) pps = (int)need;
-  p.pages_per_split = pps;
-  p.splits = (int)((umax + pps - 1) / pps);
-  p.cap = pps * s.page_size;
+  pps = fit_pps(s, pps, true, budget);
+  SplitPlan p = finish_plan(s, umax, pps);
   p.list_cap = keep * s.page_size;
   return p;
 }
 
 SplitPlan plan_full(const LaunchShape& s) {
-  SplitPlan p;
   int pps = kFullTokensPerSplit / s.page_size;
   if (pps < 1) pps = 1;
-  const int need = (s.max_pages + kMaxSplits - 1) / kMaxSplits;
-  if (pps < need) pps = need;
-  p.pages_per_split = pps;
-  p.splits = (s.max_pages + pps - 1) / pps;
-  p.cap = pps * s.page_size;
+  pps = fit_pps(s, pps, false, 0);
+  SplitPlan p = finish_plan(s, s.max_pages, pps);
   p.list_cap = s.max_pages * s.page_size;
   return p;
 }
@@ -115,11 +136,11 @@ DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p) {
   size_t o = 0;
   const size_t zb = score_bytes(s.bf16);
   w.cand = o;
-  o = align256(o + bh * p.splits * (size_t)p.cap * cand_bytes(s.bf16));
+  o = align256(o + bh * p.regions * (size_t)p.rcap * cand_bytes(s.bf16));
   w.counts = o;
-  o = align256(o + bh * p.splits * 4);
+  o = align256(o + bh * p.regions * 4);
   w.maxima = o;
-  o = align256(o + bh * p.splits * zb);
+  o = align256(o + bh * p.regions * zb);
   w.list = o;
   o = align256(o + bh * (size_t)p.list_cap * (zb + 4));
   w.total = o;
@@ -160,10 +181,13 @@ int decode_common(const entmaxkv_shape* shape, const float* q, const void* k_poo
   if (sparse && (rc = check_budget(budget))) return rc;
   if ((rc = check_alpha(alpha))) return rc;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return ENTMAXKV_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return ENTMAXKV_ERR_INVALID;
   const SplitPlan p = sparse ? plan_sparse(s, budget) : plan_full(s);
   if ((rc = score_lds_ok(s, p, sparse, budget))) return rc;
   const DecodeWs L = decode_ws_layout(s, p);
   if (!ws || ws_bytes < L.total) return ENTMAXKV_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return ENTMAXKV_ERR_INVALID;
   const float window = window_of(alpha);
   const Events ev{events, stream};
   if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
@@ -231,6 +255,7 @@ int entmaxkv_build_page_meta(const entmaxkv_shape* shape, const void* k_pool,
   int rc = check_shape(shape, &s);
   if (rc) return rc;
   if (!k_pool || !block_table || !seq_lens || !meta) return ENTMAXKV_ERR_INVALID;
+  if (!aligned(k_pool, 16) || !aligned(meta, 16)) return ENTMAXKV_ERR_INVALID;
   const Events ev{events, stream};
   if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
   if (launch_meta(s, k_pool, block_table, seq_lens, meta, stream) != hipSuccess)
@@ -248,7 +273,9 @@ int entmaxkv_score_select(const entmaxkv_shape* shape, const float* q, const voi
   if (rc) return rc;
   if ((rc = check_budget(budget_pages))) return rc;
   if (!q || !meta || !block_table || !seq_lens || !sel) return ENTMAXKV_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(meta, 16)) return ENTMAXKV_ERR_INVALID;
   if (!ws || ws_bytes < select_ws_bytes(s)) return ENTMAXKV_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return ENTMAXKV_ERR_INVALID;
   float* ub = static_cast<float*>(ws);
   const Events ev{events, stream};
   if (!ev.before(0)) return ENTMAXKV_ERR_HIP;

@@ -35,6 +35,11 @@ __device__ __forceinline__ uint32_t float_order(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of float_order.
+__device__ __forceinline__ float order_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
@@ -105,12 +110,40 @@ __device__ __forceinline__ T block_reduce(T v, T* tmp, Op op) {
   return r;
 }
 
+// Value held by a partner lane whose index differs from this lane's in bit W
+// (W < 16: in bits 0..log2(W) -- a DPP lane swap within a row, no LDS
+// traffic). The partners used are lane^1, lane^2 (quad permutes), lane^7
+// (row half-mirror) and lane^15 (row mirror); W >= 16 uses lane^W.
+template <int W>
+__device__ __forceinline__ int partner_i32(int v) {
+  if constexpr (W == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (W == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (W == 4) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  else if constexpr (W == 8) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  else return __shfl_xor(v, W, kWave);
+}
+
+template <int W, typename T>
+__device__ __forceinline__ T partner(T v) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, partner_i32<W>(__builtin_bit_cast(int, v)));
+  } else {
+    int2 p = __builtin_bit_cast(int2, v);
+    p.x = partner_i32<W>(p.x);
+    p.y = partner_i32<W>(p.y);
+    return __builtin_bit_cast(T, p);
+  }
+}
+
 // Multi-value butterfly. NV partial sums v[0..NV) are spread over groups of
 // LT lanes (lane bits below log2(LT) pick the lane within a group; LT and NV
 // are powers of two). After the call each lane holds CNT = max(1, NV/LT)
 // complete sums in v[0..CNT): value indices first_index(lane) + i. Each
 // halving step exchanges half of the values still held, so the work is
-// NV/2 + NV/4 + ... shuffles instead of NV*log2(LT).
+// NV/2 + NV/4 + ... exchanges instead of NV*log2(LT). The step for bit W
+// pairs each lane with a partner that differs from it in bit W (partner<W>);
+// the partner masks of the steps (lane^15, ^7, ^2, ^1 or lane^W) span all
+// log2(LT) lane bits, so every lane of a group ends with the full sum.
 template <int NV, int LT>
 struct Butterfly {
   static constexpr int CNT = NV > LT ? NV / LT : 1;
@@ -130,11 +163,11 @@ struct Butterfly {
         for (int i = 0; i < H; ++i) {
           T send = up ? v[i] : v[H + i];
           T keep = up ? v[H + i] : v[i];
-          v[i] = keep + shfl_xor(send, W);
+          v[i] = keep + partner<W>(send);
         }
         step<T, W / 2, H>(v, lane);
       } else {
-        v[0] += shfl_xor(v[0], W);
+        v[0] += partner<W>(v[0]);
         step<T, W / 2, C>(v, lane);
       }
     }
@@ -159,32 +192,9 @@ struct Butterfly {
   __device__ __forceinline__ static bool owner(int lane) { return (lane & (DUP - 1)) == 0; }
 };
 
-// MFMA operand types (gfx950 v_mfma_f32_16x16x32_bf16). Lane l holds
-// A[l % 16][(l / 16) * 8 + j], B[(l / 16) * 8 + j][l % 16] for j < 8, and
-// D[(l / 16) * 4 + i][l % 16] for i < 4.
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
-}
-
-// Part `part` (0, 1, 2) of the exact split x = p0 + p1 + p2 into bf16 values:
-// p0 = rne(x), p1 = rne(x - p0), p2 = x - p0 - p1. Each difference is exact
-// in float32 (the operands are within a factor of two), and the last
-// remainder has at most 8 significant bits, so it is a bf16 value.
-__device__ __forceinline__ uint32_t bf16_part(float x, int part) {
-  const uint32_t p0 = bf16_rne_bits(x);
-  const float r1 = x - __uint_as_float(p0 << 16);
-  const uint32_t p1 = bf16_rne_bits(r1);
-  const float r2 = r1 - __uint_as_float(p1 << 16);
-  const uint32_t p2 = bf16_rne_bits(r2);
-  return part == 0 ? p0 : (part == 1 ? p1 : (part == 2 ? p2 : 0u));
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
-  return __builtin_bit_cast(bf16x8, v);
+// Lanes below `lane` as a 64-bit mask.
+__device__ __forceinline__ uint64_t lanemask_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
 __device__ __forceinline__ int clamp_len(int L, int max_tokens) {

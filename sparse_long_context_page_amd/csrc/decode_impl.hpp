@@ -85,10 +85,6 @@ __device__ __forceinline__ uint4 stream_load16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
-  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
-}
-
 // First index in row[0..n) whose value (negatives read as +inf) is >= key; -1 if
 // row has no entry equal to key.
 __device__ __forceinline__ int find_slot(const int32_t* row, int n, int key) {
@@ -103,49 +99,22 @@ __device__ __forceinline__ int find_slot(const int32_t* row, int n, int key) {
   return (lo < n && row[lo] == key) ? lo : -1;
 }
 
-template <typename KV, int D, int G, int PS, bool SPARSE>
-__global__ void __launch_bounds__(kNT)
-score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
-             const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-             const int32_t* __restrict__ sel, int H, int Hkv, int U, int max_pages, int num_phys,
-             int budget, int pps, int splits, int cap, double window_d,
-             Cand<typename KvTraits<KV>::Acc>* __restrict__ cand, int* __restrict__ counts,
-             typename KvTraits<KV>::Acc* __restrict__ maxima) {
-  using Tr = KvTraits<KV>;
-  using Acc = typename Tr::Acc;  // also the score type
-  const Acc window = (Acc)window_d;
-  constexpr int VPC = Tr::VPC;
-  constexpr int LT = D / (2 * VPC);  // lanes per token row
-  constexpr int RW = kWave / LT;     // rows per wave step
-  static_assert(PS % RW == 0, "page must hold whole wave steps");
-  constexpr int STEPS = PS / RW;
-  using BF = Butterfly<G, LT>;
-  constexpr int CNT = BF::CNT;
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc));
-  Acc* rz = reinterpret_cast<Acc*>(smem + lay.rz);
-  int* ri = reinterpret_cast<int*>(smem + lay.ri);
-  Acc* wmax = reinterpret_cast<Acc*>(smem + lay.wmax);
-  int* wcnt = reinterpret_cast<int*>(smem + lay.wcnt);
-  int* slice = reinterpret_cast<int*>(smem + lay.slice);
-  int* slots = reinterpret_cast<int*>(smem + lay.slots);
-  int* tmp = reinterpret_cast<int*>(smem + lay.tmp);
-
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int u = blockIdx.x % U;
-  const int split = blockIdx.x / U;
-  const int b = u / Hkv, g = u % Hkv;
-  const int L = clamp_len(seq_lens[b], max_pages * PS);
-  const int P = (L + PS - 1) / PS;
-  const int bh0 = b * H + g * G;
-
+// This split's pages, in LDS: `slice` (sparse: logical page indices, taken
+// from the union of the G heads' selections in ascending order), `slots`
+// (sparse: each head's position of the page in its selection, -1 if the head
+// did not select it) and `sphys` (physical page ids, fetched with one
+// coalesced load per page). Returns the number of pages; ends with a barrier
+// (every thread of the block must call it).
+template <int G, bool SPARSE>
+__device__ int build_slice(const int32_t* __restrict__ sel, const int32_t* __restrict__ block_table,
+                           int b, int bh0, int budget, int P, int max_pages, int split, int pps,
+                           unsigned* bm, int32_t* ssel, int* slice, int* slots, int* sphys,
+                           int* tmp) {
+  const int tid = threadIdx.x;
   int n_slice;
   if constexpr (SPARSE) {
-    unsigned* bm = reinterpret_cast<unsigned*>(smem + lay.bitmap);
     const int32_t* selrow = sel + (size_t)bh0 * budget;
     const bool staged = (size_t)G * budget <= (size_t)kSelCopy;
-    int32_t* ssel = reinterpret_cast<int32_t*>(smem + lay.ssel);
     const int nwords = (P + 31) >> 5;
     for (int i = tid; i < nwords; i += kNT) bm[i] = 0u;
     if (staged)
@@ -183,12 +152,60 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
       const int p = i / G, h = i % G;
       slots[i] = find_slot(srow + (size_t)h * budget, budget, slice[p]);
     }
-    __syncthreads();
   } else {
     const int lo = split * pps;
     n_slice = max(0, min(P, lo + pps) - lo);
   }
+  for (int p = tid; p < n_slice; p += kNT) {
+    const int j = SPARSE ? slice[p] : split * pps + p;
+    sphys[p] = block_table[(size_t)b * max_pages + j];
+  }
+  __syncthreads();
+  return n_slice;
+}
 
+template <typename KV, int D, int G, int PS, bool SPARSE>
+__global__ void __launch_bounds__(kNT)
+score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
+             const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+             const int32_t* __restrict__ sel, int H, int Hkv, int U, int max_pages, int num_phys,
+             int budget, int pps, int splits, int cap, double window_d,
+             Cand<typename KvTraits<KV>::Acc>* __restrict__ cand, int* __restrict__ counts,
+             typename KvTraits<KV>::Acc* __restrict__ maxima) {
+  using Tr = KvTraits<KV>;
+  using Acc = typename Tr::Acc;  // also the score type
+  const Acc window = (Acc)window_d;
+  constexpr int VPC = Tr::VPC;
+  constexpr int LT = D / (2 * VPC);  // lanes per token row
+  constexpr int RW = kWave / LT;     // rows per wave step
+  static_assert(PS % RW == 0, "page must hold whole wave steps");
+  constexpr int STEPS = PS / RW;
+  using BF = Butterfly<G, LT>;
+  constexpr int CNT = BF::CNT;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc));
+  Acc* rz = reinterpret_cast<Acc*>(smem + lay.rz);
+  int* ri = reinterpret_cast<int*>(smem + lay.ri);
+  Acc* wmax = reinterpret_cast<Acc*>(smem + lay.wmax);
+  int* wcnt = reinterpret_cast<int*>(smem + lay.wcnt);
+  int* slice = reinterpret_cast<int*>(smem + lay.slice);
+  int* slots = reinterpret_cast<int*>(smem + lay.slots);
+  int* sphys = reinterpret_cast<int*>(smem + lay.phys);
+  int* tmp = reinterpret_cast<int*>(smem + lay.tmp);
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int u = blockIdx.x % U;
+  const int split = blockIdx.x / U;
+  const int b = u / Hkv, g = u % Hkv;
+  const int L = clamp_len(seq_lens[b], max_pages * PS);
+  const int P = (L + PS - 1) / PS;
+  const int bh0 = b * H + g * G;
+
+  const int n_slice = build_slice<G, SPARSE>(
+      sel, block_table, b, bh0, budget, P, max_pages, split, pps,
+      reinterpret_cast<unsigned*>(smem + lay.bitmap), reinterpret_cast<int32_t*>(smem + lay.ssel),
+      slice, slots, sphys, tmp);
   if (n_slice == 0) {
     if (tid < G) {
       const size_t r = (size_t)(bh0 + tid) * splits + split;
@@ -198,7 +215,7 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
     return;
   }
 
-  const uint64_t ltm = lanemask_lt(lane);
+  const uint64_t ltm = lanemask_below(lane);
   const int c = lane % LT;
   const int rsub = lane / LT;
   Acc qv[G][2 * VPC];
@@ -234,7 +251,7 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
 
   for (int p = wave; p < n_slice; p += kNW) {
     const int j = SPARSE ? slice[p] : split * pps + p;
-    const int phys = block_table[(size_t)b * max_pages + j];
+    const int phys = sphys[p];
     if (phys < 0 || phys >= num_phys) continue;
     const int nvalid = min(PS, L - j * PS);
     int myslot[CNT];
@@ -472,7 +489,7 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
   const ZT* mx = maxima + (size_t)bh * splits;
   const int* cn = counts + (size_t)bh * splits;
   const Cand<ZT>* creg = cand + (size_t)bh * splits * cap;
-  const uint64_t ltm = lanemask_lt(lane);
+  const uint64_t ltm = lanemask_below(lane);
 
   // Region counts and maxima: every thread loads its contiguous block of
   // regions at once; one block scan turns counts into offsets.
@@ -800,7 +817,7 @@ hipError_t launch_tau_pv_t(const LaunchShape& s, const SplitPlan& p, const void*
   hipLaunchKernelGGL((tau_pv_kernel<KV, D, SPARSE>), dim3(U * s.group), dim3(kNT), 0, st,
                      static_cast<const KV*>(v_pool), bt, lens, sel, s.num_q_heads,
                      s.num_kv_heads, s.group, U, s.page_size, s.max_pages, s.num_phys, budget,
-                     p.splits, p.cap, p.list_cap, alpha, (double)window,
+                     p.regions, p.rcap, p.list_cap, alpha, (double)window,
                      reinterpret_cast<const Cand<ZT>*>(w + L.cand),
                      reinterpret_cast<const int*>(w + L.counts),
                      reinterpret_cast<const ZT*>(w + L.maxima), list_z, list_i, out, tau,

@@ -16,8 +16,8 @@ struct LaunchShape {
 };
 
 // Tokens handled by one workgroup of the gather-score kernels.
-constexpr int kSparseTokensPerSplit = 256;
-constexpr int kFullTokensPerSplit = 1024;
+constexpr int kSparseTokensPerSplit = 512;
+constexpr int kFullTokensPerSplit = 2048;
 constexpr int kMaxSplits = 4096;  // candidate regions per head (LDS-sized in the threshold kernel)
 
 constexpr int kNT = 256;
@@ -30,7 +30,7 @@ constexpr int kSelCopy = 8192;  // selection ints staged in LDS by the sparse sc
 // LDS layout of the score kernel (bytes), shared by host sizing and device carving.
 struct ScoreLds {
   int wcap;  // candidate slots per (wave, head)
-  size_t rz, ri, wmax, wcnt, slice, slots, tmp, bitmap, ssel, total;
+  size_t rz, ri, wmax, wcnt, slice, slots, phys, tmp, bitmap, ssel, total;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -48,6 +48,7 @@ __host__ __device__ inline ScoreLds score_lds_layout(int G, int ps, int pps, boo
   l.wcnt = o; o = align16(o + (size_t)kNW * G * 4);
   l.slice = o; o = align16(o + (size_t)pps * 4);
   l.slots = o; o = align16(o + (size_t)pps * G * 4);
+  l.phys = o; o = align16(o + (size_t)pps * 4);
   l.tmp = o; o = align16(o + (kNW + 2) * 4);
   l.bitmap = o;
   if (sparse) o = align16(o + (size_t)((max_pages + 31) / 32) * 4);
@@ -58,11 +59,14 @@ __host__ __device__ inline ScoreLds score_lds_layout(int G, int ps, int pps, boo
 }
 
 
-// Partition of one (sequence, KV head) unit's pages into workgroups.
+// Partition of one (sequence, KV head) unit's pages into workgroups, and of
+// each head's candidates into regions (one per head and workgroup).
 struct SplitPlan {
   int pages_per_split;  // pages one workgroup streams
   int splits;           // workgroups per unit
-  int cap;              // candidate slots per (head, split) = pages_per_split * page_size
+  int cap;              // tokens one workgroup streams per head = pages_per_split * page_size
+  int regions;          // candidate regions per head
+  int rcap;             // candidate slots per region (every token it covers)
   int list_cap;         // threshold-list slots per head (worst case: every gathered token)
 };
 
@@ -78,6 +82,9 @@ struct DecodeWs {
 __host__ __device__ inline int score_bytes(bool bf16) { return bf16 ? 4 : 8; }
 __host__ __device__ inline int cand_bytes(bool bf16) { return bf16 ? 8 : 16; }
 DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p);
+// Row stride (floats) of the per-head page bounds in the select workspace:
+// padded to a multiple of 4 so every row starts 16-byte aligned.
+inline int ub_ld(int max_pages) { return (max_pages + 3) & ~3; }
 size_t select_ws_bytes(const LaunchShape& s);
 
 hipError_t launch_meta(const LaunchShape& s, const void* k_pool, const int32_t* bt,

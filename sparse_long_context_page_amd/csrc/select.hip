@@ -5,8 +5,10 @@
 //
 // bounds_kernel: one workgroup per (chunk of pages, sequence, KV head). The
 //   G query heads that share the KV head are bounded together, so each page's
-//   box is read once. Each page's (k_min, k_max) row pair is split over LP
-//   lanes (16 bytes of each per lane). Per coordinate the lane takes k_max
+//   box is read once. Each page's (k_min, k_max) row pair is split over D/4
+//   lanes (four coordinates of each per lane); a workgroup covers 32 pages
+//   and issues all of its box loads before using the first, so the chip has
+//   many small workgroups in flight and little tail. Per coordinate the lane takes k_max
 //   where q_d >= 0 and k_min otherwise (the box maximum of q_d k_d), forms the
 //   products in float64 (exact: 24-bit x 8- or 24-bit significands) and sums
 //   in float64; a multi-value butterfly finishes the G sums across the LP
@@ -17,74 +19,86 @@
 //   8 bits per pass, stopping as soon as the boundary digit is taken whole.
 //   Ties on the full 32 bits go to the lower page index. The kept pages are
 //   written in ascending order with two block scans.
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace ekv {
 
 constexpr int kSelNT = 256;
 constexpr int kSelLds = 16384;  // bounds staged in LDS when the sequence has at most this many pages
-constexpr int kBoundSteps = 4;  // page groups per workgroup
+constexpr int kBoundPages = 32;  // pages per workgroup of the bounds kernel
 
 template <typename KV, int D, int G>
 __global__ void __launch_bounds__(256)
 bounds_kernel(const float* __restrict__ q, const KV* __restrict__ meta,
               const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-              float* __restrict__ ub, int H, int Hkv, int ps, int max_pages, int num_phys, int U) {
-  constexpr int VPC = 16 / sizeof(KV);    // box coordinates per lane (per bound side)
+              float* __restrict__ ub, int H, int Hkv, int ps, int max_pages, int num_phys, int U,
+              int ldu) {
+  constexpr int VPC = 4;                  // box coordinates per lane (per bound side)
   constexpr int LP = D / VPC;             // lanes per page
   constexpr int PPB = 256 / LP;           // pages per block step
+  constexpr int STEPS = kBoundPages / PPB;
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  using Chunk = typename std::conditional<sizeof(KV) == 2, u32x2, u32x4>::type;
   using BF = Butterfly<G, LP>;
   static_assert(BF::CNT == 1, "group size must not exceed lanes per page");
+  static_assert(kBoundPages % PPB == 0, "whole block steps");
+  __shared__ int sphys[kBoundPages];
 
   const int u = blockIdx.x % U;
   const int chunk = blockIdx.x / U;
   const int b = u / Hkv, g = u % Hkv;
   const int L = clamp_len(seq_lens[b], max_pages * ps);
   const int P = (L + ps - 1) / ps;
-  const int j0 = chunk * PPB * kBoundSteps;
+  const int j0 = chunk * kBoundPages;
   if (j0 >= P) return;
+  const int n = min(kBoundPages, P - j0);
+
+  // physical pages of the chunk: one coalesced load, then LDS
+  if (threadIdx.x < kBoundPages)
+    sphys[threadIdx.x] = threadIdx.x < n ? block_table[(size_t)b * max_pages + j0 + threadIdx.x] : -1;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int c = threadIdx.x % LP;
   const int h0 = b * H + g * G;
-
-  double qd[G][VPC];
+  float qf[G][VPC];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < VPC; ++e) qd[h][e] = (double)q[(size_t)(h0 + h) * D + c * VPC + e];
-
+  for (int h = 0; h < G; ++h) {
+    const float4 v = *reinterpret_cast<const float4*>(q + (size_t)(h0 + h) * D + c * VPC);
+    qf[h][0] = v.x; qf[h][1] = v.y; qf[h][2] = v.z; qf[h][3] = v.w;
+  }
   const int my_head = BF::first_index(lane);
   const bool owner = BF::owner(lane);
+  __syncthreads();
 
+  // every box load of the workgroup is in flight before the first is used;
+  // boxes are read once per call, so the loads are marked streaming
+  Chunk xlo[STEPS], xhi[STEPS];
+  bool ok[STEPS];
 #pragma unroll
-  for (int s = 0; s < kBoundSteps; ++s) {
-    const int j = j0 + s * PPB + threadIdx.x / LP;
-    int phys = -1;
-    if (j < P) phys = block_table[(size_t)b * max_pages + j];
-    const bool ok = phys >= 0 && phys < num_phys;
-    uint4 xlo = make_uint4(0, 0, 0, 0), xhi = make_uint4(0, 0, 0, 0);
-    if (ok) {
-      const KV* row = meta + ((size_t)phys * Hkv + g) * 2 * D + c * VPC;
-      xlo = *reinterpret_cast<const uint4*>(row);
-      xhi = *reinterpret_cast<const uint4*>(row + D);
-    }
+  for (int t = 0; t < STEPS; ++t) {
+    const int phys = sphys[t * PPB + threadIdx.x / LP];
+    ok[t] = phys >= 0 && phys < num_phys;
+    // page 0 stands in for an empty slot; its result is dropped
+    const KV* row = meta + ((size_t)(ok[t] ? phys : 0) * Hkv + g) * 2 * D + c * VPC;
+    xlo[t] = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(row));
+    xhi[t] = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(row + D));
+  }
+#pragma unroll
+  for (int t = 0; t < STEPS; ++t) {
     float lo[VPC], hi[VPC];
     if constexpr (sizeof(KV) == 2) {
-      const uint32_t wl[4] = {xlo.x, xlo.y, xlo.z, xlo.w};
-      const uint32_t wh[4] = {xhi.x, xhi.y, xhi.z, xhi.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[2 * i] = bf16_lo(wl[i]);
-        lo[2 * i + 1] = bf16_hi(wl[i]);
-        hi[2 * i] = bf16_lo(wh[i]);
-        hi[2 * i + 1] = bf16_hi(wh[i]);
-      }
+      lo[0] = bf16_lo(xlo[t].x); lo[1] = bf16_hi(xlo[t].x);
+      lo[2] = bf16_lo(xlo[t].y); lo[3] = bf16_hi(xlo[t].y);
+      hi[0] = bf16_lo(xhi[t].x); hi[1] = bf16_hi(xhi[t].x);
+      hi[2] = bf16_lo(xhi[t].y); hi[3] = bf16_hi(xhi[t].y);
     } else {
-      lo[0] = __uint_as_float(xlo.x); lo[1] = __uint_as_float(xlo.y);
-      lo[2] = __uint_as_float(xlo.z); lo[3] = __uint_as_float(xlo.w);
-      hi[0] = __uint_as_float(xhi.x); hi[1] = __uint_as_float(xhi.y);
-      hi[2] = __uint_as_float(xhi.z); hi[3] = __uint_as_float(xhi.w);
+      lo[0] = __uint_as_float(xlo[t].x); lo[1] = __uint_as_float(xlo[t].y);
+      lo[2] = __uint_as_float(xlo[t].z); lo[3] = __uint_as_float(xlo[t].w);
+      hi[0] = __uint_as_float(xhi[t].x); hi[1] = __uint_as_float(xhi[t].y);
+      hi[2] = __uint_as_float(xhi[t].z); hi[3] = __uint_as_float(xhi[t].w);
     }
     double acc[G];
 #pragma unroll
@@ -92,16 +106,14 @@ bounds_kernel(const float* __restrict__ q, const KV* __restrict__ meta,
       double a = 0.0;
 #pragma unroll
       for (int e = 0; e < VPC; ++e) {
-        const float k = qd[h][e] >= 0.0 ? hi[e] : lo[e];
-        a = fma(qd[h][e], (double)k, a);
+        const float k = qf[h][e] >= 0.0f ? hi[e] : lo[e];
+        a = fma((double)qf[h][e], (double)k, a);
       }
       acc[h] = a;
     }
     BF::reduce(acc, lane);
-    if (ok && owner) {
-      const float key = (float)acc[0] + 0.0f;
-      ub[(size_t)(h0 + my_head) * max_pages + j] = key;
-    }
+    const int jj = t * PPB + threadIdx.x / LP;
+    if (ok[t] && owner) ub[(size_t)(h0 + my_head) * ldu + j0 + jj] = (float)acc[0] + 0.0f;
   }
 }
 
@@ -109,14 +121,15 @@ bounds_kernel(const float* __restrict__ q, const KV* __restrict__ meta,
 
 __global__ void __launch_bounds__(kSelNT)
 select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens, int H, int G,
-              int Hkv, int U, int ps, int max_pages, int budget, int32_t* __restrict__ sel,
-              float* __restrict__ sel_ub) {
+              int Hkv, int U, int ps, int max_pages, int ldu, int budget,
+              int32_t* __restrict__ sel, float* __restrict__ sel_ub) {
   constexpr int NW = kSelNT / kWave;
-  __shared__ uint32_t sord[kSelLds];
-  __shared__ int hist[256];
-  __shared__ unsigned int ured[NW];
+  constexpr int UNR = 4;  // 16-byte loads in flight per thread
+  __shared__ __align__(16) uint32_t sord[kSelLds];
+  __shared__ int hist[2][256];
+  __shared__ unsigned int ured[NW][2];
   __shared__ int wcnt[NW][2];
-  __shared__ int bc[2];
+  __shared__ int bc[3];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int u = blockIdx.x % U, hh = blockIdx.x / U;
@@ -124,37 +137,76 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   const int bh = b * H + g * G + hh;
   const int L = clamp_len(seq_lens[b], max_pages * ps);
   const int P = (L + ps - 1) / ps;
-  const float* row = ub + (size_t)bh * max_pages;
+  const float* row = ub + (size_t)bh * ldu;
   int32_t* out = sel + (size_t)bh * budget;
   float* out_ub = sel_ub ? sel_ub + (size_t)bh * budget : nullptr;
 
   if (P <= budget) {
     for (int i = tid; i < budget; i += kSelNT) {
       out[i] = i < P ? i : -1;
-      if (out_ub) out_ub[i] = i < P ? row[i] : -__builtin_inff();
+      if (out_ub) out_ub[i] = i < P ? row[i] + 0.0f : -__builtin_inff();
     }
     return;
   }
 
-  // Order-preserving 32-bit keys; staged in LDS when they fit.
+  // Order-preserving 32-bit keys, handled four at a time (rows are padded to
+  // a multiple of 4 floats; a quad's entries at or past P are masked). They
+  // are staged in LDS when they fit, else re-read from the bounds row.
   const bool staged = P <= kSelLds;
-  if (staged) {
-    for (int i = tid; i < P; i += kSelNT) sord[i] = float_order(row[i] + 0.0f);
-    __syncthreads();
-  }
-  auto ord = [&](int i) -> uint32_t { return staged ? sord[i] : float_order(row[i] + 0.0f); };
+  const int n4 = (P + 3) >> 2;
+  const float4* row4 = reinterpret_cast<const float4*>(row);
+  auto from_global = [&](int i4) -> uint4 {
+    const float4 f = row4[i4];
+    return make_uint4(float_order(f.x + 0.0f), float_order(f.y + 0.0f), float_order(f.z + 0.0f),
+                      float_order(f.w + 0.0f));
+  };
+  auto quad = [&](int i4) -> uint4 {
+    return staged ? *reinterpret_cast<const uint4*>(&sord[4 * i4]) : from_global(i4);
+  };
+  auto at = [](const uint4& v, int e) -> uint32_t {
+    return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+  };
 
   uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int i = tid; i < P; i += kSelNT) {
-    const uint32_t o = ord(i);
-    mn = min(mn, o);
-    mx = max(mx, o);
+  for (int base = 0; base < n4; base += UNR * kSelNT) {
+    uint4 v[UNR] = {};
+#pragma unroll
+    for (int r = 0; r < UNR; ++r) {
+      const int i4 = base + r * kSelNT + tid;
+      if (i4 < n4) v[r] = from_global(i4);
+    }
+#pragma unroll
+    for (int r = 0; r < UNR; ++r) {
+      const int i4 = base + r * kSelNT + tid;
+      if (i4 < n4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (4 * i4 + e < P) {
+            mn = min(mn, at(v[r], e));
+            mx = max(mx, at(v[r], e));
+          }
+        }
+        if (staged) *reinterpret_cast<uint4*>(&sord[4 * i4]) = v[r];
+      }
+    }
   }
-  mn = block_reduce<kSelNT>(mn, ured, [](uint32_t a, uint32_t c) { return min(a, c); });
-  mx = block_reduce<kSelNT>(mx, ured, [](uint32_t a, uint32_t c) { return max(a, c); });
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (lane == 0) {
+    ured[wave][0] = mn;
+    ured[wave][1] = mx;
+  }
+  hist[0][tid] = 0;  // kSelNT == 256 bins
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mn = min(mn, ured[w][0]);
+    mx = max(mx, ured[w][1]);
+  }
 
   // Radix select of the budget-th largest key, 8 bits per pass from the
-  // highest bit where keys differ; stop once the boundary digit is taken whole.
+  // highest bit where keys differ; stop once the boundary digit is taken
+  // whole. Two histograms alternate so that a pass needs two barriers.
   uint32_t prefix, pmask;
   int k = budget;  // rank still to place among keys matching the prefix
   if (mn == mx) {
@@ -164,15 +216,29 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
     int hb = 31 - __clz(mn ^ mx);
     pmask = ~((2u << hb) - 1u);
     prefix = mx & pmask;
+    int cur = 0;
     while (true) {
       const int lo = hb >= 7 ? hb - 7 : 0;
       const int width = hb - lo + 1;
       const uint32_t dmask = (1u << width) - 1u;
-      hist[tid] = 0;  // kSelNT == 256 bins
-      __syncthreads();
-      for (int i = tid; i < P; i += kSelNT) {
-        const uint32_t o = ord(i);
-        if ((o & pmask) == prefix) atomicAdd(&hist[(o >> lo) & dmask], 1);
+      hist[cur ^ 1][tid] = 0;
+      for (int base = 0; base < n4; base += UNR * kSelNT) {
+        uint4 v[UNR] = {};
+#pragma unroll
+        for (int r = 0; r < UNR; ++r) {
+          const int i4 = base + r * kSelNT + tid;
+          if (i4 < n4) v[r] = quad(i4);
+        }
+#pragma unroll
+        for (int r = 0; r < UNR; ++r) {
+          const int i4 = base + r * kSelNT + tid;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t o = at(v[r], e);
+            if (i4 < n4 && 4 * i4 + e < P && (o & pmask) == prefix)
+              atomicAdd(&hist[cur][(o >> lo) & dmask], 1);
+          }
+        }
       }
       __syncthreads();
       if (wave == 0) {
@@ -180,7 +246,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
         int s = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          c4[i] = hist[4 * lane + i];
+          c4[i] = hist[cur][4 * lane + i];
           s += c4[i];
         }
         int suf = s;  // keys in this lane's bins and above
@@ -196,6 +262,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
             if (above < k && k <= above + c4[i]) {
               bc[0] = 4 * lane + i;
               bc[1] = above;
+              bc[2] = c4[i];
             }
             above += c4[i];
           }
@@ -203,30 +270,45 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
       }
       __syncthreads();
       const int d = bc[0];
-      const int cnt_d = hist[d];
+      const int cnt_d = bc[2];
       k -= bc[1];
       prefix |= ((uint32_t)d) << lo;
       pmask |= dmask << lo;
       if (cnt_d == k || lo == 0) break;
       hb = lo - 1;
-      __syncthreads();
+      cur ^= 1;
     }
   }
 
   // Keep keys above the prefix and the first k (by page index) equal to it,
-  // written in ascending page order. Wave w owns a contiguous page range and
-  // walks it 64 pages at a time (consecutive LDS words, no bank conflicts).
-  const int span = ((P + NW * kWave - 1) / (NW * kWave)) * kWave;
-  const int j0 = min(P, wave * span), j1 = min(P, j0 + span);
-  const uint64_t ltm = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  // written in ascending page order. Wave w owns a contiguous range of quads
+  // and walks it 64 quads at a time: page 4*i4+e comes after every page of
+  // lower lanes and after entries e' < e of its own lane.
+  const int spq = ((n4 + NW * kWave - 1) / (NW * kWave)) * kWave;
+  const int q0 = min(n4, wave * spq), q1 = min(n4, q0 + spq);
+  const uint64_t ltm = lanemask_below(lane);
   int n_eq = 0, n_gt = 0;
-  for (int base = j0; base < j1; base += kWave) {
-    const int j = base + lane;
-    uint32_t m = 0;
-    if (j < j1) m = ord(j) & pmask;
-    n_eq += __popcll(__ballot(j < j1 && m == prefix));
-    n_gt += __popcll(__ballot(j < j1 && m > prefix));
+  for (int base = q0; base < q1; base += UNR * kWave) {
+    uint4 v[UNR] = {};
+#pragma unroll
+    for (int r = 0; r < UNR; ++r) {
+      const int i4 = base + r * kWave + lane;
+      if (i4 < q1) v[r] = quad(i4);
+    }
+#pragma unroll
+    for (int r = 0; r < UNR; ++r) {
+      const int i4 = base + r * kWave + lane;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = i4 < q1 && 4 * i4 + e < P;
+        const uint32_t m = at(v[r], e) & pmask;
+        n_eq += (valid && m == prefix) ? 1 : 0;
+        n_gt += (valid && m > prefix) ? 1 : 0;
+      }
+    }
   }
+  n_eq = wave_sum(n_eq);
+  n_gt = wave_sum(n_gt);
   if (lane == 0) {
     wcnt[wave][0] = n_eq;
     wcnt[wave][1] = n_gt;
@@ -238,23 +320,54 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
     sel_base += wcnt[w][1] + max(0, min(e, k - eq_base));
     eq_base += e;
   }
-  for (int base = j0; base < j1; base += kWave) {
-    const int j = base + lane;
-    uint32_t m = 0;
-    if (j < j1) m = ord(j) & pmask;
-    const bool eq = j < j1 && m == prefix;
-    const bool gt = j < j1 && m > prefix;
-    const uint64_t beq = __ballot(eq);
-    const int rank = eq_base + __popcll(beq & ltm);
-    const bool take = gt || (eq && rank < k);
-    const uint64_t bt = __ballot(take);
-    if (take) {
-      const int pos = sel_base + __popcll(bt & ltm);
-      out[pos] = j;
-      if (out_ub) out_ub[pos] = row[j] + 0.0f;
+  for (int base = q0; base < q1; base += UNR * kWave) {
+    uint4 v[UNR] = {};
+#pragma unroll
+    for (int r = 0; r < UNR; ++r) {
+      const int i4 = base + r * kWave + lane;
+      if (i4 < q1) v[r] = quad(i4);
     }
-    eq_base += __popcll(beq);
-    sel_base += __popcll(bt);
+#pragma unroll
+    for (int r = 0; r < UNR; ++r) {
+      const int i4 = base + r * kWave + lane;
+      bool eq[4], gt[4];
+      uint64_t beq[4];
+      int eq_below = 0;  // equal keys on lower lanes of this step
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = i4 < q1 && 4 * i4 + e < P;
+        const uint32_t m = at(v[r], e) & pmask;
+        eq[e] = valid && m == prefix;
+        gt[e] = valid && m > prefix;
+        beq[e] = __ballot(eq[e]);
+        eq_below += __popcll(beq[e] & ltm);
+      }
+      bool take[4];
+      int own_eq = 0;
+      uint64_t btk[4];
+      int tk_below = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        take[e] = gt[e] || (eq[e] && eq_base + eq_below + own_eq < k);
+        own_eq += eq[e] ? 1 : 0;
+        btk[e] = __ballot(take[e]);
+        tk_below += __popcll(btk[e] & ltm);
+      }
+      int pos = sel_base + tk_below;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (take[e] && pos < budget) {
+          out[pos] = 4 * i4 + e;
+          if (out_ub) out_ub[pos] = order_float(at(v[r], e));
+          ++pos;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        eq_base += __popcll(beq[e]);
+        sel_base += __popcll(btk[e]);
+      }
+    }
   }
 }
 
@@ -262,13 +375,11 @@ template <typename KV, int D, int G>
 static hipError_t launch_bounds_t(const LaunchShape& s, const float* q, const void* meta,
                                   const int32_t* bt, const int32_t* lens, float* ub,
                                   hipStream_t st) {
-  constexpr int LP = D / (16 / sizeof(KV));
-  constexpr int PPW = (256 / LP) * kBoundSteps;
   const int U = s.batch * s.num_kv_heads;
-  const int chunks = (s.max_pages + PPW - 1) / PPW;
+  const int chunks = (s.max_pages + kBoundPages - 1) / kBoundPages;
   hipLaunchKernelGGL((bounds_kernel<KV, D, G>), dim3(U * chunks), dim3(256), 0, st, q,
                      static_cast<const KV*>(meta), bt, lens, ub, s.num_q_heads, s.num_kv_heads,
-                     s.page_size, s.max_pages, s.num_phys, U);
+                     s.page_size, s.max_pages, s.num_phys, U, ub_ld(s.max_pages));
   return hipGetLastError();
 }
 
@@ -298,13 +409,14 @@ hipError_t launch_select(const LaunchShape& s, const float* ub, const int32_t* l
                          int32_t* sel, float* sel_ub, hipStream_t st) {
   const int U = s.batch * s.num_kv_heads;
   hipLaunchKernelGGL(select_kernel, dim3(U * s.group), dim3(kSelNT), 0, st, ub, lens,
-                     s.num_q_heads, s.group, s.num_kv_heads, U, s.page_size, s.max_pages, budget,
+                     s.num_q_heads, s.group, s.num_kv_heads, U, s.page_size, s.max_pages,
+                     ub_ld(s.max_pages), budget,
                      sel, sel_ub);
   return hipGetLastError();
 }
 
 size_t select_ws_bytes(const LaunchShape& s) {
-  return (size_t)s.batch * s.num_q_heads * s.max_pages * sizeof(float);
+  return (size_t)s.batch * s.num_q_heads * ub_ld(s.max_pages) * sizeof(float);
 }
 
 }  // namespace ekv

@@ -132,3 +132,30 @@ def test_binding_rejects_host_tensors(ek):
                                     torch.zeros(1, 4, dtype=torch.int32),
                                     torch.zeros(1, dtype=torch.int32),
                                     torch.zeros(4, 1, 2, 128, dtype=torch.bfloat16))
+
+
+def test_alignment_checks(ek):
+    """Pointers the kernels read with 16-byte loads must be 16-byte aligned,
+    the workspace 256-byte aligned; anything else is rejected up front."""
+    s = shape(ek)
+    d = ctypes.c_void_p(256)
+    mis8 = ctypes.c_void_p(256 + 8)      # 8-byte aligned only
+    mis16 = ctypes.c_void_p(256 + 16)    # 16-byte aligned, not 256
+    big = 1 << 40
+    assert ek.lib.entmaxkv_build_page_meta(ctypes.byref(s), mis8, d, d, d, None, None) == -1
+    assert ek.lib.entmaxkv_build_page_meta(ctypes.byref(s), d, d, d, mis8, None, None) == -1
+    assert ek.lib.entmaxkv_score_select(ctypes.byref(s), mis8, d, d, d, 82, d, None, d, big,
+                                        None, None) == -1
+    assert ek.lib.entmaxkv_score_select(ctypes.byref(s), d, mis8, d, d, 82, d, None, d, big,
+                                        None, None) == -1
+    assert ek.lib.entmaxkv_score_select(ctypes.byref(s), d, d, d, d, 82, d, None, mis16, big,
+                                        None, None) == -1
+    for args in ((mis8, d, d), (d, mis8, d), (d, d, mis8)):
+        assert ek.lib.entmaxkv_decode_full(ctypes.byref(s), *args, d, d, 1.5, d, None, None, d,
+                                           big, None, None) == -1
+        assert ek.lib.entmaxkv_decode_sparse(ctypes.byref(s), *args, d, d, d, 82, 1.5, d, None,
+                                             None, d, big, None, None) == -1
+    assert ek.lib.entmaxkv_decode_full(ctypes.byref(s), d, d, d, d, d, 1.5, d, None, None, mis16,
+                                       big, None, None) == -1
+    assert ek.lib.entmaxkv_decode_sparse(ctypes.byref(s), d, d, d, d, d, d, 82, 1.5, d, None,
+                                         None, mis16, big, None, None) == -1
