@@ -69,7 +69,9 @@ float window_of(float alpha) {
 
 int score_lds_ok(const LaunchShape& s, const SplitPlan& p, bool sparse, int budget) {
   const size_t total = score_lds_layout(s.group, s.page_size, p.pages_per_split, sparse,
-                                        s.max_pages, budget, score_bytes(s.bf16)).total;
+                                        s.max_pages, budget, score_bytes(s.bf16),
+                                        score_kbuf_bytes(s.bf16, s.page_size, s.head_dim, sparse))
+                           .total;
   return total <= kMaxScoreLds ? ENTMAXKV_OK : ENTMAXKV_ERR_UNSUPPORTED;
 }
 
@@ -89,7 +91,9 @@ namespace ekv {
 // float32 caches and many heads per KV head need shorter splits.
 static int fit_pps(const LaunchShape& s, int pps, bool sparse, int budget) {
   while (pps > 1 && score_lds_layout(s.group, s.page_size, pps, sparse, s.max_pages, budget,
-                                     score_bytes(s.bf16)).total > kMaxScoreLds)
+                                     score_bytes(s.bf16),
+                                     score_kbuf_bytes(s.bf16, s.page_size, s.head_dim, sparse))
+                            .total > kMaxScoreLds)
     pps /= 2;
   return pps;
 }
@@ -143,6 +147,11 @@ DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p) {
   o = align256(o + bh * p.regions * zb);
   w.list = o;
   o = align256(o + bh * (size_t)p.list_cap * (zb + 4));
+  // score-kernel spill areas: one per (head, workgroup, wave), each holding
+  // every token the wave streams
+  const size_t wcap = (size_t)((p.pages_per_split + kNW - 1) / kNW) * s.page_size;
+  w.spill = o;
+  o = align256(o + bh * p.splits * (size_t)kNW * wcap * cand_bytes(s.bf16));
   w.total = o;
   return w;
 }

@@ -7,7 +7,7 @@
 //
 // score_kernel (one workgroup per (page split, sequence, KV head)):
 //   Streams the split's K pages once for the G query heads of the KV head.
-//   A token row is spread over LT lanes, each holding two 16-byte chunks; the
+//   A token row is spread over LT lanes, each holding NCH 16-byte chunks; the
 //   G partial dot products finish in a multi-value butterfly. Only tokens that
 //   can be in the support are kept: every token with p > 0 has
 //   z > max(z) - 1/(alpha-1) (at tau = (alpha-1) max z - 1 the top token alone
@@ -79,6 +79,31 @@ __device__ __forceinline__ float neg_inf<float>() {
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Matrix-core operand types (v_mfma_f32_16x16x32_bf16): lane l holds
+// A[l % 16][(l / 16) * 8 + j] and B[(l / 16) * 8 + j][l % 16] for j < 8, and
+// D[(l / 16) * 4 + i][l % 16] for i < 4.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 bits of x rounded to nearest even (x finite).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Part `part` (0, 1, 2; 0 bits otherwise) of the exact split
+// x = p0 + p1 + p2 into bf16 values: p0 = rne(x), p1 = rne(x - p0),
+// p2 = x - p0 - p1. Each remainder is exact in float32 and the last one has
+// at most 8 significant bits, so it is itself a bf16 value.
+__device__ __forceinline__ uint32_t bf16_part(float x, int part) {
+  const uint32_t p0 = bf16_rne_bits(x);
+  const float r1 = x - __uint_as_float(p0 << 16);
+  const uint32_t p1 = bf16_rne_bits(r1);
+  const float r2 = r1 - __uint_as_float(p1 << 16);
+  const uint32_t p2 = bf16_rne_bits(r2);
+  return part == 0 ? p0 : (part == 1 ? p1 : (part == 2 ? p2 : 0u));
+}
 
 __device__ __forceinline__ uint4 stream_load16(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -164,6 +189,58 @@ __device__ int build_slice(const int32_t* __restrict__ sel, const int32_t* __res
   return n_slice;
 }
 
+// Candidate lists of the score kernel: a wave appends the survivors of each
+// head in page order; the first kListSlots of them stay in LDS, the rest go
+// to the wave's spill area in global memory (only when scores are nearly
+// uniform does a wave keep more).
+template <typename Acc>
+struct CandLists {
+  Acc* rz;              // LDS scores  [wave][head][kListSlots]
+  int* ri;              // LDS indices [wave][head][kListSlots]
+  Cand<Acc>* spill;     // this workgroup's spill areas [wave][head][wcap]
+  int wcap;
+  __device__ __forceinline__ void put(int wave, int h, int G, int pos, Acc z, int idx) const {
+    if (pos < kListSlots) {
+      const int o = (wave * G + h) * kListSlots + pos;
+      rz[o] = z;
+      ri[o] = idx;
+    } else {
+      Cand<Acc> cv;
+      cv.z = z;
+      cv.idx = idx;
+      spill[(size_t)(wave * G + h) * wcap + (pos - kListSlots)] = cv;
+    }
+  }
+  __device__ __forceinline__ void get(int wave, int h, int G, int pos, Acc& z, int& idx) const {
+    if (pos < kListSlots) {
+      const int o = (wave * G + h) * kListSlots + pos;
+      z = rz[o];
+      idx = ri[o];
+    } else {
+      const Cand<Acc> cv = spill[(size_t)(wave * G + h) * wcap + (pos - kListSlots)];
+      z = cv.z;
+      idx = cv.idx;
+    }
+  }
+};
+
+// Direct-to-LDS 16-byte streaming load: lane i of the wave writes the 16
+// bytes at its `src` to LDS bytes [16i, 16i + 16) past `lds` (uniform across
+// the wave). Marked non-temporal (cache-policy bit 2): the data is read
+// once, and without the hint these loads stream at well under HBM speed.
+// Counted by vmcnt like any vector-memory load.
+__device__ __forceinline__ void lds_load16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 2);
+}
+
+// s_waitcnt that waits until at most n vector-memory operations of this wave
+// are outstanding (other counters left alone); n < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((((N >> 4) & 3) << 14) | (0xF << 8) | (0x7 << 4) | (N & 15));
+}
+
 template <typename KV, int D, int G, int PS, bool SPARSE>
 __global__ void __launch_bounds__(kNT)
 score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
@@ -171,22 +248,16 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
              const int32_t* __restrict__ sel, int H, int Hkv, int U, int max_pages, int num_phys,
              int budget, int pps, int splits, int cap, double window_d,
              Cand<typename KvTraits<KV>::Acc>* __restrict__ cand, int* __restrict__ counts,
-             typename KvTraits<KV>::Acc* __restrict__ maxima) {
+             typename KvTraits<KV>::Acc* __restrict__ maxima,
+             Cand<typename KvTraits<KV>::Acc>* __restrict__ spill) {
   using Tr = KvTraits<KV>;
   using Acc = typename Tr::Acc;  // also the score type
+  constexpr bool MFMA = kMfmaScores && sizeof(KV) == 2;
   const Acc window = (Acc)window_d;
-  constexpr int VPC = Tr::VPC;
-  constexpr int LT = D / (2 * VPC);  // lanes per token row
-  constexpr int RW = kWave / LT;     // rows per wave step
-  static_assert(PS % RW == 0, "page must hold whole wave steps");
-  constexpr int STEPS = PS / RW;
-  using BF = Butterfly<G, LT>;
-  constexpr int CNT = BF::CNT;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc));
-  Acc* rz = reinterpret_cast<Acc*>(smem + lay.rz);
-  int* ri = reinterpret_cast<int*>(smem + lay.ri);
+  const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc),
+                                        score_kbuf_bytes(sizeof(KV) == 2, PS, D, SPARSE));
   Acc* wmax = reinterpret_cast<Acc*>(smem + lay.wmax);
   int* wcnt = reinterpret_cast<int*>(smem + lay.wcnt);
   int* slice = reinterpret_cast<int*>(smem + lay.slice);
@@ -201,6 +272,11 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
   const int L = clamp_len(seq_lens[b], max_pages * PS);
   const int P = (L + PS - 1) / PS;
   const int bh0 = b * H + g * G;
+  const CandLists<Acc> lists{reinterpret_cast<Acc*>(smem + lay.rz),
+                             reinterpret_cast<int*>(smem + lay.ri),
+                             spill + (size_t)(b * Hkv + g) * splits * kNW * G * lay.wcap +
+                                 (size_t)split * kNW * G * lay.wcap,
+                             lay.wcap};
 
   const int n_slice = build_slice<G, SPARSE>(
       sel, block_table, b, bh0, budget, P, max_pages, split, pps,
@@ -216,130 +292,319 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
   }
 
   const uint64_t ltm = lanemask_below(lane);
-  const int c = lane % LT;
-  const int rsub = lane / LT;
-  Acc qv[G][2 * VPC];
+  if constexpr (MFMA) {
+    // Matrix-core scores. Each wave streams its pages into its own two LDS
+    // page buffers with direct-to-LDS 16-byte loads: every load instruction
+    // reads 1 KiB of the page contiguously, and lane i of it writes LDS bytes
+    // [16i, 16i + 16); the lanes' source chunks are permuted within each row
+    // (chunk c of row r sits in slot c ^ swz(r)) so that the operand reads
+    // below hit distinct LDS banks. z for 16 tokens x 4 heads is a chain of
+    // v_mfma_f32_16x16x32_bf16 over head_dim: A rows are (head, part) =
+    // 4 * head + part with q split exactly into three bf16 parts, B columns
+    // are the 16 token rows of a page tile. Lane l ends with head l/16's three
+    // part sums for token l%16 and adds them.
+    constexpr int KS = D / 32;        // k-steps of 32 dims
+    constexpr int NMB = (G + 3) / 4;  // blocks of 4 heads
+    constexpr int TILES = PS / 16;    // 16-token tiles per page
+    constexpr int RB = D * 2;         // bytes per K row
+    constexpr int PB = PS * RB;       // bytes per page
+    constexpr int NI = PB / 1024;     // 1 KiB load instructions per page
+    constexpr int RPI = 1024 / RB;    // rows per load instruction
+    constexpr int CPR = RB / 16;      // 16-byte chunks per row
+    static_assert(NI >= 1 && NI * 1024 == PB && CPR * 16 == RB, "page tiling");
+    auto swz = [](int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & (CPR - 1)); };
+    const int kgrp = lane >> 4, tok = lane & 15;
+    constexpr int NBUF = score_kbuf_pages(SPARSE);
+    unsigned char* kbuf = smem + lay.kbuf + (size_t)wave * NBUF * PB;
+
+    // A operand: lane l holds row l%16 = (head, part) and dims
+    // ks*32 + (l/16)*8 .. +8; q is read with unconditional 16-byte loads
+    // (rows past the group read head 0 and are zeroed).
+    bf16x8 qa[NMB][KS];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float* qh = q + (size_t)(bh0 + h) * D;
+    for (int blk = 0; blk < NMB; ++blk) {
+      const int h = blk * 4 + ((lane & 15) >> 2), part = lane & 3;
+      const bool live = h < G && part < 3;
+      const float* qh = q + (size_t)(bh0 + (h < G ? h : 0)) * D + kgrp * 8;
+      float4 qv[KS][2];
 #pragma unroll
-    for (int e = 0; e < VPC; ++e) {
-      qv[h][e] = (Acc)qh[c * VPC + e];
-      qv[h][VPC + e] = (Acc)qh[D / 2 + c * VPC + e];
+      for (int ks = 0; ks < KS; ++ks) {
+        qv[ks][0] = *reinterpret_cast<const float4*>(qh + ks * 32);
+        qv[ks][1] = *reinterpret_cast<const float4*>(qh + ks * 32 + 4);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const float x[8] = {qv[ks][0].x, qv[ks][0].y, qv[ks][0].z, qv[ks][0].w,
+                            qv[ks][1].x, qv[ks][1].y, qv[ks][1].z, qv[ks][1].w};
+        uint32_t w[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t lo = live ? bf16_part(x[2 * jj], part) : 0u;
+          const uint32_t hi = live ? bf16_part(x[2 * jj + 1], part) : 0u;
+          w[jj] = lo | (hi << 16);
+        }
+        qa[blk][ks] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      }
     }
-  }
-  const int first = BF::first_index(lane);
-  const bool owner = BF::owner(lane);
-  uint64_t mymask[CNT];
+    // Source byte offset, within a page, of the chunk this lane stores in
+    // load instruction i.
+    int src_off[NI];
 #pragma unroll
-  for (int i = 0; i < CNT; ++i) {
-    mymask[i] = 0;
+    for (int i = 0; i < NI; ++i) {
+      const int r = i * RPI + lane / CPR;
+      src_off[i] = r * RB + (((lane % CPR) ^ swz(r)) * 16);
+    }
+    const uint64_t gmask = 0xffffull << (16 * kgrp);
+    Acc M[NMB];
+    int mycnt[NMB];
+#pragma unroll
+    for (int blk = 0; blk < NMB; ++blk) {
+      M[blk] = neg_inf<Acc>();
+      mycnt[blk] = 0;
+    }
+    // Page pp into buffer `bsel` (an invalid physical page, or a page past
+    // the slice, reads page 0 of the pool; its scores are dropped). The loads
+    // are issued on every path, so the waits below count them exactly.
+    auto issue = [&](int pp, int bsel) {
+      const int ph = pp < n_slice ? sphys[pp] : 0;
+      const bool okp = ph >= 0 && ph < num_phys;
+      const unsigned char* base = reinterpret_cast<const unsigned char*>(
+          k_pool + ((size_t)(okp ? ph : 0) * Hkv + g) * (size_t)PS * D);
+      unsigned char* dst = kbuf + bsel * PB;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        lds_load16(base + src_off[i], dst + i * 1024);
+    };
+    auto score_page = [&](int p, int bsel) {
+      const int j = SPARSE ? slice[p] : split * pps + p;
+      const int phys = sphys[p];
+      const int nvalid = (phys >= 0 && phys < num_phys) ? min(PS, L - j * PS) : 0;
+      int myslot[NMB];
+#pragma unroll
+      for (int blk = 0; blk < NMB; ++blk) {
+        const int h = blk * 4 + kgrp;
+        if constexpr (SPARSE) {
+          int v = -1;
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh)
+            if (hh == h) v = slots[p * G + hh];
+          myslot[blk] = v;
+        } else {
+          myslot[blk] = h < G ? j : -1;
+        }
+      }
+      const unsigned char* src = kbuf + bsel * PB;
+      Acc zz[TILES][NMB];
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        const int row = t * 16 + tok;
+        bf16x8 kv[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kv[ks] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const uint4*>(
+                          src + row * RB + (((ks * 4 + kgrp) ^ swz(row)) * 16)));
+#pragma unroll
+        for (int blk = 0; blk < NMB; ++blk) {
+          f32x4 cacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[blk][ks], kv[ks], cacc, 0, 0, 0);
+          const bool ok = row < nvalid && myslot[blk] >= 0;
+          zz[t][blk] = ok ? (cacc[0] + cacc[1]) + cacc[2] : neg_inf<Acc>();
+        }
+      }
+#pragma unroll
+      for (int blk = 0; blk < NMB; ++blk) {
+        Acc pm = zz[0][blk];
+#pragma unroll
+        for (int t = 1; t < TILES; ++t) pm = max(pm, zz[t][blk]);
+        pm = max(pm, partner<1>(pm));
+        pm = max(pm, partner<2>(pm));
+        pm = max(pm, partner<4>(pm));
+        pm = max(pm, partner<8>(pm));
+        M[blk] = max(M[blk], pm);
+        const Acc thr = M[blk] - window;
+        const int h = blk * 4 + kgrp;
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          const Acc z = zz[t][blk];
+          const bool f = z > neg_inf<Acc>() && z >= thr;
+          const uint64_t bal = __ballot(f);
+          if (f)
+            lists.put(wave, h, G, mycnt[blk] + __popcll(bal & gmask & ltm), z,
+                      myslot[blk] * PS + t * 16 + tok);
+          mycnt[blk] += __popcll(bal & gmask);
+        }
+      }
+    };
+    if constexpr (NBUF == 2) {
+      // Two page buffers alternate, each refilled as soon as its page has
+      // been read, so two pages are in flight while one is scored. Before a
+      // buffer is read, only the other buffer's NI loads may be outstanding.
+      issue(wave, 0);
+      issue(wave + kNW, 1);
+      for (int p = wave; p < n_slice; p += 2 * kNW) {
+        wait_vmcnt<NI>();
+        score_page(p, 0);
+        issue(p + 2 * kNW, 0);
+        if (p + kNW >= n_slice) break;
+        wait_vmcnt<NI>();
+        score_page(p + kNW, 1);
+        issue(p + 3 * kNW, 1);
+      }
+      wait_vmcnt<0>();  // no load into LDS is left in flight
+    } else {
+      // One buffer: short slices (the sparse path) keep more workgroups
+      // resident instead.
+      for (int p = wave; p < n_slice; p += kNW) {
+        issue(p, 0);
+        wait_vmcnt<0>();
+        score_page(p, 0);
+      }
+    }
+#pragma unroll
+    for (int blk = 0; blk < NMB; ++blk) {
+      const int h = blk * 4 + kgrp;
+      if (tok == 0 && h < G) {
+        wmax[wave * G + h] = M[blk];
+        wcnt[wave * G + h] = mycnt[blk];
+      }
+    }
+  } else {
+    // Vector-ALU scores: a token row is spread over LT lanes, each holding
+    // NCH 16-byte chunks; the G partial dot products finish in a multi-value
+    // butterfly.
+    constexpr int VPC = Tr::VPC;
+    constexpr int NCH = kScoreChunks;
+    constexpr int LT = D / (NCH * VPC);  // lanes per token row
+    constexpr int RW = kWave / LT;       // rows per wave step
+    static_assert(PS % RW == 0, "page must hold whole wave steps");
+    constexpr int STEPS = PS / RW;
+    using BF = Butterfly<G, LT>;
+    constexpr int CNT = BF::CNT;
+    const int c = lane % LT;
+    const int rsub = lane / LT;
+    Acc qv[G][NCH][VPC];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const uint64_t m = __ballot(owner && (first + i) == h);
-      if (first + i == h) mymask[i] = m;
-    }
-  }
-
-  Acc M[CNT];
-  int mycnt[CNT];
+      const float* qh = q + (size_t)(bh0 + h) * D;
 #pragma unroll
-  for (int i = 0; i < CNT; ++i) {
-    M[i] = neg_inf<Acc>();
-    mycnt[i] = 0;
-  }
-
-  for (int p = wave; p < n_slice; p += kNW) {
-    const int j = SPARSE ? slice[p] : split * pps + p;
-    const int phys = sphys[p];
-    if (phys < 0 || phys >= num_phys) continue;
-    const int nvalid = min(PS, L - j * PS);
-    int myslot[CNT];
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) qv[h][ch][e] = (Acc)qh[ch * (D / NCH) + c * VPC + e];
+    }
+    const int first = BF::first_index(lane);
+    const bool owner = BF::owner(lane);
+    uint64_t mymask[CNT];
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
-      if constexpr (SPARSE) {
-        int v = -1;
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-          if (first + i == h) v = slots[p * G + h];
-        myslot[i] = v;
-      } else {
-        myslot[i] = j;
-      }
-    }
-    const KV* base = k_pool + ((size_t)phys * Hkv + g) * (size_t)PS * D;
-    uint4 xa[STEPS], xb[STEPS];
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      const KV* rp = base + (size_t)(s * RW + rsub) * D;
-      xa[s] = stream_load16(rp + c * VPC);
-      xb[s] = stream_load16(rp + D / 2 + c * VPC);
-    }
-    Acc zz[STEPS][CNT];
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      Acc fa[VPC], fb[VPC];
-      widen<KV>(xa[s], fa);
-      widen<KV>(xb[s], fb);
-      Acc acc[G];
+      mymask[i] = 0;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        Acc a0 = 0, a1 = 0;
-#pragma unroll
-        for (int e = 0; e < VPC; ++e) {
-          a0 = fma(qv[h][e], fa[e], a0);
-          a1 = fma(qv[h][VPC + e], fb[e], a1);
-        }
-        acc[h] = a0 + a1;
+        const uint64_t m = __ballot(owner && (first + i) == h);
+        if (first + i == h) mymask[i] = m;
       }
-      BF::reduce(acc, lane);
-#pragma unroll
-      for (int i = 0; i < CNT; ++i) zz[s][i] = acc[i];
     }
-    // mask invalid rows and heads that did not select this page
-    Acc pm[CNT];
+    Acc M[CNT];
+    int mycnt[CNT];
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
-      pm[i] = neg_inf<Acc>();
+      M[i] = neg_inf<Acc>();
+      mycnt[i] = 0;
+    }
+    for (int p = wave; p < n_slice; p += kNW) {
+      const int j = SPARSE ? slice[p] : split * pps + p;
+      const int phys = sphys[p];
+      if (phys < 0 || phys >= num_phys) continue;
+      const int nvalid = min(PS, L - j * PS);
+      int myslot[CNT];
+#pragma unroll
+      for (int i = 0; i < CNT; ++i) {
+        if constexpr (SPARSE) {
+          int v = -1;
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            if (first + i == h) v = slots[p * G + h];
+          myslot[i] = v;
+        } else {
+          myslot[i] = j;
+        }
+      }
+      const KV* base = k_pool + ((size_t)phys * Hkv + g) * (size_t)PS * D;
+      uint4 x[STEPS][NCH];
 #pragma unroll
       for (int s = 0; s < STEPS; ++s) {
-        const bool ok = owner && (s * RW + rsub) < nvalid && myslot[i] >= 0;
-        if (!ok) zz[s][i] = neg_inf<Acc>();
-        pm[i] = max(pm[i], zz[s][i]);
+        const KV* rp = base + (size_t)(s * RW + rsub) * D;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) x[s][ch] = stream_load16(rp + ch * (D / NCH) + c * VPC);
+      }
+      Acc zz[STEPS][CNT];
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        Acc acc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = 0;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+          Acc f[VPC];
+          widen<KV>(x[s][ch], f);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            Acc a = 0;
+#pragma unroll
+            for (int e = 0; e < VPC; ++e) a = fma(qv[h][ch][e], f[e], a);
+            acc[h] += a;
+          }
+        }
+        BF::reduce(acc, lane);
+#pragma unroll
+        for (int i = 0; i < CNT; ++i) zz[s][i] = acc[i];
+      }
+      // mask invalid rows and heads that did not select this page
+      Acc pm[CNT];
+#pragma unroll
+      for (int i = 0; i < CNT; ++i) {
+        pm[i] = neg_inf<Acc>();
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+          const bool ok = owner && (s * RW + rsub) < nvalid && myslot[i] >= 0;
+          if (!ok) zz[s][i] = neg_inf<Acc>();
+          pm[i] = max(pm[i], zz[s][i]);
+        }
+#pragma unroll
+        for (int w = LT; w < kWave; w <<= 1) pm[i] = max(pm[i], shfl_xor(pm[i], w));
+#pragma unroll
+        for (int w = 1; w < BF::DUP; w <<= 1) pm[i] = max(pm[i], shfl_xor(pm[i], w));
+        M[i] = max(M[i], pm[i]);
       }
 #pragma unroll
-      for (int w = LT; w < kWave; w <<= 1) pm[i] = max(pm[i], shfl_xor(pm[i], w));
+      for (int i = 0; i < CNT; ++i) {
+        const Acc thr = M[i] - window;
 #pragma unroll
-      for (int w = 1; w < BF::DUP; w <<= 1) pm[i] = max(pm[i], shfl_xor(pm[i], w));
-      M[i] = max(M[i], pm[i]);
+        for (int s = 0; s < STEPS; ++s) {
+          const Acc z = zz[s][i];
+          const bool f = z > neg_inf<Acc>() && z >= thr;
+          const uint64_t bal = __ballot(f);
+          if (f)
+            lists.put(wave, first + i, G, mycnt[i] + __popcll(bal & mymask[i] & ltm), z,
+                      myslot[i] * PS + s * RW + rsub);
+          mycnt[i] += __popcll(bal & mymask[i]);
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
-      const Acc thr = M[i] - window;
-      const int reg = (wave * G + first + i) * lay.wcap;
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s) {
-        const Acc z = zz[s][i];
-        const bool f = z > neg_inf<Acc>() && z >= thr;
-        const uint64_t bal = __ballot(f);
-        if (f) {
-          const int pos = mycnt[i] + __popcll(bal & mymask[i] & ltm);
-          rz[reg + pos] = z;
-          ri[reg + pos] = myslot[i] * PS + s * RW + rsub;
-        }
-        mycnt[i] += __popcll(bal & mymask[i]);
+      if (owner && rsub == 0) {
+        wmax[wave * G + first + i] = M[i];
+        wcnt[wave * G + first + i] = mycnt[i];
       }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < CNT; ++i) {
-    if (owner && rsub == 0) {
-      wmax[wave * G + first + i] = M[i];
-      wcnt[wave * G + first + i] = mycnt[i];
     }
   }
   __syncthreads();
 
+  // Workgroup pass: keep the candidates within the window of the workgroup
+  // maximum, in (wave, page) order, as this split's region of each head.
   for (int h = wave; h < G; h += kNW) {
     Acc mg = neg_inf<Acc>();
 #pragma unroll
@@ -350,15 +615,11 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
     int o = 0;
     for (int w = 0; w < kNW; ++w) {
       const int n = wcnt[w * G + h];
-      const int reg = (w * G + h) * lay.wcap;
       for (int e0 = 0; e0 < n; e0 += kWave) {
         const int e = e0 + lane;
         Acc z = neg_inf<Acc>();
         int ix = 0;
-        if (e < n) {
-          z = rz[reg + e];
-          ix = ri[reg + e];
-        }
+        if (e < n) lists.get(w, h, G, e, z, ix);
         const bool f = e < n && z >= thr;
         const uint64_t bal = __ballot(f);
         if (f) {
@@ -748,8 +1009,8 @@ hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float*
                           const DecodeWs& L, hipStream_t st) {
   using ZT = typename KvTraits<KV>::Acc;
   const int U = s.batch * s.num_kv_heads;
-  const ScoreLds lay =
-      score_lds_layout(G, PS, p.pages_per_split, SPARSE, s.max_pages, budget, sizeof(ZT));
+  const ScoreLds lay = score_lds_layout(G, PS, p.pages_per_split, SPARSE, s.max_pages, budget,
+                                        sizeof(ZT), score_kbuf_bytes(s.bf16, PS, D, SPARSE));
   auto kern = score_kernel<KV, D, G, PS, SPARSE>;
   if (lay.total > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -762,7 +1023,8 @@ hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float*
                      static_cast<const KV*>(k_pool), bt, lens, sel, s.num_q_heads,
                      s.num_kv_heads, U, s.max_pages, s.num_phys, budget, p.pages_per_split,
                      p.splits, p.cap, (double)window, reinterpret_cast<Cand<ZT>*>(w + L.cand),
-                     reinterpret_cast<int*>(w + L.counts), reinterpret_cast<ZT*>(w + L.maxima));
+                     reinterpret_cast<int*>(w + L.counts), reinterpret_cast<ZT*>(w + L.maxima),
+                     reinterpret_cast<Cand<ZT>*>(w + L.spill));
   return hipGetLastError();
 }
 

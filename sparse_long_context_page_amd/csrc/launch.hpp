@@ -21,27 +21,42 @@ constexpr int kFullTokensPerSplit = 2048;
 constexpr int kMaxSplits = 4096;  // candidate regions per head (LDS-sized in the threshold kernel)
 
 constexpr int kNT = 256;
+constexpr int kScoreChunks = 2;  // 16-byte K chunks per lane and token row in the score kernel
+constexpr bool kMfmaScores = true;  // bf16 caches: q.k on the matrix cores
 constexpr int kNW = kNT / kWave;
 constexpr int kListCap = 4096;  // threshold list entries held in LDS
 constexpr int kSupCap = 4096;   // support entries held in LDS
 constexpr int kSelCopy = 8192;  // selection ints staged in LDS by the sparse score kernel
 
 
+constexpr int kListSlots = 64;  // LDS candidate slots per (wave, head) in the score kernel
+
 // LDS layout of the score kernel (bytes), shared by host sizing and device carving.
 struct ScoreLds {
-  int wcap;  // candidate slots per (wave, head)
-  size_t rz, ri, wmax, wcnt, slice, slots, phys, tmp, bitmap, ssel, total;
+  int wcap;  // candidates one wave can produce per head: every token of its pages
+  size_t kbuf, rz, ri, wmax, wcnt, slice, slots, phys, tmp, bitmap, ssel, total;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// zbytes: bytes of one score (4 for bf16 caches, 8 for float32 caches).
+// Pages of K staged per wave on the matrix-core path: two (double-buffered)
+// for the long full-cache slices, one for the short sparse ones.
+__host__ __device__ constexpr int score_kbuf_pages(bool sparse) { return sparse ? 1 : 2; }
+// Bytes of K staging per wave on the matrix-core path, else 0.
+__host__ __device__ inline int score_kbuf_bytes(bool bf16, int ps, int head_dim, bool sparse) {
+  return (kMfmaScores && bf16) ? score_kbuf_pages(sparse) * ps * head_dim * 2 : 0;
+}
+
+// zbytes: bytes of one score (4 for bf16 caches, 8 for float32 caches);
+// kbuf_wave: score_kbuf_bytes.
 __host__ __device__ inline ScoreLds score_lds_layout(int G, int ps, int pps, bool sparse,
-                                                     int max_pages, int budget, int zbytes) {
+                                                     int max_pages, int budget, int zbytes,
+                                                     int kbuf_wave) {
   ScoreLds l;
   l.wcap = ((pps + kNW - 1) / kNW) * ps;
   size_t o = 0;
-  const size_t nreg = (size_t)kNW * G * l.wcap;
+  l.kbuf = o; o = align16(o + (size_t)kNW * kbuf_wave);
+  const size_t nreg = (size_t)kNW * G * kListSlots;
   l.rz = o; o = align16(o + nreg * zbytes);
   l.ri = o; o = align16(o + nreg * 4);
   l.wmax = o; o = align16(o + (size_t)kNW * G * zbytes);
@@ -75,7 +90,7 @@ SplitPlan plan_full(const LaunchShape& s);
 
 // Workspace carve-up of the decode calls (byte offsets, 256-aligned).
 struct DecodeWs {
-  size_t cand, counts, maxima, list, total;
+  size_t cand, counts, maxima, list, spill, total;
 };
 // Scores are kept in the accumulation precision: float for bf16 caches,
 // double for float32 caches. A candidate is (score, token index).
