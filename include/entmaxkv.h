@@ -60,7 +60,8 @@
  *
  * Supported: head_dim in {64, 128}; page_size in {16, 32, 64};
  * num_q_heads / num_kv_heads in {1, 2, 4, 8}; kv_dtype F32 or BF16;
- * max_pages_per_seq <= 262144. Anything else returns ENTMAXKV_ERR_UNSUPPORTED.
+ * max_pages_per_seq <= 262144; num_phys_pages * page_size < 2^31. Anything
+ * else returns ENTMAXKV_ERR_UNSUPPORTED.
  */
 #ifndef ENTMAXKV_H
 #define ENTMAXKV_H

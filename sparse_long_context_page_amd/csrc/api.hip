@@ -33,6 +33,8 @@ int check_shape(const entmaxkv_shape* s, LaunchShape* out) {
   if (s->kv_dtype != ENTMAXKV_F32 && s->kv_dtype != ENTMAXKV_BF16)
     return ENTMAXKV_ERR_UNSUPPORTED;
   if (s->max_pages_per_seq > kMaxPagesPerSeq) return ENTMAXKV_ERR_UNSUPPORTED;
+  // a candidate token is named by its V row, physical_page * page_size + row
+  if ((long long)s->num_phys_pages * s->page_size > 0x7fffffffLL) return ENTMAXKV_ERR_UNSUPPORTED;
   // grid sizes stay far below 2^31 blocks and byte offsets fit 64 bits
   if ((long long)s->batch * s->num_q_heads > (1LL << 24)) return ENTMAXKV_ERR_UNSUPPORTED;
   if (out) {

@@ -135,6 +135,31 @@ __device__ __forceinline__ T partner(T v) {
   }
 }
 
+// Value of v on lane `src` (uniform), for 4- and 8-byte types.
+template <typename T>
+__device__ __forceinline__ T lane_value(T v, int src) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+  } else {
+    int2 p = __builtin_bit_cast(int2, v);
+    p.x = __builtin_amdgcn_readlane(p.x, src);
+    p.y = __builtin_amdgcn_readlane(p.y, src);
+    return __builtin_bit_cast(T, p);
+  }
+}
+
+// Sum over the 64 lanes, the same value in every lane, with no LDS traffic:
+// DPP lane swaps add up each row of 16 lanes, then the four row sums are
+// read from lanes 0, 16, 32, 48 and added in a fixed order.
+template <typename T>
+__device__ __forceinline__ T wave_allsum(T v) {
+  v += partner<1>(v);
+  v += partner<2>(v);
+  v += partner<4>(v);
+  v += partner<8>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
 // Multi-value butterfly. NV partial sums v[0..NV) are spread over groups of
 // LT lanes (lane bits below log2(LT) pick the lane within a group; LT and NV
 // are powers of two). After the call each lane holds CNT = max(1, NV/LT)

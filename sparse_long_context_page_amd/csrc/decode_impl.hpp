@@ -433,7 +433,7 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
           const uint64_t bal = __ballot(f);
           if (f)
             lists.put(wave, h, G, mycnt[blk] + __popcll(bal & gmask & ltm), z,
-                      myslot[blk] * PS + t * 16 + tok);
+                      phys * PS + t * 16 + tok);
           mycnt[blk] += __popcll(bal & gmask);
         }
       }
@@ -588,7 +588,7 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
           const uint64_t bal = __ballot(f);
           if (f)
             lists.put(wave, first + i, G, mycnt[i] + __popcll(bal & mymask[i] & ltm), z,
-                      myslot[i] * PS + s * RW + rsub);
+                      phys * PS + s * RW + rsub);
           mycnt[i] += __popcll(bal & mymask[i]);
         }
       }
@@ -641,21 +641,27 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
 // ---------------------------------------------------------------------------
 // threshold and P.V
 
-// d^(m-1) for the common exponents, exp2/log2 otherwise (d > 0).
+// d^e through exp2/log2 (d > 0); kept out of line so that its registers do
+// not add to those of the loops that call it.
+__device__ __attribute__((noinline)) double pow_general(double d, double e) {
+  return exp2(e * log2(d));
+}
+
+// d^(m-1) for the common exponents, pow_general otherwise (d > 0).
 __device__ __forceinline__ double pow_m1(double d, double m, int mcode) {
   switch (mcode) {
     case 1: return 1.0;
     case 2: return d;
     case 3: return d * d;
     case 4: return d * d * d;
-    default: return exp2((m - 1.0) * log2(d));
+    default: return pow_general(d, m - 1.0);
   }
 }
 
 template <int SNT>
 __device__ __forceinline__ void scope_sum2(double& a, double& c, double* red) {
-  a = wave_sum(a);
-  c = wave_sum(c);
+  a = wave_allsum(a);
+  c = wave_allsum(c);
   if constexpr (SNT > kWave) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     if (lane == 0) {
@@ -714,6 +720,46 @@ __device__ double solve_tau(const ZT* z, int n, double am1, double m, int mcode,
 
 __device__ __forceinline__ double pow_m(double d, double m, int mcode) {
   return d * pow_m1(d, m, mcode);
+}
+
+// The safeguarded Newton iteration of solve_tau for one wave whose lanes
+// hold the list's a_i = am1 * z_i in registers (K per lane; -DBL_MAX marks an
+// empty slot), so an iteration reads no memory. Same steps and stopping rules.
+template <int K>
+__device__ double solve_tau_regs(const double (&a)[K], double am1, double m, int mcode,
+                                 double amax) {
+  (void)am1;
+  double lo = amax - 1.0, hi = amax, t = lo;
+  for (int it = 0; it < 200; ++it) {
+    double f = 0.0, fp = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const double d = a[k] - t;
+      if (d > 0.0) {
+        const double pm1 = pow_m1(d, m, mcode);
+        fp += pm1;
+        f += pm1 * d;
+      }
+    }
+    f = wave_allsum(f);
+    fp = wave_allsum(fp) * m;
+    if (f >= 1.0) lo = t;
+    else hi = t;
+    if (f == 1.0) break;
+    const double scale = fmax(1.0, fabs(t));
+    double tn = fp > 0.0 ? t + (f - 1.0) / fp : 0.5 * (lo + hi);
+    if (fp > 0.0 && fabs(tn - t) <= 2.0 * DBL_EPSILON * scale) {
+      t = fmin(fmax(tn, lo), hi);
+      break;
+    }
+    if (!(tn > lo && tn < hi)) tn = 0.5 * (lo + hi);
+    if (hi - lo <= 4.0 * DBL_EPSILON * scale) {
+      t = 0.5 * (lo + hi);
+      break;
+    }
+    t = tn;
+  }
+  return t;
 }
 
 template <typename KV, int D, bool SPARSE>
@@ -790,44 +836,43 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
   int* di;
   int n_list;
   if (n_cand <= kListCap) {
-    // Flat gather: entry i belongs to the last region whose offset is <= i.
-    // All loads are independent, so they are in flight together.
-    for (int i = tid; i < n_cand; i += kNT) {
-      int lo = 0, hi = splits;  // roff[lo] <= i < roff[hi]
+    // Gather and window filter in one pass: thread t takes the contiguous
+    // entries [t*per, t*per + per) (all of its loads in flight together),
+    // keeps those with z >= thr, and one block scan places them in order.
+    const int per = (n_cand + kNT - 1) / kNT;  // <= kListCap / kNT
+    constexpr int kMaxPer = kListCap / kNT;
+    const int e0 = min(n_cand, tid * per), e1 = min(n_cand, e0 + per);
+    Cand<ZT> v[kMaxPer];
+    int keep = 0;
+    if (e0 < e1) {
+      int lo = 0, hi = splits;  // roff[lo] <= e0 < roff[hi]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (roff[mid] <= i) lo = mid;
+        if (roff[mid] <= e0) lo = mid;
         else hi = mid;
       }
-      const Cand<ZT> v = creg[(size_t)lo * cap + (i - roff[lo])];
-      lz[i] = v.z;
-      li[i] = v.idx;
-    }
-    __syncthreads();
-    // Keep only the window, in place and in order (one wave; each chunk is
-    // read before any write, and writes never pass the read position).
-    if (wave == 0) {
-      int o = 0;
-      for (int e0 = 0; e0 < n_cand; e0 += kWave) {
-        const int e = e0 + lane;
-        ZT z = neg_inf<ZT>();
-        int ix = 0;
-        if (e < n_cand) {
-          z = lz[e];
-          ix = li[e];
+      int r = lo;
+#pragma unroll
+      for (int k = 0; k < kMaxPer; ++k) {
+        const int e = e0 + k;
+        if (e < e1) {
+          while (roff[r + 1] <= e) ++r;
+          v[k] = creg[(size_t)r * cap + (e - roff[r])];
         }
-        const bool f = e < n_cand && z >= thr;
-        const uint64_t bal = __ballot(f);
-        if (f) {
-          lz[o + __popcll(bal & ltm)] = z;
-          li[o + __popcll(bal & ltm)] = ix;
-        }
-        o += __popcll(bal);
       }
-      if (lane == 0) nb[0] = o;
+#pragma unroll
+      for (int k = 0; k < kMaxPer; ++k) keep += (e0 + k < e1 && v[k].z >= thr) ? 1 : 0;
+    }
+    int base = block_excl_scan<kNT>(keep, tmp, &n_list);
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
+      if (e0 + k < e1 && v[k].z >= thr) {
+        lz[base] = v[k].z;
+        li[base] = v[k].idx;
+        ++base;
+      }
     }
     __syncthreads();
-    n_list = nb[0];
     dz = lz;
     di = li;
   } else {
@@ -882,36 +927,30 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
   const double m = 1.0 / am1;
   const int mcode = (m == 1.0) ? 1 : (m == 2.0) ? 2 : (m == 3.0) ? 3 : (m == 4.0) ? 4 : 0;
   const double amax = am1 * (double)M;
-  if (n_list <= kWave * 4) {
-    if (wave == 0) {
-      const double t = solve_tau<kWave>(dz, n_list, am1, m, mcode, amax, lane, red);
-      if (lane == 0) tau_b = t;
-    }
-    __syncthreads();
-  } else {
-    const double t = solve_tau<kNT>(dz, n_list, am1, m, mcode, amax, tid, red);
-    if (tid == 0) tau_b = t;
-    __syncthreads();
-  }
-  const double tau = tau_b;
+  const bool list_lds = dz == lz;
 
-  // Support (a_i > tau) with p_i = (a_i - tau)^m; sum p in float64.
+  // Threshold, support (a_i > tau) with p_i = (a_i - tau)^m, sum p in float64.
+  double tau;
   int n_sup;
   double psum = 0.0;
-  const bool list_lds = dz == lz;
-  if (list_lds) {
-    // compact (idx, p) in place, in list order, by one wave
+  if (list_lds && n_list <= kWave * kRegList) {
+    // Short lists: wave 0 holds a_i = am1 * z_i in registers for the whole
+    // solve, then compacts (V row, p) in list order.
     if (wave == 0) {
+      double a[kRegList];
+#pragma unroll
+      for (int k = 0; k < kRegList; ++k) {
+        const int e = k * kWave + lane;
+        a[k] = e < n_list ? am1 * (double)lz[e] : -DBL_MAX;
+      }
+      const double t = solve_tau_regs<kRegList>(a, am1, m, mcode, amax);
       int o = 0;
-      for (int e0 = 0; e0 < n_list; e0 += kWave) {
-        const int e = e0 + lane;
-        double d = -1.0;
-        int ix = 0;
-        if (e < n_list) {
-          d = am1 * (double)lz[e] - tau;
-          ix = li[e];
-        }
-        const bool f = d > 0.0;
+#pragma unroll
+      for (int k = 0; k < kRegList; ++k) {
+        const int e = k * kWave + lane;
+        const double d = a[k] - t;
+        const bool f = e < n_list && d > 0.0;
+        const int ix = f ? li[e] : 0;
         const uint64_t bal = __ballot(f);
         if (f) {
           const double pv = pow_m(d, m, mcode);
@@ -921,43 +960,79 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
         }
         o += __popcll(bal);
       }
-      psum = wave_sum(psum);
+      psum = wave_allsum(psum);
       if (lane == 0) {
         nb[1] = o;
         red[0] = psum;
+        tau_b = t;
       }
     }
     __syncthreads();
+    tau = tau_b;
     n_sup = nb[1];
     psum = red[0];
   } else {
-    int ns = 0;
-    for (int i = tid; i < n_list; i += kNT) {
-      const double d = am1 * (double)dz[i] - tau;
-      if (d > 0.0) {
-        ++ns;
-        psum += pow_m(d, m, mcode);
+    const double t = solve_tau<kNT>(dz, n_list, am1, m, mcode, amax, tid, red);
+    if (tid == 0) tau_b = t;
+    __syncthreads();
+    tau = tau_b;
+    if (list_lds) {
+      // compact (V row, p) in place, in list order, by one wave
+      if (wave == 0) {
+        int o = 0;
+        for (int e0 = 0; e0 < n_list; e0 += kWave) {
+          const int e = e0 + lane;
+          double d = -1.0;
+          int ix = 0;
+          if (e < n_list) {
+            d = am1 * (double)lz[e] - tau;
+            ix = li[e];
+          }
+          const bool f = d > 0.0;
+          const uint64_t bal = __ballot(f);
+          if (f) {
+            const double pv = pow_m(d, m, mcode);
+            psum += pv;
+            li[o + __popcll(bal & ltm)] = ix;
+            sp[o + __popcll(bal & ltm)] = (float)pv;
+          }
+          o += __popcll(bal);
+        }
+        psum = wave_allsum(psum);
+        if (lane == 0) {
+          nb[1] = o;
+          red[0] = psum;
+        }
       }
+      __syncthreads();
+      n_sup = nb[1];
+      psum = red[0];
+    } else {
+      int ns = 0;
+      for (int i = tid; i < n_list; i += kNT) {
+        const double d = am1 * (double)dz[i] - tau;
+        if (d > 0.0) {
+          ++ns;
+          psum += pow_m(d, m, mcode);
+        }
+      }
+      double nsd = (double)ns;
+      scope_sum2<kNT>(psum, nsd, red);
+      n_sup = (int)nsd;
     }
-    double nsd = (double)ns;
-    scope_sum2<kNT>(psum, nsd, red);
-    n_sup = (int)nsd;
   }
 
+  // o = sum p v / sum p. A candidate's index is its V row,
+  // physical_page * page_size + row.
   const int grp = tid / LR, c = tid % LR;
-  const int32_t* selrow = SPARSE ? sel + (size_t)bh * budget : nullptr;
-  auto row_ptr = [&](int idx) -> const KV* {
-    const int slot = idx / PS, r = idx - slot * PS;
-    const int j = SPARSE ? selrow[slot] : slot;
-    const int phys = block_table[(size_t)b * max_pages + j];
-    if (phys < 0 || phys >= num_phys) return nullptr;
+  auto row_ptr = [&](int vrow) -> const KV* {
+    const int phys = vrow / PS, r = vrow - phys * PS;
     return v_pool + (((size_t)phys * Hkv + g) * PS + r) * D + c * VPC;
   };
   float acc[VPC];
 #pragma unroll
   for (int e = 0; e < VPC; ++e) acc[e] = 0.0f;
   auto accumulate = [&](const KV* vp, float pk) {
-    if (!vp) return;
     const uint4 x = *reinterpret_cast<const uint4*>(vp);
     typename KvTraits<KV>::Acc f[VPC];
     widen<KV>(x, f);

@@ -26,6 +26,7 @@ constexpr bool kMfmaScores = true;  // bf16 caches: q.k on the matrix cores
 constexpr int kNW = kNT / kWave;
 constexpr int kListCap = 4096;  // threshold list entries held in LDS
 constexpr int kSupCap = 4096;   // support entries held in LDS
+constexpr int kRegList = 4;     // list entries per lane kept in registers by the threshold solve
 constexpr int kSelCopy = 8192;  // selection ints staged in LDS by the sparse score kernel
 
 

@@ -187,6 +187,43 @@ def test_bitwise_determinism():
                            b.view(torch.int32) if b.dtype == torch.float32 else b)
 
 
+def test_workspace_reused_across_calls():
+    """One workspace serves many calls: repeated calls of both paths on the
+    same workspaces give the same, correct outputs."""
+    from sparse_long_context_page_amd import entmaxkv as E
+    w = synth.shrink(synth.WORKLOADS["gqa_32k"], context=3000, batch=2, n_planted=12)
+    inp = synth.generate(w, 4)
+    dev = Dev(inp)
+    dev.build_meta()
+    budget = 24
+    sel, _ = dev.select(budget)
+    ws_sp = E.workspace(dev.shape, budget, E.ENTMAXKV_WS_SPARSE, "cuda")
+    ws_fu = E.workspace(dev.shape, budget, E.ENTMAXKV_WS_FULL, "cuda")
+    announce("workspace reuse")
+    results = []
+    for it in range(3):
+        for path, ws in (("sparse", ws_sp), ("full", ws_fu)):
+            out, tau, sup = dev._outs()
+            if path == "sparse":
+                E.entmaxkv_decode_sparse(dev.shape, dev.q, dev.k, dev.v, dev.bt, dev.lens, sel,
+                                         budget, 1.5, out, tau, sup, ws=ws)
+            else:
+                E.entmaxkv_decode_full(dev.shape, dev.q, dev.k, dev.v, dev.bt, dev.lens, 1.5, out,
+                                       tau, sup, ws=ws)
+            torch.cuda.synchronize()
+            results.append((path, out.cpu(), tau.cpu(), sup.cpu()))
+    for path, out, tau, sup in results[2:]:
+        first = results[0] if path == "sparse" else results[1]
+        assert torch.equal(out, first[1]) and torch.equal(tau, first[2]) and torch.equal(sup, first[3])
+    sel_np = sel.cpu().numpy()
+    for b, h in ((0, 0), (1, 17)):
+        for path, out, tau, sup in results[:2]:
+            ref = (O.decode_sparse(inp, b, h, 1.5, sel_np[b, h]) if path == "sparse"
+                   else O.decode_full(inp, b, h, 1.5))
+            check_decode(ref, out.numpy()[b, h], tau.numpy()[b, h], sup.numpy()[b, h],
+                         w.kv_dtype, 1.5, f"reuse {path} b{b} h{h}")
+
+
 def test_invalid_selection_entries_are_ignored():
     w = synth.shrink(synth.WORKLOADS["gqa_32k"], context=1000, batch=1, n_planted=8)
     inp = synth.generate(w, 2)
