@@ -3,10 +3,12 @@
 // 2605.21649), section 2.A: the box is the lightweight per-page metadata
 // that bounds a page's best score.
 //
-// One workgroup per (logical page, sequence, KV head); the page's keys are a
-// contiguous page_size x head_dim block. Threads own one 16-byte column
-// chunk each and walk a strided subset of the rows; partial results meet in
-// LDS. min/max does no rounding, so the output is the stored key values.
+// Each lane owns one 16-byte column chunk of one (page, KV head) item and
+// walks all of the page's valid rows, so no cross-lane reduction is needed:
+// a wave covers 64 / (head_dim chunks) items at once, and the items of a
+// wave are consecutive KV heads of one page (contiguous in the pool). Rows
+// are read eight at a time with streaming loads. min/max does no rounding,
+// so the output is the stored key values.
 #include "launch.hpp"
 
 namespace ekv {
@@ -14,23 +16,26 @@ namespace ekv {
 template <typename KV, int D>
 __global__ void __launch_bounds__(256)
 meta_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_table,
-            const int32_t* __restrict__ seq_lens, KV* __restrict__ meta, int Hkv, int ps,
+            const int32_t* __restrict__ seq_lens, KV* __restrict__ meta, int B, int Hkv, int ps,
             int max_pages, int num_phys) {
   constexpr int VPC = 16 / sizeof(KV);  // values per 16-byte chunk
-  constexpr int CPR = D / VPC;          // chunks per row
-  constexpr int RG = 256 / CPR;         // row groups
-  __shared__ float smin[RG][CPR][VPC];
-  __shared__ float smax[RG][CPR][VPC];
-
-  const int j = blockIdx.x, b = blockIdx.y, g = blockIdx.z;
+  constexpr int CPR = D / VPC;          // lanes per item (chunks per row)
+  constexpr int IPW = kWave / CPR;      // items per wave
+  constexpr int RB = 8;                 // rows per batch of loads
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int c = lane % CPR;
+  const long long item = ((long long)blockIdx.x * (256 / kWave) + wave) * IPW + lane / CPR;
+  const int g = (int)(item % Hkv);
+  const long long bj = item / Hkv;
+  const int j = (int)(bj % max_pages);
+  const int b = (int)(bj / max_pages);
+  if (b >= B) return;
   const int L = clamp_len(seq_lens[b], max_pages * ps);
   if (j * ps >= L) return;
   const int phys = block_table[(size_t)b * max_pages + j];
   if (phys < 0 || phys >= num_phys) return;
   const int nv = min(ps, L - j * ps);
-
-  const int c = threadIdx.x % CPR;
-  const int r0 = threadIdx.x / CPR;
   const KV* base = k_pool + ((size_t)phys * Hkv + g) * (size_t)ps * D + c * VPC;
 
   float lo[VPC], hi[VPC];
@@ -39,68 +44,61 @@ meta_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_tab
     lo[e] = __builtin_inff();
     hi[e] = -__builtin_inff();
   }
-  for (int r = r0; r < nv; r += RG) {
-    uint4 x = *reinterpret_cast<const uint4*>(base + (size_t)r * D);
-    float f[VPC];
-    if constexpr (sizeof(KV) == 2) {
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  for (int r0 = 0; r0 < nv; r0 += RB) {
+    u32x4 x[RB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_lo(w[i]);
-        f[2 * i + 1] = bf16_hi(w[i]);
+    for (int i = 0; i < RB; ++i)
+      if (r0 + i < nv)
+        x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)(r0 + i) * D));
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if (r0 + i >= nv) break;
+      float f[VPC];
+      if constexpr (sizeof(KV) == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          f[2 * w] = bf16_lo(x[i][w]);
+          f[2 * w + 1] = bf16_hi(x[i][w]);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) f[w] = __uint_as_float(x[i][w]);
       }
-    } else {
-      f[0] = __uint_as_float(x.x);
-      f[1] = __uint_as_float(x.y);
-      f[2] = __uint_as_float(x.z);
-      f[3] = __uint_as_float(x.w);
-    }
 #pragma unroll
-    for (int e = 0; e < VPC; ++e) {
-      lo[e] = fminf(lo[e], f[e]);
-      hi[e] = fmaxf(hi[e], f[e]);
+      for (int e = 0; e < VPC; ++e) {
+        lo[e] = fminf(lo[e], f[e]);
+        hi[e] = fmaxf(hi[e], f[e]);
+      }
     }
   }
+  KV* dst = meta + ((size_t)phys * Hkv + g) * 2 * D + c * VPC;
+  uint4 o[2];
 #pragma unroll
-  for (int e = 0; e < VPC; ++e) {
-    smin[r0][c][e] = lo[e];
-    smax[r0][c][e] = hi[e];
-  }
-  __syncthreads();
-  if (threadIdx.x < 2 * CPR) {
-    const bool want_max = threadIdx.x >= CPR;
-    const int cc = threadIdx.x % CPR;
-    float acc[VPC];
-#pragma unroll
-    for (int e = 0; e < VPC; ++e) acc[e] = want_max ? smax[0][cc][e] : smin[0][cc][e];
-    const int used = min(RG, nv);
-    for (int rg = 1; rg < used; ++rg) {
-#pragma unroll
-      for (int e = 0; e < VPC; ++e)
-        acc[e] = want_max ? fmaxf(acc[e], smax[rg][cc][e]) : fminf(acc[e], smin[rg][cc][e]);
-    }
-    KV* dst = meta + (((size_t)phys * Hkv + g) * 2 + (want_max ? 1 : 0)) * D + cc * VPC;
-    uint4 o;
+  for (int side = 0; side < 2; ++side) {
+    const float* a = side ? hi : lo;
     if constexpr (sizeof(KV) == 2) {
       uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        w[i] = (__float_as_uint(acc[2 * i]) >> 16) | (__float_as_uint(acc[2 * i + 1]) & 0xffff0000u);
-      o = make_uint4(w[0], w[1], w[2], w[3]);
+        w[i] = (__float_as_uint(a[2 * i]) >> 16) | (__float_as_uint(a[2 * i + 1]) & 0xffff0000u);
+      o[side] = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
-      o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                     __float_as_uint(acc[3]));
+      o[side] = make_uint4(__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
+                           __float_as_uint(a[3]));
     }
-    *reinterpret_cast<uint4*>(dst) = o;
   }
+  *reinterpret_cast<uint4*>(dst) = o[0];
+  *reinterpret_cast<uint4*>(dst + D) = o[1];
 }
 
 template <typename KV, int D>
 static hipError_t launch_meta_t(const LaunchShape& s, const void* k_pool, const int32_t* bt,
                                 const int32_t* lens, void* meta, hipStream_t st) {
-  dim3 grid(s.max_pages, s.batch, s.num_kv_heads);
-  hipLaunchKernelGGL((meta_kernel<KV, D>), grid, dim3(256), 0, st,
-                     static_cast<const KV*>(k_pool), bt, lens, static_cast<KV*>(meta),
+  constexpr int IPB = (256 / kWave) * (kWave / (D / (16 / sizeof(KV))));  // items per block
+  const long long items = (long long)s.batch * s.max_pages * s.num_kv_heads;
+  const long long blocks = (items + IPB - 1) / IPB;
+  hipLaunchKernelGGL((meta_kernel<KV, D>), dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const KV*>(k_pool), bt, lens, static_cast<KV*>(meta), s.batch,
                      s.num_kv_heads, s.page_size, s.max_pages, s.num_phys);
   return hipGetLastError();
 }
