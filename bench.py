@@ -188,6 +188,89 @@ def _pin_blas():
 # ---------------------------------------------------------------------------
 
 
+def contained(sup_s, sup_f, tau_s, tau_f, rel: float = 1e-6) -> np.ndarray:
+    """Per (sequence, head): did the selection contain the full-cache support?
+    When it does, the sparse problem is the full one restricted to a superset
+    of the support, so tau and the support size come out the same; a missing
+    support token lowers tau and the support size."""
+    return (sup_s == sup_f) & (np.abs(tau_s - tau_f) <= rel * np.maximum(1.0, np.abs(tau_f)))
+
+
+def containment_report(args):
+    """Fraction of trials (one trial = one (sequence, query head) decode) whose
+    selected pages contain the full-cache support, for every (alpha, budget)
+    cell of the workload's sweep; sampled trials are checked against the
+    oracle's support pages."""
+    import torch
+    from oracle import entmax_oracle as O
+    from sparse_long_context_page_amd import entmaxkv as E
+    w = synth.WORKLOADS[args.workload]
+    log = lambda m: (sys.stderr.write(f"[report] {m}\n"), sys.stderr.flush())
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS[w.name])
+    log(f"generated {w.name}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kv_t = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+
+    def pool(a):
+        if w.kv_dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q = torch.from_numpy(inp["q"]).to(dev)
+    k, v = pool(inp["k_pool"]), pool(inp["v_pool"])
+    bt = torch.from_numpy(inp["block_table"]).to(dev)
+    lens = torch.from_numpy(inp["seq_lens"]).to(dev)
+    shape = E.make_shape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                         inp["max_pages"], inp["num_phys_pages"], w.kv_dtype)
+    meta = torch.empty((inp["num_phys_pages"], w.num_kv_heads, 2, w.head_dim), dtype=kv_t,
+                       device=dev)
+    E.entmaxkv_build_page_meta(shape, k, bt, lens, meta)
+    B, H, D = w.batch, w.num_q_heads, w.head_dim
+    G = H // w.num_kv_heads
+    rng = np.random.default_rng(0)
+    n_check = max(0, args.oracle_heads // (len(w.alphas) * len(w.budgets)))
+    full = {}
+    for alpha in w.alphas:
+        out = torch.empty((B, H, D), device=dev)
+        tau = torch.empty((B, H), device=dev)
+        sup = torch.empty((B, H), dtype=torch.int32, device=dev)
+        E.entmaxkv_decode_full(shape, q, k, v, bt, lens, alpha, out, tau, sup)
+        torch.cuda.synchronize()
+        full[alpha] = (tau.cpu().numpy(), sup.cpu().numpy())
+    cells = []
+    for budget in w.budgets:
+        sel = torch.empty((B, H, budget), dtype=torch.int32, device=dev)
+        E.entmaxkv_score_select(shape, q, meta, bt, lens, budget, sel)
+        torch.cuda.synchronize()
+        sel_np = sel.cpu().numpy()
+        for alpha in w.alphas:
+            out = torch.empty((B, H, D), device=dev)
+            tau = torch.empty((B, H), device=dev)
+            sup = torch.empty((B, H), dtype=torch.int32, device=dev)
+            E.entmaxkv_decode_sparse(shape, q, k, v, bt, lens, sel, budget, alpha, out, tau, sup)
+            torch.cuda.synchronize()
+            tau_f, sup_f = full[alpha]
+            c = contained(sup.cpu().numpy(), sup_f, tau.cpu().numpy(), tau_f)
+            agree = 0
+            checks = [(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(n_check)]
+            for b, h in checks:
+                res = O.decode_full(inp, b, h, alpha)
+                ref = set(O.support_pages(res, w.page_size)) <= set(int(j) for j in sel_np[b, h])
+                agree += int(ref == bool(c[b, h]))
+            cells.append({"alpha": alpha, "budget_pages": budget, "trials": int(c.size),
+                          "contained_fraction": round(float(c.mean()), 4),
+                          "mean_support_full": round(float(sup_f.mean()), 2),
+                          "oracle_checked": len(checks), "oracle_agree": agree})
+            log(f"alpha {alpha} budget {budget}: contained {c.mean():.4f}")
+    print(json.dumps({"report": "containment", "workload": w.name, "data": "synthetic",
+                      "trial": "one (sequence, query head) decode",
+                      "criterion": "selected pages contain the full-cache support (GPU: equal "
+                                   "support size and tau within 1e-6; sampled trials re-checked "
+                                   "against the oracle's support pages)",
+                      "cells": cells}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +282,10 @@ def main():
     ap.add_argument("--oracle-heads", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="hot-cache timing (diagnostic)")
+    ap.add_argument("--report", choices=["containment"], default=None,
+                    help="instead of the timed step: the alpha/budget sweep report of how often "
+                         "the selected pages contain the full-cache support (default workload "
+                         "alpha_sweep_64k); prints its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the steps, run a plain 1 GiB device copy three times (a known-size "
                          "reference for the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -208,6 +295,12 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(collectives and sharding are out of scope; see DESIGN.md).", file=sys.stderr)
         sys.exit(2)
+
+    if args.report == "containment":
+        if "--workload" not in sys.argv:
+            args.workload = "alpha_sweep_64k"
+        containment_report(args)
+        return
 
     w = synth.WORKLOADS[args.workload]
     alpha = args.alpha if args.alpha is not None else w.alphas[0]

@@ -11,7 +11,7 @@ using namespace ekv;
 namespace {
 
 constexpr int kMaxPagesPerSeq = 262144;
-constexpr size_t kMaxScoreLds = 150 * 1024;
+constexpr size_t kMaxScoreLds = kMaxScoreLdsBytes;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -164,10 +164,11 @@ namespace {
 
 hipError_t launch_score(const LaunchShape& s, const SplitPlan& p, const float* q,
                         const void* k_pool, const int32_t* bt, const int32_t* lens,
-                        const int32_t* sel, int budget, float window, void* ws,
+                        const int32_t* sel, int budget, float alpha, float window, void* ws,
                         const DecodeWs& L, hipStream_t st) {
-  return s.bf16 ? launch_score_bf16(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st)
-                : launch_score_f32(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+  return s.bf16
+             ? launch_score_bf16(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st)
+             : launch_score_f32(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
 }
 
 hipError_t launch_tau_pv(const LaunchShape& s, const SplitPlan& p, const void* v_pool,
@@ -202,8 +203,8 @@ int decode_common(const entmaxkv_shape* shape, const float* q, const void* k_poo
   const float window = window_of(alpha);
   const Events ev{events, stream};
   if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
-  if (launch_score(s, p, q, k_pool, block_table, seq_lens, sel, budget, window, ws, L, stream) !=
-      hipSuccess)
+  if (launch_score(s, p, q, k_pool, block_table, seq_lens, sel, budget, alpha, window, ws, L,
+                   stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
   if (launch_tau_pv(s, p, v_pool, block_table, seq_lens, sel, budget, alpha, window, out, tau,

@@ -6,9 +6,9 @@ namespace ekv {
 
 hipError_t launch_score_f32(const LaunchShape& s, const SplitPlan& p, const float* q,
                           const void* k_pool, const int32_t* bt, const int32_t* lens,
-                          const int32_t* sel, int budget, float window, void* ws,
+                          const int32_t* sel, int budget, float alpha, float window, void* ws,
                           const DecodeWs& L, hipStream_t st) {
-  return launch_score_kv<float>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+  return launch_score_kv<float>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
 }
 
 hipError_t launch_tau_pv_f32(const LaunchShape& s, const SplitPlan& p, const void* v_pool,

@@ -189,6 +189,169 @@ __device__ int build_slice(const int32_t* __restrict__ sel, const int32_t* __res
   return n_slice;
 }
 
+// ---------------------------------------------------------------------------
+// threshold and P.V
+
+// d^e through exp2/log2 (d > 0); kept out of line so that its registers do
+// not add to those of the loops that call it.
+__device__ __attribute__((noinline)) double pow_general(double d, double e) {
+  return exp2(e * log2(d));
+}
+
+// d^(m-1) for the common exponents, pow_general otherwise (d > 0).
+__device__ __forceinline__ double pow_m1(double d, double m, int mcode) {
+  switch (mcode) {
+    case 1: return 1.0;
+    case 2: return d;
+    case 3: return d * d;
+    case 4: return d * d * d;
+    default: return pow_general(d, m - 1.0);
+  }
+}
+
+template <int SNT>
+__device__ __forceinline__ void scope_sum2(double& a, double& c, double* red) {
+  a = wave_allsum(a);
+  c = wave_allsum(c);
+  if constexpr (SNT > kWave) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    if (lane == 0) {
+      red[2 * wid] = a;
+      red[2 * wid + 1] = c;
+    }
+    __syncthreads();
+    a = 0.0;
+    c = 0.0;
+#pragma unroll
+    for (int w = 0; w < SNT / kWave; ++w) {
+      a += red[2 * w];
+      c += red[2 * w + 1];
+    }
+    __syncthreads();
+  }
+}
+
+// Safeguarded Newton for sum_i [a_i - t]_+^m = 1 with a_i = am1 * z_i. The
+// root lies in [a_max - 1, a_max): f(a_max - 1) >= 1 (top term is 1) and
+// f(a_max) = 0. Called by the SNT threads t0 = 0..SNT-1 of the scope.
+template <int SNT, typename ZT>
+__device__ double solve_tau(const ZT* z, int n, double am1, double m, int mcode, double amax,
+                            int t0, double* red) {
+  double lo = amax - 1.0, hi = amax, t = lo;
+  for (int it = 0; it < 200; ++it) {
+    double f = 0.0, fp = 0.0;
+    for (int i = t0; i < n; i += SNT) {
+      const double d = am1 * (double)z[i] - t;
+      if (d > 0.0) {
+        const double pm1 = pow_m1(d, m, mcode);
+        fp += pm1;
+        f += pm1 * d;
+      }
+    }
+    scope_sum2<SNT>(f, fp, red);
+    fp *= m;
+    if (f >= 1.0) lo = t;
+    else hi = t;
+    if (f == 1.0) break;
+    const double scale = fmax(1.0, fabs(t));
+    double tn = fp > 0.0 ? t + (f - 1.0) / fp : 0.5 * (lo + hi);
+    if (fp > 0.0 && fabs(tn - t) <= 2.0 * DBL_EPSILON * scale) {
+      t = fmin(fmax(tn, lo), hi);
+      break;
+    }
+    if (!(tn > lo && tn < hi)) tn = 0.5 * (lo + hi);
+    if (hi - lo <= 4.0 * DBL_EPSILON * scale) {
+      t = 0.5 * (lo + hi);
+      break;
+    }
+    t = tn;
+  }
+  return t;
+}
+
+__device__ __forceinline__ double pow_m(double d, double m, int mcode) {
+  return d * pow_m1(d, m, mcode);
+}
+
+// The same safeguarded Newton iteration for the whole workgroup, each thread
+// holding K of the a_i in registers (-DBL_MAX marks an empty slot); every
+// thread of the block must call it and gets the same result.
+template <int K>
+__device__ double solve_tau_block(const double (&a)[K], double m, int mcode, double amax,
+                                  double* red) {
+  double lo = amax - 1.0, hi = amax, t = lo;
+  for (int it = 0; it < 200; ++it) {
+    double f = 0.0, fp = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const double d = a[k] - t;
+      if (d > 0.0) {
+        const double pm1 = pow_m1(d, m, mcode);
+        fp += pm1;
+        f += pm1 * d;
+      }
+    }
+    scope_sum2<kNT>(f, fp, red);
+    fp *= m;
+    if (f >= 1.0) lo = t;
+    else hi = t;
+    if (f == 1.0) break;
+    const double scale = fmax(1.0, fabs(t));
+    double tn = fp > 0.0 ? t + (f - 1.0) / fp : 0.5 * (lo + hi);
+    if (fp > 0.0 && fabs(tn - t) <= 2.0 * DBL_EPSILON * scale) {
+      t = fmin(fmax(tn, lo), hi);
+      break;
+    }
+    if (!(tn > lo && tn < hi)) tn = 0.5 * (lo + hi);
+    if (hi - lo <= 4.0 * DBL_EPSILON * scale) {
+      t = 0.5 * (lo + hi);
+      break;
+    }
+    t = tn;
+  }
+  return t;
+}
+
+// The safeguarded Newton iteration of solve_tau for one wave whose lanes
+// hold the list's a_i = am1 * z_i in registers (K per lane; -DBL_MAX marks an
+// empty slot), so an iteration reads no memory. Same steps and stopping rules.
+template <int K>
+__device__ double solve_tau_regs(const double (&a)[K], double am1, double m, int mcode,
+                                 double amax) {
+  (void)am1;
+  double lo = amax - 1.0, hi = amax, t = lo;
+  for (int it = 0; it < 200; ++it) {
+    double f = 0.0, fp = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const double d = a[k] - t;
+      if (d > 0.0) {
+        const double pm1 = pow_m1(d, m, mcode);
+        fp += pm1;
+        f += pm1 * d;
+      }
+    }
+    f = wave_allsum(f);
+    fp = wave_allsum(fp) * m;
+    if (f >= 1.0) lo = t;
+    else hi = t;
+    if (f == 1.0) break;
+    const double scale = fmax(1.0, fabs(t));
+    double tn = fp > 0.0 ? t + (f - 1.0) / fp : 0.5 * (lo + hi);
+    if (fp > 0.0 && fabs(tn - t) <= 2.0 * DBL_EPSILON * scale) {
+      t = fmin(fmax(tn, lo), hi);
+      break;
+    }
+    if (!(tn > lo && tn < hi)) tn = 0.5 * (lo + hi);
+    if (hi - lo <= 4.0 * DBL_EPSILON * scale) {
+      t = 0.5 * (lo + hi);
+      break;
+    }
+    t = tn;
+  }
+  return t;
+}
+
 // Candidate lists of the score kernel: a wave appends the survivors of each
 // head in page order; the first kListSlots of them stay in LDS, the rest go
 // to the wave's spill area in global memory (only when scores are nearly
@@ -639,135 +802,102 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
 }
 
 // ---------------------------------------------------------------------------
-// threshold and P.V
+// threshold and P.V kernel
 
-// d^e through exp2/log2 (d > 0); kept out of line so that its registers do
-// not add to those of the loops that call it.
-__device__ __attribute__((noinline)) double pow_general(double d, double e) {
-  return exp2(e * log2(d));
-}
-
-// d^(m-1) for the common exponents, pow_general otherwise (d > 0).
-__device__ __forceinline__ double pow_m1(double d, double m, int mcode) {
-  switch (mcode) {
-    case 1: return 1.0;
-    case 2: return d;
-    case 3: return d * d;
-    case 4: return d * d * d;
-    default: return pow_general(d, m - 1.0);
-  }
-}
-
-template <int SNT>
-__device__ __forceinline__ void scope_sum2(double& a, double& c, double* red) {
-  a = wave_allsum(a);
-  c = wave_allsum(c);
-  if constexpr (SNT > kWave) {
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    if (lane == 0) {
-      red[2 * wid] = a;
-      red[2 * wid + 1] = c;
+// One batch of the threshold kernel's gather (see there): thread t takes
+// entries [bbase + t*per, bbase + t*per + per) of the head's concatenated
+// candidate regions, per <= R; returns the window members counted so far.
+template <typename ZT>
+struct GatherArgs {
+  const int* roff;
+  const Cand<ZT>* creg;
+  int splits, cap;
+  ZT thr;
+  ZT* lz;
+  int* li;
+  ZT* gz;
+  int* gi;
+  int lcap;
+  int* tmp;
+};
+template <int R, typename ZT>
+__device__ int gather_batch(const GatherArgs<ZT>& a, int bbase, int nb, int n_list) {
+  const int tid = threadIdx.x;
+  const int per = (nb + kNT - 1) / kNT;
+  const int e0 = bbase + min(nb, tid * per), e1 = bbase + min(nb, tid * per + per);
+  // Offsets first (LDS only), then every load unconditionally and
+  // branch-free, so all of them are in flight before the first is used
+  // (slots past the run reload its last entry, or entry 0 of region 0).
+  int off[R];  // < regions * cap: the head's gathered tokens (< 2^31)
+  {
+    const int ef = e0 < e1 ? e0 : 0;
+    int lo = 0, hi = a.splits;  // roff[lo] <= ef < roff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.roff[mid] <= ef) lo = mid;
+      else hi = mid;
     }
-    __syncthreads();
-    a = 0.0;
-    c = 0.0;
+    int r = lo, rbeg = a.roff[lo], rend = a.roff[lo + 1];
 #pragma unroll
-    for (int w = 0; w < SNT / kWave; ++w) {
-      a += red[2 * w];
-      c += red[2 * w + 1];
-    }
-    __syncthreads();
-  }
-}
-
-// Safeguarded Newton for sum_i [a_i - t]_+^m = 1 with a_i = am1 * z_i. The
-// root lies in [a_max - 1, a_max): f(a_max - 1) >= 1 (top term is 1) and
-// f(a_max) = 0. Called by the SNT threads t0 = 0..SNT-1 of the scope.
-template <int SNT, typename ZT>
-__device__ double solve_tau(const ZT* z, int n, double am1, double m, int mcode, double amax,
-                            int t0, double* red) {
-  double lo = amax - 1.0, hi = amax, t = lo;
-  for (int it = 0; it < 200; ++it) {
-    double f = 0.0, fp = 0.0;
-    for (int i = t0; i < n; i += SNT) {
-      const double d = am1 * (double)z[i] - t;
-      if (d > 0.0) {
-        const double pm1 = pow_m1(d, m, mcode);
-        fp += pm1;
-        f += pm1 * d;
+    for (int k = 0; k < R; ++k) {
+      const int e = e0 + k < e1 ? e0 + k : (e0 < e1 ? e1 - 1 : 0);
+      while (e >= rend && r + 1 < a.splits) {  // next non-empty region (LDS read on crossings)
+        ++r;
+        rbeg = rend;
+        rend = a.roff[r + 1];
       }
+      off[k] = r * a.cap + (e - rbeg);
     }
-    scope_sum2<SNT>(f, fp, red);
-    fp *= m;
-    if (f >= 1.0) lo = t;
-    else hi = t;
-    if (f == 1.0) break;
-    const double scale = fmax(1.0, fabs(t));
-    double tn = fp > 0.0 ? t + (f - 1.0) / fp : 0.5 * (lo + hi);
-    if (fp > 0.0 && fabs(tn - t) <= 2.0 * DBL_EPSILON * scale) {
-      t = fmin(fmax(tn, lo), hi);
-      break;
-    }
-    if (!(tn > lo && tn < hi)) tn = 0.5 * (lo + hi);
-    if (hi - lo <= 4.0 * DBL_EPSILON * scale) {
-      t = 0.5 * (lo + hi);
-      break;
-    }
-    t = tn;
   }
-  return t;
-}
-
-__device__ __forceinline__ double pow_m(double d, double m, int mcode) {
-  return d * pow_m1(d, m, mcode);
-}
-
-// The safeguarded Newton iteration of solve_tau for one wave whose lanes
-// hold the list's a_i = am1 * z_i in registers (K per lane; -DBL_MAX marks an
-// empty slot), so an iteration reads no memory. Same steps and stopping rules.
-template <int K>
-__device__ double solve_tau_regs(const double (&a)[K], double am1, double m, int mcode,
-                                 double amax) {
-  (void)am1;
-  double lo = amax - 1.0, hi = amax, t = lo;
-  for (int it = 0; it < 200; ++it) {
-    double f = 0.0, fp = 0.0;
+  Cand<ZT> v[R];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const double d = a[k] - t;
-      if (d > 0.0) {
-        const double pm1 = pow_m1(d, m, mcode);
-        fp += pm1;
-        f += pm1 * d;
+  for (int k = 0; k < R; ++k) v[k] = a.creg[off[k]];
+  int keep = 0;
+#pragma unroll
+  for (int k = 0; k < R; ++k) keep += (e0 + k < e1 && v[k].z >= a.thr) ? 1 : 0;
+  int kept;
+  int pos = n_list + block_excl_scan<kNT>(keep, a.tmp, &kept);
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (e0 + k < e1 && v[k].z >= a.thr) {
+      if (pos < a.lcap) {
+        a.lz[pos] = v[k].z;
+        a.li[pos] = v[k].idx;
+      } else {
+        a.gz[pos] = v[k].z;
+        a.gi[pos] = v[k].idx;
       }
+      ++pos;
     }
-    f = wave_allsum(f);
-    fp = wave_allsum(fp) * m;
-    if (f >= 1.0) lo = t;
-    else hi = t;
-    if (f == 1.0) break;
-    const double scale = fmax(1.0, fabs(t));
-    double tn = fp > 0.0 ? t + (f - 1.0) / fp : 0.5 * (lo + hi);
-    if (fp > 0.0 && fabs(tn - t) <= 2.0 * DBL_EPSILON * scale) {
-      t = fmin(fmax(tn, lo), hi);
-      break;
-    }
-    if (!(tn > lo && tn < hi)) tn = 0.5 * (lo + hi);
-    if (hi - lo <= 4.0 * DBL_EPSILON * scale) {
-      t = 0.5 * (lo + hi);
-      break;
-    }
-    t = tn;
   }
-  return t;
+  return n_list + kept;
+}
+
+// LDS of the threshold kernel: region offsets, `lcap` window members
+// (score, V row, weight), the P.V partial rows and the region maxima used for
+// the lower bound. Longer lists take a global-memory path.
+constexpr int kTauMaxList = 8192;  // most window members one workgroup holds in LDS
+constexpr int kTauBoundFrom = 2048;  // candidates from which the window is tightened first
+struct TauLds {
+  size_t lz, li, sp, pv, rmax, total;
+};
+__host__ __device__ inline TauLds tau_lds_layout(int regions, int lcap, int zbytes, int ng,
+                                                 int D) {
+  TauLds l;
+  size_t o = align16((size_t)(regions + 1) * 4);
+  l.lz = o; o = align16(o + (size_t)lcap * zbytes);
+  l.li = o; o = align16(o + (size_t)lcap * 4);
+  l.sp = o; o = align16(o + (size_t)lcap * 4);
+  l.pv = o; o = align16(o + (size_t)ng * D * 4);
+  l.rmax = o; o = align16(o + (size_t)kNT * 8);
+  l.total = o;
+  return l;
 }
 
 template <typename KV, int D, bool SPARSE>
 __global__ void __launch_bounds__(kNT)
-tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_table,
-              const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel, int H,
-              int Hkv, int G, int U, int PS, int max_pages, int num_phys, int budget, int splits,
-              int cap, int list_cap, float alpha, double window_d,
+tau_pv_kernel(const KV* __restrict__ v_pool, int H, int Hkv, int G, int U, int PS, int splits,
+              int cap, int list_cap, int lcap, float alpha, double window_d,
               const Cand<typename KvTraits<KV>::Acc>* __restrict__ cand,
               const int* __restrict__ counts, const typename KvTraits<KV>::Acc* __restrict__ maxima,
               typename KvTraits<KV>::Acc* __restrict__ list_z, int* __restrict__ list_i,
@@ -777,11 +907,15 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
   constexpr int VPC = 16 / sizeof(KV);
   constexpr int LR = D / VPC;     // lanes per V row
   constexpr int NG = kNT / LR;    // rows in flight per pass
-  __shared__ int roff[kMaxSplits + 1];  // region offsets
-  __shared__ ZT lz[kListCap];
-  __shared__ int li[kListCap];
-  __shared__ float sp[kListCap];
-  __shared__ float pvacc[NG][D];
+  constexpr int KB = kTauMaxList / kNT;  // most list entries per thread in block-wide steps
+  extern __shared__ __align__(16) unsigned char smem[];
+  const TauLds lay = tau_lds_layout(splits, lcap, sizeof(ZT), NG, D);
+  int* roff = reinterpret_cast<int*>(smem);  // region offsets
+  ZT* lz = reinterpret_cast<ZT*>(smem + lay.lz);
+  int* li = reinterpret_cast<int*>(smem + lay.li);
+  float* sp = reinterpret_cast<float*>(smem + lay.sp);
+  float (*pvacc)[D] = reinterpret_cast<float (*)[D]>(smem + lay.pv);
+  double* rmax = reinterpret_cast<double*>(smem + lay.rmax);  // kNT doubles
   __shared__ double red[2 * kNW];
   __shared__ ZT fred[kNW];
   __shared__ int tmp[kNW + 2];
@@ -797,6 +931,9 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
   const int* cn = counts + (size_t)bh * splits;
   const Cand<ZT>* creg = cand + (size_t)bh * splits * cap;
   const uint64_t ltm = lanemask_below(lane);
+  const double am1 = (double)alpha - 1.0;
+  const double m = 1.0 / am1;
+  const int mcode = (m == 1.0) ? 1 : (m == 2.0) ? 2 : (m == 3.0) ? 3 : (m == 4.0) ? 4 : 0;
 
   // Region counts and maxima: every thread loads its contiguous block of
   // regions at once; one block scan turns counts into offsets.
@@ -830,103 +967,59 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
     }
     return;
   }
-  const ZT thr = M - window;
-
-  ZT* dz;
-  int* di;
-  int n_list;
-  if (n_cand <= kListCap) {
-    // Gather and window filter in one pass: thread t takes the contiguous
-    // entries [t*per, t*per + per) (all of its loads in flight together),
-    // keeps those with z >= thr, and one block scan places them in order.
-    const int per = (n_cand + kNT - 1) / kNT;  // <= kListCap / kNT
-    constexpr int kMaxPer = kListCap / kNT;
-    const int e0 = min(n_cand, tid * per), e1 = min(n_cand, e0 + per);
-    Cand<ZT> v[kMaxPer];
-    int keep = 0;
-    if (e0 < e1) {
-      int lo = 0, hi = splits;  // roff[lo] <= e0 < roff[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (roff[mid] <= e0) lo = mid;
-        else hi = mid;
-      }
-      int r = lo;
+  const double amax = am1 * (double)M;
+  ZT thr = M - window;
+  if (n_cand > kTauBoundFrom) {
+    // Many candidates: tighten the window with a lower bound on tau. The
+    // threshold t_S of any subset S of the head's tokens is at most tau (the
+    // left side of the equation only grows when tokens are added and it
+    // decreases in t); S = the per-thread region maxima (up to 256 token
+    // scores), solved by wave 0 in registers. Every support token then has
+    // a > t_S, and the kept set a > t_S - 1e-6 max(1, |t_S|) still holds it.
+    rmax[tid] = mloc == neg_inf<ZT>() ? -DBL_MAX : am1 * (double)mloc;
+    __syncthreads();
+    if (wave == 0) {
+      double a[kRegList];
 #pragma unroll
-      for (int k = 0; k < kMaxPer; ++k) {
-        const int e = e0 + k;
-        if (e < e1) {
-          while (roff[r + 1] <= e) ++r;
-          v[k] = creg[(size_t)r * cap + (e - roff[r])];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kMaxPer; ++k) keep += (e0 + k < e1 && v[k].z >= thr) ? 1 : 0;
-    }
-    int base = block_excl_scan<kNT>(keep, tmp, &n_list);
-#pragma unroll
-    for (int k = 0; k < kMaxPer; ++k) {
-      if (e0 + k < e1 && v[k].z >= thr) {
-        lz[base] = v[k].z;
-        li[base] = v[k].idx;
-        ++base;
-      }
+      for (int k = 0; k < kRegList; ++k) a[k] = rmax[k * kWave + lane];
+      const double ts = solve_tau_regs<kRegList>(a, am1, m, mcode, amax);
+      if (lane == 0) tau_b = ts;
     }
     __syncthreads();
-    dz = lz;
-    di = li;
-  } else {
-    // Large candidate sets: window members go to this head's global list
-    // (counted per region, then gathered, one wave per region).
-    for (int r = wave; r < splits; r += kNW) {
-      const int n = cn[r];
-      const Cand<ZT>* src = creg + (size_t)r * cap;
-      int cnt = 0;
-      for (int e = lane; e < n; e += kWave) cnt += src[e].z >= thr;
-      cnt = wave_sum(cnt);
-      if (lane == 0) roff[r] = cnt;  // only this wave touches roff[r] here
-    }
-    __syncthreads();
-    // roff now holds per-region window counts for r < splits; rebuild offsets
-    int s2 = 0;
-    for (int r = r0; r < r1; ++r) s2 += roff[r];
-    int base = block_excl_scan<kNT>(s2, tmp, &n_list);
-    __syncthreads();
-    for (int r = r0; r < r1; ++r) {
-      const int v = roff[r];
-      roff[r] = base;
-      base += v;
-    }
-    __syncthreads();
-    dz = list_z + (size_t)bh * list_cap;
-    di = list_i + (size_t)bh * list_cap;
-    for (int r = wave; r < splits; r += kNW) {
-      const int n = cn[r];
-      const Cand<ZT>* src = creg + (size_t)r * cap;
-      int o = roff[r];
-      for (int e0 = 0; e0 < n; e0 += kWave) {
-        const int e = e0 + lane;
-        Cand<ZT> v;
-        v.z = neg_inf<ZT>();
-        v.idx = 0;
-        if (e < n) v = src[e];
-        const bool f = e < n && v.z >= thr;
-        const uint64_t bal = __ballot(f);
-        if (f) {
-          const int pos = o + __popcll(bal & ltm);
-          dz[pos] = v.z;
-          di[pos] = v.idx;
-        }
-        o += __popcll(bal);
-      }
-    }
-    __syncthreads();
+    const double ts = tau_b;
+    const ZT lb = (ZT)((ts - 1e-6 * fmax(1.0, fabs(ts))) / am1);
+    if (lb > thr) thr = lb;
   }
 
-  const double am1 = (double)alpha - 1.0;
-  const double m = 1.0 / am1;
-  const int mcode = (m == 1.0) ? 1 : (m == 2.0) ? 2 : (m == 3.0) ? 3 : (m == 4.0) ? 4 : 0;
-  const double amax = am1 * (double)M;
+  // Gather and window filter, in batches of up to kNT * KB entries: thread t
+  // takes a contiguous run of the batch (all of its loads in flight
+  // together), keeps those with z >= thr, and one block scan places them in
+  // order; members beyond the LDS capacity go to the head's global list. The
+  // run length is a compile-time 2, 8 or KB, picked from the batch size.
+  ZT* gz = list_z + (size_t)bh * list_cap;
+  int* gi = list_i + (size_t)bh * list_cap;
+  int n_list = 0;
+  for (int bbase = 0; bbase < n_cand; bbase += kNT * KB) {
+    const int nb_ = min(kNT * KB, n_cand - bbase);
+    const int per = (nb_ + kNT - 1) / kNT;
+    const GatherArgs<ZT> ga{roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp};
+    if (per <= 2) n_list = gather_batch<2>(ga, bbase, nb_, n_list);
+    else if (per <= 8) n_list = gather_batch<8>(ga, bbase, nb_, n_list);
+    else n_list = gather_batch<KB>(ga, bbase, nb_, n_list);
+  }
+  __syncthreads();
+  ZT* dz = lz;
+  int* di = li;
+  if (n_list > lcap) {
+    // the whole list goes to global memory
+    for (int i = tid; i < lcap; i += kNT) {
+      gz[i] = lz[i];
+      gi[i] = li[i];
+    }
+    __syncthreads();
+    dz = gz;
+    di = gi;
+  }
   const bool list_lds = dz == lz;
 
   // Threshold, support (a_i > tau) with p_i = (a_i - tau)^m, sum p in float64.
@@ -971,55 +1064,48 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
     tau = tau_b;
     n_sup = nb[1];
     psum = red[0];
-  } else {
-    const double t = solve_tau<kNT>(dz, n_list, am1, m, mcode, amax, tid, red);
-    if (tid == 0) tau_b = t;
-    __syncthreads();
-    tau = tau_b;
-    if (list_lds) {
-      // compact (V row, p) in place, in list order, by one wave
-      if (wave == 0) {
-        int o = 0;
-        for (int e0 = 0; e0 < n_list; e0 += kWave) {
-          const int e = e0 + lane;
-          double d = -1.0;
-          int ix = 0;
-          if (e < n_list) {
-            d = am1 * (double)lz[e] - tau;
-            ix = li[e];
-          }
-          const bool f = d > 0.0;
-          const uint64_t bal = __ballot(f);
-          if (f) {
-            const double pv = pow_m(d, m, mcode);
-            psum += pv;
-            li[o + __popcll(bal & ltm)] = ix;
-            sp[o + __popcll(bal & ltm)] = (float)pv;
-          }
-          o += __popcll(bal);
-        }
-        psum = wave_allsum(psum);
-        if (lane == 0) {
-          nb[1] = o;
-          red[0] = psum;
-        }
+  } else if (list_lds) {
+    // Long lists: thread t holds the contiguous entries [t*per, t*per + per)
+    // in registers for the whole solve; one block scan compacts the support.
+    const int per = (n_list + kNT - 1) / kNT;  // <= KB
+    const int e0 = min(n_list, tid * per), e1 = min(n_list, e0 + per);
+    double a[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) a[k] = (e0 + k < e1) ? am1 * (double)lz[e0 + k] : -DBL_MAX;
+    tau = solve_tau_block<KB>(a, m, mcode, amax, red);
+    int ns = 0;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) ns += (a[k] - tau > 0.0) ? 1 : 0;
+    int ix[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) ix[k] = (e0 + k < e1) ? li[e0 + k] : 0;
+    int base = block_excl_scan<kNT>(ns, tmp, &n_sup);  // (its barriers order the reads above)
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const double d = a[k] - tau;
+      if (d > 0.0) {
+        const double pv = pow_m(d, m, mcode);
+        psum += pv;
+        li[base] = ix[k];
+        sp[base] = (float)pv;
+        ++base;
       }
-      __syncthreads();
-      n_sup = nb[1];
-      psum = red[0];
-    } else {
-      int ns = 0;
-      for (int i = tid; i < n_list; i += kNT) {
-        const double d = am1 * (double)dz[i] - tau;
-        if (d > 0.0) {
-          ++ns;
-          psum += pow_m(d, m, mcode);
-        }
-      }
-      double nsd = (double)ns;
-      scope_sum2<kNT>(psum, nsd, red);
-      n_sup = (int)nsd;
     }
+    double zero = 0.0;
+    scope_sum2<kNT>(psum, zero, red);
+  } else {
+    tau = solve_tau<kNT>(dz, n_list, am1, m, mcode, amax, tid, red);
+    int ns = 0;
+    for (int i = tid; i < n_list; i += kNT) {
+      const double d = am1 * (double)dz[i] - tau;
+      if (d > 0.0) {
+        ++ns;
+        psum += pow_m(d, m, mcode);
+      }
+    }
+    double nsd = (double)ns;
+    scope_sum2<kNT>(psum, nsd, red);
+    n_sup = (int)nsd;
   }
 
   // o = sum p v / sum p. A candidate's index is its V row,
@@ -1080,18 +1166,20 @@ tau_pv_kernel(const KV* __restrict__ v_pool, const int32_t* __restrict__ block_t
 template <typename KV, int D, int G, int PS, bool SPARSE>
 hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float* q,
                           const void* k_pool, const int32_t* bt, const int32_t* lens,
-                          const int32_t* sel, int budget, float window, void* ws,
+                          const int32_t* sel, int budget, float alpha, float window, void* ws,
                           const DecodeWs& L, hipStream_t st) {
   using ZT = typename KvTraits<KV>::Acc;
   const int U = s.batch * s.num_kv_heads;
   const ScoreLds lay = score_lds_layout(G, PS, p.pages_per_split, SPARSE, s.max_pages, budget,
                                         sizeof(ZT), score_kbuf_bytes(s.bf16, PS, D, SPARSE));
   auto kern = score_kernel<KV, D, G, PS, SPARSE>;
-  if (lay.total > 64 * 1024) {
+  static bool lds_raised = false;  // the attribute is per kernel; set it once, to the most
+  if (!lds_raised) {               // any plan asks for
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lay.total);
+                                       (int)kMaxScoreLdsBytes);
     if (e != hipSuccess) return e;
+    lds_raised = true;
   }
   char* w = static_cast<char*>(ws);
   hipLaunchKernelGGL(kern, dim3(U * p.splits), dim3(kNT), lay.total, st, q,
@@ -1106,39 +1194,39 @@ hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float*
 template <typename KV, int D, int G, bool SPARSE>
 hipError_t launch_score_ps(const LaunchShape& s, const SplitPlan& p, const float* q,
                            const void* k_pool, const int32_t* bt, const int32_t* lens,
-                           const int32_t* sel, int budget, float window, void* ws,
+                           const int32_t* sel, int budget, float alpha, float window, void* ws,
                            const DecodeWs& L, hipStream_t st) {
   switch (s.page_size) {
-    case 16: return launch_score_t<KV, D, G, 16, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
-    case 32: return launch_score_t<KV, D, G, 32, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
-    default: return launch_score_t<KV, D, G, 64, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+    case 16: return launch_score_t<KV, D, G, 16, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
+    case 32: return launch_score_t<KV, D, G, 32, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
+    default: return launch_score_t<KV, D, G, 64, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
   }
 }
 
 template <typename KV, int D, bool SPARSE>
 hipError_t launch_score_g(const LaunchShape& s, const SplitPlan& p, const float* q,
                           const void* k_pool, const int32_t* bt, const int32_t* lens,
-                          const int32_t* sel, int budget, float window, void* ws,
+                          const int32_t* sel, int budget, float alpha, float window, void* ws,
                           const DecodeWs& L, hipStream_t st) {
   switch (s.group) {
-    case 1: return launch_score_ps<KV, D, 1, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
-    case 2: return launch_score_ps<KV, D, 2, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
-    case 4: return launch_score_ps<KV, D, 4, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
-    default: return launch_score_ps<KV, D, 8, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+    case 1: return launch_score_ps<KV, D, 1, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
+    case 2: return launch_score_ps<KV, D, 2, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
+    case 4: return launch_score_ps<KV, D, 4, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
+    default: return launch_score_ps<KV, D, 8, SPARSE>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
   }
 }
 
 template <typename KV>
 hipError_t launch_score_kv(const LaunchShape& s, const SplitPlan& p, const float* q,
                            const void* k_pool, const int32_t* bt, const int32_t* lens,
-                           const int32_t* sel, int budget, float window, void* ws,
+                           const int32_t* sel, int budget, float alpha, float window, void* ws,
                            const DecodeWs& L, hipStream_t st) {
   if (sel) {
-    if (s.head_dim == 64) return launch_score_g<KV, 64, true>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
-    return launch_score_g<KV, 128, true>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+    if (s.head_dim == 64) return launch_score_g<KV, 64, true>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
+    return launch_score_g<KV, 128, true>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
   }
-  if (s.head_dim == 64) return launch_score_g<KV, 64, false>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
-  return launch_score_g<KV, 128, false>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L, st);
+  if (s.head_dim == 64) return launch_score_g<KV, 64, false>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
+  return launch_score_g<KV, 128, false>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
 }
 
 template <typename KV, int D, bool SPARSE>
@@ -1146,15 +1234,29 @@ hipError_t launch_tau_pv_t(const LaunchShape& s, const SplitPlan& p, const void*
                            const int32_t* bt, const int32_t* lens, const int32_t* sel, int budget,
                            float alpha, float window, float* out, float* tau, int32_t* support,
                            void* ws, const DecodeWs& L, hipStream_t st) {
+  (void)bt; (void)lens; (void)sel; (void)budget;
   using ZT = typename KvTraits<KV>::Acc;
+  constexpr int NG = kNT / (D / (16 / (int)sizeof(KV)));
   const int U = s.batch * s.num_kv_heads;
+  // Up to 256 workgroups (one per CU) hold 8192 window members each; larger
+  // grids hold 4096 so that two workgroups fit a CU.
+  const int lcap = U * s.group > 256 ? kTauMaxList / 2 : kTauMaxList;
+  const size_t lds = tau_lds_layout(p.regions, lcap, sizeof(ZT), NG, D).total;
+  auto kern = tau_pv_kernel<KV, D, SPARSE>;
+  static bool lds_raised = false;  // the attribute is per kernel; set it once
+  if (!lds_raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)tau_lds_layout(kMaxSplits, kTauMaxList, 8, NG, D).total);
+    if (e != hipSuccess) return e;
+    lds_raised = true;
+  }
   char* w = static_cast<char*>(ws);
   ZT* list_z = reinterpret_cast<ZT*>(w + L.list);
   int* list_i = reinterpret_cast<int*>(list_z + (size_t)s.batch * s.num_q_heads * p.list_cap);
-  hipLaunchKernelGGL((tau_pv_kernel<KV, D, SPARSE>), dim3(U * s.group), dim3(kNT), 0, st,
-                     static_cast<const KV*>(v_pool), bt, lens, sel, s.num_q_heads,
-                     s.num_kv_heads, s.group, U, s.page_size, s.max_pages, s.num_phys, budget,
-                     p.regions, p.rcap, p.list_cap, alpha, (double)window,
+  hipLaunchKernelGGL(kern, dim3(U * s.group), dim3(kNT), lds, st, static_cast<const KV*>(v_pool),
+                     s.num_q_heads, s.num_kv_heads, s.group, U, s.page_size, p.regions, p.rcap,
+                     p.list_cap, lcap, alpha, (double)window,
                      reinterpret_cast<const Cand<ZT>*>(w + L.cand),
                      reinterpret_cast<const int*>(w + L.counts),
                      reinterpret_cast<const ZT*>(w + L.maxima), list_z, list_i, out, tau,

@@ -31,6 +31,7 @@ constexpr int kSelCopy = 8192;  // selection ints staged in LDS by the sparse sc
 
 
 constexpr int kListSlots = 64;  // LDS candidate slots per (wave, head) in the score kernel
+constexpr size_t kMaxScoreLdsBytes = 150 * 1024;  // most LDS a score-kernel plan may use
 
 // LDS layout of the score kernel (bytes), shared by host sizing and device carving.
 struct ScoreLds {
@@ -115,11 +116,11 @@ hipError_t launch_select(const LaunchShape& s, const float* ub, const int32_t* l
 // Per-dtype instantiations (decode_bf16.hip, decode_f32.hip).
 hipError_t launch_score_bf16(const LaunchShape& s, const SplitPlan& p, const float* q,
                              const void* k_pool, const int32_t* bt, const int32_t* lens,
-                             const int32_t* sel, int budget, float window, void* ws,
+                             const int32_t* sel, int budget, float alpha, float window, void* ws,
                              const DecodeWs& L, hipStream_t st);
 hipError_t launch_score_f32(const LaunchShape& s, const SplitPlan& p, const float* q,
                             const void* k_pool, const int32_t* bt, const int32_t* lens,
-                            const int32_t* sel, int budget, float window, void* ws,
+                            const int32_t* sel, int budget, float alpha, float window, void* ws,
                             const DecodeWs& L, hipStream_t st);
 hipError_t launch_tau_pv_bf16(const LaunchShape& s, const SplitPlan& p, const void* v_pool,
                               const int32_t* bt, const int32_t* lens, const int32_t* sel,

@@ -40,3 +40,13 @@ def test_multi_gpu_request_exits(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_containment_criterion():
+    """Equal support size and tau (within 1e-6 relative) count as contained."""
+    sup_s = np.array([[3, 3], [2, 5]])
+    sup_f = np.array([[3, 4], [2, 5]])
+    tau_f = np.array([[1.0, 1.0], [-2.0, 0.5]])
+    tau_s = np.array([[1.0, 1.0], [-2.0 - 1e-5, 0.5 + 5e-7]])
+    c = bench.contained(sup_s, sup_f, tau_s, tau_f)
+    assert c.tolist() == [[True, False], [False, True]]

@@ -107,3 +107,37 @@ def test_full_size_alpha_sweep():
                 for b, h in heads:
                     check_decode(O.decode_full(inp, b, h, alpha), fo[b, h], ft[b, h], fs[b, h],
                                  w.kv_dtype, alpha, f"sweep full a{alpha} b{b} h{h}")
+
+
+def test_containment_report_matches_oracle():
+    """The GPU containment criterion used by the sweep report (equal support
+    size and tau) against the oracle's definition (the support's pages are a
+    subset of the selection) on every trial of a shrunk alpha sweep; they may
+    differ only where the oracle's support has a marginal token."""
+    import bench
+    from parity_util import marginal_tokens
+    w = synth.shrink(synth.WORKLOADS["alpha_sweep_64k"], context=4096, batch=2, name="sweep_small")
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS["alpha_sweep_64k"])
+    dev = Dev(inp)
+    dev.build_meta()
+    B, H = w.batch, w.num_q_heads
+    announce("containment criterion")
+    for budget in (16, 64):
+        sel, _ = dev.select(budget)
+        torch.cuda.synchronize()
+        sel_np = sel.cpu().numpy()
+        for alpha in w.alphas:
+            _, ts, ss = dev.sparse(sel, budget, alpha)
+            _, tf, sf = dev.full(alpha)
+            torch.cuda.synchronize()
+            c = bench.contained(ss.cpu().numpy(), sf.cpu().numpy(), ts.cpu().numpy(),
+                                tf.cpu().numpy())
+            mismatches = 0
+            for b in range(B):
+                for h in range(H):
+                    res = O.decode_full(inp, b, h, alpha)
+                    ref = set(O.support_pages(res, w.page_size)) <= set(int(j) for j in sel_np[b, h])
+                    if ref != bool(c[b, h]):
+                        assert marginal_tokens(res, alpha, 1e-6) > 0, (alpha, budget, b, h)
+                        mismatches += 1
+            assert mismatches <= 2, (alpha, budget, mismatches)
