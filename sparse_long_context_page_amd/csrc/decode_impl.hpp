@@ -69,6 +69,57 @@ struct alignas(2 * sizeof(ZT)) Cand {
   int idx;
 };
 
+// Stores and loads of data that one workgroup hands to another within a
+// launch (selections, candidate regions, their counts and maxima): made at
+// device scope, so they bypass this XCD's L2 for the memory side that the
+// other XCDs see, and no cache-wide write-back or invalidate is needed. A
+// writer waits for its stores to complete before it announces them.
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  if constexpr (sizeof(T) == 4) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    static_assert(sizeof(T) == 8, "4- or 8-byte values");
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __hip_atomic_load(reinterpret_cast<const uint32_t*>(p),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  } else {
+    static_assert(sizeof(T) == 8, "4- or 8-byte values");
+    return __builtin_bit_cast(T, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
+}
+template <typename ZT>
+__device__ __forceinline__ void st_dev_cand(Cand<ZT>* p, ZT z, int idx) {
+  if constexpr (sizeof(ZT) == 4) {
+    st_dev(reinterpret_cast<uint64_t*>(p),
+           (uint64_t)__builtin_bit_cast(uint32_t, z) | ((uint64_t)(uint32_t)idx << 32));
+  } else {
+    st_dev(&p->z, z);
+    st_dev(&p->idx, idx);
+  }
+}
+template <typename ZT>
+__device__ __forceinline__ Cand<ZT> ld_dev_cand(const Cand<ZT>* p) {
+  Cand<ZT> c;
+  if constexpr (sizeof(ZT) == 4) {
+    const uint64_t v = ld_dev(reinterpret_cast<const uint64_t*>(p));
+    c.z = __builtin_bit_cast(float, (uint32_t)v);
+    c.idx = (int)(uint32_t)(v >> 32);
+  } else {
+    c.z = ld_dev(&p->z);
+    c.idx = ld_dev(&p->idx);
+  }
+  return c;
+}
+
 template <typename T>
 __device__ __forceinline__ T neg_inf() {
   return -__builtin_huge_val();
@@ -130,7 +181,7 @@ __device__ __forceinline__ int find_slot(const int32_t* row, int n, int key) {
 // did not select it) and `sphys` (physical page ids, fetched with one
 // coalesced load per page). Returns the number of pages; ends with a barrier
 // (every thread of the block must call it).
-template <int G, bool SPARSE>
+template <int G, bool SPARSE, bool DEV = false>
 __device__ int build_slice(const int32_t* __restrict__ sel, const int32_t* __restrict__ block_table,
                            int b, int bh0, int budget, int P, int max_pages, int split, int pps,
                            unsigned* bm, int32_t* ssel, int* slice, int* slots, int* sphys,
@@ -143,7 +194,7 @@ __device__ int build_slice(const int32_t* __restrict__ sel, const int32_t* __res
     const int nwords = (P + 31) >> 5;
     for (int i = tid; i < nwords; i += kNT) bm[i] = 0u;
     if (staged)
-      for (int i = tid; i < G * budget; i += kNT) ssel[i] = selrow[i];
+      for (int i = tid; i < G * budget; i += kNT) ssel[i] = DEV ? ld_dev(selrow + i) : selrow[i];
     __syncthreads();
     const int32_t* srow = staged ? ssel : selrow;
     for (int i = tid; i < G * budget; i += kNT) {
@@ -404,21 +455,53 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((((N >> 4) & 3) << 14) | (0xF << 8) | (0x7 << 4) | (N & 15));
 }
 
-template <typename KV, int D, int G, int PS, bool SPARSE>
-__global__ void __launch_bounds__(kNT)
-score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
-             const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-             const int32_t* __restrict__ sel, int H, int Hkv, int U, int max_pages, int num_phys,
-             int budget, int pps, int splits, int cap, double window_d,
-             Cand<typename KvTraits<KV>::Acc>* __restrict__ cand, int* __restrict__ counts,
-             typename KvTraits<KV>::Acc* __restrict__ maxima,
-             Cand<typename KvTraits<KV>::Acc>* __restrict__ spill) {
+// Arguments of the score step (device pointers; regions are this call's
+// candidate regions, spill the per-wave overflow areas).
+template <typename KV>
+struct ScoreArgs {
+  const float* q;
+  const KV* k_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* sel;
+  int H, Hkv, U, max_pages, num_phys, budget, pps, splits, cap;
+  double window_d;
+  Cand<typename KvTraits<KV>::Acc>* cand;
+  int* counts;
+  typename KvTraits<KV>::Acc* maxima;
+  Cand<typename KvTraits<KV>::Acc>* spill;
+};
+
+// One split of one (sequence, KV head) unit, by the whole workgroup. DEV:
+// the selection is read, and the candidate region written, at device scope
+// (handed between workgroups of one launch).
+template <typename KV, int D, int G, int PS, bool SPARSE, bool DEV>
+__device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split, int u, unsigned char* smem) {
   using Tr = KvTraits<KV>;
   using Acc = typename Tr::Acc;  // also the score type
   constexpr bool MFMA = kMfmaScores && sizeof(KV) == 2;
-  const Acc window = (Acc)window_d;
+  const float* __restrict__ q = args.q;
+  const KV* __restrict__ k_pool = args.k_pool;
+  const int32_t* __restrict__ block_table = args.block_table;
+  const int32_t* __restrict__ seq_lens = args.seq_lens;
+  const int32_t* __restrict__ sel = args.sel;
+  const int H = args.H, Hkv = args.Hkv, max_pages = args.max_pages, num_phys = args.num_phys;
+  const int budget = args.budget, pps = args.pps, splits = args.splits, cap = args.cap;
+  Cand<Acc>* __restrict__ cand = args.cand;
+  int* __restrict__ counts = args.counts;
+  Acc* __restrict__ maxima = args.maxima;
+  Cand<Acc>* __restrict__ spill = args.spill;
+  const Acc window = (Acc)args.window_d;
+  auto put_count = [&](size_t r, int n, Acc mval) {
+    if constexpr (DEV) {
+      st_dev(&counts[r], n);
+      st_dev(&maxima[r], mval);
+    } else {
+      counts[r] = n;
+      maxima[r] = mval;
+    }
+  };
 
-  extern __shared__ __align__(16) unsigned char smem[];
   const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc),
                                         score_kbuf_bytes(sizeof(KV) == 2, PS, D, SPARSE));
   Acc* wmax = reinterpret_cast<Acc*>(smem + lay.wmax);
@@ -429,8 +512,6 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
   int* tmp = reinterpret_cast<int*>(smem + lay.tmp);
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int u = blockIdx.x % U;
-  const int split = blockIdx.x / U;
   const int b = u / Hkv, g = u % Hkv;
   const int L = clamp_len(seq_lens[b], max_pages * PS);
   const int P = (L + PS - 1) / PS;
@@ -441,16 +522,12 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
                                  (size_t)split * kNW * G * lay.wcap,
                              lay.wcap};
 
-  const int n_slice = build_slice<G, SPARSE>(
+  const int n_slice = build_slice<G, SPARSE, DEV>(
       sel, block_table, b, bh0, budget, P, max_pages, split, pps,
       reinterpret_cast<unsigned*>(smem + lay.bitmap), reinterpret_cast<int32_t*>(smem + lay.ssel),
       slice, slots, sphys, tmp);
   if (n_slice == 0) {
-    if (tid < G) {
-      const size_t r = (size_t)(bh0 + tid) * splits + split;
-      counts[r] = 0;
-      maxima[r] = neg_inf<Acc>();
-    }
+    if (tid < G) put_count((size_t)(bh0 + tid) * splits + split, 0, neg_inf<Acc>());
     return;
   }
 
@@ -786,19 +863,27 @@ score_kernel(const float* __restrict__ q, const KV* __restrict__ k_pool,
         const bool f = e < n && z >= thr;
         const uint64_t bal = __ballot(f);
         if (f) {
-          Cand<Acc> cv;
-          cv.z = z;
-          cv.idx = ix;
-          dst[o + __popcll(bal & ltm)] = cv;
+          if constexpr (DEV) {
+            st_dev_cand(dst + o + __popcll(bal & ltm), z, ix);
+          } else {
+            Cand<Acc> cv;
+            cv.z = z;
+            cv.idx = ix;
+            dst[o + __popcll(bal & ltm)] = cv;
+          }
         }
         o += __popcll(bal);
       }
     }
-    if (lane == 0) {
-      counts[r] = o;
-      maxima[r] = mg;
-    }
+    if (lane == 0) put_count(r, o, mg);
   }
+}
+
+template <typename KV, int D, int G, int PS, bool SPARSE>
+__global__ void __launch_bounds__(kNT)
+score_kernel(ScoreArgs<KV> args) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  score_split<KV, D, G, PS, SPARSE, false>(args, blockIdx.x / args.U, blockIdx.x % args.U, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -820,7 +905,7 @@ struct GatherArgs {
   int lcap;
   int* tmp;
 };
-template <int R, typename ZT>
+template <int R, bool DEV, typename ZT>
 __device__ int gather_batch(const GatherArgs<ZT>& a, int bbase, int nb, int n_list) {
   const int tid = threadIdx.x;
   const int per = (nb + kNT - 1) / kNT;
@@ -851,7 +936,7 @@ __device__ int gather_batch(const GatherArgs<ZT>& a, int bbase, int nb, int n_li
   }
   Cand<ZT> v[R];
 #pragma unroll
-  for (int k = 0; k < R; ++k) v[k] = a.creg[off[k]];
+  for (int k = 0; k < R; ++k) v[k] = DEV ? ld_dev_cand(a.creg + off[k]) : a.creg[off[k]];
   int keep = 0;
 #pragma unroll
   for (int k = 0; k < R; ++k) keep += (e0 + k < e1 && v[k].z >= a.thr) ? 1 : 0;
@@ -894,21 +979,45 @@ __host__ __device__ inline TauLds tau_lds_layout(int regions, int lcap, int zbyt
   return l;
 }
 
-template <typename KV, int D, bool SPARSE>
-__global__ void __launch_bounds__(kNT)
-tau_pv_kernel(const KV* __restrict__ v_pool, int H, int Hkv, int G, int U, int PS, int splits,
-              int cap, int list_cap, int lcap, float alpha, double window_d,
-              const Cand<typename KvTraits<KV>::Acc>* __restrict__ cand,
-              const int* __restrict__ counts, const typename KvTraits<KV>::Acc* __restrict__ maxima,
-              typename KvTraits<KV>::Acc* __restrict__ list_z, int* __restrict__ list_i,
-              float* __restrict__ out, float* __restrict__ tau_out, int32_t* __restrict__ sup_out) {
+// Arguments of the threshold + P.V step.
+template <typename KV>
+struct TauArgs {
+  const KV* v_pool;
+  int H, Hkv, G, U, PS, splits, cap, list_cap, lcap;
+  float alpha;
+  double window_d;
+  const Cand<typename KvTraits<KV>::Acc>* cand;
+  const int* counts;
+  const typename KvTraits<KV>::Acc* maxima;
+  typename KvTraits<KV>::Acc* list_z;
+  int* list_i;
+  float* out;
+  float* tau_out;
+  int32_t* sup_out;
+};
+
+// One query head (unit u, head hh of its group), by the whole workgroup.
+// DEV: the candidate regions are read at device scope.
+template <typename KV, int D, bool SPARSE, bool DEV>
+__device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh, unsigned char* smem) {
   using ZT = typename KvTraits<KV>::Acc;
-  const ZT window = (ZT)window_d;
+  const KV* __restrict__ v_pool = args.v_pool;
+  const int H = args.H, Hkv = args.Hkv, G = args.G, PS = args.PS, splits = args.splits;
+  const int cap = args.cap, list_cap = args.list_cap, lcap = args.lcap;
+  const float alpha = args.alpha;
+  const Cand<ZT>* __restrict__ cand = args.cand;
+  const int* __restrict__ counts = args.counts;
+  const ZT* __restrict__ maxima = args.maxima;
+  ZT* __restrict__ list_z = args.list_z;
+  int* __restrict__ list_i = args.list_i;
+  float* __restrict__ out = args.out;
+  float* __restrict__ tau_out = args.tau_out;
+  int32_t* __restrict__ sup_out = args.sup_out;
+  const ZT window = (ZT)args.window_d;
   constexpr int VPC = 16 / sizeof(KV);
   constexpr int LR = D / VPC;     // lanes per V row
   constexpr int NG = kNT / LR;    // rows in flight per pass
   constexpr int KB = kTauMaxList / kNT;  // most list entries per thread in block-wide steps
-  extern __shared__ __align__(16) unsigned char smem[];
   const TauLds lay = tau_lds_layout(splits, lcap, sizeof(ZT), NG, D);
   int* roff = reinterpret_cast<int*>(smem);  // region offsets
   ZT* lz = reinterpret_cast<ZT*>(smem + lay.lz);
@@ -923,7 +1032,6 @@ tau_pv_kernel(const KV* __restrict__ v_pool, int H, int Hkv, int G, int U, int P
   __shared__ int nb[2];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int u = blockIdx.x % U, hh = blockIdx.x / U;
   const int b = u / Hkv, g = u % Hkv;
   const int h = g * G + hh;
   const int bh = b * H + h;
@@ -942,10 +1050,10 @@ tau_pv_kernel(const KV* __restrict__ v_pool, int H, int Hkv, int G, int U, int P
   int s = 0;
   ZT mloc = neg_inf<ZT>();
   for (int r = r0; r < r1; ++r) {
-    const int c = cn[r];
+    const int c = DEV ? ld_dev(cn + r) : cn[r];
     roff[r] = c;
     s += c;
-    mloc = max(mloc, mx[r]);
+    mloc = max(mloc, DEV ? ld_dev(mx + r) : mx[r]);
   }
   const ZT M = block_reduce<kNT>(mloc, fred, [](ZT a, ZT c) { return max(a, c); });
   int n_cand;
@@ -1003,9 +1111,9 @@ tau_pv_kernel(const KV* __restrict__ v_pool, int H, int Hkv, int G, int U, int P
     const int nb_ = min(kNT * KB, n_cand - bbase);
     const int per = (nb_ + kNT - 1) / kNT;
     const GatherArgs<ZT> ga{roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp};
-    if (per <= 2) n_list = gather_batch<2>(ga, bbase, nb_, n_list);
-    else if (per <= 8) n_list = gather_batch<8>(ga, bbase, nb_, n_list);
-    else n_list = gather_batch<KB>(ga, bbase, nb_, n_list);
+    if (per <= 2) n_list = gather_batch<2, DEV>(ga, bbase, nb_, n_list);
+    else if (per <= 8) n_list = gather_batch<8, DEV>(ga, bbase, nb_, n_list);
+    else n_list = gather_batch<KB, DEV>(ga, bbase, nb_, n_list);
   }
   __syncthreads();
   ZT* dz = lz;
@@ -1160,8 +1268,45 @@ tau_pv_kernel(const KV* __restrict__ v_pool, int H, int Hkv, int G, int U, int P
   }
 }
 
+template <typename KV, int D, bool SPARSE>
+__global__ void __launch_bounds__(kNT)
+tau_pv_kernel(TauArgs<KV> args) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  tau_head<KV, D, SPARSE, false>(args, blockIdx.x % args.U, blockIdx.x / args.U, smem);
+}
+
 // ---------------------------------------------------------------------------
 // host launchers (instantiated per cache dtype in decode_*.hip)
+
+template <typename KV>
+ScoreArgs<KV> score_args(const LaunchShape& s, const SplitPlan& p, const float* q,
+                         const void* k_pool, const int32_t* bt, const int32_t* lens,
+                         const int32_t* sel, int budget, float window, void* ws,
+                         const DecodeWs& L) {
+  using ZT = typename KvTraits<KV>::Acc;
+  char* w = static_cast<char*>(ws);
+  ScoreArgs<KV> a;
+  a.q = q;
+  a.k_pool = static_cast<const KV*>(k_pool);
+  a.block_table = bt;
+  a.seq_lens = lens;
+  a.sel = sel;
+  a.H = s.num_q_heads;
+  a.Hkv = s.num_kv_heads;
+  a.U = s.batch * s.num_kv_heads;
+  a.max_pages = s.max_pages;
+  a.num_phys = s.num_phys;
+  a.budget = budget;
+  a.pps = p.pages_per_split;
+  a.splits = p.splits;
+  a.cap = p.cap;
+  a.window_d = (double)window;
+  a.cand = reinterpret_cast<Cand<ZT>*>(w + L.cand);
+  a.counts = reinterpret_cast<int*>(w + L.counts);
+  a.maxima = reinterpret_cast<ZT*>(w + L.maxima);
+  a.spill = reinterpret_cast<Cand<ZT>*>(w + L.spill);
+  return a;
+}
 
 template <typename KV, int D, int G, int PS, bool SPARSE>
 hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float* q,
@@ -1182,12 +1327,8 @@ hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float*
     lds_raised = true;
   }
   char* w = static_cast<char*>(ws);
-  hipLaunchKernelGGL(kern, dim3(U * p.splits), dim3(kNT), lay.total, st, q,
-                     static_cast<const KV*>(k_pool), bt, lens, sel, s.num_q_heads,
-                     s.num_kv_heads, U, s.max_pages, s.num_phys, budget, p.pages_per_split,
-                     p.splits, p.cap, (double)window, reinterpret_cast<Cand<ZT>*>(w + L.cand),
-                     reinterpret_cast<int*>(w + L.counts), reinterpret_cast<ZT*>(w + L.maxima),
-                     reinterpret_cast<Cand<ZT>*>(w + L.spill));
+  const ScoreArgs<KV> args = score_args<KV>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L);
+  hipLaunchKernelGGL(kern, dim3(U * p.splits), dim3(kNT), lay.total, st, args);
   return hipGetLastError();
 }
 
@@ -1229,6 +1370,36 @@ hipError_t launch_score_kv(const LaunchShape& s, const SplitPlan& p, const float
   return launch_score_g<KV, 128, false>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L, st);
 }
 
+template <typename KV>
+TauArgs<KV> tau_args(const LaunchShape& s, const SplitPlan& p, const void* v_pool, float alpha,
+                     float window, float* out, float* tau, int32_t* support, void* ws,
+                     const DecodeWs& L, int lcap) {
+  using ZT = typename KvTraits<KV>::Acc;
+  char* w = static_cast<char*>(ws);
+  TauArgs<KV> a;
+  a.v_pool = static_cast<const KV*>(v_pool);
+  a.H = s.num_q_heads;
+  a.Hkv = s.num_kv_heads;
+  a.G = s.group;
+  a.U = s.batch * s.num_kv_heads;
+  a.PS = s.page_size;
+  a.splits = p.regions;
+  a.cap = p.rcap;
+  a.list_cap = p.list_cap;
+  a.lcap = lcap;
+  a.alpha = alpha;
+  a.window_d = (double)window;
+  a.cand = reinterpret_cast<const Cand<ZT>*>(w + L.cand);
+  a.counts = reinterpret_cast<const int*>(w + L.counts);
+  a.maxima = reinterpret_cast<const ZT*>(w + L.maxima);
+  a.list_z = reinterpret_cast<ZT*>(w + L.list);
+  a.list_i = reinterpret_cast<int*>(a.list_z + (size_t)s.batch * s.num_q_heads * p.list_cap);
+  a.out = out;
+  a.tau_out = tau;
+  a.sup_out = support;
+  return a;
+}
+
 template <typename KV, int D, bool SPARSE>
 hipError_t launch_tau_pv_t(const LaunchShape& s, const SplitPlan& p, const void* v_pool,
                            const int32_t* bt, const int32_t* lens, const int32_t* sel, int budget,
@@ -1251,16 +1422,8 @@ hipError_t launch_tau_pv_t(const LaunchShape& s, const SplitPlan& p, const void*
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  char* w = static_cast<char*>(ws);
-  ZT* list_z = reinterpret_cast<ZT*>(w + L.list);
-  int* list_i = reinterpret_cast<int*>(list_z + (size_t)s.batch * s.num_q_heads * p.list_cap);
-  hipLaunchKernelGGL(kern, dim3(U * s.group), dim3(kNT), lds, st, static_cast<const KV*>(v_pool),
-                     s.num_q_heads, s.num_kv_heads, s.group, U, s.page_size, p.regions, p.rcap,
-                     p.list_cap, lcap, alpha, (double)window,
-                     reinterpret_cast<const Cand<ZT>*>(w + L.cand),
-                     reinterpret_cast<const int*>(w + L.counts),
-                     reinterpret_cast<const ZT*>(w + L.maxima), list_z, list_i, out, tau,
-                     support);
+  const TauArgs<KV> args = tau_args<KV>(s, p, v_pool, alpha, window, out, tau, support, ws, L, lcap);
+  hipLaunchKernelGGL(kern, dim3(U * s.group), dim3(kNT), lds, st, args);
   return hipGetLastError();
 }
 
