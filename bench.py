@@ -420,6 +420,40 @@ def main():
     kern_ms = np.array([[ev_kern.elapsed_ms(12 * i + 2 * j, 12 * i + 2 * j + 1) for j in range(6)]
                         for i in range(K)])
 
+    # Graph pass: the same step captured once as a HIP graph (on a stream of
+    # its own, default priority) and replayed K times, the flush still outside
+    # the timed region; every replay must reproduce the eager outputs bitwise.
+    eager = [x.clone() for x in (sel, out_s, out_f, tau_s, tau_f)]
+    gstream = torch.cuda.Stream(dev)
+    g_calls = [
+        E.Prepared("score_select", shape, q, meta, bt, lens, budget, sel, sel_ub, ws=ws_sel,
+                   stream=gstream),
+        E.Prepared("decode_sparse", shape, q, k, v, bt, lens, sel, budget, alpha, out_s, tau_s,
+                   sup_s, ws=ws_sp, stream=gstream),
+        E.Prepared("decode_full", shape, q, k, v, bt, lens, alpha, out_f, tau_f, sup_f, ws=ws_fu,
+                   stream=gstream)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gstream):
+        for c in g_calls:
+            c()
+    ev_graph = E.HipEvents(2 * K)
+    graph_same = True
+    for i in range(K):
+        flush(i)
+        ev_graph.record(2 * i, stream)
+        graph.replay()
+        ev_graph.record(2 * i + 1, stream)
+        if i == 0:
+            torch.cuda.synchronize()
+            graph_same = all(torch.equal(a, b) for a, b in
+                             zip(eager, (sel, out_s, out_f, tau_s, tau_f)))
+    torch.cuda.synchronize()
+    graph_ms = np.array([ev_graph.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)])
+    graph_same = graph_same and all(torch.equal(a, b) for a, b in
+                                    zip(eager, (sel, out_s, out_f, tau_s, tau_f)))
+    log(f"graph step {graph_ms.mean():.4f} ms, replays match eager: {graph_same}")
+
     sel_np = sel.cpu().numpy()
     nbytes = algorithmic_bytes(w, inp["seq_lens"], budget, sel_np, sup_s.cpu().numpy(),
                                sup_f.cpu().numpy())
@@ -438,6 +472,12 @@ def main():
                        "p90_ms": round(float(np.percentile(ms, 90)), 4),
                        "steps_per_s": round(1e3 / float(ms.mean()), 1), "bytes": by,
                        "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    paths["graph_step"] = {"ms": round(float(graph_ms.mean()), 4),
+                           "p10_ms": round(float(np.percentile(graph_ms, 10)), 4),
+                           "p90_ms": round(float(np.percentile(graph_ms, 90)), 4),
+                           "steps_per_s": round(1e3 / float(graph_ms.mean()), 1),
+                           "matches_eager": bool(graph_same),
+                           "note": "the whole step (sparse + full) replayed as one HIP graph"}
     meta_gbps = nbytes["_meta_build"] / (meta_ms * 1e-3) / 1e9
     paths["page_boxes"] = {"ms": round(meta_ms, 4), "bytes": nbytes["_meta_build"],
                            "GBps": round(meta_gbps, 1), "frac": round(meta_gbps / PEAK_HBM_GBPS, 4),

@@ -119,9 +119,15 @@ SplitPlan plan_sparse(const LaunchShape& s, int budget) {
   const int keep = budget < s.max_pages ? budget : s.max_pages;
   long long umax = (long long)s.group * keep;
   if (umax > s.max_pages) umax = s.max_pages;
-  int pps = kSparseTokensPerSplit / s.page_size;
+  const long long units = (long long)s.batch * s.num_kv_heads;
+  const long long page_bytes = (long long)s.page_size * s.head_dim * (s.bf16 ? 2 : 4);
+  const auto grid = [&](long long n) { return units * ((umax + n - 1) / n); };
+  long long pps = kSparseSplitBytes / page_bytes;
   if (pps < 1) pps = 1;
-  pps = fit_pps(s, pps, true, budget);
+  while (pps > 1 && grid(pps) < kSparseMinGrid) pps /= 2;
+  while (2 * pps * s.page_size <= kFullTokensPerSplit && pps < umax && grid(pps) >= kSparseMaxGrid)
+    pps *= 2;
+  pps = fit_pps(s, (int)pps, true, budget);
   SplitPlan p = finish_plan(s, umax, pps);
   p.list_cap = keep * s.page_size;
   return p;

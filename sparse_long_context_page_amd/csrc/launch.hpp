@@ -15,9 +15,16 @@ struct LaunchShape {
   bool bf16;
 };
 
-// Tokens handled by one workgroup of the gather-score kernels.
-constexpr int kSparseTokensPerSplit = 512;
+// Work of one workgroup of the gather-score kernels. Full cache: a fixed
+// 2048 tokens. Sparse: about kSparseSplitBytes of K, halved while the grid
+// would have fewer than kSparseMinGrid workgroups (short selections: more,
+// smaller splits keep the chip busy) and doubled, up to kFullTokensPerSplit
+// tokens, while it would have kSparseMaxGrid or more (long selections: each
+// workgroup's fixed cost is spread over more pages).
 constexpr int kFullTokensPerSplit = 2048;
+constexpr long long kSparseSplitBytes = 256 * 1024;
+constexpr long long kSparseMinGrid = 512;
+constexpr long long kSparseMaxGrid = 2048;
 constexpr int kMaxSplits = 4096;  // candidate regions per head (LDS-sized in the threshold kernel)
 
 constexpr int kNT = 256;
