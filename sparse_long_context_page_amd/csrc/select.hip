@@ -3,16 +3,20 @@
 // box metadata gives a deterministic upper bound on a page's best q.k) and
 // section 2.B policy 1 (keep the k pages with the highest bounds).
 //
-// bounds_kernel: one workgroup per (chunk of pages, sequence, KV head). The
-//   G query heads that share the KV head are bounded together, so each page's
-//   box is read once. Each page's (k_min, k_max) row pair is split over D/4
-//   lanes (four coordinates of each per lane); a workgroup covers 32 pages
-//   and issues all of its box loads before using the first, so the chip has
-//   many small workgroups in flight and little tail. Per coordinate the lane takes k_max
-//   where q_d >= 0 and k_min otherwise (the box maximum of q_d k_d), forms the
-//   products in float64 (exact: 24-bit x 8- or 24-bit significands) and sums
-//   in float64; a multi-value butterfly finishes the G sums across the LP
-//   lanes. Result rounded once to float32 (+0 for a zero).
+// bounds_mfma_kernel (bf16 boxes): the bound as a dot product on the matrix
+//   cores (described at the kernel); float32 sums of exact products, so a
+//   bound can differ from the exactly rounded one by float32 accumulation
+//   error (far inside the 1e-5 near-tie band of the selection).
+// bounds_kernel (float32 boxes): one workgroup per (chunk of pages,
+//   sequence, KV head). The G query heads that share the KV head are bounded
+//   together, so each page's box is read once. Each page's (k_min, k_max) row
+//   pair is split over D/4 lanes (four coordinates of each per lane); a
+//   workgroup covers 32 pages and issues all of its box loads before using
+//   the first. Per coordinate the lane takes k_max where q_d >= 0 and k_min
+//   otherwise (the box maximum of q_d k_d), forms the products in float64
+//   (exact: 24-bit x 24-bit significands) and sums in float64; a multi-value
+//   butterfly finishes the G sums across the LP lanes. Result rounded once
+//   to float32 (+0 for a zero).
 // select_kernel: one workgroup per (sequence, query head). Radix select on
 //   the order-preserving 32-bit image of the float32 bound, starting at the
 //   highest bit where the bounds differ (so the first histogram is spread),
@@ -22,6 +26,7 @@
 #include <type_traits>
 
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace ekv {
 
@@ -50,15 +55,19 @@ bounds_kernel(const float* __restrict__ q, const KV* __restrict__ meta,
   const int u = blockIdx.x % U;
   const int chunk = blockIdx.x / U;
   const int b = u / Hkv, g = u % Hkv;
+  const int j0 = chunk * kBoundPages;
+  // the chunk's block-table entries are read together with the length (not
+  // after it); entries past the sequence are dropped below
+  const int jt = j0 + (int)threadIdx.x;
+  const int bt_entry = threadIdx.x < kBoundPages && jt < max_pages
+                           ? block_table[(size_t)b * max_pages + jt] : -1;
   const int L = clamp_len(seq_lens[b], max_pages * ps);
   const int P = (L + ps - 1) / ps;
-  const int j0 = chunk * kBoundPages;
   if (j0 >= P) return;
   const int n = min(kBoundPages, P - j0);
 
-  // physical pages of the chunk: one coalesced load, then LDS
-  if (threadIdx.x < kBoundPages)
-    sphys[threadIdx.x] = threadIdx.x < n ? block_table[(size_t)b * max_pages + j0 + threadIdx.x] : -1;
+  // physical pages of the chunk, in LDS
+  if (threadIdx.x < kBoundPages) sphys[threadIdx.x] = (int)threadIdx.x < n ? bt_entry : -1;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int c = threadIdx.x % LP;
@@ -115,6 +124,193 @@ bounds_kernel(const float* __restrict__ q, const KV* __restrict__ meta,
     const int jj = t * PPB + threadIdx.x / LP;
     if (ok[t] && owner) ub[(size_t)(h0 + my_head) * ldu + j0 + jj] = (float)acc[0] + 0.0f;
   }
+}
+
+// Matrix-core bounds for bf16 boxes. Coordinate-wise,
+// max(q_d kmin_d, q_d kmax_d) = min(q_d, 0) kmin_d + max(q_d, 0) kmax_d, and a
+// box record is [kmin | kmax] (2D values), so a page's bound is the dot
+// product of c = [min(q, 0) | max(q, 0)] with its record: bounds of 16 pages
+// x 4 heads are a chain of v_mfma_f32_16x16x32_bf16 over the 2D record
+// values, the same operand scheme as the score kernel (c split exactly into
+// three bf16 parts, one (head, part) per A row; records as B columns, so
+// every product is exact and the sums are float32). Each wave streams tiles
+// of 16 records into two LDS buffers with direct-to-LDS 16-byte loads (one
+// instruction reads 1 KiB: two or four whole records, chunk c of record r
+// stored at slot c ^ (r & 15) so the operand reads hit distinct banks) and
+// scores one tile while the next is in flight. A workgroup covers
+// 64 * nt pages of one (sequence, KV head), the physical ids staged in LDS.
+//
+// Workgroups of the matrix-core bounds kernel: about 256 in all (one per CU,
+// a single round; on the 32K-512K workloads this beat 512-4096 shorter ones),
+// each wave taking `nt` tiles of 16 pages.
+constexpr long long kBoundsGrid = 256;
+constexpr int kBoundsMaxTiles = 16;
+
+// LDS of the matrix-core bounds kernel: two 16-record tiles per wave, the
+// chunk's physical page ids, then the split q table.
+__host__ __device__ constexpr size_t bounds_lds_bytes(int D, int G, int cp) {
+  return (size_t)kNW * 2 * 16 * 4 * D + (size_t)cp * 4 + (size_t)G * 3 * (2 * D + 8) * 2;
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(256)
+bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
+                   const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+                   float* __restrict__ ub, int H, int Hkv, int ps, int max_pages, int num_phys,
+                   int U, int ldu, int nt) {
+  constexpr int K2 = 2 * D;        // values per record
+  constexpr int RB = K2 * 2;       // bytes per record
+  constexpr int TP = 16;           // records (pages) per tile
+  constexpr int PB = TP * RB;      // bytes per tile
+  constexpr int NI = PB / 1024;    // 1 KiB load instructions per tile
+  constexpr int RPI = 1024 / RB;   // records per load instruction
+  constexpr int CPR = RB / 16;     // 16-byte chunks per record
+  constexpr int KS = K2 / 32;      // k-steps of 32 values
+  constexpr int NMB = (G + 3) / 4; // blocks of 4 heads
+  static_assert(NI * 1024 == PB && RPI * RB == 1024 && D % 32 == 0, "tiling");
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* sphys = reinterpret_cast<int*>(smem + kNW * 2 * PB);
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int u = blockIdx.x % U, chunk = blockIdx.x / U;
+  const int b = u / Hkv, g = u % Hkv;
+  const int cp = kNW * TP * nt;
+  const int j0 = chunk * cp;
+  // the chunk's block-table entries (up to kBoundsMaxTiles * 64, four per
+  // thread) are read together with the length, not after it
+  constexpr int BPT = kBoundsMaxTiles * kNW * TP / 256;
+  int bt_entry[BPT];
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    const int i = k * 256 + tid;
+    bt_entry[k] = i < cp && j0 + i < max_pages ? block_table[(size_t)b * max_pages + j0 + i] : -1;
+  }
+  // and so are this thread's q values of the group
+  const int h0 = b * H + g * G;
+  constexpr int QPT = (G * D + 255) / 256;
+  float qx[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = k * 256 + tid;
+    qx[k] = i < G * D ? q[(size_t)h0 * D + i] : 0.0f;
+  }
+  const int L = clamp_len(seq_lens[b], max_pages * ps);
+  const int P = (L + ps - 1) / ps;
+  if (j0 >= P) return;
+  const int n = min(cp, P - j0);
+  const int ntl = (n + TP - 1) / TP;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    const int i = k * 256 + tid;
+    if (i < ntl * TP) sphys[i] = i < n ? bt_entry[k] : -1;
+  }
+
+  const int kgrp = lane >> 4, col = lane & 15;
+  // c = [min(q, 0) | max(q, 0)] of the group's heads, split exactly into
+  // three bf16 parts, staged in LDS as rows (head, part) of 2D values (rows
+  // padded by 16 bytes against bank conflicts): each thread splits two or
+  // more q values, each lane then reads its A fragments with 16-byte loads.
+  bf16x8 qa[NMB][KS];
+  constexpr int QP = K2 + 8;  // row pitch in bf16 values
+  uint16_t* qtab = reinterpret_cast<uint16_t*>(smem + kNW * 2 * PB + (size_t)cp * 4);
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = k * 256 + tid;
+    if (i >= G * D) break;
+    const int h = i / D, d = i % D;
+    const float x = qx[k];
+    const uint32_t p0 = bf16_rne_bits(x);
+    const float r1 = x - __uint_as_float(p0 << 16);
+    const uint32_t p1 = bf16_rne_bits(r1);
+    const uint32_t p2 = bf16_rne_bits(r1 - __uint_as_float(p1 << 16));
+    const uint32_t pp[3] = {p0, p1, p2};
+#pragma unroll
+    for (int part = 0; part < 3; ++part) {
+      uint16_t* row = qtab + (size_t)(h * 3 + part) * QP;
+      row[d] = x < 0.0f ? (uint16_t)pp[part] : (uint16_t)0;
+      row[D + d] = x > 0.0f ? (uint16_t)pp[part] : (uint16_t)0;
+    }
+  }
+  // Source byte offset, within a record, of the chunk this lane stores in
+  // load instruction i (record i * RPI + lane / CPR of the tile).
+  int src_off[NI], rec_of[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = i * RPI + lane / CPR;
+    rec_of[i] = r;
+    src_off[i] = (((lane % CPR) ^ (r & 15)) * 16);
+  }
+  __syncthreads();
+
+  unsigned char* kbuf = smem + (size_t)wave * 2 * PB;
+  // Tile t into buffer bsel; records past the chunk, or with an invalid
+  // physical id, read page 0's record (its bound is not stored). Loads are
+  // issued on every path so that the waits count them exactly.
+  auto issue = [&](int t, int bsel) {
+    unsigned char* dst = kbuf + bsel * PB;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int p = t * TP + rec_of[i];
+      const int ph = p < ntl * TP ? sphys[p] : -1;
+      const bool ok = ph >= 0 && ph < num_phys;
+      const unsigned char* src = reinterpret_cast<const unsigned char*>(
+          meta + ((size_t)(ok ? ph : 0) * Hkv + g) * K2);
+      lds_load16(src + src_off[i], dst + i * 1024);
+    }
+  };
+  auto bound_tile = [&](int t, int bsel) {
+    const unsigned char* src = kbuf + bsel * PB;
+    bf16x8 kv[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kv[ks] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(
+                      src + col * RB + (((ks * 4 + kgrp) ^ (col & 15)) * 16)));
+    const int p = t * TP + col;
+    const int ph = sphys[p];
+    const bool ok = ph >= 0 && ph < num_phys;
+#pragma unroll
+    for (int blk = 0; blk < NMB; ++blk) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[blk][ks], kv[ks], acc, 0, 0, 0);
+      const int h = blk * 4 + kgrp;
+      if (h < G && p < n)
+        ub[(size_t)(h0 + h) * ldu + j0 + p] =
+            ok ? ((acc[0] + acc[1]) + acc[2]) + 0.0f : -__builtin_inff();
+    }
+  };
+  // A operand, read before any load into LDS is in flight: lane l holds row
+  // l % 16 = (head, part) and record values ks * 32 + (l / 16) * 8 .. +8 of
+  // c; rows past the group are zero.
+#pragma unroll
+  for (int blk = 0; blk < NMB; ++blk) {
+    const int h = blk * 4 + ((lane & 15) >> 2), part = lane & 3;
+    const bool live = h < G && part < 3;
+    const uint16_t* row = qtab + (size_t)((live ? h : 0) * 3 + (live ? part : 0)) * QP + kgrp * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + ks * 32);
+      qa[blk][ks] = __builtin_bit_cast(bf16x8, live ? v : make_uint4(0u, 0u, 0u, 0u));
+    }
+  }
+
+  // Two buffers alternate, each refilled as soon as its tile is bounded:
+  // before a buffer is read only the other buffer's NI loads may be
+  // outstanding.
+  issue(wave, 0);
+  issue(wave + kNW, 1);
+  for (int t = wave; t < ntl; t += 2 * kNW) {
+    wait_vmcnt<NI>();
+    bound_tile(t, 0);
+    issue(t + 2 * kNW, 0);
+    if (t + kNW >= ntl) break;
+    wait_vmcnt<NI>();
+    bound_tile(t + kNW, 1);
+    issue(t + 3 * kNW, 1);
+  }
+  wait_vmcnt<0>();  // no load into LDS is left in flight
 }
 
 // --------------------------------------------------------------------------
@@ -371,6 +567,33 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   }
 }
 
+template <int D, int G>
+static hipError_t launch_bounds_mfma(const LaunchShape& s, const float* q, const void* meta,
+                                     const int32_t* bt, const int32_t* lens, float* ub,
+                                     hipStream_t st) {
+  const int U = s.batch * s.num_kv_heads;
+  const long long tiles = (long long)U * ((s.max_pages + 15) / 16);
+  long long nt = (tiles + kBoundsGrid * kNW - 1) / (kBoundsGrid * kNW);
+  nt = nt < 1 ? 1 : (nt > kBoundsMaxTiles ? kBoundsMaxTiles : nt);
+  const int cp = kNW * 16 * (int)nt;
+  const long long chunks = (s.max_pages + cp - 1) / cp;
+  const size_t lds = bounds_lds_bytes(D, G, cp);
+  auto kern = bounds_mfma_kernel<D, G>;
+  static bool lds_raised = false;  // the attribute is per kernel; set it once
+  if (!lds_raised) {
+    const int most = (int)bounds_lds_bytes(D, 8, kNW * 16 * kBoundsMaxTiles);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, most);
+    if (e != hipSuccess) return e;
+    lds_raised = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)(U * chunks)), dim3(256), lds, st, q,
+                     static_cast<const bf16_t*>(meta), bt, lens, ub, s.num_q_heads,
+                     s.num_kv_heads, s.page_size, s.max_pages, s.num_phys, U,
+                     ub_ld(s.max_pages), (int)nt);
+  return hipGetLastError();
+}
+
 template <typename KV, int D, int G>
 static hipError_t launch_bounds_t(const LaunchShape& s, const float* q, const void* meta,
                                   const int32_t* bt, const int32_t* lens, float* ub,
@@ -387,11 +610,20 @@ template <typename KV, int D>
 static hipError_t launch_bounds_d(const LaunchShape& s, const float* q, const void* meta,
                                   const int32_t* bt, const int32_t* lens, float* ub,
                                   hipStream_t st) {
-  switch (s.group) {
-    case 1: return launch_bounds_t<KV, D, 1>(s, q, meta, bt, lens, ub, st);
-    case 2: return launch_bounds_t<KV, D, 2>(s, q, meta, bt, lens, ub, st);
-    case 4: return launch_bounds_t<KV, D, 4>(s, q, meta, bt, lens, ub, st);
-    default: return launch_bounds_t<KV, D, 8>(s, q, meta, bt, lens, ub, st);
+  if constexpr (sizeof(KV) == 2) {
+    switch (s.group) {
+      case 1: return launch_bounds_mfma<D, 1>(s, q, meta, bt, lens, ub, st);
+      case 2: return launch_bounds_mfma<D, 2>(s, q, meta, bt, lens, ub, st);
+      case 4: return launch_bounds_mfma<D, 4>(s, q, meta, bt, lens, ub, st);
+      default: return launch_bounds_mfma<D, 8>(s, q, meta, bt, lens, ub, st);
+    }
+  } else {
+    switch (s.group) {
+      case 1: return launch_bounds_t<KV, D, 1>(s, q, meta, bt, lens, ub, st);
+      case 2: return launch_bounds_t<KV, D, 2>(s, q, meta, bt, lens, ub, st);
+      case 4: return launch_bounds_t<KV, D, 4>(s, q, meta, bt, lens, ub, st);
+      default: return launch_bounds_t<KV, D, 8>(s, q, meta, bt, lens, ub, st);
+    }
   }
 }
 
