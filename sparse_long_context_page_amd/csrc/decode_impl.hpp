@@ -462,7 +462,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
   };
 
   const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc),
-                                        score_kbuf_bytes(sizeof(KV) == 2, PS, D, SPARSE));
+                                        score_kbuf_bytes(sizeof(KV) == 2, PS, D, SPARSE), D);
   Acc* wmax = reinterpret_cast<Acc*>(smem + lay.wmax);
   int* wcnt = reinterpret_cast<int*>(smem + lay.wcnt);
   int* slice = reinterpret_cast<int*>(smem + lay.slice);
@@ -480,6 +480,18 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
                              spill + (size_t)(b * Hkv + g) * splits * kNW * G * lay.wcap +
                                  (size_t)split * kNW * G * lay.wcap,
                              lay.wcap};
+
+  // Matrix-core path: this thread's q values of the group, read now so that
+  // their latency overlaps the slice set-up.
+  constexpr int QPT = (G * D + kNT - 1) / kNT;
+  float qx[QPT];
+  if constexpr (MFMA) {
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int i = k * kNT + tid;
+      qx[k] = i < G * D ? q[(size_t)bh0 * D + i] : 0.0f;
+    }
+  }
 
   const int n_slice = build_slice<G, SPARSE, DEV>(
       sel, block_table, b, bh0, budget, P, max_pages, split, pps,
@@ -516,33 +528,37 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     constexpr int NBUF = score_kbuf_pages(SPARSE);
     unsigned char* kbuf = smem + lay.kbuf + (size_t)wave * NBUF * PB;
 
-    // A operand: lane l holds row l%16 = (head, part) and dims
-    // ks*32 + (l/16)*8 .. +8; q is read with unconditional 16-byte loads
-    // (rows past the group read head 0 and are zeroed).
+    // q split exactly into three bf16 parts, staged in LDS as rows
+    // (head, part): each thread splits its q values, then lane l reads its A
+    // fragments (row l%16 = (head, part), dims ks*32 + (l/16)*8 .. +8) with
+    // 16-byte loads; rows past the group are zero.
+    constexpr int QP = qtab_pitch(D);
+    uint16_t* qtab = reinterpret_cast<uint16_t*>(smem + lay.qtab);
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int i = k * kNT + tid;
+      if (i >= G * D) break;
+      const float x = qx[k];
+      const uint32_t p0 = bf16_rne_bits(x);
+      const float r1 = x - __uint_as_float(p0 << 16);
+      const uint32_t p1 = bf16_rne_bits(r1);
+      const uint32_t p2 = bf16_rne_bits(r1 - __uint_as_float(p1 << 16));
+      uint16_t* row = qtab + (size_t)(i / D) * 3 * QP + (i % D);
+      row[0] = (uint16_t)p0;
+      row[QP] = (uint16_t)p1;
+      row[2 * QP] = (uint16_t)p2;
+    }
+    __syncthreads();
     bf16x8 qa[NMB][KS];
 #pragma unroll
     for (int blk = 0; blk < NMB; ++blk) {
       const int h = blk * 4 + ((lane & 15) >> 2), part = lane & 3;
       const bool live = h < G && part < 3;
-      const float* qh = q + (size_t)(bh0 + (h < G ? h : 0)) * D + kgrp * 8;
-      float4 qv[KS][2];
+      const uint16_t* row = qtab + (size_t)((live ? h : 0) * 3 + (live ? part : 0)) * QP + kgrp * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        qv[ks][0] = *reinterpret_cast<const float4*>(qh + ks * 32);
-        qv[ks][1] = *reinterpret_cast<const float4*>(qh + ks * 32 + 4);
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const float x[8] = {qv[ks][0].x, qv[ks][0].y, qv[ks][0].z, qv[ks][0].w,
-                            qv[ks][1].x, qv[ks][1].y, qv[ks][1].z, qv[ks][1].w};
-        uint32_t w[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const uint32_t lo = live ? bf16_part(x[2 * jj], part) : 0u;
-          const uint32_t hi = live ? bf16_part(x[2 * jj + 1], part) : 0u;
-          w[jj] = lo | (hi << 16);
-        }
-        qa[blk][ks] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        const uint4 v = *reinterpret_cast<const uint4*>(row + ks * 32);
+        qa[blk][ks] = __builtin_bit_cast(bf16x8, live ? v : make_uint4(0u, 0u, 0u, 0u));
       }
     }
     // Source byte offset, within a page, of the chunk this lane stores in
@@ -1275,7 +1291,7 @@ hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float*
   using ZT = typename KvTraits<KV>::Acc;
   const int U = s.batch * s.num_kv_heads;
   const ScoreLds lay = score_lds_layout(G, PS, p.pages_per_split, SPARSE, s.max_pages, budget,
-                                        sizeof(ZT), score_kbuf_bytes(s.bf16, PS, D, SPARSE));
+                                        sizeof(ZT), score_kbuf_bytes(s.bf16, PS, D, SPARSE), D);
   auto kern = score_kernel<KV, D, G, PS, SPARSE>;
   static bool lds_raised = false;  // the attribute is per kernel; set it once, to the most
   if (!lds_raised) {               // any plan asks for

@@ -43,8 +43,12 @@ constexpr size_t kMaxScoreLdsBytes = 150 * 1024;  // most LDS a score-kernel pla
 // LDS layout of the score kernel (bytes), shared by host sizing and device carving.
 struct ScoreLds {
   int wcap;  // candidates one wave can produce per head: every token of its pages
-  size_t kbuf, rz, ri, wmax, wcnt, slice, slots, phys, tmp, bitmap, ssel, total;
+  size_t kbuf, qtab, rz, ri, wmax, wcnt, slice, slots, phys, tmp, bitmap, ssel, total;
 };
+
+// Row pitch (bf16 values) of the split-q table of the matrix-core kernels:
+// one row per (head, part), padded by 16 bytes against LDS bank conflicts.
+__host__ __device__ constexpr int qtab_pitch(int k) { return k + 8; }
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
@@ -57,14 +61,16 @@ __host__ __device__ inline int score_kbuf_bytes(bool bf16, int ps, int head_dim,
 }
 
 // zbytes: bytes of one score (4 for bf16 caches, 8 for float32 caches);
-// kbuf_wave: score_kbuf_bytes.
+// kbuf_wave: score_kbuf_bytes (the matrix-core path when > 0).
 __host__ __device__ inline ScoreLds score_lds_layout(int G, int ps, int pps, bool sparse,
                                                      int max_pages, int budget, int zbytes,
-                                                     int kbuf_wave) {
+                                                     int kbuf_wave, int head_dim) {
   ScoreLds l;
   l.wcap = ((pps + kNW - 1) / kNW) * ps;
   size_t o = 0;
   l.kbuf = o; o = align16(o + (size_t)kNW * kbuf_wave);
+  l.qtab = o;
+  if (kbuf_wave > 0) o = align16(o + (size_t)G * 3 * qtab_pitch(head_dim) * 2);
   const size_t nreg = (size_t)kNW * G * kListSlots;
   l.rz = o; o = align16(o + nreg * zbytes);
   l.ri = o; o = align16(o + nreg * 4);
