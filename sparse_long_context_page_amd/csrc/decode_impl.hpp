@@ -379,6 +379,47 @@ __device__ double solve_tau_regs(const double (&a)[K], double am1, double m, int
   return t;
 }
 
+// Exact threshold for m = 1 (alpha = 2) and m = 2 (alpha = 1.5) by the
+// sort-based rule, without sorting: one wave, lane i holding a_i (-DBL_MAX
+// past the n <= 64 entries). Lane i finds its rank k_i in descending order
+// (ties to the lower lane) and the sums S1, S2 of b = a - amax over the k_i
+// largest entries; the support size k* is the largest rank with
+// sum_{j <= k} (a_(j) - a_(k))^m < 1 (the sum grows with k), and tau = amax + t with t the root of
+// sum_{j <= k*} (b_(j) - t)^m = 1: (S1 - 1) / k* for m = 1, the smaller root
+// (S1 - sqrt(S1^2 - k* (S2 - 1))) / k* for m = 2. Every lane returns tau.
+__device__ double solve_tau_ranked(double a, int n, int mcode, double amax) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const double bi = a - amax;
+  int k = 0;
+  double s1 = 0.0, s2 = 0.0;
+  for (int j = 0; j < n; ++j) {
+    const uint64_t bits = __double_as_longlong(a);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)bits, j);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(bits >> 32), j);
+    const double aj = __longlong_as_double(((uint64_t)hi << 32) | lo);
+    if (aj > a || (aj == a && j <= lane)) {
+      const double bj = aj - amax;
+      ++k;
+      s1 += bj;
+      s2 = fma(bj, bj, s2);
+    }
+  }
+  const bool live = lane < n;
+  const double F = mcode == 1 ? s1 - k * bi : s2 - 2.0 * bi * s1 + k * bi * bi;
+  const int kstar = wave_max((live && F < 1.0) ? k : 0);  // >= 1: F = 0 at rank 1
+  const uint64_t at = __ballot(live && k == kstar);
+  const int src = __ffsll((unsigned long long)at) - 1;
+  const double S1 = __shfl(s1, src), S2 = __shfl(s2, src);
+  double t;
+  if (mcode == 1) {
+    t = (S1 - 1.0) / kstar;
+  } else {
+    const double disc = fmax(0.0, S1 * S1 - kstar * (S2 - 1.0));
+    t = (S1 - sqrt(disc)) / kstar;
+  }
+  return amax + t;
+}
+
 // Candidate lists of the score kernel: a wave appends the survivors of each
 // head in page order; the first kListSlots of them stay in LDS, the rest go
 // to the wave's spill area in global memory (only when scores are nearly
@@ -1119,7 +1160,9 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
         const int e = k * kWave + lane;
         a[k] = e < n_list ? am1 * (double)lz[e] : -DBL_MAX;
       }
-      const double t = solve_tau_regs<kRegList>(a, am1, m, mcode, amax);
+      const double t = (n_list <= kWave && (mcode == 1 || mcode == 2))
+                           ? solve_tau_ranked(a[0], n_list, mcode, amax)
+                           : solve_tau_regs<kRegList>(a, am1, m, mcode, amax);
       int o = 0;
 #pragma unroll
       for (int k = 0; k < kRegList; ++k) {

@@ -30,7 +30,10 @@
 
 namespace ekv {
 
-constexpr int kSelNT = 256;
+// Threads of the select kernel: 512 when there are few heads (fewer keys
+// per thread shorten each pass), 256 from kSelWideFrom heads on (the grid
+// then fills the chip and smaller workgroups pack better).
+constexpr int kSelWideFrom = 256;
 constexpr int kSelLds = 16384;  // bounds staged in LDS when the sequence has at most this many pages
 constexpr int kBoundPages = 32;  // pages per workgroup of the bounds kernel
 
@@ -145,11 +148,12 @@ bounds_kernel(const float* __restrict__ q, const KV* __restrict__ meta,
 // each wave taking `nt` tiles of 16 pages.
 constexpr long long kBoundsGrid = 256;
 constexpr int kBoundsMaxTiles = 16;
+constexpr int kBoundsBufs = 2;  // tile buffers per wave
 
-// LDS of the matrix-core bounds kernel: two 16-record tiles per wave, the
+// LDS of the matrix-core bounds kernel: kBoundsBufs 16-record tiles per wave, the
 // chunk's physical page ids, then the split q table.
 __host__ __device__ constexpr size_t bounds_lds_bytes(int D, int G, int cp) {
-  return (size_t)kNW * 2 * 16 * 4 * D + (size_t)cp * 4 + (size_t)G * 3 * (2 * D + 8) * 2;
+  return (size_t)kNW * kBoundsBufs * 16 * 4 * D + (size_t)cp * 4 + (size_t)G * 3 * (2 * D + 8) * 2;
 }
 
 template <int D, int G>
@@ -169,7 +173,7 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
   constexpr int NMB = (G + 3) / 4; // blocks of 4 heads
   static_assert(NI * 1024 == PB && RPI * RB == 1024 && D % 32 == 0, "tiling");
   extern __shared__ __align__(16) unsigned char smem[];
-  int* sphys = reinterpret_cast<int*>(smem + kNW * 2 * PB);
+  int* sphys = reinterpret_cast<int*>(smem + kNW * kBoundsBufs * PB);
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int u = blockIdx.x % U, chunk = blockIdx.x / U;
@@ -212,7 +216,7 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
   // more q values, each lane then reads its A fragments with 16-byte loads.
   bf16x8 qa[NMB][KS];
   constexpr int QP = K2 + 8;  // row pitch in bf16 values
-  uint16_t* qtab = reinterpret_cast<uint16_t*>(smem + kNW * 2 * PB + (size_t)cp * 4);
+  uint16_t* qtab = reinterpret_cast<uint16_t*>(smem + kNW * kBoundsBufs * PB + (size_t)cp * 4);
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
     const int i = k * 256 + tid;
@@ -242,7 +246,7 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
   }
   __syncthreads();
 
-  unsigned char* kbuf = smem + (size_t)wave * 2 * PB;
+  unsigned char* kbuf = smem + (size_t)wave * kBoundsBufs * PB;
   // Tile t into buffer bsel; records past the chunk, or with an invalid
   // physical id, read page 0's record (its bound is not stored). Loads are
   // issued on every path so that the waits count them exactly.
@@ -296,25 +300,23 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
     }
   }
 
-  // Two buffers alternate, each refilled as soon as its tile is bounded:
-  // before a buffer is read only the other buffer's NI loads may be
+  // kBoundsBufs buffers form a ring, each refilled as soon as its tile is
+  // bounded: before a buffer is read only the other buffers' loads may be
   // outstanding.
-  issue(wave, 0);
-  issue(wave + kNW, 1);
-  for (int t = wave; t < ntl; t += 2 * kNW) {
-    wait_vmcnt<NI>();
-    bound_tile(t, 0);
-    issue(t + 2 * kNW, 0);
-    if (t + kNW >= ntl) break;
-    wait_vmcnt<NI>();
-    bound_tile(t + kNW, 1);
-    issue(t + 3 * kNW, 1);
+#pragma unroll
+  for (int k = 0; k < kBoundsBufs; ++k) issue(wave + k * kNW, k);
+  for (int t = wave, k = 0; t < ntl; t += kNW) {
+    wait_vmcnt<(kBoundsBufs - 1) * NI>();
+    bound_tile(t, k);
+    issue(t + kBoundsBufs * kNW, k);
+    k = k + 1 == kBoundsBufs ? 0 : k + 1;
   }
   wait_vmcnt<0>();  // no load into LDS is left in flight
 }
 
 // --------------------------------------------------------------------------
 
+template <int kSelNT>
 __global__ void __launch_bounds__(kSelNT)
 select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens, int H, int G,
               int Hkv, int U, int ps, int max_pages, int ldu, int budget,
@@ -392,7 +394,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
     ured[wave][0] = mn;
     ured[wave][1] = mx;
   }
-  hist[0][tid] = 0;  // kSelNT == 256 bins
+  if (tid < 256) hist[0][tid] = 0;
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -417,7 +419,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
       const int lo = hb >= 7 ? hb - 7 : 0;
       const int width = hb - lo + 1;
       const uint32_t dmask = (1u << width) - 1u;
-      hist[cur ^ 1][tid] = 0;
+      if (tid < 256) hist[cur ^ 1][tid] = 0;
       for (int base = 0; base < n4; base += UNR * kSelNT) {
         uint4 v[UNR] = {};
 #pragma unroll
@@ -640,7 +642,13 @@ hipError_t launch_bounds(const LaunchShape& s, const float* q, const void* meta,
 hipError_t launch_select(const LaunchShape& s, const float* ub, const int32_t* lens, int budget,
                          int32_t* sel, float* sel_ub, hipStream_t st) {
   const int U = s.batch * s.num_kv_heads;
-  hipLaunchKernelGGL(select_kernel, dim3(U * s.group), dim3(kSelNT), 0, st, ub, lens,
+  if (U * s.group >= kSelWideFrom)
+    hipLaunchKernelGGL(select_kernel<256>, dim3(U * s.group), dim3(256), 0, st, ub, lens,
+                     s.num_q_heads, s.group, s.num_kv_heads, U, s.page_size, s.max_pages,
+                     ub_ld(s.max_pages), budget,
+                     sel, sel_ub);
+  else
+    hipLaunchKernelGGL(select_kernel<512>, dim3(U * s.group), dim3(512), 0, st, ub, lens,
                      s.num_q_heads, s.group, s.num_kv_heads, U, s.page_size, s.max_pages,
                      ub_ld(s.max_pages), budget,
                      sel, sel_ub);
