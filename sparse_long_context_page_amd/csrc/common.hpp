@@ -40,74 +40,19 @@ __device__ __forceinline__ float order_float(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
-  return v;
-}
-
-template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, shfl_xor(v, m));
-  return v;
-}
-
-template <typename T>
-__device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = min(v, shfl_xor(v, m));
-  return v;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active), with
+// DPP only: shifts by 1, 2, 4 and 8 within each row of 16 lanes, then the
+// last lane of row 0 (and 2) is added to row 1 (and 3), and that of row 1 to
+// rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
+  (void)lane;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
-}
-
-// Exclusive block prefix sum of one int per thread. `tmp` holds at least
-// NT/64 ints of LDS. Returns the exclusive prefix; *total gets the sum.
-// Contains barriers: every thread of the block must call it.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  constexpr int NW = NT / kWave;
-  int inc = wave_incl_scan(v, lane);
-  if (lane == kWave - 1) tmp[wid] = inc;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    int s = tmp[w];
-    base += (w < wid) ? s : 0;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + inc - v;
-}
-
-template <int NT, typename T, typename Op>
-__device__ __forceinline__ T block_reduce(T v, T* tmp, Op op) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  constexpr int NW = NT / kWave;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = op(v, shfl_xor(v, m));
-  if (lane == 0) tmp[wid] = v;
-  __syncthreads();
-  T r = tmp[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) r = op(r, tmp[w]);
-  __syncthreads();
-  return r;
 }
 
 // Value held by a partner lane whose index differs from this lane's in bit W
@@ -158,6 +103,67 @@ __device__ __forceinline__ T wave_allsum(T v) {
   v += partner<4>(v);
   v += partner<8>(v);
   return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// op over the 64 lanes (every lane active), the same value in every lane:
+// DPP lane swaps within each row of 16, then the four row results.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_allreduce(T v, Op op) {
+  v = op(v, partner<1>(v));
+  v = op(v, partner<2>(v));
+  v = op(v, partner<4>(v));
+  v = op(v, partner<8>(v));
+  return op(op(lane_value(v, 0), lane_value(v, 16)), op(lane_value(v, 32), lane_value(v, 48)));
+}
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  return wave_allreduce(v, [](T a, T b) { return a + b; });
+}
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+  return wave_allreduce(v, [](T a, T b) { return max(a, b); });
+}
+template <typename T>
+__device__ __forceinline__ T wave_min(T v) {
+  return wave_allreduce(v, [](T a, T b) { return min(a, b); });
+}
+
+// Exclusive block prefix sum of one int per thread. `tmp` holds at least
+// NT/64 ints of LDS. Returns the exclusive prefix; *total gets the sum.
+// Contains barriers: every thread of the block must call it.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  constexpr int NW = NT / kWave;
+  int inc = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) tmp[wid] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    int s = tmp[w];
+    base += (w < wid) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+template <int NT, typename T, typename Op>
+__device__ __forceinline__ T block_reduce(T v, T* tmp, Op op) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  constexpr int NW = NT / kWave;
+  v = wave_allreduce(v, op);
+  if (lane == 0) tmp[wid] = v;
+  __syncthreads();
+  T r = tmp[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = op(r, tmp[w]);
+  __syncthreads();
+  return r;
 }
 
 // Multi-value butterfly. NV partial sums v[0..NV) are spread over groups of

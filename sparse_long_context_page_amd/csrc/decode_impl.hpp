@@ -409,7 +409,7 @@ __device__ double solve_tau_ranked(double a, int n, int mcode, double amax) {
   const int kstar = wave_max((live && F < 1.0) ? k : 0);  // >= 1: F = 0 at rank 1
   const uint64_t at = __ballot(live && k == kstar);
   const int src = __ffsll((unsigned long long)at) - 1;
-  const double S1 = __shfl(s1, src), S2 = __shfl(s2, src);
+  const double S1 = lane_value(s1, src), S2 = lane_value(s2, src);
   double t;
   if (mcode == 1) {
     t = (S1 - 1.0) / kstar;

@@ -324,7 +324,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   constexpr int NW = kSelNT / kWave;
   constexpr int UNR = 4;  // 16-byte loads in flight per thread
   __shared__ __align__(16) uint32_t sord[kSelLds];
-  __shared__ int hist[2][256];
+  __shared__ __align__(16) int hist[2][256];
   __shared__ unsigned int ured[NW][2];
   __shared__ int wcnt[NW][2];
   __shared__ int bc[3];
@@ -447,12 +447,10 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
           c4[i] = hist[cur][4 * lane + i];
           s += c4[i];
         }
-        int suf = s;  // keys in this lane's bins and above
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-          const int o = __shfl_down(suf, d, kWave);
-          if (lane + d < kWave) suf += o;
-        }
+        // keys in this lane's bins and above: the total less the keys in
+        // lower lanes' bins
+        const int incl = wave_incl_scan(s, lane);
+        const int suf = lane_value(incl, kWave - 1) - incl + s;
         int above = suf - s;
         if (above < k && k <= suf) {
 #pragma unroll
