@@ -151,6 +151,31 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   return base + inc - v;
 }
 
+// Exclusive block prefix sums of two ints per thread at once (one barrier
+// pair). `tmp` holds at least 2 * NT/64 ints of LDS. Every thread of the
+// block must call it.
+template <int NT>
+__device__ __forceinline__ void block_excl_scan2(int a, int b, int* tmp, int* ea, int* eb) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  constexpr int NW = NT / kWave;
+  const int ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
+  if (lane == kWave - 1) {
+    tmp[2 * wid] = ia;
+    tmp[2 * wid + 1] = ib;
+  }
+  __syncthreads();
+  int ba = 0, bb = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    ba += (w < wid) ? tmp[2 * w] : 0;
+    bb += (w < wid) ? tmp[2 * w + 1] : 0;
+  }
+  __syncthreads();
+  *ea = ba + ia - a;
+  *eb = bb + ib - b;
+}
+
 template <int NT, typename T, typename Op>
 __device__ __forceinline__ T block_reduce(T v, T* tmp, Op op) {
   const int lane = threadIdx.x & (kWave - 1);

@@ -477,91 +477,41 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   }
 
   // Keep keys above the prefix and the first k (by page index) equal to it,
-  // written in ascending page order. Wave w owns a contiguous range of quads
-  // and walks it 64 quads at a time: page 4*i4+e comes after every page of
-  // lower lanes and after entries e' < e of its own lane.
-  const int spq = ((n4 + NW * kWave - 1) / (NW * kWave)) * kWave;
-  const int q0 = min(n4, wave * spq), q1 = min(n4, q0 + spq);
-  const uint64_t ltm = lanemask_below(lane);
-  int n_eq = 0, n_gt = 0;
-  for (int base = q0; base < q1; base += UNR * kWave) {
-    uint4 v[UNR] = {};
+  // written in ascending page order: thread t owns a contiguous run of quads,
+  // one block scan of the runs' (above, equal) counts places each run, and
+  // the thread writes its kept pages in order.
+  const int qpt = (n4 + kSelNT - 1) / kSelNT;
+  const int q0 = min(n4, tid * qpt), q1 = min(n4, q0 + qpt);
+  int n_gt = 0, n_eq = 0;
+  for (int i4 = q0; i4 < q1; ++i4) {
+    const uint4 v = quad(i4);
 #pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      const int i4 = base + r * kWave + lane;
-      if (i4 < q1) v[r] = quad(i4);
-    }
-#pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      const int i4 = base + r * kWave + lane;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool valid = i4 < q1 && 4 * i4 + e < P;
-        const uint32_t m = at(v[r], e) & pmask;
-        n_eq += (valid && m == prefix) ? 1 : 0;
-        n_gt += (valid && m > prefix) ? 1 : 0;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const bool valid = 4 * i4 + e < P;
+      const uint32_t m = at(v, e) & pmask;
+      n_eq += (valid && m == prefix) ? 1 : 0;
+      n_gt += (valid && m > prefix) ? 1 : 0;
     }
   }
-  n_eq = wave_sum(n_eq);
-  n_gt = wave_sum(n_gt);
-  if (lane == 0) {
-    wcnt[wave][0] = n_eq;
-    wcnt[wave][1] = n_gt;
-  }
-  __syncthreads();
-  int eq_base = 0, sel_base = 0;
-  for (int w = 0; w < wave; ++w) {
-    const int e = wcnt[w][0];
-    sel_base += wcnt[w][1] + max(0, min(e, k - eq_base));
-    eq_base += e;
-  }
-  for (int base = q0; base < q1; base += UNR * kWave) {
-    uint4 v[UNR] = {};
+  int gt_base, eq_base;
+  block_excl_scan2<kSelNT>(n_gt, n_eq, &wcnt[0][0], &gt_base, &eq_base);
+  int pos = gt_base + min(eq_base, k);
+  int eqc = eq_base;  // equal keys on lower pages
+  for (int i4 = q0; i4 < q1 && pos < budget; ++i4) {
+    const uint4 v = quad(i4);
 #pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      const int i4 = base + r * kWave + lane;
-      if (i4 < q1) v[r] = quad(i4);
-    }
-#pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      const int i4 = base + r * kWave + lane;
-      bool eq[4], gt[4];
-      uint64_t beq[4];
-      int eq_below = 0;  // equal keys on lower lanes of this step
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool valid = i4 < q1 && 4 * i4 + e < P;
-        const uint32_t m = at(v[r], e) & pmask;
-        eq[e] = valid && m == prefix;
-        gt[e] = valid && m > prefix;
-        beq[e] = __ballot(eq[e]);
-        eq_below += __popcll(beq[e] & ltm);
-      }
-      bool take[4];
-      int own_eq = 0;
-      uint64_t btk[4];
-      int tk_below = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        take[e] = gt[e] || (eq[e] && eq_base + eq_below + own_eq < k);
-        own_eq += eq[e] ? 1 : 0;
-        btk[e] = __ballot(take[e]);
-        tk_below += __popcll(btk[e] & ltm);
-      }
-      int pos = sel_base + tk_below;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (take[e] && pos < budget) {
+    for (int e = 0; e < 4; ++e) {
+      const bool valid = 4 * i4 + e < P;
+      const uint32_t m = at(v, e) & pmask;
+      const bool eq = valid && m == prefix;
+      const bool take = (valid && m > prefix) || (eq && eqc < k);
+      eqc += eq ? 1 : 0;
+      if (take) {
+        if (pos < budget) {
           out[pos] = 4 * i4 + e;
-          if (out_ub) out_ub[pos] = order_float(at(v[r], e));
-          ++pos;
+          if (out_ub) out_ub[pos] = order_float(at(v, e));
         }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        eq_base += __popcll(beq[e]);
-        sel_base += __popcll(btk[e]);
+        ++pos;
       }
     }
   }
