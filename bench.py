@@ -44,7 +44,7 @@ METRIC = ("decode steps/s + achieved HBM GB/s (% of peak), sparse vs full entmax
           "32K–512K")
 PEAK_HBM_GBPS = 8000.0
 KERNEL_NAMES = ["bounds", "select", "score_sparse", "tau_pv_sparse", "score_full", "tau_pv_full"]
-KERNEL_SOURCES = ["common.hpp", "launch.hpp", "select.hip", "decode_impl.hpp", "decode_bf16.hip",
+KERNEL_SOURCES = ["common.hpp", "launch.hpp", "mfma.hpp", "select.hip", "decode_impl.hpp", "decode_bf16.hip",
                   "decode_f32.hip", "meta.hip", "api.hip"]
 
 
