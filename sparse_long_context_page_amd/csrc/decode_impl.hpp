@@ -868,23 +868,56 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     const Acc thr = mg - window;
     const size_t r = (size_t)(bh0 + h) * splits + split;
     Cand<Acc>* dst = cand + r * (size_t)cap;
-    int o = 0;
+    // The waves' lists, concatenated in wave order, are read kWave *
+    // kPassRegs entries at a time with every read of a batch issued before
+    // the first is used (spilled entries then cost one round trip per batch,
+    // not one per 64 entries).
+    int nb[kNW + 1];  // list starts in the concatenation
+    nb[0] = 0;
+    int nsp = 0;      // spilled entries of this head
+#pragma unroll
     for (int w = 0; w < kNW; ++w) {
       const int n = wcnt[w * G + h];
-      for (int e0 = 0; e0 < n; e0 += kWave) {
-        const int e = e0 + lane;
-        Acc z = neg_inf<Acc>();
-        int ix = 0;
-        if (e < n) lists.get(w, h, G, e, z, ix);
-        const bool f = e < n && z >= thr;
+      nb[w + 1] = nb[w] + n;
+      nsp += max(0, n - kListSlots);
+    }
+    const int ntot = nb[kNW];
+    int o = 0;
+    for (int base = 0; base < ntot; base += kWave * kPassRegs) {
+      Acc zr[kPassRegs];
+      int ir[kPassRegs], pr[kPassRegs];
+      Cand<Acc> cs[kPassRegs];
+#pragma unroll
+      for (int k = 0; k < kPassRegs; ++k) {
+        const int t = min(base + k * kWave + lane, ntot - 1);
+        int w = 0;
+#pragma unroll
+        for (int v = 1; v < kNW; ++v) w += (t >= nb[v]) ? 1 : 0;
+        const int pos = t - nb[w];
+        pr[k] = pos;
+        const int lo = (w * G + h) * kListSlots + min(pos, kListSlots - 1);
+        zr[k] = lists.rz[lo];
+        ir[k] = lists.ri[lo];
+        if (nsp > 0)  // (uniform) the spill slot, or the area's first slot
+          cs[k] = lists.spill[pos >= kListSlots
+                                  ? (size_t)(w * G + h) * lists.wcap + (pos - kListSlots)
+                                  : 0];
+      }
+#pragma unroll
+      for (int k = 0; k < kPassRegs; ++k) {
+        if (nsp > 0 && pr[k] >= kListSlots) {
+          zr[k] = cs[k].z;
+          ir[k] = cs[k].idx;
+        }
+        const bool f = base + k * kWave + lane < ntot && zr[k] >= thr;
         const uint64_t bal = __ballot(f);
         if (f) {
           if constexpr (DEV) {
-            st_dev_cand(dst + o + __popcll(bal & ltm), z, ix);
+            st_dev_cand(dst + o + __popcll(bal & ltm), zr[k], ir[k]);
           } else {
             Cand<Acc> cv;
-            cv.z = z;
-            cv.idx = ix;
+            cv.z = zr[k];
+            cv.idx = ir[k];
             dst[o + __popcll(bal & ltm)] = cv;
           }
         }

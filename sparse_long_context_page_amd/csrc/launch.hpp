@@ -38,6 +38,7 @@ constexpr int kSelCopy = 8192;  // selection ints staged in LDS by the sparse sc
 
 
 constexpr int kListSlots = 64;  // LDS candidate slots per (wave, head) in the score kernel
+constexpr int kPassRegs = 4;    // candidates per lane read at once by the score kernel's final pass
 constexpr size_t kMaxScoreLdsBytes = 150 * 1024;  // most LDS a score-kernel plan may use
 
 // LDS layout of the score kernel (bytes), shared by host sizing and device carving.
