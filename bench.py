@@ -141,6 +141,10 @@ def _oracle_head(args):
     return b, h, dt, sel, sp.out, fu.out
 
 
+ONE_CORE_WORKLOADS = ("tiny_4k_f32", "extreme_512k")  # also timed on one core
+ONE_CORE_HEADS = 4
+
+
 def cpu_baseline(inp, budget, alpha, n_heads: int, seed: int = 0):
     """Time the oracle's step (bounds+selection, sparse decode, full decode)
     on a sample of (sequence, head) pairs; page boxes are built before timing,
@@ -167,6 +171,18 @@ def cpu_baseline(inp, budget, alpha, n_heads: int, seed: int = 0):
         results = pool.map(_oracle_head, [(b, h, budget, alpha) for b, h in pairs])
     wall = time.perf_counter() - t0
     step_s = wall * (w.batch * w.num_q_heads) / n_heads
+    one_core = None
+    if w.name in ONE_CORE_WORKLOADS:
+        # the same work on one core, in this process, on the first few pairs
+        from threadpoolctl import threadpool_limits
+        n1 = min(ONE_CORE_HEADS, n_heads)
+        with threadpool_limits(1):
+            t1 = time.perf_counter()
+            for b, h in pairs[:n1]:
+                _oracle_head((b, h, budget, alpha))
+            wall1 = time.perf_counter() - t1
+        one_core = {"value": 1.0 / (wall1 * (w.batch * w.num_q_heads) / n1), "unit": "steps/s",
+                    "cores": 1, "sample": f"{n1} (sequence, head) pairs, scaled per step"}
     return {
         "value": 1.0 / step_s,
         "unit": "steps/s",
@@ -176,6 +192,7 @@ def cpu_baseline(inp, budget, alpha, n_heads: int, seed: int = 0):
                    f"selection, sparse and full fp64 decode each; wall {wall:.2f} s on {workers} "
                    f"processes, scaled by {w.batch * w.num_q_heads}/{n_heads} heads per step; "
                    f"page boxes prebuilt"),
+        "one_core": one_core,
         "_results": results,
     }
 
@@ -468,11 +485,13 @@ def main():
     paths = {}
     for name, ms, by in (("sparse", sparse_ms, sparse_bytes), ("full", full_ms, full_bytes)):
         gbps = by / (ms.mean() * 1e-3) / 1e9
-        paths[name] = {"ms": round(float(ms.mean()), 4), "p10_ms": round(float(np.percentile(ms, 10)), 4),
+        paths[name] = {"ms": round(float(ms.mean()), 4), "median_ms": round(float(np.median(ms)), 4),
+                       "p10_ms": round(float(np.percentile(ms, 10)), 4),
                        "p90_ms": round(float(np.percentile(ms, 90)), 4),
                        "steps_per_s": round(1e3 / float(ms.mean()), 1), "bytes": by,
                        "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
     paths["graph_step"] = {"ms": round(float(graph_ms.mean()), 4),
+                           "median_ms": round(float(np.median(graph_ms)), 4),
                            "p10_ms": round(float(np.percentile(graph_ms, 10)), 4),
                            "p90_ms": round(float(np.percentile(graph_ms, 90)), 4),
                            "steps_per_s": round(1e3 / float(graph_ms.mean()), 1),
@@ -504,6 +523,8 @@ def main():
                   "max_rel_err_sparse": max(errs_s), "max_rel_err_full": max(errs_f),
                   "tolerance_rel": 2e-3}
         cpu_line = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        if cpu["one_core"] is not None:
+            cpu_line["one_core"] = cpu["one_core"]
 
     record = {
         "metric": METRIC,
