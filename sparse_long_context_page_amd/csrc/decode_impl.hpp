@@ -300,6 +300,19 @@ __device__ __forceinline__ double pow_m(double d, double m, int mcode) {
   return d * pow_m1(d, m, mcode);
 }
 
+// pow_m1 / pow_m for a caller that only sees integer m (mcode 1..4): no call
+// to pow_general, so a caller holding many values in registers spills none
+// around it.
+template <bool GEN>
+__device__ __forceinline__ double pow_m1_t(double d, double m, int mcode) {
+  if constexpr (GEN) {
+    return pow_m1(d, m, mcode);
+  } else {
+    (void)m;
+    return mcode == 1 ? 1.0 : (mcode == 2 ? d : (mcode == 3 ? d * d : d * d * d));
+  }
+}
+
 // The same safeguarded Newton iteration for the whole workgroup, each thread
 // holding K of the a_i in registers (-DBL_MAX marks an empty slot); every
 // thread of the block must call it and gets the same result.
@@ -342,7 +355,7 @@ __device__ double solve_tau_block(const double (&a)[K], double m, int mcode, dou
 // The safeguarded Newton iteration of solve_tau for one wave whose lanes
 // hold the list's a_i = am1 * z_i in registers (K per lane; -DBL_MAX marks an
 // empty slot), so an iteration reads no memory. Same steps and stopping rules.
-template <int K>
+template <int K, bool GEN = true>
 __device__ double solve_tau_regs(const double (&a)[K], double am1, double m, int mcode,
                                  double amax) {
   (void)am1;
@@ -353,7 +366,7 @@ __device__ double solve_tau_regs(const double (&a)[K], double am1, double m, int
     for (int k = 0; k < K; ++k) {
       const double d = a[k] - t;
       if (d > 0.0) {
-        const double pm1 = pow_m1(d, m, mcode);
+        const double pm1 = pow_m1_t<GEN>(d, m, mcode);
         fp += pm1;
         f += pm1 * d;
       }
@@ -418,6 +431,46 @@ __device__ double solve_tau_ranked(double a, int n, int mcode, double amax) {
     t = (S1 - sqrt(disc)) / kstar;
   }
   return amax + t;
+}
+
+// One wave solves tau over a window list held K entries per lane in
+// registers (a_i = am1 * z_i), then compacts the support (V row, p) to the
+// front of the list in list order; returns the support size, the wave's
+// sum of p and tau (every lane). Lists of up to 64 entries at m = 1, 2 take
+// the rank-based closed form.
+template <int K, bool GEN, typename ZT>
+__device__ __forceinline__ void wave_solve_list(const ZT* lz, int* li, float* sp, int n_list, double am1, double m,
+                                int mcode, double amax, int lane, uint64_t ltm, int& n_sup,
+                                double& psum, double& tau) {
+  double a[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int e = k * kWave + lane;
+    a[k] = e < n_list ? am1 * (double)lz[e] : -DBL_MAX;
+  }
+  const double t = (n_list <= kWave && (mcode == 1 || mcode == 2))
+                       ? solve_tau_ranked(a[0], n_list, mcode, amax)
+                       : solve_tau_regs<K, GEN>(a, am1, m, mcode, amax);
+  int o = 0;
+  double ps = 0.0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int e = k * kWave + lane;
+    const double d = a[k] - t;
+    const bool f = e < n_list && d > 0.0;
+    const int ix = f ? li[e] : 0;
+    const uint64_t bal = __ballot(f);
+    if (f) {
+      const double pv = d * pow_m1_t<GEN>(d, m, mcode);
+      ps += pv;
+      li[o + __popcll(bal & ltm)] = ix;
+      sp[o + __popcll(bal & ltm)] = (float)pv;
+    }
+    o += __popcll(bal);
+  }
+  psum = wave_allsum(ps);
+  n_sup = o;
+  tau = t;
 }
 
 // Candidate lists of the score kernel: a wave appends the survivors of each
@@ -1183,36 +1236,19 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
   double tau;
   int n_sup;
   double psum = 0.0;
-  if (list_lds && n_list <= kWave * kRegList) {
-    // Short lists: wave 0 holds a_i = am1 * z_i in registers for the whole
-    // solve, then compacts (V row, p) in list order.
+  if (list_lds && (n_list <= kWave * kRegList || (n_list <= kWave * kRegListLong && mcode != 0))) {
+    // Short lists (up to 256, or up to 1024 for integer m): wave 0 holds
+    // a_i = am1 * z_i in registers for the whole solve (no barrier per
+    // iteration), then compacts (V row, p) in list order.
     if (wave == 0) {
-      double a[kRegList];
-#pragma unroll
-      for (int k = 0; k < kRegList; ++k) {
-        const int e = k * kWave + lane;
-        a[k] = e < n_list ? am1 * (double)lz[e] : -DBL_MAX;
-      }
-      const double t = (n_list <= kWave && (mcode == 1 || mcode == 2))
-                           ? solve_tau_ranked(a[0], n_list, mcode, amax)
-                           : solve_tau_regs<kRegList>(a, am1, m, mcode, amax);
-      int o = 0;
-#pragma unroll
-      for (int k = 0; k < kRegList; ++k) {
-        const int e = k * kWave + lane;
-        const double d = a[k] - t;
-        const bool f = e < n_list && d > 0.0;
-        const int ix = f ? li[e] : 0;
-        const uint64_t bal = __ballot(f);
-        if (f) {
-          const double pv = pow_m(d, m, mcode);
-          psum += pv;
-          li[o + __popcll(bal & ltm)] = ix;
-          sp[o + __popcll(bal & ltm)] = (float)pv;
-        }
-        o += __popcll(bal);
-      }
-      psum = wave_allsum(psum);
+      int o;
+      double t;
+      if (n_list <= kWave * kRegList)
+        wave_solve_list<kRegList, true>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm, o,
+                                        psum, t);
+      else  // integer m only
+        wave_solve_list<kRegListLong, false>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm,
+                                             o, psum, t);
       if (lane == 0) {
         nb[1] = o;
         red[0] = psum;

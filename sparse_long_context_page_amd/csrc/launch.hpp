@@ -34,6 +34,7 @@ constexpr int kNW = kNT / kWave;
 constexpr int kListCap = 4096;  // threshold list entries held in LDS
 constexpr int kSupCap = 4096;   // support entries held in LDS
 constexpr int kRegList = 4;     // list entries per lane kept in registers by the threshold solve
+constexpr int kRegListLong = 16;  // the same, for lists of up to 1024 entries (one wave, no barriers)
 constexpr int kSelCopy = 8192;  // selection ints staged in LDS by the sparse score kernel
 
 
