@@ -382,6 +382,16 @@ def main():
         E.entmaxkv_build_page_meta(shape, k, bt, lens, meta, events=list(ev_meta)[2 * i:2 * i + 2])
     torch.cuda.synchronize()
     meta_ms = float(np.mean([ev_meta.elapsed_ms(2 * i, 2 * i + 1) for i in range(n_meta)]))
+    # a decode step's box maintenance: one appended token per sequence (the
+    # boxes already hold it, so the update leaves them as they are)
+    old_lens = (lens - 1).clamp(min=0)
+    ev_app = E.HipEvents(2 * n_meta)
+    for i in range(n_meta):
+        flush(i)
+        E.entmaxkv_append_page_meta(shape, k, bt, old_lens, lens, 1, meta,
+                                    events=list(ev_app)[2 * i:2 * i + 2])
+    torch.cuda.synchronize()
+    append_us = float(np.mean([ev_app.elapsed_ms(2 * i, 2 * i + 1) for i in range(n_meta)])) * 1e3
 
     call_sel = E.Prepared("score_select", shape, q, meta, bt, lens, budget, sel, sel_ub, ws=ws_sel,
                           stream=stream)
@@ -501,6 +511,9 @@ def main():
     paths["page_boxes"] = {"ms": round(meta_ms, 4), "bytes": nbytes["_meta_build"],
                            "GBps": round(meta_gbps, 1), "frac": round(meta_gbps / PEAK_HBM_GBPS, 4),
                            "note": "built once per page, outside the step"}
+    paths["page_boxes_append"] = {"us": round(append_us, 2),
+                                  "note": "box update for one appended token per sequence "
+                                          "(a decode step's box maintenance), outside the step"}
     dom = int(np.argmax(kmean))
     dname = KERNEL_NAMES[dom]
     achieved = nbytes[dname] / (kmean[dom] * 1e-3) / 1e9

@@ -115,6 +115,31 @@ int entmaxkv_build_page_meta(const entmaxkv_shape* shape, const void* k_pool,
                              void* meta, hipStream_t stream, hipEvent_t* events);
 
 /*
+ * Page boxes after an append ([EntmaxKV page] section 2.A: the boxes are
+ * per-page state that a decode loop keeps current as tokens arrive). The
+ * caller has written the keys of tokens old_lens[b] <= t < new_lens[b] of
+ * each sequence into k_pool (their pages already in block_table). For every
+ * page holding such a token, the box becomes the min/max of its valid keys
+ * t < new_lens[b]: a page whose first row is new is rebuilt from its rows; a
+ * page that already held tokens combines its current box (which must be the
+ * box of its rows below old_lens[b]) with the new rows. The result equals
+ * entmaxkv_build_page_meta with seq_lens = new_lens on those pages (bit for
+ * bit up to the sign of a zero); no other page is touched.
+ *   old_lens, new_lens  int32 [batch] device arrays
+ *   max_new_tokens      host int >= 1, at least new_lens[b] - old_lens[b] for
+ *                       every b; it sizes the grid (pages beyond
+ *                       ceil(max_new_tokens / page_size) + 1 per sequence are
+ *                       not updated)
+ * A sequence with new_lens[b] <= old_lens[b] is left as it is. Returns
+ * ENTMAXKV_ERR_INVALID for a null pointer or max_new_tokens < 1. Kernels
+ * launched: 1.
+ */
+int entmaxkv_append_page_meta(const entmaxkv_shape* shape, const void* k_pool,
+                              const int32_t* block_table, const int32_t* old_lens,
+                              const int32_t* new_lens, int32_t max_new_tokens, void* meta,
+                              hipStream_t stream, hipEvent_t* events);
+
+/*
  * Page bounds and fixed-budget top-k ([EntmaxKV page] sections 2.A and 2.B
  * policy 1). For each (b, h) and logical page j < P_b = ceil(seq_lens[b] /
  * page_size):

@@ -284,6 +284,25 @@ int entmaxkv_build_page_meta(const entmaxkv_shape* shape, const void* k_pool,
   return ENTMAXKV_OK;
 }
 
+int entmaxkv_append_page_meta(const entmaxkv_shape* shape, const void* k_pool,
+                              const int32_t* block_table, const int32_t* old_lens,
+                              const int32_t* new_lens, int32_t max_new_tokens, void* meta,
+                              hipStream_t stream, hipEvent_t* events) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  if (!k_pool || !block_table || !old_lens || !new_lens || !meta) return ENTMAXKV_ERR_INVALID;
+  if (max_new_tokens <= 0) return ENTMAXKV_ERR_INVALID;
+  if (!aligned(k_pool, 16) || !aligned(meta, 16)) return ENTMAXKV_ERR_INVALID;
+  const Events ev{events, stream};
+  if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
+  if (launch_append_meta(s, k_pool, block_table, old_lens, new_lens, max_new_tokens, meta,
+                         stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(0)) return ENTMAXKV_ERR_HIP;
+  return ENTMAXKV_OK;
+}
+
 int entmaxkv_score_select(const entmaxkv_shape* shape, const float* q, const void* meta,
                           const int32_t* block_table, const int32_t* seq_lens,
                           int32_t budget_pages, int32_t* sel, float* sel_ub, void* ws,

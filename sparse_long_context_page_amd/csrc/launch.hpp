@@ -119,6 +119,9 @@ DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p);
 inline int ub_ld(int max_pages) { return (max_pages + 3) & ~3; }
 size_t select_ws_bytes(const LaunchShape& s);
 
+hipError_t launch_append_meta(const LaunchShape& s, const void* k_pool, const int32_t* bt,
+                              const int32_t* old_lens, const int32_t* new_lens, int max_new,
+                              void* meta, hipStream_t st);
 hipError_t launch_meta(const LaunchShape& s, const void* k_pool, const int32_t* bt,
                        const int32_t* lens, void* meta, hipStream_t st);
 

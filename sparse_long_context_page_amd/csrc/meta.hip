@@ -1,7 +1,8 @@
 // Page bounding-box metadata: per (page, KV head) coordinate-wise min and max
-// of the page's valid keys. EntmaxKV summary page (gist.science paper
-// 2605.21649), section 2.A: the box is the lightweight per-page metadata
-// that bounds a page's best score.
+// of the page's valid keys, built for whole sequences (meta_kernel) or
+// updated after tokens are appended (append_meta_kernel). EntmaxKV summary
+// page (gist.science paper 2605.21649), section 2.A: the box is the
+// lightweight per-page metadata that bounds a page's best score.
 //
 // Each lane owns one 16-byte column chunk of one (page, KV head) item and
 // walks all of the page's valid rows, so no cross-lane reduction is needed:
@@ -89,6 +90,130 @@ meta_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_tab
   }
   *reinterpret_cast<uint4*>(dst) = o[0];
   *reinterpret_cast<uint4*>(dst + D) = o[1];
+}
+
+// Boxes after an append: item = (sequence, KV head, i-th page touched by the
+// new tokens [L0, L1)). Same lane layout as meta_kernel; a page whose first
+// valid row is new starts from +-inf, a page that already held tokens starts
+// from its current box, and both take the min/max of the new rows.
+template <typename KV, int D>
+__global__ void __launch_bounds__(256)
+append_meta_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_table,
+                   const int32_t* __restrict__ old_lens, const int32_t* __restrict__ new_lens,
+                   KV* __restrict__ meta, int B, int Hkv, int ps, int max_pages, int num_phys,
+                   int slots) {
+  constexpr int VPC = 16 / sizeof(KV);
+  constexpr int CPR = D / VPC;
+  constexpr int IPW = kWave / CPR;
+  constexpr int RB = 8;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int c = lane % CPR;
+  const long long item = ((long long)blockIdx.x * (256 / kWave) + wave) * IPW + lane / CPR;
+  const int i = (int)(item % slots);
+  const long long bg = item / slots;
+  const int g = (int)(bg % Hkv);
+  const int b = (int)(bg / Hkv);
+  if (b >= B) return;
+  const int L1 = clamp_len(new_lens[b], max_pages * ps);
+  const int L0 = min(clamp_len(old_lens[b], max_pages * ps), L1);
+  if (L0 == L1) return;
+  const int j = L0 / ps + i;
+  if (j * ps >= L1) return;
+  const int phys = block_table[(size_t)b * max_pages + j];
+  if (phys < 0 || phys >= num_phys) return;
+  const int r0 = max(0, L0 - j * ps), r1 = min(ps, L1 - j * ps);
+  const KV* base = k_pool + ((size_t)phys * Hkv + g) * (size_t)ps * D + c * VPC;
+  KV* dst = meta + ((size_t)phys * Hkv + g) * 2 * D + c * VPC;
+
+  float lo[VPC], hi[VPC];
+  auto widen4 = [](const uint4& x, float (&f)[VPC]) {
+    if constexpr (sizeof(KV) == 2) {
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f[2 * k] = bf16_lo(w[k]);
+        f[2 * k + 1] = bf16_hi(w[k]);
+      }
+    } else {
+      f[0] = __uint_as_float(x.x); f[1] = __uint_as_float(x.y);
+      f[2] = __uint_as_float(x.z); f[3] = __uint_as_float(x.w);
+    }
+  };
+  if (r0 == 0) {
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) {
+      lo[e] = __builtin_inff();
+      hi[e] = -__builtin_inff();
+    }
+  } else {
+    widen4(*reinterpret_cast<const uint4*>(dst), lo);
+    widen4(*reinterpret_cast<const uint4*>(dst + D), hi);
+  }
+  for (int rr = r0; rr < r1; rr += RB) {
+    u32x4 x[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k)
+      if (rr + k < r1) x[k] = *reinterpret_cast<const u32x4*>(base + (size_t)(rr + k) * D);
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      if (rr + k >= r1) break;
+      float f[VPC];
+      widen4(make_uint4(x[k][0], x[k][1], x[k][2], x[k][3]), f);
+#pragma unroll
+      for (int e = 0; e < VPC; ++e) {
+        lo[e] = fminf(lo[e], f[e]);
+        hi[e] = fmaxf(hi[e], f[e]);
+      }
+    }
+  }
+  uint4 o[2];
+#pragma unroll
+  for (int side = 0; side < 2; ++side) {
+    const float* a = side ? hi : lo;
+    if constexpr (sizeof(KV) == 2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = (__float_as_uint(a[2 * k]) >> 16) | (__float_as_uint(a[2 * k + 1]) & 0xffff0000u);
+      o[side] = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      o[side] = make_uint4(__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
+                           __float_as_uint(a[3]));
+    }
+  }
+  *reinterpret_cast<uint4*>(dst) = o[0];
+  *reinterpret_cast<uint4*>(dst + D) = o[1];
+}
+
+template <typename KV, int D>
+static hipError_t launch_append_meta_t(const LaunchShape& s, const void* k_pool, const int32_t* bt,
+                                       const int32_t* old_lens, const int32_t* new_lens,
+                                       int max_new, void* meta, hipStream_t st) {
+  constexpr int IPB = (256 / kWave) * (kWave / (D / (16 / sizeof(KV))));  // items per block
+  // pages one sequence's new tokens can touch: the partly filled last page
+  // plus ceil(max_new / ps) more, never more than the table has
+  long long slots = ((long long)max_new + s.page_size - 1) / s.page_size + 1;
+  if (slots > s.max_pages) slots = s.max_pages;
+  const long long items = (long long)s.batch * s.num_kv_heads * slots;
+  const long long blocks = (items + IPB - 1) / IPB;
+  hipLaunchKernelGGL((append_meta_kernel<KV, D>), dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const KV*>(k_pool), bt, old_lens, new_lens, static_cast<KV*>(meta),
+                     s.batch, s.num_kv_heads, s.page_size, s.max_pages, s.num_phys, (int)slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_meta(const LaunchShape& s, const void* k_pool, const int32_t* bt,
+                              const int32_t* old_lens, const int32_t* new_lens, int max_new,
+                              void* meta, hipStream_t st) {
+  if (s.bf16) {
+    if (s.head_dim == 64)
+      return launch_append_meta_t<bf16_t, 64>(s, k_pool, bt, old_lens, new_lens, max_new, meta, st);
+    return launch_append_meta_t<bf16_t, 128>(s, k_pool, bt, old_lens, new_lens, max_new, meta, st);
+  }
+  if (s.head_dim == 64)
+    return launch_append_meta_t<float, 64>(s, k_pool, bt, old_lens, new_lens, max_new, meta, st);
+  return launch_append_meta_t<float, 128>(s, k_pool, bt, old_lens, new_lens, max_new, meta, st);
 }
 
 template <typename KV, int D>

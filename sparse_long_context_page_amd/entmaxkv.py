@@ -62,6 +62,7 @@ def _load() -> ctypes.CDLL:
     P, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     SP = ctypes.POINTER(Shape)
     lib.entmaxkv_build_page_meta.argtypes = [SP, P, P, P, P, P, P]
+    lib.entmaxkv_append_page_meta.argtypes = [SP, P, P, P, P, I32, P, P, P]
     lib.entmaxkv_score_select.argtypes = [SP, P, P, P, P, I32, P, P, P, SZ, P, P]
     lib.entmaxkv_decode_sparse.argtypes = [SP, P, P, P, P, P, P, I32, F32, P, P, P, P, SZ, P, P]
     lib.entmaxkv_decode_full.argtypes = [SP, P, P, P, P, P, F32, P, P, P, P, SZ, P, P]
@@ -157,6 +158,15 @@ def _args_build_page_meta(shape: Shape, k_pool, block_table, seq_lens, meta, str
         _ptr(meta, "meta", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
 
 
+def _args_append_page_meta(shape: Shape, k_pool, block_table, old_lens, new_lens,
+                           max_new_tokens, meta, stream=None):
+    return lib.entmaxkv_append_page_meta, [
+        ctypes.byref(shape), _ptr(k_pool, "k_pool", _kv_dtypes(shape)),
+        _ptr(block_table, "block_table", (torch.int32,)), _ptr(old_lens, "old_lens", (torch.int32,)),
+        _ptr(new_lens, "new_lens", (torch.int32,)), int(max_new_tokens),
+        _ptr(meta, "meta", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
+
+
 def _args_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_pages, sel,
                        sel_ub=None, ws=None, stream=None):
     if ws is None:
@@ -211,6 +221,13 @@ def entmaxkv_build_page_meta(shape: Shape, k_pool, block_table, seq_lens, meta, 
     _run("entmaxkv_build_page_meta", fn, args, events)
 
 
+def entmaxkv_append_page_meta(shape: Shape, k_pool, block_table, old_lens, new_lens,
+                              max_new_tokens, meta, stream=None, events=None):
+    fn, args = _args_append_page_meta(shape, k_pool, block_table, old_lens, new_lens,
+                                      max_new_tokens, meta, stream)
+    _run("entmaxkv_append_page_meta", fn, args, events)
+
+
 def entmaxkv_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_pages, sel,
                           sel_ub=None, ws=None, stream=None, events=None):
     fn, args, _ = _args_score_select(shape, q, meta, block_table, seq_lens, budget_pages, sel,
@@ -241,7 +258,8 @@ class Prepared:
         call()                 # or call(events=[e0, e1, e2, e3])
     """
 
-    _makers = {"build_page_meta": _args_build_page_meta, "score_select": _args_score_select,
+    _makers = {"build_page_meta": _args_build_page_meta,
+               "append_page_meta": _args_append_page_meta, "score_select": _args_score_select,
                "decode_sparse": _args_decode_sparse, "decode_full": _args_decode_full}
 
     def __init__(self, name: str, *args, **kwargs):

@@ -159,3 +159,23 @@ def test_alignment_checks(ek):
                                        big, None, None) == -1
     assert ek.lib.entmaxkv_decode_sparse(ctypes.byref(s), d, d, d, d, d, d, 82, 1.5, d, None,
                                          None, mis16, big, None, None) == -1
+
+
+def test_append_page_meta_validation(ek):
+    """The append entry point rejects null pointers, a non-positive
+    max_new_tokens and misaligned pools before any HIP call."""
+    s = shape(ek)
+    d = ctypes.c_void_p(256)
+    f = ek.lib.entmaxkv_append_page_meta
+    assert f(None, d, d, d, d, 1, d, None, None) == -1
+    for i in range(5):
+        args = [d, d, d, d, d]
+        args[i] = None
+        assert f(ctypes.byref(s), *args[:4], 1, args[4], None, None) == -1
+    for m in (0, -1):
+        assert f(ctypes.byref(s), d, d, d, d, m, d, None, None) == -1
+    odd = ctypes.c_void_p(256 + 8)
+    assert f(ctypes.byref(s), odd, d, d, d, 1, d, None, None) == -1
+    assert f(ctypes.byref(s), d, d, d, d, 1, odd, None, None) == -1
+    bad = shape(ek, head_dim=96)
+    assert f(ctypes.byref(bad), d, d, d, d, 1, d, None, None) == -2
