@@ -141,7 +141,7 @@ def _oracle_head(args):
     return b, h, dt, sel, sp.out, fu.out
 
 
-ONE_CORE_WORKLOADS = ("tiny_4k_f32", "extreme_512k")  # also timed on one core
+ONE_CORE_WORKLOADS = ("tiny_4k_f32", "extreme_512k", "extreme_1m")  # also timed on one core
 ONE_CORE_HEADS = 4
 
 

@@ -75,7 +75,7 @@ class Workload:
 
 _S128 = 1.0 / math.sqrt(128.0)
 
-# The five decode workloads. Names say what they are.
+# The decode workloads. Names say what they are.
 WORKLOADS = {
     # Single head, fp32 cache, 4K tokens; small enough for a pure-CPU check.
     "tiny_4k_f32": Workload(
@@ -97,11 +97,16 @@ WORKLOADS = {
     "extreme_512k": Workload(
         "extreme_512k", 1, 32, 8, 128, 64, 524288, "bf16", (1.5,), (64,), 4.0 * _S128,
         plant="group_mean", n_planted=256),
+    # The same recipe at 1,048,576 tokens (16384 pages of 64 tokens), the
+    # longest context the EntmaxKV page measures.
+    "extreme_1m": Workload(
+        "extreme_1m", 1, 32, 8, 128, 64, 1048576, "bf16", (1.5,), (64,), 4.0 * _S128,
+        plant="group_mean", n_planted=256),
 }
 
 # Seeds: each workload has a fixed seed so every run sees the same data.
 WORKLOAD_SEEDS = {"tiny_4k_f32": 1, "gqa_32k": 2, "long_128k": 3,
-                  "alpha_sweep_64k": 4, "extreme_512k": 5}
+                  "alpha_sweep_64k": 4, "extreme_512k": 5, "extreme_1m": 6}
 
 
 def shrink(w: Workload, context: int | None = None, batch: int | None = None,

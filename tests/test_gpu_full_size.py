@@ -39,7 +39,7 @@ def whole_batch_properties(w, sel, sel_ub, out, tau, sup, budget, lens):
     assert np.isfinite(tau.cpu().numpy()).all()
 
 
-@pytest.mark.parametrize("name", ["tiny_4k_f32", "gqa_32k", "long_128k", "extreme_512k"])
+@pytest.mark.parametrize("name", ["tiny_4k_f32", "gqa_32k", "long_128k", "extreme_512k", "extreme_1m"])
 def test_full_size_workload(name):
     w = synth.WORKLOADS[name]
     announce(f"full size {name}: generate")
