@@ -127,7 +127,8 @@ SplitPlan plan_sparse(const LaunchShape& s, int budget) {
   long long pps = kSparseSplitBytes / page_bytes;
   if (pps < 1) pps = 1;
   while (pps > 1 && grid(pps) < kSparseMinGrid) pps /= 2;
-  while (2 * pps * s.page_size <= kFullTokensPerSplit && pps < umax && grid(pps) >= kSparseMaxGrid)
+  while (2 * pps * s.page_size <= kSparseMaxTokensPerSplit && pps < umax &&
+         grid(pps) >= kSparseMaxGrid)
     pps *= 2;
   pps = fit_pps(s, (int)pps, true, budget);
   SplitPlan p = finish_plan(s, umax, pps);
