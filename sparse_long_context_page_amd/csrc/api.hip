@@ -139,6 +139,9 @@ SplitPlan plan_sparse(const LaunchShape& s, int budget) {
 SplitPlan plan_full(const LaunchShape& s) {
   int pps = kFullTokensPerSplit / s.page_size;
   if (pps < 1) pps = 1;
+  // short caches: halve the split while the grid would be under kFullMinGrid
+  const long long units = (long long)s.batch * s.num_kv_heads;
+  while (pps > 1 && units * ((s.max_pages + pps - 1) / pps) < kFullMinGrid) pps /= 2;
   pps = fit_pps(s, pps, false, 0);
   SplitPlan p = finish_plan(s, s.max_pages, pps);
   p.list_cap = s.max_pages * s.page_size;

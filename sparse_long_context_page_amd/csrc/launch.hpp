@@ -15,15 +15,16 @@ struct LaunchShape {
   bool bf16;
 };
 
-// Work of one workgroup of the gather-score kernels. Full cache: a fixed
-// 4096 tokens (measured against 1024, 2048 and 8192 on the 64K-1M
-// workloads). Sparse: about kSparseSplitBytes of K, halved while the grid
+// Work of one workgroup of the gather-score kernels. Full cache: 4096 tokens
+// (measured against 1024, 2048 and 8192 on the 64K-1M workloads), halved
+// while the grid would have fewer than kFullMinGrid workgroups. Sparse: about kSparseSplitBytes of K, halved while the grid
 // would have fewer than kSparseMinGrid workgroups (short selections: more,
 // smaller splits keep the chip busy) and doubled, up to
 // kSparseMaxTokensPerSplit tokens, while it would have kSparseMaxGrid or
 // more (long selections: each workgroup's fixed cost is spread over more
 // pages).
 constexpr int kFullTokensPerSplit = 4096;
+constexpr long long kFullMinGrid = 512;  // full-cache splits halve below this many workgroups
 constexpr int kSparseMaxTokensPerSplit = 2048;
 constexpr long long kSparseSplitBytes = 256 * 1024;
 constexpr long long kSparseMinGrid = 512;
