@@ -258,3 +258,15 @@ def test_kernel_events_are_recorded():
     assert ev.elapsed_ms(0, 1) > 0 and ev.elapsed_ms(2, 3) > 0
     assert ev.elapsed_ms(0, 3) >= ev.elapsed_ms(0, 1)
     ev.close()
+
+
+@pytest.mark.parametrize("alpha", [1.05, 4.0])
+def test_extreme_alpha(alpha):
+    """alpha near 1 (window 20 in z: every token is a candidate, lists take
+    the long and global paths, m = 20) and alpha = 4 (m = 1/3, bisection
+    steps): both paths still match the oracle."""
+    w = synth.shrink(synth.WORKLOADS["gqa_32k"], context=2500, batch=1, n_planted=8)
+    inp = synth.generate(w, 9)
+    full_compare(inp, 24, alpha, heads=[(0, h) for h in (0, 7, 13, 31)])
+    wt = synth.shrink(synth.WORKLOADS["tiny_4k_f32"], context=3000)
+    full_compare(synth.generate(wt, 1), 16, alpha)
