@@ -6,23 +6,27 @@
 // sum p = 1 (Peters, Niculae & Martins 2019).
 //
 // score_kernel (one workgroup per (page split, sequence, KV head)):
-//   Streams the split's K pages once for the G query heads of the KV head.
-//   A token row is spread over LT lanes, each holding NCH 16-byte chunks; the
-//   G partial dot products finish in a multi-value butterfly. Only tokens that
-//   can be in the support are kept: every token with p > 0 has
-//   z > max(z) - 1/(alpha-1) (at tau = (alpha-1) max z - 1 the top token alone
-//   has weight 1), and a running maximum can only underestimate max(z), so
-//   filtering against it keeps a superset. Survivors go to per-wave LDS lists,
-//   are filtered again against the workgroup maximum and written, in a fixed
-//   order, as this split's candidate region (z, token index) with its count
-//   and maximum. Sparse: the split is a slice of the union of the G heads'
-//   selected pages (each page read once), built from a bitmap in LDS.
+//   Streams the split's K pages once for the G query heads of the KV head:
+//   bf16 caches on the matrix cores (q split exactly into three bf16 parts,
+//   keys through direct-to-LDS loads), float32 caches on the vector ALU (a
+//   token row spread over LT lanes, the G partial dot products finished in a
+//   multi-value butterfly). Only tokens that can be in the support are kept:
+//   every token with p > 0 has z > max(z) - 1/(alpha-1) (at
+//   tau = (alpha-1) max z - 1 the top token alone has weight 1), and a
+//   running maximum can only underestimate max(z), so filtering against it
+//   keeps a superset. Survivors go to per-wave LDS lists, are filtered again
+//   against the workgroup maximum and written, in a fixed order, as this
+//   split's candidate region (z, token index) with its count and maximum.
+//   Sparse: the split is a slice of the union of the G heads' selected pages
+//   (each page read once), built from a bitmap in LDS.
 // tau_pv_kernel (one workgroup per (sequence, query head)):
 //   Takes the global maximum over the regions, gathers the candidates inside
-//   the window into a list, solves tau by a safeguarded Newton iteration on
-//   f(tau) = sum [a_i - tau]_+^m (bracketed by [a_max - 1, a_max], bisection
-//   when a Newton step leaves the bracket), then reads V rows only for the
-//   tokens with p > 0 and writes o = sum p v / sum p.
+//   the window into a list (tightened first by a lower bound on tau when
+//   there are many), solves tau on f(tau) = sum [a_i - tau]_+^m = 1 -- by
+//   the sort-based closed form for m = 1, 2 on short lists, else by a
+//   safeguarded Newton iteration bracketed by [a_max - 1, a_max] with
+//   bisection when a step leaves the bracket -- then reads V rows only for
+//   the tokens with p > 0 and writes o = sum p v / sum p.
 #pragma once
 
 #include <float.h>
