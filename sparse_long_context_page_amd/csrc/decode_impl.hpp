@@ -487,6 +487,18 @@ struct CandLists {
   int* ri;              // LDS indices [wave][head][kListSlots]
   Cand<Acc>* spill;     // this workgroup's spill areas [wave][head][wcap]
   int wcap;
+  __device__ __forceinline__ void put_lds(int wave, int h, int G, int pos, Acc z, int idx) const {
+    const int o = (wave * G + h) * kListSlots + pos;
+    rz[o] = z;
+    ri[o] = idx;
+  }
+  __device__ __forceinline__ void put_spill(int wave, int h, int G, int pos, Acc z,
+                                            int idx) const {
+    Cand<Acc> cv;
+    cv.z = z;
+    cv.idx = idx;
+    spill[(size_t)(wave * G + h) * wcap + (pos - kListSlots)] = cv;
+  }
   __device__ __forceinline__ void put(int wave, int h, int G, int pos, Acc z, int idx) const {
     if (pos < kListSlots) {
       const int o = (wave * G + h) * kListSlots + pos;
@@ -688,7 +700,11 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
       for (int i = 0; i < NI; ++i)
         lds_load16(base + src_off[i], dst + i * 1024);
     };
-    auto score_page = [&](int p, int bsel) {
+    // Scores one page; returns the number of store instructions it issued
+    // (spilled candidates), which the waits below must allow in flight:
+    // vmcnt counts stores as well as loads.
+    auto score_page = [&](int p, int bsel) -> int {
+      int nst = 0;
       const int j = SPARSE ? slice[p] : split * pps + p;
       const int phys = sphys[p];
       const int nvalid = (phys >= 0 && phys < num_phys) ? min(PS, L - j * PS) : 0;
@@ -744,26 +760,35 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
           const Acc z = zz[t][blk];
           const bool f = z > neg_inf<Acc>() && z >= thr;
           const uint64_t bal = __ballot(f);
-          if (f)
-            lists.put(wave, h, G, mycnt[blk] + __popcll(bal & gmask & ltm), z,
-                      phys * PS + t * 16 + tok);
+          const int pos = mycnt[blk] + __popcll(bal & gmask & ltm);
+          const int ix = phys * PS + t * 16 + tok;
+          if (f && pos < kListSlots) lists.put_lds(wave, h, G, pos, z, ix);
+          // spilled entries: one store instruction for the wave, counted
+          if (__ballot(f && pos >= kListSlots) != 0ull) {
+            ++nst;
+            if (f && pos >= kListSlots) lists.put_spill(wave, h, G, pos, z, ix);
+          }
           mycnt[blk] += __popcll(bal & gmask);
         }
       }
+      return nst;
     };
     if constexpr (NBUF == 2) {
       // Two page buffers alternate, each refilled as soon as its page has
       // been read, so two pages are in flight while one is scored. Before a
-      // buffer is read, only the other buffer's NI loads may be outstanding.
+      // buffer is read, only the other buffer's NI loads and the stores of
+      // the page scored in between may be outstanding (vmcnt completes in
+      // issue order).
       issue(wave, 0);
       issue(wave + kNW, 1);
+      int nst = 0;
       for (int p = wave; p < n_slice; p += 2 * kNW) {
-        wait_vmcnt<NI>();
-        score_page(p, 0);
+        wait_vmcnt_plus<NI>(nst);
+        nst = score_page(p, 0);
         issue(p + 2 * kNW, 0);
         if (p + kNW >= n_slice) break;
-        wait_vmcnt<NI>();
-        score_page(p + kNW, 1);
+        wait_vmcnt_plus<NI>(nst);
+        nst = score_page(p + kNW, 1);
         issue(p + 3 * kNW, 1);
       }
       wait_vmcnt<0>();  // no load into LDS is left in flight

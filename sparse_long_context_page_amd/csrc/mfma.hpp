@@ -62,4 +62,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((((N >> 4) & 3) << 14) | (0xF << 8) | (0x7 << 4) | (N & 15));
 }
 
+// s_waitcnt for at most N + extra outstanding vector-memory operations,
+// extra a wave-uniform count of stores issued after the operations waited
+// for (more than 8 waits as for 8, i.e. longer: never too short).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_plus(int extra) {
+  switch (extra) {
+    case 0: wait_vmcnt<N>(); break;
+    case 1: wait_vmcnt<N + 1>(); break;
+    case 2: wait_vmcnt<N + 2>(); break;
+    case 3: wait_vmcnt<N + 3>(); break;
+    case 4: wait_vmcnt<N + 4>(); break;
+    case 5: wait_vmcnt<N + 5>(); break;
+    case 6: wait_vmcnt<N + 6>(); break;
+    case 7: wait_vmcnt<N + 7>(); break;
+    default: wait_vmcnt<N + 8>(); break;
+  }
+}
+
 }  // namespace ekv
