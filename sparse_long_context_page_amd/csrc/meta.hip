@@ -8,7 +8,7 @@
 // walks all of the page's valid rows, so no cross-lane reduction is needed:
 // a wave covers 64 / (head_dim chunks) items at once, and the items of a
 // wave are consecutive KV heads of one page (contiguous in the pool). Rows
-// are read eight at a time with streaming loads. min/max does no rounding,
+// are read sixteen at a time with streaming loads. min/max does no rounding,
 // so the output is the stored key values.
 #include "launch.hpp"
 
@@ -22,7 +22,7 @@ meta_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_tab
   constexpr int VPC = 16 / sizeof(KV);  // values per 16-byte chunk
   constexpr int CPR = D / VPC;          // lanes per item (chunks per row)
   constexpr int IPW = kWave / CPR;      // items per wave
-  constexpr int RB = 8;                 // rows per batch of loads
+  constexpr int RB = 16;                // rows per batch of loads
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int c = lane % CPR;
@@ -46,14 +46,16 @@ meta_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_tab
     hi[e] = -__builtin_inff();
   }
   for (int r0 = 0; r0 < nv; r0 += RB) {
+    // every load of the batch issued unconditionally (rows past the valid
+    // ones re-read the last valid row, which leaves min and max unchanged),
+    // so all RB are in flight before the first is used
     u32x4 x[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i)
-      if (r0 + i < nv)
-        x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)(r0 + i) * D));
+      x[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(base + (size_t)min(r0 + i, nv - 1) * D));
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      if (r0 + i >= nv) break;
       float f[VPC];
       if constexpr (sizeof(KV) == 2) {
 #pragma unroll
