@@ -111,6 +111,23 @@ __device__ __forceinline__ void st_dev_cand(Cand<ZT>* p, ZT z, int idx) {
     st_dev(&p->idx, idx);
   }
 }
+
+// A candidate read through a pointer into global memory, addressed as such
+// (a global load even where the compiler cannot see the pointer's origin).
+template <typename ZT>
+__device__ __forceinline__ Cand<ZT> ld_global_cand(const Cand<ZT>* p) {
+  Cand<ZT> c;
+  if constexpr (sizeof(ZT) == 4) {
+    const uint64_t v = *(const __attribute__((address_space(1))) uint64_t*)p;
+    c.z = __builtin_bit_cast(float, (uint32_t)v);
+    c.idx = (int)(uint32_t)(v >> 32);
+  } else {
+    c.z = *(const __attribute__((address_space(1))) double*)&p->z;
+    c.idx = *(const __attribute__((address_space(1))) int*)&p->idx;
+  }
+  return c;
+}
+
 template <typename ZT>
 __device__ __forceinline__ Cand<ZT> ld_dev_cand(const Cand<ZT>* p) {
   Cand<ZT> c;
@@ -1037,7 +1054,7 @@ struct GatherArgs {
   int* tmp;
 };
 template <int R, bool DEV, typename ZT>
-__device__ int gather_batch(const GatherArgs<ZT>& a, int bbase, int nb, int n_list) {
+__device__ __forceinline__ int gather_batch(const GatherArgs<ZT>& a, int bbase, int nb, int n_list) {
   const int tid = threadIdx.x;
   const int per = (nb + kNT - 1) / kNT;
   const int e0 = bbase + min(nb, tid * per), e1 = bbase + min(nb, tid * per + per);
@@ -1067,7 +1084,7 @@ __device__ int gather_batch(const GatherArgs<ZT>& a, int bbase, int nb, int n_li
   }
   Cand<ZT> v[R];
 #pragma unroll
-  for (int k = 0; k < R; ++k) v[k] = DEV ? ld_dev_cand(a.creg + off[k]) : a.creg[off[k]];
+  for (int k = 0; k < R; ++k) v[k] = DEV ? ld_dev_cand(a.creg + off[k]) : ld_global_cand(a.creg + off[k]);
   int keep = 0;
 #pragma unroll
   for (int k = 0; k < R; ++k) keep += (e0 + k < e1 && v[k].z >= a.thr) ? 1 : 0;
@@ -1111,6 +1128,177 @@ __host__ __device__ inline TauLds tau_lds_layout(int regions, int lcap, int zbyt
 }
 
 // Arguments of the threshold + P.V step.
+// The threshold kernel's rarely taken steps (many candidates, long window
+// lists, lists beyond the LDS capacity) are out-of-line functions: the
+// common step (a short list solved by one wave) then runs through a compact
+// block of instructions, which matters when the kernel starts with a cold
+// instruction cache.
+struct TauSolution {
+  double tau, psum;
+  int n_sup;
+};
+
+// A generic pointer that points into LDS, re-qualified so that accesses
+// through it compile to LDS instructions inside an out-of-line function
+// (where the compiler cannot see where the pointer came from).
+template <typename T>
+__device__ __forceinline__ T* lds_view(T* p) {
+#if __HIP_DEVICE_COMPILE__  // (the builtin exists in the device pass only)
+  __builtin_assume(__builtin_amdgcn_is_shared((const void*)p));
+#endif
+  return p;
+}
+
+// Gather runs of more than 8 entries per thread (batches of over 2048
+// candidates). The arguments come one by one (an aggregate argument would
+// pass through scratch memory).
+template <int R, bool DEV, typename ZT>
+__device__ __attribute__((noinline)) int gather_batch_wide(const int* roff, const Cand<ZT>* creg,
+                                                           int splits, int cap, ZT thr, ZT* lz,
+                                                           int* li, ZT* gz, int* gi, int lcap,
+                                                           int* tmp, int bbase, int nb,
+                                                           int n_list) {
+  const GatherArgs<ZT> a{lds_view(roff), creg, splits, cap, thr, lds_view(lz), lds_view(li),
+                         gz, gi, lcap, lds_view(tmp)};
+  return gather_batch<R, DEV>(a, bbase, nb, n_list);
+}
+
+// Lower bound on tau from a subset of the head's tokens. The threshold t_S of
+// any subset S is at most tau (the left side of the threshold equation only
+// grows when tokens are added, and it decreases in t); S = the per-thread
+// maxima of the region maxima (up to 256 token scores), solved by wave 0 in
+// registers. Every support token has a > t_S, so the window may start at
+// t_S - 1e-6 max(1, |t_S|) (returned in score units, z = a / (alpha - 1)).
+template <typename ZT>
+__device__ __attribute__((noinline)) ZT tau_window_bound(ZT mloc, double* rmax, double* tau_b,
+                                                         double am1, double m, int mcode,
+                                                         double amax) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  rmax = lds_view(rmax);
+  tau_b = lds_view(tau_b);
+  rmax[tid] = mloc == neg_inf<ZT>() ? -DBL_MAX : am1 * (double)mloc;
+  __syncthreads();
+  if (tid < kWave) {
+    double a[kRegList];
+#pragma unroll
+    for (int k = 0; k < kRegList; ++k) a[k] = rmax[k * kWave + lane];
+    const double ts = solve_tau_regs<kRegList>(a, am1, m, mcode, amax);
+    if (lane == 0) *tau_b = ts;
+  }
+  __syncthreads();
+  const double ts = *tau_b;
+  return (ZT)((ts - 1e-6 * fmax(1.0, fabs(ts))) / am1);
+}
+
+// Window lists in LDS too long for one wave: thread t holds the contiguous
+// entries [t*per, t*per + per) (per <= KB) in registers for the whole solve,
+// and one block scan compacts the support's (V row, p) to the front of
+// (li, sp) in list order. Every thread of the workgroup calls it.
+template <typename ZT, int KB>
+__device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int* li, float* sp,
+                                                               int n_list, double am1, double m,
+                                                               int mcode, double amax, double* red,
+                                                               int* tmp) {
+  const int tid = threadIdx.x;
+  lz = lds_view(lz);
+  li = lds_view(li);
+  sp = lds_view(sp);
+  red = lds_view(red);
+  tmp = lds_view(tmp);
+  TauSolution r;
+  const int per = (n_list + kNT - 1) / kNT;
+  const int e0 = min(n_list, tid * per), e1 = min(n_list, e0 + per);
+  double a[KB];
+#pragma unroll
+  for (int k = 0; k < KB; ++k) a[k] = (e0 + k < e1) ? am1 * (double)lz[e0 + k] : -DBL_MAX;
+  const double tau = solve_tau_block<KB>(a, m, mcode, amax, red);
+  int ns = 0;
+#pragma unroll
+  for (int k = 0; k < KB; ++k) ns += (a[k] - tau > 0.0) ? 1 : 0;
+  int ix[KB];
+#pragma unroll
+  for (int k = 0; k < KB; ++k) ix[k] = (e0 + k < e1) ? li[e0 + k] : 0;
+  int base = block_excl_scan<kNT>(ns, tmp, &r.n_sup);  // (its barriers order the reads above)
+  double psum = 0.0;
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    const double d = a[k] - tau;
+    if (d > 0.0) {
+      const double pv = pow_m(d, m, mcode);
+      psum += pv;
+      li[base] = ix[k];
+      sp[base] = (float)pv;
+      ++base;
+    }
+  }
+  double zero = 0.0;
+  scope_sum2<kNT>(psum, zero, red);
+  r.tau = tau;
+  r.psum = psum;
+  return r;
+}
+
+// A window list in global memory (longer than the LDS capacity): the
+// block-wide Newton solve over it, the support size and the sum of p.
+template <typename ZT>
+__device__ __attribute__((noinline)) TauSolution tau_global_list(const ZT* dz, int n_list,
+                                                                 double am1, double m, int mcode,
+                                                                 double amax, double* red) {
+  const int tid = threadIdx.x;
+  red = lds_view(red);
+  TauSolution r;
+  r.tau = solve_tau<kNT>(dz, n_list, am1, m, mcode, amax, tid, red);
+  int ns = 0;
+  double psum = 0.0;
+  for (int i = tid; i < n_list; i += kNT) {
+    const double d = am1 * (double)dz[i] - r.tau;
+    if (d > 0.0) {
+      ++ns;
+      psum += pow_m(d, m, mcode);
+    }
+  }
+  double nsd = (double)ns;
+  scope_sum2<kNT>(psum, nsd, red);
+  r.psum = psum;
+  r.n_sup = (int)nsd;
+  return r;
+}
+
+// P.V over a global-memory window list: thread (grp, c) accumulates the
+// weighted 16-byte slice c of every grp-th support row and writes its partial
+// sums to prow.
+template <typename KV, int D>
+__device__ __attribute__((noinline)) void pv_global_list(const KV* v_pool, int Hkv, int g, int PS,
+                                                         const typename KvTraits<KV>::Acc* dz,
+                                                         const int* di, int n_list, double am1,
+                                                         double m, int mcode, double tau,
+                                                         float* prow) {
+  constexpr int VPC = 16 / sizeof(KV);
+  constexpr int LR = D / VPC;
+  constexpr int NG = kNT / LR;
+  const int grp = threadIdx.x / LR, c = threadIdx.x % LR;
+  float acc[VPC];
+#pragma unroll
+  for (int e = 0; e < VPC; ++e) acc[e] = 0.0f;
+  for (int i = grp; i < n_list; i += NG) {
+    const double d = am1 * (double)dz[i] - tau;
+    if (d > 0.0) {
+      const int vrow = di[i];
+      const int phys = vrow / PS, rr = vrow - phys * PS;
+      const uint4 x = *reinterpret_cast<const uint4*>(
+          v_pool + (((size_t)phys * Hkv + g) * PS + rr) * D + c * VPC);
+      typename KvTraits<KV>::Acc f[VPC];
+      widen<KV>(x, f);
+      const float pk = (float)pow_m(d, m, mcode);
+#pragma unroll
+      for (int e = 0; e < VPC; ++e) acc[e] = fmaf(pk, (float)f[e], acc[e]);
+    }
+  }
+  prow = lds_view(prow);
+#pragma unroll
+  for (int e = 0; e < VPC; ++e) prow[e] = acc[e];
+}
+
 template <typename KV>
 struct TauArgs {
   const KV* v_pool;
@@ -1129,7 +1317,7 @@ struct TauArgs {
 
 // One query head (unit u, head hh of its group), by the whole workgroup.
 // DEV: the candidate regions are read at device scope.
-template <typename KV, int D, bool SPARSE, bool DEV>
+template <typename KV, int D, bool DEV>
 __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh, unsigned char* smem) {
   using ZT = typename KvTraits<KV>::Acc;
   const KV* __restrict__ v_pool = args.v_pool;
@@ -1209,24 +1397,8 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
   const double amax = am1 * (double)M;
   ZT thr = M - window;
   if (n_cand > kTauBoundFrom) {
-    // Many candidates: tighten the window with a lower bound on tau. The
-    // threshold t_S of any subset S of the head's tokens is at most tau (the
-    // left side of the equation only grows when tokens are added and it
-    // decreases in t); S = the per-thread region maxima (up to 256 token
-    // scores), solved by wave 0 in registers. Every support token then has
-    // a > t_S, and the kept set a > t_S - 1e-6 max(1, |t_S|) still holds it.
-    rmax[tid] = mloc == neg_inf<ZT>() ? -DBL_MAX : am1 * (double)mloc;
-    __syncthreads();
-    if (wave == 0) {
-      double a[kRegList];
-#pragma unroll
-      for (int k = 0; k < kRegList; ++k) a[k] = rmax[k * kWave + lane];
-      const double ts = solve_tau_regs<kRegList>(a, am1, m, mcode, amax);
-      if (lane == 0) tau_b = ts;
-    }
-    __syncthreads();
-    const double ts = tau_b;
-    const ZT lb = (ZT)((ts - 1e-6 * fmax(1.0, fabs(ts))) / am1);
+    // Many candidates: tighten the window with a lower bound on tau.
+    const ZT lb = tau_window_bound(mloc, rmax, &tau_b, am1, m, mcode, amax);
     if (lb > thr) thr = lb;
   }
 
@@ -1244,7 +1416,9 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
     const GatherArgs<ZT> ga{roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp};
     if (per <= 2) n_list = gather_batch<2, DEV>(ga, bbase, nb_, n_list);
     else if (per <= 8) n_list = gather_batch<8, DEV>(ga, bbase, nb_, n_list);
-    else n_list = gather_batch<KB, DEV>(ga, bbase, nb_, n_list);
+    else
+      n_list = gather_batch_wide<KB, DEV>(roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp,
+                                          bbase, nb_, n_list);
   }
   __syncthreads();
   ZT* dz = lz;
@@ -1265,19 +1439,15 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
   double tau;
   int n_sup;
   double psum = 0.0;
-  if (list_lds && (n_list <= kWave * kRegList || (n_list <= kWave * kRegListLong && mcode != 0))) {
-    // Short lists (up to 256, or up to 1024 for integer m): wave 0 holds
-    // a_i = am1 * z_i in registers for the whole solve (no barrier per
-    // iteration), then compacts (V row, p) in list order.
+  if (list_lds && n_list <= kWave * kRegList) {
+    // Short lists (up to 256): wave 0 holds a_i = am1 * z_i in registers for
+    // the whole solve (no barrier per iteration), then compacts (V row, p)
+    // in list order.
     if (wave == 0) {
       int o;
       double t;
-      if (n_list <= kWave * kRegList)
-        wave_solve_list<kRegList, true>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm, o,
-                                        psum, t);
-      else  // integer m only
-        wave_solve_list<kRegListLong, false>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm,
-                                             o, psum, t);
+      wave_solve_list<kRegList, true>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm, o, psum,
+                                      t);
       if (lane == 0) {
         nb[1] = o;
         red[0] = psum;
@@ -1288,48 +1458,33 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
     tau = tau_b;
     n_sup = nb[1];
     psum = red[0];
-  } else if (list_lds) {
-    // Long lists: thread t holds the contiguous entries [t*per, t*per + per)
-    // in registers for the whole solve; one block scan compacts the support.
-    const int per = (n_list + kNT - 1) / kNT;  // <= KB
-    const int e0 = min(n_list, tid * per), e1 = min(n_list, e0 + per);
-    double a[KB];
-#pragma unroll
-    for (int k = 0; k < KB; ++k) a[k] = (e0 + k < e1) ? am1 * (double)lz[e0 + k] : -DBL_MAX;
-    tau = solve_tau_block<KB>(a, m, mcode, amax, red);
-    int ns = 0;
-#pragma unroll
-    for (int k = 0; k < KB; ++k) ns += (a[k] - tau > 0.0) ? 1 : 0;
-    int ix[KB];
-#pragma unroll
-    for (int k = 0; k < KB; ++k) ix[k] = (e0 + k < e1) ? li[e0 + k] : 0;
-    int base = block_excl_scan<kNT>(ns, tmp, &n_sup);  // (its barriers order the reads above)
-#pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      const double d = a[k] - tau;
-      if (d > 0.0) {
-        const double pv = pow_m(d, m, mcode);
-        psum += pv;
-        li[base] = ix[k];
-        sp[base] = (float)pv;
-        ++base;
+  } else if (list_lds && n_list <= kWave * kRegListLong && mcode != 0) {
+    // Up to 1024 entries at integer m: the same by wave 0 with 16 entries
+    // per lane (no call to the general power).
+    if (wave == 0) {
+      int o;
+      double t;
+      wave_solve_list<kRegListLong, false>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm, o,
+                                           psum, t);
+      if (lane == 0) {
+        nb[1] = o;
+        red[0] = psum;
+        tau_b = t;
       }
     }
-    double zero = 0.0;
-    scope_sum2<kNT>(psum, zero, red);
+    __syncthreads();
+    tau = tau_b;
+    n_sup = nb[1];
+    psum = red[0];
   } else {
-    tau = solve_tau<kNT>(dz, n_list, am1, m, mcode, amax, tid, red);
-    int ns = 0;
-    for (int i = tid; i < n_list; i += kNT) {
-      const double d = am1 * (double)dz[i] - tau;
-      if (d > 0.0) {
-        ++ns;
-        psum += pow_m(d, m, mcode);
-      }
-    }
-    double nsd = (double)ns;
-    scope_sum2<kNT>(psum, nsd, red);
-    n_sup = (int)nsd;
+    // Longer lists, out of line: up to the LDS capacity by the workgroup,
+    // beyond it from global memory.
+    const TauSolution r = list_lds ? tau_long_list<ZT, KB>(lz, li, sp, n_list, am1, m, mcode, amax,
+                                                          red, tmp)
+                                   : tau_global_list<ZT>(dz, n_list, am1, m, mcode, amax, red);
+    tau = r.tau;
+    n_sup = r.n_sup;
+    psum = r.psum;
   }
 
   // o = sum p v / sum p. A candidate's index is its V row,
@@ -1362,14 +1517,12 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
       accumulate(p3, sp[k + 3 * NG]);
     }
     for (; k < n_sup; k += NG) accumulate(row_ptr(li[k]), sp[k]);
-  } else {
-    for (int i = grp; i < n_list; i += NG) {
-      const double d = am1 * (double)dz[i] - tau;
-      if (d > 0.0) accumulate(row_ptr(di[i]), (float)pow_m(d, m, mcode));
-    }
-  }
 #pragma unroll
-  for (int e = 0; e < VPC; ++e) pvacc[grp][c * VPC + e] = acc[e];
+    for (int e = 0; e < VPC; ++e) pvacc[grp][c * VPC + e] = acc[e];
+  } else {
+    pv_global_list<KV, D>(v_pool, Hkv, g, PS, dz, di, n_list, am1, m, mcode, tau,
+                          &pvacc[grp][c * VPC]);
+  }
   __syncthreads();
   const double inv = psum > 0.0 ? 1.0 / psum : 0.0;
   for (int d = tid; d < D; d += kNT) {
@@ -1384,11 +1537,14 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
   }
 }
 
-template <typename KV, int D, bool SPARSE>
+// One kernel serves the budgeted and the full-cache decode (the step is the
+// same over either path's candidates), so a decode step that runs both finds
+// its code in the instruction cache the second time.
+template <typename KV, int D>
 __global__ void __launch_bounds__(kNT)
 tau_pv_kernel(TauArgs<KV> args) {
   extern __shared__ __align__(16) unsigned char smem[];
-  tau_head<KV, D, SPARSE, false>(args, blockIdx.x % args.U, blockIdx.x / args.U, smem);
+  tau_head<KV, D, false>(args, blockIdx.x % args.U, blockIdx.x / args.U, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1529,8 +1685,9 @@ hipError_t launch_tau_pv_t(const LaunchShape& s, const SplitPlan& p, const void*
   // grids hold 4096 so that two workgroups fit a CU.
   const int lcap = U * s.group > 256 ? kTauMaxList / 2 : kTauMaxList;
   const size_t lds = tau_lds_layout(p.regions, lcap, sizeof(ZT), NG, D).total;
-  auto kern = tau_pv_kernel<KV, D, SPARSE>;
-  static bool lds_raised = false;  // the attribute is per kernel; set it once
+  auto kern = tau_pv_kernel<KV, D>;
+  static bool lds_raised = false;  // the attribute is per kernel; set it once (setting it
+                                  // again from the other path's launcher is harmless)
   if (!lds_raised) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
