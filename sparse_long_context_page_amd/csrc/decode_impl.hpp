@@ -590,7 +590,10 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
 
   const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc),
                                         score_kbuf_bytes(sizeof(KV) == 2, PS, D, SPARSE), D);
-  Acc* wmax = reinterpret_cast<Acc*>(smem + lay.wmax);
+  // The waves' running maxima per head: a static LDS array, so the compiler
+  // can tell it apart from the page buffers that direct-to-LDS loads fill
+  // (reads of it then need not wait for those loads).
+  __shared__ Acc wmax[kNW * G];
   int* wcnt = reinterpret_cast<int*>(smem + lay.wcnt);
   int* slice = reinterpret_cast<int*>(smem + lay.slice);
   int* slots = reinterpret_cast<int*>(smem + lay.slots);
@@ -661,6 +664,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     // 16-byte loads; rows past the group are zero.
     constexpr int QP = qtab_pitch(D);
     uint16_t* qtab = reinterpret_cast<uint16_t*>(smem + lay.qtab);
+    if (tid < kNW * G) wmax[tid] = neg_inf<Acc>();  // the waves' shared running maxima
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
       const int i = k * kNT + tid;
@@ -739,6 +743,24 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
           myslot[blk] = h < G ? j : -1;
         }
       }
+      // The waves' running maxima of these heads (wmax[w][h], updated after
+      // every page without a barrier; a read sees some earlier value, each
+      // the maximum of some of this split's tokens): filtering against the
+      // largest still keeps every token within the window of the split's
+      // maximum, and far fewer others than a wave's own maximum would.
+      // Plain 32/64-bit LDS accesses (single-copy atomic on the hardware);
+      // atomic forms would lose the alias information that lets the
+      // compiler skip waiting for the page loads in flight.
+      Acc om[NMB];
+#pragma unroll
+      for (int blk = 0; blk < NMB; ++blk) {
+        const int h = blk * 4 + kgrp;
+        Acc v = neg_inf<Acc>();
+#pragma unroll
+        for (int w = 0; w < kNW; ++w)
+          if (h < G) v = max(v, wmax[w * G + h]);
+        om[blk] = v;
+      }
       const unsigned char* src = kbuf + bsel * PB;
       Acc zz[TILES][NMB];
 #pragma unroll
@@ -770,8 +792,9 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
         pm = max(pm, partner<4>(pm));
         pm = max(pm, partner<8>(pm));
         M[blk] = max(M[blk], pm);
-        const Acc thr = M[blk] - window;
+        const Acc thr = max(M[blk], om[blk]) - window;
         const int h = blk * 4 + kgrp;
+        if (tok == 0 && h < G) wmax[wave * G + h] = M[blk];
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
           const Acc z = zz[t][blk];

@@ -49,7 +49,7 @@ constexpr size_t kMaxScoreLdsBytes = 150 * 1024;  // most LDS a score-kernel pla
 // LDS layout of the score kernel (bytes), shared by host sizing and device carving.
 struct ScoreLds {
   int wcap;  // candidates one wave can produce per head: every token of its pages
-  size_t kbuf, qtab, rz, ri, wmax, wcnt, slice, slots, phys, tmp, bitmap, ssel, total;
+  size_t kbuf, qtab, rz, ri, wcnt, slice, slots, phys, tmp, bitmap, ssel, total;
 };
 
 // Row pitch (bf16 values) of the split-q table of the matrix-core kernels:
@@ -80,7 +80,6 @@ __host__ __device__ inline ScoreLds score_lds_layout(int G, int ps, int pps, boo
   const size_t nreg = (size_t)kNW * G * kListSlots;
   l.rz = o; o = align16(o + nreg * zbytes);
   l.ri = o; o = align16(o + nreg * 4);
-  l.wmax = o; o = align16(o + (size_t)kNW * G * zbytes);
   l.wcnt = o; o = align16(o + (size_t)kNW * G * 4);
   l.slice = o; o = align16(o + (size_t)pps * 4);
   l.slots = o; o = align16(o + (size_t)pps * G * 4);
