@@ -90,8 +90,12 @@ meta_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_tab
                            __float_as_uint(a[3]));
     }
   }
-  *reinterpret_cast<uint4*>(dst) = o[0];
-  *reinterpret_cast<uint4*>(dst + D) = o[1];
+  // streaming stores: plain ones made the build ~5 % slower (and the key
+  // stream alone, with no store at all, takes ~70 % of the time)
+  __builtin_nontemporal_store((u32x4){o[0].x, o[0].y, o[0].z, o[0].w},
+                              reinterpret_cast<u32x4*>(dst));
+  __builtin_nontemporal_store((u32x4){o[1].x, o[1].y, o[1].z, o[1].w},
+                              reinterpret_cast<u32x4*>(dst + D));
 }
 
 // Boxes after an append: item = (sequence, KV head, i-th page touched by the
