@@ -1458,6 +1458,28 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
   }
   const bool list_lds = dz == lz;
 
+  // A candidate's index is its V row, physical_page * page_size + row; thread
+  // (grp, c) handles 16-byte slice c of rows grp, grp + NG, ...
+  const int grp = tid / LR, c = tid % LR;
+  auto row_ptr = [&](int vrow) -> const KV* {
+    const int phys = vrow / PS, r = vrow - phys * PS;
+    return v_pool + (((size_t)phys * Hkv + g) * PS + r) * D + c * VPC;
+  };
+  // Short lists (up to kVPre entries, the common case): the V rows of every
+  // list entry are requested now, so that their latency overlaps the solve;
+  // the P.V step then weights the rows it holds (p = 0 off the support).
+  constexpr int kVPre = 32;
+  constexpr int NPRE = (kVPre + NG - 1) / NG;
+  const bool vpre = list_lds && n_list >= 1 && n_list <= NPRE * NG;
+  uint4 vrow[NPRE];
+  if (vpre) {
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) {
+      const int k = min(grp + i * NG, n_list - 1);
+      vrow[i] = *reinterpret_cast<const uint4*>(row_ptr(li[k]));
+    }
+  }
+
   // Threshold, support (a_i > tau) with p_i = (a_i - tau)^m, sum p in float64.
   double tau;
   int n_sup;
@@ -1510,24 +1532,33 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
     psum = r.psum;
   }
 
-  // o = sum p v / sum p. A candidate's index is its V row,
-  // physical_page * page_size + row.
-  const int grp = tid / LR, c = tid % LR;
-  auto row_ptr = [&](int vrow) -> const KV* {
-    const int phys = vrow / PS, r = vrow - phys * PS;
-    return v_pool + (((size_t)phys * Hkv + g) * PS + r) * D + c * VPC;
-  };
+  // o = sum p v / sum p.
   float acc[VPC];
 #pragma unroll
   for (int e = 0; e < VPC; ++e) acc[e] = 0.0f;
-  auto accumulate = [&](const KV* vp, float pk) {
-    const uint4 x = *reinterpret_cast<const uint4*>(vp);
+  auto accumulate_x = [&](const uint4& x, float pk) {
     typename KvTraits<KV>::Acc f[VPC];
     widen<KV>(x, f);
 #pragma unroll
     for (int e = 0; e < VPC; ++e) acc[e] = fmaf(pk, (float)f[e], acc[e]);
   };
-  if (list_lds) {
+  auto accumulate = [&](const KV* vp, float pk) {
+    accumulate_x(*reinterpret_cast<const uint4*>(vp), pk);
+  };
+  if (vpre) {
+    // p from the list's scores (z is not moved by the support compaction),
+    // by the same expression the solve summed
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) {
+      const int k = grp + i * NG;
+      if (k < n_list) {
+        const double d = am1 * (double)lz[k] - tau;
+        if (d > 0.0) accumulate_x(vrow[i], (float)(d * pow_m1(d, m, mcode)));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) pvacc[grp][c * VPC + e] = acc[e];
+  } else if (list_lds) {
     int k = grp;
     for (; k + 3 * NG < n_sup; k += 4 * NG) {
       const KV* p0 = row_ptr(li[k]);
