@@ -36,7 +36,8 @@
  *    page_size). Kernels clamp seq_lens into that range and treat a block
  *    table entry outside it as an empty page, so bad values give wrong
  *    results, never out-of-bounds accesses.
- *  - The library keeps no state between calls and is safe to call from
+ *  - The library keeps no state between calls (apart from each kernel's
+ *    LDS limit, raised once on its first launch) and is safe to call from
  *    several host threads (each call uses only its own arguments).
  *
  * Layouts (row-major, all dense):

@@ -1644,14 +1644,13 @@ hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float*
   const ScoreLds lay = score_lds_layout(G, PS, p.pages_per_split, SPARSE, s.max_pages, budget,
                                         sizeof(ZT), score_kbuf_bytes(s.bf16, PS, D, SPARSE), D);
   auto kern = score_kernel<KV, D, G, PS, SPARSE>;
-  static bool lds_raised = false;  // the attribute is per kernel; set it once, to the most
-  if (!lds_raised) {               // any plan asks for
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kMaxScoreLdsBytes);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  // The LDS limit is a kernel attribute: raised once, to the most any plan
+  // asks for (a function-local static is initialised exactly once, also when
+  // several host threads launch).
+  static const hipError_t lds_raised =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxScoreLdsBytes);
+  if (lds_raised != hipSuccess) return lds_raised;
   char* w = static_cast<char*>(ws);
   const ScoreArgs<KV> args = score_args<KV>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L);
   hipLaunchKernelGGL(kern, dim3(U * p.splits), dim3(kNT), lay.total, st, args);
@@ -1740,15 +1739,14 @@ hipError_t launch_tau_pv_t(const LaunchShape& s, const SplitPlan& p, const void*
   const int lcap = U * s.group > 256 ? kTauMaxList / 2 : kTauMaxList;
   const size_t lds = tau_lds_layout(p.regions, lcap, sizeof(ZT), NG, D).total;
   auto kern = tau_pv_kernel<KV, D>;
-  static bool lds_raised = false;  // the attribute is per kernel; set it once (setting it
-                                  // again from the other path's launcher is harmless)
-  if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)tau_lds_layout(kMaxSplits, kTauMaxList, 8, NG, D).total);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  // The LDS limit is a kernel attribute: raised once per launcher, to the
+  // most any plan asks for (a function-local static is initialised exactly
+  // once, also when several host threads launch; the other path's launcher
+  // setting it again is harmless).
+  static const hipError_t lds_raised = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)tau_lds_layout(kMaxSplits, kTauMaxList, 8, NG, D).total);
+  if (lds_raised != hipSuccess) return lds_raised;
   const TauArgs<KV> args = tau_args<KV>(s, p, v_pool, alpha, window, out, tau, support, ws, L, lcap);
   hipLaunchKernelGGL(kern, dim3(U * s.group), dim3(kNT), lds, st, args);
   return hipGetLastError();

@@ -529,14 +529,13 @@ static hipError_t launch_bounds_mfma(const LaunchShape& s, const float* q, const
   const long long chunks = (s.max_pages + cp - 1) / cp;
   const size_t lds = bounds_lds_bytes(D, G, cp);
   auto kern = bounds_mfma_kernel<D, G>;
-  static bool lds_raised = false;  // the attribute is per kernel; set it once
-  if (!lds_raised) {
-    const int most = (int)bounds_lds_bytes(D, 8, kNW * 16 * kBoundsMaxTiles);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, most);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  // The LDS limit is a kernel attribute: raised once, to the most any plan
+  // asks for (a function-local static is initialised exactly once, also when
+  // several host threads launch).
+  static const hipError_t lds_raised = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)bounds_lds_bytes(D, 8, kNW * 16 * kBoundsMaxTiles));
+  if (lds_raised != hipSuccess) return lds_raised;
   hipLaunchKernelGGL(kern, dim3((unsigned)(U * chunks)), dim3(256), lds, st, q,
                      static_cast<const bf16_t*>(meta), bt, lens, ub, s.num_q_heads,
                      s.num_kv_heads, s.page_size, s.max_pages, s.num_phys, U,
