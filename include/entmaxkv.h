@@ -8,6 +8,8 @@
  *   section 2.A  per-page key bounding boxes (k_min, k_max) and the
  *                deterministic upper bound they give on a page's best score;
  *   section 2.B  policy 1, a fixed budget of the top-k pages by that bound;
+ *                policy 2, pages kept by a tau estimated from per-page
+ *                Gaussian statistics of the keys (mean and variance);
  *   section 2.C  only the selected pages' K/V are read and alpha-entmax is
  *                solved on that reduced set;
  *   section 4    (efficiency) full-cache entmax decode as the baseline.
@@ -101,7 +103,12 @@ typedef struct {
 } entmaxkv_shape;
 
 /* Which call a workspace is for (entmaxkv_workspace_bytes). */
-enum { ENTMAXKV_WS_SELECT = 0, ENTMAXKV_WS_SPARSE = 1, ENTMAXKV_WS_FULL = 2 };
+enum {
+  ENTMAXKV_WS_SELECT = 0,
+  ENTMAXKV_WS_SPARSE = 1,
+  ENTMAXKV_WS_FULL = 2,
+  ENTMAXKV_WS_GAUSS = 3
+};
 
 /*
  * Page bounding boxes ([EntmaxKV page] section 2.A): for every logical page
@@ -139,6 +146,48 @@ int entmaxkv_append_page_meta(const entmaxkv_shape* shape, const void* k_pool,
                               const int32_t* block_table, const int32_t* old_lens,
                               const int32_t* new_lens, int32_t max_new_tokens, void* meta,
                               hipStream_t stream, hipEvent_t* events);
+
+/*
+ * Page key moments ([EntmaxKV page] section 2.A, the Gaussian statistics):
+ * for every logical page j < ceil(seq_lens[b]/page_size) of every sequence
+ * and each KV head, the per-coordinate mean and population variance (divisor
+ * n, the page's valid rows t < seq_lens[b]) of the page's keys, written to
+ *     moments[block_table[b, j], g, 0, :]  (mean)
+ *     moments[block_table[b, j], g, 1, :]  (variance)
+ * moments: kv_dtype [num_phys_pages, num_kv_heads, 2, head_dim] (the layout
+ * of meta). Sums in float64, rounded to float32 and then to the cache dtype
+ * (each to nearest even). Pages not referenced are left untouched. Returns
+ * ENTMAXKV_ERR_INVALID for a null or misaligned pointer. Kernels launched: 1.
+ */
+int entmaxkv_build_page_moments(const entmaxkv_shape* shape, const void* k_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                void* moments, hipStream_t stream, hipEvent_t* events);
+
+/*
+ * Gaussian-aware entmax page selection ([EntmaxKV page] section 2.B, policy
+ * 2). The page states the policy, not its formulas; this is one reading. For
+ * each (b, h), with m = 1/(alpha-1), pages j < P_b and n_j their valid rows:
+ *   mu_j = (alpha-1) q . mean_j,   s_j = (alpha-1) sqrt(sum_d q_d^2 var_j,d)
+ *   (a page's token scores, in the units of tau, taken as N(mu_j, s_j^2));
+ *   tau_hat solves  sum_j n_j E[(A_j - t)_+^m] = 1,  A_j ~ N(mu_j, s_j^2)
+ *   (closed forms from the normal's truncated moments; float64);
+ *   est_j = mu_j + s_j sqrt(2 ln n_j)  (mu_j when n_j = 1);
+ *   the pages with est_j > tau_hat - delta are kept; if more than cap_pages
+ *   qualify, the cap_pages with the largest est_j rounded to float32, ties
+ *   to the lower j. Written ascending to sel[b, h, 0:cap_pages], -1 after.
+ * alpha must be 2, 3/2, 4/3 or 5/4 (1/(alpha-1) within 1e-4 of 1..4; else
+ * ENTMAXKV_ERR_UNSUPPORTED); delta >= 0 and finite, in the units of tau
+ * (else ENTMAXKV_ERR_INVALID); cap_pages > 0. moments is the output of
+ * entmaxkv_build_page_moments. tau_hat (nullable, float32 [batch,
+ * num_q_heads]) receives tau_hat (NaN for an empty sequence). The selection
+ * feeds entmaxkv_decode_sparse with budget_pages = cap_pages.
+ * Workspace: entmaxkv_workspace_bytes(..., ENTMAXKV_WS_GAUSS).
+ * Kernels launched: 3 (page statistics, tau_hat and keys, select).
+ */
+int entmaxkv_gauss_select(const entmaxkv_shape* shape, const float* q, const void* moments,
+                          const int32_t* block_table, const int32_t* seq_lens, float alpha,
+                          float delta, int32_t cap_pages, int32_t* sel, float* tau_hat,
+                          void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
 
 /*
  * Page bounds and fixed-budget top-k ([EntmaxKV page] sections 2.A and 2.B

@@ -267,6 +267,10 @@ int entmaxkv_workspace_bytes(const entmaxkv_shape* shape, int32_t budget_pages, 
       *bytes = decode_ws_layout(s, p).total;
       return ENTMAXKV_OK;
     }
+    case ENTMAXKV_WS_GAUSS:
+      if ((rc = check_budget(budget_pages))) return rc;
+      *bytes = align256(gauss_ws_bytes(s));
+      return ENTMAXKV_OK;
     default:
       return ENTMAXKV_ERR_INVALID;
   }
@@ -285,6 +289,59 @@ int entmaxkv_build_page_meta(const entmaxkv_shape* shape, const void* k_pool,
   if (launch_meta(s, k_pool, block_table, seq_lens, meta, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(0)) return ENTMAXKV_ERR_HIP;
+  return ENTMAXKV_OK;
+}
+
+int entmaxkv_build_page_moments(const entmaxkv_shape* shape, const void* k_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                void* moments, hipStream_t stream, hipEvent_t* events) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  if (!k_pool || !block_table || !seq_lens || !moments) return ENTMAXKV_ERR_INVALID;
+  if (!aligned(k_pool, 16) || !aligned(moments, 16)) return ENTMAXKV_ERR_INVALID;
+  const Events ev{events, stream};
+  if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
+  if (launch_moments(s, k_pool, block_table, seq_lens, moments, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(0)) return ENTMAXKV_ERR_HIP;
+  return ENTMAXKV_OK;
+}
+
+int entmaxkv_gauss_select(const entmaxkv_shape* shape, const float* q, const void* moments,
+                          const int32_t* block_table, const int32_t* seq_lens, float alpha,
+                          float delta, int32_t cap_pages, int32_t* sel, float* tau_hat,
+                          void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  if ((rc = check_budget(cap_pages))) return rc;
+  if ((rc = check_alpha(alpha))) return rc;
+  if (!isfinite(delta) || !(delta >= 0.0f)) return ENTMAXKV_ERR_INVALID;
+  // m = 1/(alpha-1) must be an integer 1..4 (alpha 2, 3/2, 4/3, 5/4)
+  const double am1 = (double)alpha - 1.0;
+  const double mr = 1.0 / am1;
+  const int m = (int)lround(mr);
+  if (m < 1 || m > 4 || fabs(mr - m) > 1e-4) return ENTMAXKV_ERR_UNSUPPORTED;
+  if (!q || !moments || !block_table || !seq_lens || !sel) return ENTMAXKV_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(moments, 16)) return ENTMAXKV_ERR_INVALID;
+  if (!ws || ws_bytes < gauss_ws_bytes(s)) return ENTMAXKV_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return ENTMAXKV_ERR_INVALID;
+  const size_t rows = (size_t)s.batch * s.num_q_heads * ub_ld(s.max_pages);
+  void* stats = ws;
+  float* keys = reinterpret_cast<float*>(static_cast<char*>(ws) + ((rows * 16 + 255) & ~(size_t)255));
+  const Events ev{events, stream};
+  if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
+  if (launch_gauss_stats(s, q, moments, block_table, seq_lens, am1, stats, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
+  if (launch_gauss_solve(s, stats, seq_lens, m, (double)delta, keys, tau_hat, stream) !=
+      hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(1) || !ev.before(2)) return ENTMAXKV_ERR_HIP;
+  if (launch_select(s, keys, seq_lens, cap_pages, sel, nullptr, true, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(2)) return ENTMAXKV_ERR_HIP;
   return ENTMAXKV_OK;
 }
 
@@ -325,7 +382,7 @@ int entmaxkv_score_select(const entmaxkv_shape* shape, const float* q, const voi
   if (launch_bounds(s, q, meta, block_table, seq_lens, ub, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
-  if (launch_select(s, ub, seq_lens, budget_pages, sel, sel_ub, stream) != hipSuccess)
+  if (launch_select(s, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
   return ENTMAXKV_OK;

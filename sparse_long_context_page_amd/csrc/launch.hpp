@@ -131,8 +131,26 @@ hipError_t launch_meta(const LaunchShape& s, const void* k_pool, const int32_t* 
 hipError_t launch_bounds(const LaunchShape& s, const float* q, const void* meta,
                          const int32_t* bt, const int32_t* lens, float* ub, hipStream_t st);
 
+// drop_neg_inf: pages whose key is -inf are not candidates (the Gaussian
+// selection marks the pages that fail its rule that way); when no more than
+// `budget` candidates remain, all are kept and the rest of the row is -1.
 hipError_t launch_select(const LaunchShape& s, const float* ub, const int32_t* lens,
-                         int budget, int32_t* sel, float* sel_ub, hipStream_t st);
+                         int budget, int32_t* sel, float* sel_ub, bool drop_neg_inf,
+                         hipStream_t st);
+
+hipError_t launch_moments(const LaunchShape& s, const void* k_pool, const int32_t* bt,
+                          const int32_t* lens, void* moments, hipStream_t st);
+
+// Gaussian-aware selection, before the top-cap select: per-page score
+// statistics (mu_a, s_a) into `stats` ([B*H, ub_ld] double2), then per head
+// tau_hat and the keys (estimated maximum, or -inf when it fails the rule)
+// into `keys` ([B*H, ub_ld] float).
+hipError_t launch_gauss_stats(const LaunchShape& s, const float* q, const void* moments,
+                              const int32_t* bt, const int32_t* lens, double am1, void* stats,
+                              hipStream_t st);
+hipError_t launch_gauss_solve(const LaunchShape& s, const void* stats, const int32_t* lens, int m,
+                              double delta, float* keys, float* tau_hat, hipStream_t st);
+size_t gauss_ws_bytes(const LaunchShape& s);
 
 // Per-dtype instantiations (decode_bf16.hip, decode_f32.hip).
 hipError_t launch_score_bf16(const LaunchShape& s, const SplitPlan& p, const float* q,

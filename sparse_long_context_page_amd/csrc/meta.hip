@@ -11,6 +11,7 @@
 // are read sixteen at a time with streaming loads. min/max does no rounding,
 // so the output is the stored key values.
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace ekv {
 
@@ -96,6 +97,104 @@ meta_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_tab
                               reinterpret_cast<u32x4*>(dst));
   __builtin_nontemporal_store((u32x4){o[1].x, o[1].y, o[1].z, o[1].w},
                               reinterpret_cast<u32x4*>(dst + D));
+}
+
+// Page key moments ([EntmaxKV page] section 2.A, the Gaussian statistics):
+// per (page, KV head) and coordinate, the mean and the population variance of
+// the page's valid keys. Same lane layout as meta_kernel. The sums run in
+// float64 around the page's first row k0 (d = k - k0), so the variance
+// s2/n - (s1/n)^2 does not cancel; for bf16 keys every d, d^2 and sum of a
+// page is exact. Results are rounded to float32 and then, for bf16 caches,
+// to bf16 (each to nearest even).
+template <typename KV, int D>
+__global__ void __launch_bounds__(256)
+moments_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_table,
+               const int32_t* __restrict__ seq_lens, KV* __restrict__ moments, int B, int Hkv,
+               int ps, int max_pages, int num_phys) {
+  constexpr int VPC = 16 / sizeof(KV);
+  constexpr int CPR = D / VPC;
+  constexpr int IPW = kWave / CPR;
+  constexpr int RB = 8;  // rows per batch of loads (two float64 sums per value)
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int c = lane % CPR;
+  const long long item = ((long long)blockIdx.x * (256 / kWave) + wave) * IPW + lane / CPR;
+  const int g = (int)(item % Hkv);
+  const long long bj = item / Hkv;
+  const int j = (int)(bj % max_pages);
+  const int b = (int)(bj / max_pages);
+  if (b >= B) return;
+  const int L = clamp_len(seq_lens[b], max_pages * ps);
+  if (j * ps >= L) return;
+  const int phys = block_table[(size_t)b * max_pages + j];
+  if (phys < 0 || phys >= num_phys) return;
+  const int nv = min(ps, L - j * ps);
+  const KV* base = k_pool + ((size_t)phys * Hkv + g) * (size_t)ps * D + c * VPC;
+
+  auto widen8 = [](const u32x4& x, float (&f)[VPC]) {
+    if constexpr (sizeof(KV) == 2) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        f[2 * w] = bf16_lo(x[w]);
+        f[2 * w + 1] = bf16_hi(x[w]);
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) f[w] = __uint_as_float(x[w]);
+    }
+  };
+  float k0[VPC];
+  widen8(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base)), k0);
+  double s1[VPC], s2[VPC];
+#pragma unroll
+  for (int e = 0; e < VPC; ++e) {
+    s1[e] = 0.0;
+    s2[e] = 0.0;
+  }
+  for (int r0 = 0; r0 < nv; r0 += RB) {
+    // every load of the batch issued (rows past the valid ones re-read the
+    // last valid row and are not summed)
+    u32x4 x[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      x[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(base + (size_t)min(r0 + i, nv - 1) * D));
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if (r0 + i < nv) {
+        float f[VPC];
+        widen8(x[i], f);
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) {
+          const double d = (double)f[e] - (double)k0[e];
+          s1[e] += d;
+          s2[e] = fma(d, d, s2[e]);
+        }
+      }
+    }
+  }
+  const double n = (double)nv;
+  float mean[VPC], var[VPC];
+#pragma unroll
+  for (int e = 0; e < VPC; ++e) {
+    const double m1 = s1[e] / n;
+    mean[e] = (float)((double)k0[e] + m1);
+    var[e] = (float)fmax(s2[e] / n - m1 * m1, 0.0);
+  }
+  KV* dst = moments + ((size_t)phys * Hkv + g) * 2 * D + c * VPC;
+#pragma unroll
+  for (int side = 0; side < 2; ++side) {
+    const float* a = side ? var : mean;
+    u32x4 o;
+    if constexpr (sizeof(KV) == 2) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = bf16_rne_bits(a[2 * k]) | (bf16_rne_bits(a[2 * k + 1]) << 16);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = __float_as_uint(a[k]);
+    }
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + side * D));
+  }
 }
 
 // Boxes after an append: item = (sequence, KV head, i-th page touched by the
@@ -232,6 +331,28 @@ static hipError_t launch_meta_t(const LaunchShape& s, const void* k_pool, const 
                      static_cast<const KV*>(k_pool), bt, lens, static_cast<KV*>(meta), s.batch,
                      s.num_kv_heads, s.page_size, s.max_pages, s.num_phys);
   return hipGetLastError();
+}
+
+template <typename KV, int D>
+static hipError_t launch_moments_t(const LaunchShape& s, const void* k_pool, const int32_t* bt,
+                                   const int32_t* lens, void* moments, hipStream_t st) {
+  constexpr int IPB = (256 / kWave) * (kWave / (D / (16 / sizeof(KV))));  // items per block
+  const long long items = (long long)s.batch * s.max_pages * s.num_kv_heads;
+  const long long blocks = (items + IPB - 1) / IPB;
+  hipLaunchKernelGGL((moments_kernel<KV, D>), dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const KV*>(k_pool), bt, lens, static_cast<KV*>(moments),
+                     s.batch, s.num_kv_heads, s.page_size, s.max_pages, s.num_phys);
+  return hipGetLastError();
+}
+
+hipError_t launch_moments(const LaunchShape& s, const void* k_pool, const int32_t* bt,
+                          const int32_t* lens, void* moments, hipStream_t st) {
+  if (s.bf16) {
+    if (s.head_dim == 64) return launch_moments_t<bf16_t, 64>(s, k_pool, bt, lens, moments, st);
+    return launch_moments_t<bf16_t, 128>(s, k_pool, bt, lens, moments, st);
+  }
+  if (s.head_dim == 64) return launch_moments_t<float, 64>(s, k_pool, bt, lens, moments, st);
+  return launch_moments_t<float, 128>(s, k_pool, bt, lens, moments, st);
 }
 
 hipError_t launch_meta(const LaunchShape& s, const void* k_pool, const int32_t* bt,

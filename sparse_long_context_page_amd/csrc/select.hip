@@ -320,13 +320,14 @@ template <int kSelNT>
 __global__ void __launch_bounds__(kSelNT)
 select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens, int H, int G,
               int Hkv, int U, int ps, int max_pages, int ldu, int budget,
-              int32_t* __restrict__ sel, float* __restrict__ sel_ub) {
+              int32_t* __restrict__ sel, float* __restrict__ sel_ub, uint32_t drop_below) {
   constexpr int NW = kSelNT / kWave;
   constexpr int UNR = 4;  // 16-byte loads in flight per thread
   __shared__ __align__(16) uint32_t sord[kSelLds];
   __shared__ __align__(16) int hist[2][256];
   __shared__ unsigned int ured[NW][2];
   __shared__ int wcnt[NW][2];
+  __shared__ int vcnt[NW];
   __shared__ int bc[3];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -339,7 +340,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   int32_t* out = sel + (size_t)bh * budget;
   float* out_ub = sel_ub ? sel_ub + (size_t)bh * budget : nullptr;
 
-  if (P <= budget) {
+  if (drop_below == 0u && P <= budget) {
     for (int i = tid; i < budget; i += kSelNT) {
       out[i] = i < P ? i : -1;
       if (out_ub) out_ub[i] = i < P ? row[i] + 0.0f : -__builtin_inff();
@@ -365,7 +366,11 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
     return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
   };
 
+  // A key counts when its page is below P and its order value is above
+  // drop_below (0: every page's key counts).
+  auto valid = [&](int j, uint32_t o) { return j < P && o > drop_below; };
   uint32_t mn = 0xffffffffu, mx = 0u;
+  int nvalid = 0;
   for (int base = 0; base < n4; base += UNR * kSelNT) {
     uint4 v[UNR] = {};
 #pragma unroll
@@ -379,9 +384,10 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
       if (i4 < n4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (4 * i4 + e < P) {
+          if (valid(4 * i4 + e, at(v[r], e))) {
             mn = min(mn, at(v[r], e));
             mx = max(mx, at(v[r], e));
+            ++nvalid;
           }
         }
         if (staged) *reinterpret_cast<uint4*>(&sord[4 * i4]) = v[r];
@@ -390,16 +396,20 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   }
   mn = wave_min(mn);
   mx = wave_max(mx);
+  nvalid = wave_sum(nvalid);
   if (lane == 0) {
     ured[wave][0] = mn;
     ured[wave][1] = mx;
+    vcnt[wave] = nvalid;
   }
   if (tid < 256) hist[0][tid] = 0;
   __syncthreads();
+  nvalid = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     mn = min(mn, ured[w][0]);
     mx = max(mx, ured[w][1]);
+    nvalid += vcnt[w];
   }
 
   // Radix select of the budget-th largest key, 8 bits per pass from the
@@ -407,7 +417,16 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   // whole. Two histograms alternate so that a pass needs two barriers.
   uint32_t prefix, pmask;
   int k = budget;  // rank still to place among keys matching the prefix
-  if (mn == mx) {
+  if (nvalid <= budget) {
+    // every counted key is kept: all of them "equal" an empty prefix
+    prefix = 0u;
+    pmask = 0u;
+    k = nvalid;
+    for (int i = nvalid + tid; i < budget; i += kSelNT) {
+      out[i] = -1;
+      if (out_ub) out_ub[i] = -__builtin_inff();
+    }
+  } else if (mn == mx) {
     prefix = mx;
     pmask = 0xffffffffu;
   } else {
@@ -433,7 +452,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t o = at(v[r], e);
-            if (i4 < n4 && 4 * i4 + e < P && (o & pmask) == prefix)
+            if (i4 < n4 && valid(4 * i4 + e, o) && (o & pmask) == prefix)
               atomicAdd(&hist[cur][(o >> lo) & dmask], 1);
           }
         }
@@ -487,10 +506,10 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
     const uint4 v = quad(i4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool valid = 4 * i4 + e < P;
+      const bool ok = valid(4 * i4 + e, at(v, e));
       const uint32_t m = at(v, e) & pmask;
-      n_eq += (valid && m == prefix) ? 1 : 0;
-      n_gt += (valid && m > prefix) ? 1 : 0;
+      n_eq += (ok && m == prefix) ? 1 : 0;
+      n_gt += (ok && m > prefix) ? 1 : 0;
     }
   }
   int gt_base, eq_base;
@@ -501,10 +520,10 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
     const uint4 v = quad(i4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool valid = 4 * i4 + e < P;
+      const bool ok = valid(4 * i4 + e, at(v, e));
       const uint32_t m = at(v, e) & pmask;
-      const bool eq = valid && m == prefix;
-      const bool take = (valid && m > prefix) || (eq && eqc < k);
+      const bool eq = ok && m == prefix;
+      const bool take = (ok && m > prefix) || (eq && eqc < k);
       eqc += eq ? 1 : 0;
       if (take) {
         if (pos < budget) {
@@ -587,18 +606,18 @@ hipError_t launch_bounds(const LaunchShape& s, const float* q, const void* meta,
 }
 
 hipError_t launch_select(const LaunchShape& s, const float* ub, const int32_t* lens, int budget,
-                         int32_t* sel, float* sel_ub, hipStream_t st) {
+                         int32_t* sel, float* sel_ub, bool drop_neg_inf, hipStream_t st) {
   const int U = s.batch * s.num_kv_heads;
+  // order value of -inf: keys at or below it are dropped when asked
+  const uint32_t drop_below = drop_neg_inf ? 0x007fffffu : 0u;
   if (U * s.group >= kSelWideFrom)
     hipLaunchKernelGGL(select_kernel<256>, dim3(U * s.group), dim3(256), 0, st, ub, lens,
                      s.num_q_heads, s.group, s.num_kv_heads, U, s.page_size, s.max_pages,
-                     ub_ld(s.max_pages), budget,
-                     sel, sel_ub);
+                     ub_ld(s.max_pages), budget, sel, sel_ub, drop_below);
   else
     hipLaunchKernelGGL(select_kernel<512>, dim3(U * s.group), dim3(512), 0, st, ub, lens,
                      s.num_q_heads, s.group, s.num_kv_heads, U, s.page_size, s.max_pages,
-                     ub_ld(s.max_pages), budget,
-                     sel, sel_ub);
+                     ub_ld(s.max_pages), budget, sel, sel_ub, drop_below);
   return hipGetLastError();
 }
 

@@ -6,8 +6,9 @@ kernels. Importing this module loads the library and raises if it is not
 built (there is no fallback path).
 
 The function names match the C ABI:
-    entmaxkv_build_page_meta, entmaxkv_score_select, entmaxkv_decode_sparse,
-    entmaxkv_decode_full, entmaxkv_workspace_bytes, entmaxkv_strerror
+    entmaxkv_build_page_meta, entmaxkv_append_page_meta, entmaxkv_score_select,
+    entmaxkv_decode_sparse, entmaxkv_decode_full, entmaxkv_build_page_moments,
+    entmaxkv_gauss_select, entmaxkv_workspace_bytes, entmaxkv_strerror
 """
 from __future__ import annotations
 
@@ -30,9 +31,11 @@ ENTMAXKV_BF16 = 1
 ENTMAXKV_WS_SELECT = 0
 ENTMAXKV_WS_SPARSE = 1
 ENTMAXKV_WS_FULL = 2
+ENTMAXKV_WS_GAUSS = 3
 
 # kernels each entry point launches (for per-kernel event timing)
-KERNELS = {"build_page_meta": 1, "score_select": 2, "decode_sparse": 2, "decode_full": 2}
+KERNELS = {"build_page_meta": 1, "append_page_meta": 1, "score_select": 2, "decode_sparse": 2,
+           "decode_full": 2, "build_page_moments": 1, "gauss_select": 3}
 
 
 class Shape(ctypes.Structure):
@@ -66,12 +69,16 @@ def _load() -> ctypes.CDLL:
     lib.entmaxkv_score_select.argtypes = [SP, P, P, P, P, I32, P, P, P, SZ, P, P]
     lib.entmaxkv_decode_sparse.argtypes = [SP, P, P, P, P, P, P, I32, F32, P, P, P, P, SZ, P, P]
     lib.entmaxkv_decode_full.argtypes = [SP, P, P, P, P, P, F32, P, P, P, P, SZ, P, P]
+    lib.entmaxkv_build_page_moments.argtypes = [SP, P, P, P, P, P, P]
+    lib.entmaxkv_gauss_select.argtypes = [SP, P, P, P, P, F32, F32, I32, P, P, P, SZ, P, P]
     lib.entmaxkv_workspace_bytes.argtypes = [SP, I32, I32, ctypes.POINTER(SZ)]
     lib.entmaxkv_strerror.argtypes = [ctypes.c_int]
     lib.entmaxkv_strerror.restype = ctypes.c_char_p
     lib.entmaxkv_version.argtypes = []
-    for name in ("entmaxkv_build_page_meta", "entmaxkv_score_select", "entmaxkv_decode_sparse",
-                 "entmaxkv_decode_full", "entmaxkv_workspace_bytes", "entmaxkv_version"):
+    for name in ("entmaxkv_build_page_meta", "entmaxkv_append_page_meta",
+                 "entmaxkv_score_select", "entmaxkv_decode_sparse", "entmaxkv_decode_full",
+                 "entmaxkv_build_page_moments", "entmaxkv_gauss_select",
+                 "entmaxkv_workspace_bytes", "entmaxkv_version"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -167,6 +174,26 @@ def _args_append_page_meta(shape: Shape, k_pool, block_table, old_lens, new_lens
         _ptr(meta, "meta", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
 
 
+def _args_build_page_moments(shape: Shape, k_pool, block_table, seq_lens, moments, stream=None):
+    return lib.entmaxkv_build_page_moments, [
+        ctypes.byref(shape), _ptr(k_pool, "k_pool", _kv_dtypes(shape)),
+        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
+        _ptr(moments, "moments", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
+
+
+def _args_gauss_select(shape: Shape, q, moments, block_table, seq_lens, alpha, delta, cap_pages,
+                       sel, tau_hat=None, ws=None, stream=None):
+    if ws is None:
+        ws = workspace(shape, cap_pages, ENTMAXKV_WS_GAUSS, q.device)
+    return lib.entmaxkv_gauss_select, [
+        ctypes.byref(shape), _ptr(q, "q", (torch.float32,)),
+        _ptr(moments, "moments", _kv_dtypes(shape)),
+        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
+        float(alpha), float(delta), int(cap_pages), _ptr(sel, "sel", (torch.int32,)),
+        _ptr(tau_hat, "tau_hat", (torch.float32,), nullable=True), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream, q.device), None], ws
+
+
 def _args_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_pages, sel,
                        sel_ub=None, ws=None, stream=None):
     if ws is None:
@@ -228,6 +255,19 @@ def entmaxkv_append_page_meta(shape: Shape, k_pool, block_table, old_lens, new_l
     _run("entmaxkv_append_page_meta", fn, args, events)
 
 
+def entmaxkv_build_page_moments(shape: Shape, k_pool, block_table, seq_lens, moments,
+                                stream=None, events=None):
+    fn, args = _args_build_page_moments(shape, k_pool, block_table, seq_lens, moments, stream)
+    _run("entmaxkv_build_page_moments", fn, args, events)
+
+
+def entmaxkv_gauss_select(shape: Shape, q, moments, block_table, seq_lens, alpha, delta,
+                          cap_pages, sel, tau_hat=None, ws=None, stream=None, events=None):
+    fn, args, _ = _args_gauss_select(shape, q, moments, block_table, seq_lens, alpha, delta,
+                                     cap_pages, sel, tau_hat, ws, stream)
+    _run("entmaxkv_gauss_select", fn, args, events)
+
+
 def entmaxkv_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_pages, sel,
                           sel_ub=None, ws=None, stream=None, events=None):
     fn, args, _ = _args_score_select(shape, q, meta, block_table, seq_lens, budget_pages, sel,
@@ -260,7 +300,9 @@ class Prepared:
 
     _makers = {"build_page_meta": _args_build_page_meta,
                "append_page_meta": _args_append_page_meta, "score_select": _args_score_select,
-               "decode_sparse": _args_decode_sparse, "decode_full": _args_decode_full}
+               "decode_sparse": _args_decode_sparse, "decode_full": _args_decode_full,
+               "build_page_moments": _args_build_page_moments,
+               "gauss_select": _args_gauss_select}
 
     def __init__(self, name: str, *args, **kwargs):
         r = Prepared._makers[name](*args, **kwargs)

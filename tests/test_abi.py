@@ -179,3 +179,53 @@ def test_append_page_meta_validation(ek):
     assert f(ctypes.byref(s), d, d, d, d, 1, odd, None, None) == -1
     bad = shape(ek, head_dim=96)
     assert f(ctypes.byref(bad), d, d, d, d, 1, d, None, None) == -2
+
+
+def test_page_moments_validation(ek):
+    """The moments entry point rejects a null shape or pointer, misaligned
+    buffers and unsupported shapes before any HIP call."""
+    s = shape(ek)
+    d = ctypes.c_void_p(256)
+    f = ek.lib.entmaxkv_build_page_moments
+    assert f(None, d, d, d, d, None, None) == -1
+    for i in range(4):
+        args = [d, d, d, d]
+        args[i] = None
+        assert f(ctypes.byref(s), *args, None, None) == -1
+    odd = ctypes.c_void_p(256 + 8)
+    assert f(ctypes.byref(s), odd, d, d, d, None, None) == -1
+    assert f(ctypes.byref(s), d, d, d, odd, None, None) == -1
+    assert f(ctypes.byref(shape(ek, head_dim=96)), d, d, d, d, None, None) == -2
+
+
+def test_gauss_select_validation(ek):
+    """alpha with a non-integer 1/(alpha-1) (or outside 1..4) is unsupported;
+    alpha <= 1, a negative or non-finite delta, cap <= 0, null or misaligned
+    pointers and a short workspace are rejected, all before any HIP call."""
+    s = shape(ek)
+    d = ctypes.c_void_p(256)
+    big = 1 << 40
+    f = ek.lib.entmaxkv_gauss_select
+    ok = lambda alpha=1.5, delta=0.0, cap=64, ws=d, n=big: f(
+        ctypes.byref(s), d, d, d, d, alpha, delta, cap, d, None, ws, n, None, None)
+    need = ws_rc(ek, s, 64, ek.ENTMAXKV_WS_GAUSS)[1]
+    assert need > 0
+    for alpha in (1.1, 1.4, 1.6, 3.0):
+        assert ok(alpha=alpha) == -2
+    for alpha in (1.0, 0.5, float("nan"), float("inf")):
+        assert ok(alpha=alpha) == -1
+    for delta in (-0.1, float("nan"), float("inf")):
+        assert ok(delta=delta) == -1
+    for cap in (0, -3):
+        assert ok(cap=cap) == -1
+    assert ok(ws=None) == -3
+    assert ok(n=need - 1) == -3
+    assert ok(ws=ctypes.c_void_p(256 + 16)) == -1
+    for i in range(5):
+        args = [d, d, d, d, d]  # q, moments, block_table, seq_lens, sel
+        args[i] = None
+        assert f(ctypes.byref(s), *args[:4], 1.5, 0.0, 64, args[4], None, d, big, None,
+                 None) == -1
+    odd = ctypes.c_void_p(256 + 8)
+    assert f(ctypes.byref(s), odd, d, d, d, 1.5, 0.0, 64, d, None, d, big, None, None) == -1
+    assert f(ctypes.byref(s), d, odd, d, d, 1.5, 0.0, 64, d, None, d, big, None, None) == -1

@@ -1,0 +1,166 @@
+"""Gaussian-aware page selection on the GPU against the oracle
+(oracle/gauss_oracle.py): page moments value for value, tau_hat, the selected
+pages (identical up to pages whose estimate sits within float64 rounding of
+the threshold or of the cap's boundary), and the decode over the GPU's
+selection."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import entmax_oracle as O
+from oracle import gauss_oracle as GO
+from sparse_long_context_page_amd import synth
+from parity_util import Dev, announce, check_decode, meta_to_f64
+
+pytestmark = pytest.mark.gpu
+
+ALPHAS = (2.0, 1.5, 4.0 / 3.0, 1.25)
+
+
+def _workload(kv_dtype, D, ps, Hkv, lens, G=2, plant="group_mean", q_scale=None):
+    return synth.Workload("gauss", len(lens), G * Hkv, Hkv, D, ps, max(max(lens), 1), kv_dtype,
+                          (1.5,), (4,), q_scale or 4.0 / np.sqrt(D), plant=plant,
+                          n_planted=4 if plant else 0, seq_lens=lens)
+
+
+def build_moments(dev: Dev) -> torch.Tensor:
+    from sparse_long_context_page_amd import entmaxkv as E
+    w = dev.w
+    mom = torch.full((dev.inp["num_phys_pages"], w.num_kv_heads, 2, w.head_dim), float("nan"),
+                     dtype=dev.kv_torch, device="cuda")
+    E.entmaxkv_build_page_moments(dev.shape, dev.k, dev.bt, dev.lens, mom)
+    return mom
+
+
+def ulps(a, b, kv_dtype):
+    """Distance in units of the stored dtype's last place."""
+    b32 = np.abs(b).astype(np.float32)
+    sp = np.spacing(np.maximum(b32, np.float32(1e-30))).astype(np.float64)
+    if kv_dtype == "bf16":
+        sp *= 65536.0
+    return np.abs(a - b) / sp
+
+
+@pytest.mark.parametrize("kv_dtype,D,ps,Hkv,lens", [
+    ("bf16", 128, 32, 2, (4096, 1000, 33)),
+    ("f32", 64, 16, 1, (700, 1, 16)),
+    ("bf16", 64, 64, 4, (640, 129)),
+    ("f32", 128, 32, 2, (96, 31))])
+def test_page_moments_match_oracle(kv_dtype, D, ps, Hkv, lens):
+    inp = synth.generate(_workload(kv_dtype, D, ps, Hkv, lens), 31)
+    dev = Dev(inp)
+    announce(f"moments {kv_dtype} D{D} ps{ps}")
+    mom = meta_to_f64(build_moments(dev), kv_dtype)
+    torch.cuda.synchronize()
+    mean, var = GO.page_moments(inp["k_pool"], inp["block_table"], inp["seq_lens"], ps, kv_dtype)
+    used = sorted({int(inp["block_table"][b, j]) for b in range(len(lens))
+                   for j in range(O.num_pages(lens[b], ps))})
+    for side, ref in ((0, mean), (1, var)):
+        got = mom[used, :, side]
+        want = ref[used]
+        assert not np.isnan(got).any()
+        d = ulps(got, want, kv_dtype)
+        assert d.max() <= 1.0, f"side {side}: {d.max()} ulp"
+        assert (got == want).mean() >= 0.999, f"side {side}: {(got != want).sum()} values differ"
+    # full pages of bf16 keys: every sum is exact, so the moments are exact
+    if kv_dtype == "bf16":
+        full = [int(inp["block_table"][b, j]) for b in range(len(lens))
+                for j in range(lens[b] // ps)]
+        np.testing.assert_array_equal(mom[full, :, 0], mean[full])
+        np.testing.assert_array_equal(mom[full, :, 1], var[full])
+
+
+def _run_select(dev, mom, alpha, delta, cap):
+    from sparse_long_context_page_amd import entmaxkv as E
+    B, H = dev.w.batch, dev.w.num_q_heads
+    sel = torch.full((B, H, cap), -7, dtype=torch.int32, device="cuda")
+    tau_hat = torch.empty((B, H), device="cuda")
+    E.entmaxkv_gauss_select(dev.shape, dev.q, mom, dev.bt, dev.lens, alpha, delta, cap, sel,
+                            tau_hat)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), tau_hat.cpu().numpy()
+
+
+def _check_head(inp, b, h, alpha, delta, cap, moments, sel_row, tau_val):
+    tau_ref, est, ref = GO.gauss_select_for_head(inp, b, h, alpha, delta, cap, moments=moments)
+    assert abs(float(tau_val) - tau_ref) <= 1e-6 * max(1.0, abs(tau_ref)), (tau_val, tau_ref)
+    gpu = [int(x) for x in sel_row]
+    n = sum(1 for x in gpu if x >= 0)
+    assert gpu[n:] == [-1] * (cap - n), "padding"
+    kept = gpu[:n]
+    assert kept == sorted(kept) and len(set(kept)) == n and all(0 <= j < len(est) for j in kept)
+    diff = set(kept) ^ {j for j in ref if j >= 0}
+    if diff:
+        near = GO.gauss_near_threshold(est, tau_ref, delta, cap)
+        assert diff <= near, f"b{b} h{h}: selection differs off the threshold: {sorted(diff)[:8]}"
+    return len(diff), n
+
+
+@pytest.mark.parametrize("name,ctx", [("long_128k", 4096), ("alpha_sweep_64k", 2048)])
+def test_gauss_select_matches_oracle(name, ctx):
+    w = synth.shrink(synth.WORKLOADS[name], context=ctx, batch=2)
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS[name])
+    dev = Dev(inp)
+    announce(f"gauss select {name} ctx{ctx}")
+    mom = build_moments(dev)
+    moments = GO.page_moments(inp["k_pool"], inp["block_table"], inp["seq_lens"], w.page_size,
+                              w.kv_dtype)
+    P = O.num_pages(ctx, w.page_size)
+    near_total = 0
+    for alpha in ALPHAS:
+        for delta, cap in ((0.0, P), (1.0, P), (3.0, P), (3.0, 6)):
+            announce(f"gauss select {name} alpha {alpha:.4f} delta {delta} cap {cap}")
+            sel, tau_hat = _run_select(dev, mom, alpha, delta, cap)
+            for b in range(w.batch):
+                for h in range(w.num_q_heads):
+                    nd, _ = _check_head(inp, b, h, alpha, delta, cap, moments, sel[b, h],
+                                        tau_hat[b, h])
+                    near_total += nd
+    assert near_total <= 4, f"{near_total} near-threshold differences"
+
+
+def test_gauss_edge_cases():
+    """An empty sequence (all -1, tau_hat NaN), a one-token sequence (its page
+    has zero variance: tau_hat = mu - 1 and the page is kept), a partial last
+    page, and cap 1."""
+    inp = synth.generate(_workload("bf16", 128, 16, 2, (0, 1, 37, 256)), 41)
+    dev = Dev(inp)
+    announce("gauss edge cases")
+    mom = build_moments(dev)
+    moments = GO.page_moments(inp["k_pool"], inp["block_table"], inp["seq_lens"], 16, "bf16")
+    for alpha in (1.5, 1.25):
+        for cap in (1, 3, 16):
+            sel, tau_hat = _run_select(dev, mom, alpha, 0.25, cap)
+            assert (sel[0] == -1).all() and np.isnan(tau_hat[0]).all()
+            assert (sel[1][:, 0] == 0).all() and (sel[1][:, 1:] == -1).all()
+            for b in (1, 2, 3):
+                for h in range(dev.w.num_q_heads):
+                    _check_head(inp, b, h, alpha, 0.25, cap, moments, sel[b, h], tau_hat[b, h])
+
+
+def test_gauss_select_then_decode():
+    """The GPU's Gaussian selection fed to the sparse decode: the decode over
+    those pages equals the oracle's decode over the same pages."""
+    from sparse_long_context_page_amd import entmaxkv as E
+    w = synth.shrink(synth.WORKLOADS["long_128k"], context=4096, batch=2)
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS["long_128k"])
+    dev = Dev(inp)
+    announce("gauss select + decode")
+    mom = build_moments(dev)
+    cap, alpha = 48, 1.5
+    sel, _ = _run_select(dev, mom, alpha, 2.0, cap)
+    assert (sel >= 0).sum(axis=2).min() >= 1
+    B, H, D = w.batch, w.num_q_heads, w.head_dim
+    sel_t = torch.from_numpy(sel).cuda()
+    out = torch.empty((B, H, D), device="cuda")
+    tau = torch.empty((B, H), device="cuda")
+    sup = torch.empty((B, H), dtype=torch.int32, device="cuda")
+    E.entmaxkv_decode_sparse(dev.shape, dev.q, dev.k, dev.v, dev.bt, dev.lens, sel_t, cap, alpha,
+                             out, tau, sup)
+    torch.cuda.synchronize()
+    out, tau, sup = out.cpu().numpy(), tau.cpu().numpy(), sup.cpu().numpy()
+    for b in range(B):
+        for h in range(0, H, 3):
+            ref = O.decode_sparse(inp, b, h, alpha, sel[b, h])
+            check_decode(ref, out[b, h], tau[b, h], sup[b, h], w.kv_dtype, alpha,
+                         f"gauss decode b{b} h{h}")
