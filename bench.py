@@ -288,6 +288,116 @@ def containment_report(args):
                       "cells": cells}))
 
 
+def gauss_report(args):
+    """Gaussian-aware selection (page moments, tau_hat, pages whose estimated
+    maximum clears tau_hat - delta, at most `cap`): for each alpha of the
+    workload and each (delta, cap) cell, the pages kept per head, the fraction
+    of trials whose kept pages contain the full-cache support (criterion as in
+    the containment report, sampled trials re-checked against the oracle), and
+    the selection's time; the fixed-budget top-k at the workload's budget for
+    comparison."""
+    import torch
+    from oracle import entmax_oracle as O
+    from sparse_long_context_page_amd import entmaxkv as E
+    w = synth.WORKLOADS[args.workload]
+    log = lambda m: (sys.stderr.write(f"[report] {m}\n"), sys.stderr.flush())
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS[w.name])
+    log(f"generated {w.name}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kv_t = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+
+    def pool(a):
+        if w.kv_dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q = torch.from_numpy(inp["q"]).to(dev)
+    k, v = pool(inp["k_pool"]), pool(inp["v_pool"])
+    bt = torch.from_numpy(inp["block_table"]).to(dev)
+    lens = torch.from_numpy(inp["seq_lens"]).to(dev)
+    shape = E.make_shape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                         inp["max_pages"], inp["num_phys_pages"], w.kv_dtype)
+    B, H, D = w.batch, w.num_q_heads, w.head_dim
+    P = int(inp["max_pages"])
+    mshape = (inp["num_phys_pages"], w.num_kv_heads, 2, D)
+    meta = torch.empty(mshape, dtype=kv_t, device=dev)
+    mom = torch.empty(mshape, dtype=kv_t, device=dev)
+    E.entmaxkv_build_page_meta(shape, k, bt, lens, meta)
+    ev = E.HipEvents(6)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def timed(call, n=7):
+        ts = []
+        for i in range(n):
+            flush.fill_(i & 255)
+            call(list(ev))
+            torch.cuda.synchronize()
+            ts.append(ev.elapsed_ms(0, len(ev) - 1 if len(ev) > 2 else 1) * 1e3)
+        return float(np.median(ts[2:]))
+
+    mom_us = []
+    for i in range(5):
+        flush.fill_(i)
+        E.entmaxkv_build_page_moments(shape, k, bt, lens, mom, events=list(ev)[:2])
+        torch.cuda.synchronize()
+        mom_us.append(ev.elapsed_ms(0, 1) * 1e3)
+    rng = np.random.default_rng(0)
+    alphas = (args.alpha,) if args.alpha else w.alphas
+    budget = args.budget or w.budgets[0]
+    cells = []
+    for alpha in alphas:
+        out = torch.empty((B, H, D), device=dev)
+        tau = torch.empty((B, H), device=dev)
+        sup = torch.empty((B, H), dtype=torch.int32, device=dev)
+        E.entmaxkv_decode_full(shape, q, k, v, bt, lens, alpha, out, tau, sup)
+        torch.cuda.synchronize()
+        tau_f, sup_f = tau.cpu().numpy(), sup.cpu().numpy()
+
+        def decode_contained(sel_t, cap):
+            E.entmaxkv_decode_sparse(shape, q, k, v, bt, lens, sel_t, cap, alpha, out, tau, sup)
+            torch.cuda.synchronize()
+            return contained(sup.cpu().numpy(), sup_f, tau.cpu().numpy(), tau_f)
+
+        sel_k = torch.empty((B, H, budget), dtype=torch.int32, device=dev)
+        E.entmaxkv_score_select(shape, q, meta, bt, lens, budget, sel_k)
+        c_k = decode_contained(sel_k, budget)
+        cells.append({"policy": "top-k (box bound)", "alpha": alpha, "budget_pages": budget,
+                      "contained_fraction": round(float(c_k.mean()), 4)})
+        log(f"alpha {alpha} top-{budget}: contained {c_k.mean():.4f}")
+        for cap in (budget, P):
+            for delta in (0.0, 1.0, 2.0, 3.0, 4.0, 6.0):
+                sel = torch.empty((B, H, cap), dtype=torch.int32, device=dev)
+                ws = E.workspace(shape, cap, E.ENTMAXKV_WS_GAUSS, dev)
+                call = E.Prepared("gauss_select", shape, q, mom, bt, lens, alpha, delta, cap,
+                                  sel, None, ws=ws)
+                us = timed(call)
+                kept = (sel >= 0).sum(dim=2).cpu().numpy()
+                c = decode_contained(sel, cap)
+                sel_np = sel.cpu().numpy()
+                agree = 0
+                checks = [(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(2)]
+                for b, h in checks:
+                    res = O.decode_full(inp, b, h, alpha)
+                    ref = set(O.support_pages(res, w.page_size)) <= set(int(j) for j in sel_np[b, h])
+                    agree += int(ref == bool(c[b, h]))
+                cells.append({"policy": "gaussian", "alpha": alpha, "delta": delta, "cap": cap,
+                              "mean_pages": round(float(kept.mean()), 2),
+                              "p90_pages": int(np.percentile(kept, 90)),
+                              "contained_fraction": round(float(c.mean()), 4),
+                              "select_us": round(us, 2), "oracle_checked": len(checks),
+                              "oracle_agree": agree})
+                log(f"alpha {alpha} delta {delta} cap {cap}: pages {kept.mean():.1f} "
+                    f"contained {c.mean():.4f} select {us:.1f} us")
+    print(json.dumps({"report": "gauss", "workload": w.name, "data": "synthetic",
+                      "page_moments_us": round(float(np.median(mom_us[1:])), 2),
+                      "trial": "one (sequence, query head) decode",
+                      "criterion": "kept pages contain the full-cache support (GPU: equal "
+                                   "support size and tau within 1e-6; sampled trials re-checked "
+                                   "against the oracle's support pages)",
+                      "cells": cells}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,10 +409,12 @@ def main():
     ap.add_argument("--oracle-heads", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="hot-cache timing (diagnostic)")
-    ap.add_argument("--report", choices=["containment"], default=None,
-                    help="instead of the timed step: the alpha/budget sweep report of how often "
-                         "the selected pages contain the full-cache support (default workload "
-                         "alpha_sweep_64k); prints its own JSON line")
+    ap.add_argument("--report", choices=["containment", "gauss"], default=None,
+                    help="instead of the timed step: 'containment', the alpha/budget sweep "
+                         "report of how often the selected pages contain the full-cache support "
+                         "(default workload alpha_sweep_64k); 'gauss', the same for the "
+                         "Gaussian-aware selection over a grid of margins and caps, with its "
+                         "times (default workload long_128k); each prints its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the steps, run a plain 1 GiB device copy three times (a known-size "
                          "reference for the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -317,6 +429,9 @@ def main():
         if "--workload" not in sys.argv:
             args.workload = "alpha_sweep_64k"
         containment_report(args)
+        return
+    if args.report == "gauss":
+        gauss_report(args)
         return
 
     w = synth.WORKLOADS[args.workload]

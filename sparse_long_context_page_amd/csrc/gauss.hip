@@ -15,12 +15,12 @@
 //   a page's moment record [mean | var] is split over D/4 lanes, the G
 //   heads' two dot products are formed in float64 and finished by a
 //   multi-value butterfly; (mu_a, s_a) per (b, h, page) go to the workspace.
-// gauss_solve_kernel: one workgroup per (b, h): tau_hat by Newton's method
-//   from the left end of the bracket (the left side of the equation is convex
-//   and decreasing in t, so the iterates rise monotonically to the root),
-//   over the pages that can contribute (held in LDS); then one key per page
-//   (its estimated maximum as float32, or -inf when it fails the rule) for
-//   the top-cap select kernel.
+// gauss_solve_kernel: one workgroup of 1024 threads per (b, h), the head's
+//   page statistics staged in LDS: tau_hat by Newton steps on the logarithm
+//   of the equation's left side (nearly quadratic in t for Gaussian tails),
+//   safeguarded by a bracket that bisects when a step would leave it; then
+//   one key per page (its estimated maximum as float32, or -inf when it fails
+//   the rule) for the top-cap select kernel.
 #include <cfloat>
 #include <type_traits>
 
@@ -29,8 +29,9 @@
 namespace ekv {
 
 constexpr int kGaussPages = 32;    // pages per workgroup of the statistics kernel
-constexpr int kGaussList = 2048;   // contributing pages a solve workgroup holds in LDS
-constexpr int kGaussIters = 64;    // most Newton steps
+constexpr int kGaussNT = 1024;     // threads of a solve workgroup (one per (b, h))
+constexpr int kGaussLds = 4096;    // pages of a head a solve workgroup holds in LDS
+constexpr int kGaussIters = 100;   // most solve steps
 constexpr double kGaussReach = 9.0;  // pages with mu_a + 9 s_a <= the bracket's left end
                                      // contribute below 1e-19 n_p s_a^m: left out of the sums
 
@@ -159,17 +160,45 @@ __device__ __forceinline__ void normal_partial_moments(double c, double& pm, dou
   pm1 = expand(M - 1);
 }
 
+// The same in float32 (a cheaper first approximation of tau_hat; the
+// expansion's cancellation in the far tail only touches pages whose share
+// of the sum is negligible there).
 template <int M>
-__global__ void __launch_bounds__(256)
+__device__ __forceinline__ void normal_partial_moments_f(float c, float& pm, float& pm1) {
+  const float phi = 0.39894228f * __expf(-0.5f * c * c);
+  float J[M + 1];
+  J[0] = 0.5f * erfcf(c * 0.70710678f);
+  if constexpr (M >= 1) J[1] = phi;
+#pragma unroll
+  for (int k = 2; k <= M; ++k) {
+    float ck = 1.0f;
+#pragma unroll
+    for (int i = 0; i < k - 1; ++i) ck *= c;
+    J[k] = ck * phi + (float)(k - 1) * J[k - 2];
+  }
+  auto expand = [&](int m) {
+    float s = 0.0f, binom = 1.0f;
+    for (int k = m; k >= 0; --k) {
+      float p = 1.0f;
+      for (int i = 0; i < m - k; ++i) p *= -c;
+      s += binom * p * J[k];
+      binom = binom * (float)k / (float)(m - k + 1);
+    }
+    return fmaxf(s, 0.0f);
+  };
+  pm = expand(M);
+  pm1 = expand(M - 1);
+}
+
+template <int M>
+__global__ void __launch_bounds__(kGaussNT)
 gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict__ seq_lens,
                    int H, int ps, int max_pages, int ldu, double delta, float* __restrict__ keys,
                    float* __restrict__ tau_hat) {
-  constexpr int NT = 256;
-  __shared__ double lmu[kGaussList];
-  __shared__ double ls[kGaussList];
-  __shared__ float ln[kGaussList];
-  __shared__ double red[2 * (NT / kWave)];
-  __shared__ int tmp[NT / kWave + 2];
+  constexpr int NT = kGaussNT, NW = NT / kWave;
+  __shared__ double red[2 * NW];
+  __shared__ double smu[kGaussLds];
+  __shared__ double ss[kGaussLds];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int bh = blockIdx.x, b = bh / H;
@@ -182,38 +211,56 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
     return;
   }
   auto rows_of = [&](int j) { return (double)min(ps, L - j * ps); };
-
-  // bracket: the root lies in [max mu_a - 1, max (mu_a + 40 s_a)]
-  double mx = -DBL_MAX;
-  for (int j = tid; j < P; j += NT) mx = fmax(mx, row[j].x);
-  mx = block_reduce<NT>(mx, red, [](double a, double c) { return fmax(a, c); });
-  const double lo = mx - 1.0;
-
-  // the pages that can contribute at t >= lo, compacted into LDS when they fit
-  auto reaches = [&](const double2& v) {
-    return v.y > 0.0 ? v.x + kGaussReach * v.y > lo : v.x > lo;
-  };
-  int cnt = 0;
-  for (int j = tid; j < P; j += NT) cnt += reaches(row[j]) ? 1 : 0;
-  int n_act;
-  int pos = block_excl_scan<NT>(cnt, tmp, &n_act);
-  const bool in_lds = n_act <= kGaussList;
-  if (in_lds) {
-    for (int j = tid; j < P; j += NT) {
-      const double2 v = row[j];
-      if (reaches(v)) {
-        lmu[pos] = v.x;
-        ls[pos] = v.y;
-        ln[pos] = (float)rows_of(j);
-        ++pos;
-      }
+  // two sums (or maxima) over the workgroup, the same on every thread
+  auto block2 = [&](double& x, double& y, bool is_max) {
+    if (is_max) {
+      x = wave_max(x);
+      y = wave_max(y);
+    } else {
+      x = wave_allsum(x);
+      y = wave_allsum(y);
     }
-  }
-  __syncthreads();
+    if (lane == 0) {
+      red[2 * wid] = x;
+      red[2 * wid + 1] = y;
+    }
+    __syncthreads();
+    x = red[0];
+    y = red[1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      x = is_max ? fmax(x, red[2 * w]) : x + red[2 * w];
+      y = is_max ? fmax(y, red[2 * w + 1]) : y + red[2 * w + 1];
+    }
+    __syncthreads();
+  };
 
-  // f(t) = sum_p n_p E[(A_p - t)_+^M] and g(t) = -f'(t) / M
-  auto term = [&](double mu, double s, double n, double t, double& f, double& g) {
+  // (mu_a, s_a) of the head's pages: staged in LDS when the sequence has at
+  // most kGaussLds pages, else read from the workspace row at every step
+  const bool in_lds = P <= kGaussLds;
+  double mx = -DBL_MAX, hx = -DBL_MAX;
+  for (int j = tid; j < P; j += NT) {
+    const double2 v = row[j];
+    if (in_lds) {
+      smu[j] = v.x;
+      ss[j] = v.y;
+    }
+    mx = fmax(mx, v.x);
+    hx = fmax(hx, v.x + 40.0 * v.y);
+  }
+  block2(mx, hx, true);
+  // bracket: f(a) >= 1 at a = max mu - 1 (the top page alone gives
+  // n (E[A] - a)^M >= 1 by Jensen), f < 1 at the right end
+  double a = mx - 1.0, z = fmax(hx, a + 1.0);
+
+  // f(t) = sum_p n_p E[(A_p - t)_+^M] and g(t) = -f'(t) / M, over the pages
+  // that can reach t (a page with mu + 9 s below the bracket's left end adds
+  // less than 1e-19 n s^M). sums64 in float64; sums32 entirely in float32, a
+  // cheaper first approximation (its cancellation in the far tail only
+  // touches pages whose share of the sum is negligible there).
+  auto term64 = [&](double mu, double s, double n, double t, double& f, double& g) {
     if (s > 0.0) {
+      if (mu + kGaussReach * s <= a) return;
       double pm, pm1;
       normal_partial_moments<M>((t - mu) / s, pm, pm1);
       double sm1 = 1.0;
@@ -230,46 +277,106 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
       g += n * dm1;
     }
   };
-  double t = lo;
-  for (int it = 0; it < kGaussIters; ++it) {
-    double f = 0.0, g = 0.0;
-    if (in_lds) {
-      for (int i = tid; i < n_act; i += NT) term(lmu[i], ls[i], (double)ln[i], t, f, g);
-    } else {
-      for (int j = tid; j < P; j += NT) {
-        const double2 v = row[j];
-        if (reaches(v)) term(v.x, v.y, rows_of(j), t, f, g);
-      }
+  auto term32 = [&](float mu, float s, float n, float t, float a32, float& f, float& g) {
+    if (s > 0.0f) {
+      if (mu + (float)kGaussReach * s <= a32) return;
+      float pm, pm1;
+      normal_partial_moments_f<M>((t - mu) * __frcp_rn(s), pm, pm1);
+      float sm1 = 1.0f;
+#pragma unroll
+      for (int i = 0; i < M - 1; ++i) sm1 *= s;
+      f += n * sm1 * s * pm;
+      g += n * sm1 * pm1;
+    } else if (mu > t) {
+      const float d = mu - t;
+      float dm1 = 1.0f;
+#pragma unroll
+      for (int i = 0; i < M - 1; ++i) dm1 *= d;
+      f += n * dm1 * d;
+      g += n * dm1;
     }
-    f = wave_allsum(f);
-    g = wave_allsum(g);
-    if (lane == 0) {
-      red[2 * wid] = f;
-      red[2 * wid + 1] = g;
-    }
-    __syncthreads();
+  };
+  auto sums = [&](auto f32, double t, double& f, double& g) {
+    constexpr bool F32 = decltype(f32)::value;
     f = 0.0;
     g = 0.0;
-#pragma unroll
-    for (int w = 0; w < NT / kWave; ++w) {
-      f += red[2 * w];
-      g += red[2 * w + 1];
+    if constexpr (F32) {
+      float ff = 0.0f, gg = 0.0f;
+      const float tf = (float)t, af = (float)a;
+#pragma unroll 1
+      for (int j = tid; j < P; j += NT) {
+        double mu, sd;
+        if (in_lds) {
+          mu = smu[j];
+          sd = ss[j];
+        } else {
+          const double2 v = row[j];
+          mu = v.x;
+          sd = v.y;
+        }
+        term32((float)mu, (float)sd, (float)rows_of(j), tf, af, ff, gg);
+      }
+      f = ff;
+      g = gg;
+    } else {
+#pragma unroll 1
+      for (int j = tid; j < P; j += NT) {
+        if (in_lds) {
+          term64(smu[j], ss[j], rows_of(j), t, f, g);
+        } else {
+          const double2 v = row[j];
+          term64(v.x, v.y, rows_of(j), t, f, g);
+        }
+      }
     }
-    __syncthreads();
-    // Newton step from the left (f - 1 >= 0 here, f' = -M g < 0)
-    if (!(f > 1.0) || !(g > 0.0)) break;
-    const double step = (f - 1.0) / ((double)M * g);
-    t += step;
-    if (step <= 1e-15 * fmax(1.0, fabs(t))) break;
-  }
+    block2(f, g, false);
+  };
+  // Newton steps on ln f (nearly quadratic for Gaussian tails, so few steps)
+  // inside a bracket [lo, hi] that every step shrinks; a step that would
+  // leave it bisects instead. First in float32, to about 1e-4 of f (on a
+  // bracket of its own: float32 may misjudge which side of the root a point
+  // is on), then in float64 from there on the float64 bracket: from that
+  // start Newton's quadratic convergence reaches the sum's rounding level
+  // (|f - 1| <= 1e-13) within three steps.
+  auto newton = [&](auto f32, double t, double lo, double hi, double tol, int iters) {
+    for (int it = 0; it < iters; ++it) {
+      double f, g;
+      sums(f32, t, f, g);
+      if (f >= 1.0) lo = t;
+      else hi = t;
+      if (fabs(f - 1.0) <= tol) break;
+      double tn = 0.5 * (lo + hi);
+      if (f > 0.0 && g > 0.0) {
+        const double tt = t + log(f) * f / ((double)M * g);
+        if (tt > lo && tt < hi) tn = tt;
+      }
+      const double scale = fmax(1.0, fabs(t));
+      if (fabs(tn - t) <= 1e-14 * scale || hi - lo <= 1e-14 * scale) {
+        t = tn;
+        break;
+      }
+      t = tn;
+    }
+    return t;
+  };
+  double t = newton(std::true_type{}, a, a, z, 1e-4, kGaussIters);
+  t = newton(std::false_type{}, fmin(fmax(t, a), z), a, z, 1e-13, kGaussIters);
 
   // one key per page: the estimated maximum, or -inf off the rule
   const double cut = t - delta;
+  const double spread_full = sqrt(2.0 * log((double)ps));  // every page but the last is full
+  auto key = [&](double mu, double s, double n) {
+    const double spread = n == (double)ps ? spread_full : (n >= 2.0 ? sqrt(2.0 * log(n)) : 0.0);
+    const double est = mu + s * spread;
+    return est > cut ? (float)est + 0.0f : -__builtin_inff();
+  };
   for (int j = tid; j < P; j += NT) {
-    const double2 v = row[j];
-    const double n = rows_of(j);
-    const double est = n >= 2.0 ? v.x + v.y * sqrt(2.0 * log(n)) : v.x;
-    krow[j] = est > cut ? (float)est + 0.0f : -__builtin_inff();
+    if (in_lds) {
+      krow[j] = key(smu[j], ss[j], rows_of(j));
+    } else {
+      const double2 v = row[j];
+      krow[j] = key(v.x, v.y, rows_of(j));
+    }
   }
   if (tid == 0 && tau_hat) tau_hat[bh] = (float)t;
 }
@@ -317,19 +424,19 @@ hipError_t launch_gauss_solve(const LaunchShape& s, const void* stats, const int
   const int ldu = ub_ld(s.max_pages);
   switch (m) {
     case 1:
-      hipLaunchKernelGGL(gauss_solve_kernel<1>, dim3(heads), dim3(256), 0, st, st2, lens,
+      hipLaunchKernelGGL(gauss_solve_kernel<1>, dim3(heads), dim3(kGaussNT), 0, st, st2, lens,
                          s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat);
       break;
     case 2:
-      hipLaunchKernelGGL(gauss_solve_kernel<2>, dim3(heads), dim3(256), 0, st, st2, lens,
+      hipLaunchKernelGGL(gauss_solve_kernel<2>, dim3(heads), dim3(kGaussNT), 0, st, st2, lens,
                          s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat);
       break;
     case 3:
-      hipLaunchKernelGGL(gauss_solve_kernel<3>, dim3(heads), dim3(256), 0, st, st2, lens,
+      hipLaunchKernelGGL(gauss_solve_kernel<3>, dim3(heads), dim3(kGaussNT), 0, st, st2, lens,
                          s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat);
       break;
     default:
-      hipLaunchKernelGGL(gauss_solve_kernel<4>, dim3(heads), dim3(256), 0, st, st2, lens,
+      hipLaunchKernelGGL(gauss_solve_kernel<4>, dim3(heads), dim3(kGaussNT), 0, st, st2, lens,
                          s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat);
       break;
   }
