@@ -316,11 +316,15 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
 
 // --------------------------------------------------------------------------
 
-template <int kSelNT>
+// kDrop: keys at or below the order value of -inf are not candidates (the
+// Gaussian selection marks the pages that fail its rule that way); when no
+// more than `budget` candidates remain all are kept and the row is -1 padded.
+template <int kSelNT, bool kDrop>
 __global__ void __launch_bounds__(kSelNT)
 select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens, int H, int G,
               int Hkv, int U, int ps, int max_pages, int ldu, int budget,
-              int32_t* __restrict__ sel, float* __restrict__ sel_ub, uint32_t drop_below) {
+              int32_t* __restrict__ sel, float* __restrict__ sel_ub) {
+  constexpr uint32_t drop_below = 0x007fffffu;  // float_order(-inf)
   constexpr int NW = kSelNT / kWave;
   constexpr int UNR = 4;  // 16-byte loads in flight per thread
   __shared__ __align__(16) uint32_t sord[kSelLds];
@@ -340,7 +344,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   int32_t* out = sel + (size_t)bh * budget;
   float* out_ub = sel_ub ? sel_ub + (size_t)bh * budget : nullptr;
 
-  if (drop_below == 0u && P <= budget) {
+  if (!kDrop && P <= budget) {
     for (int i = tid; i < budget; i += kSelNT) {
       out[i] = i < P ? i : -1;
       if (out_ub) out_ub[i] = i < P ? row[i] + 0.0f : -__builtin_inff();
@@ -366,9 +370,8 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
     return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
   };
 
-  // A key counts when its page is below P and its order value is above
-  // drop_below (0: every page's key counts).
-  auto valid = [&](int j, uint32_t o) { return j < P && o > drop_below; };
+  // A key counts when its page is below P (and, with kDrop, it is above -inf).
+  auto valid = [&](int j, uint32_t o) { return j < P && (!kDrop || o > drop_below); };
   uint32_t mn = 0xffffffffu, mx = 0u;
   int nvalid = 0;
   for (int base = 0; base < n4; base += UNR * kSelNT) {
@@ -387,7 +390,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
           if (valid(4 * i4 + e, at(v[r], e))) {
             mn = min(mn, at(v[r], e));
             mx = max(mx, at(v[r], e));
-            ++nvalid;
+            if constexpr (kDrop) ++nvalid;
           }
         }
         if (staged) *reinterpret_cast<uint4*>(&sord[4 * i4]) = v[r];
@@ -396,20 +399,20 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   }
   mn = wave_min(mn);
   mx = wave_max(mx);
-  nvalid = wave_sum(nvalid);
+  if constexpr (kDrop) nvalid = wave_sum(nvalid);
   if (lane == 0) {
     ured[wave][0] = mn;
     ured[wave][1] = mx;
-    vcnt[wave] = nvalid;
+    if constexpr (kDrop) vcnt[wave] = nvalid;
   }
   if (tid < 256) hist[0][tid] = 0;
   __syncthreads();
-  nvalid = 0;
+  nvalid = kDrop ? 0 : P;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     mn = min(mn, ured[w][0]);
     mx = max(mx, ured[w][1]);
-    nvalid += vcnt[w];
+    if constexpr (kDrop) nvalid += vcnt[w];
   }
 
   // Radix select of the budget-th largest key, 8 bits per pass from the
@@ -417,7 +420,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   // whole. Two histograms alternate so that a pass needs two barriers.
   uint32_t prefix, pmask;
   int k = budget;  // rank still to place among keys matching the prefix
-  if (nvalid <= budget) {
+  if (kDrop && nvalid <= budget) {
     // every counted key is kept: all of them "equal" an empty prefix
     prefix = 0u;
     pmask = 0u;
@@ -608,16 +611,12 @@ hipError_t launch_bounds(const LaunchShape& s, const float* q, const void* meta,
 hipError_t launch_select(const LaunchShape& s, const float* ub, const int32_t* lens, int budget,
                          int32_t* sel, float* sel_ub, bool drop_neg_inf, hipStream_t st) {
   const int U = s.batch * s.num_kv_heads;
-  // order value of -inf: keys at or below it are dropped when asked
-  const uint32_t drop_below = drop_neg_inf ? 0x007fffffu : 0u;
-  if (U * s.group >= kSelWideFrom)
-    hipLaunchKernelGGL(select_kernel<256>, dim3(U * s.group), dim3(256), 0, st, ub, lens,
-                     s.num_q_heads, s.group, s.num_kv_heads, U, s.page_size, s.max_pages,
-                     ub_ld(s.max_pages), budget, sel, sel_ub, drop_below);
-  else
-    hipLaunchKernelGGL(select_kernel<512>, dim3(U * s.group), dim3(512), 0, st, ub, lens,
-                     s.num_q_heads, s.group, s.num_kv_heads, U, s.page_size, s.max_pages,
-                     ub_ld(s.max_pages), budget, sel, sel_ub, drop_below);
+  const bool wide = U * s.group >= kSelWideFrom;
+  const dim3 grid(U * s.group), block(wide ? 256 : 512);
+  auto kern = wide ? (drop_neg_inf ? select_kernel<256, true> : select_kernel<256, false>)
+                   : (drop_neg_inf ? select_kernel<512, true> : select_kernel<512, false>);
+  hipLaunchKernelGGL(kern, grid, block, 0, st, ub, lens, s.num_q_heads, s.group, s.num_kv_heads,
+                     U, s.page_size, s.max_pages, ub_ld(s.max_pages), budget, sel, sel_ub);
   return hipGetLastError();
 }
 
