@@ -121,9 +121,13 @@ gauss_stats_kernel(const float* __restrict__ q, const KV* __restrict__ moments,
     BF::reduce(mu, lane);
     BF::reduce(s2, lane);
     const int jj = t * PPB + threadIdx.x / LP;
-    if (ok[t] && owner)
+    // a page past the block table's valid range (an input outside the
+    // contract) gets a neutral entry: it adds nothing to tau_hat's sum and
+    // its key is -inf
+    if (jj < n && owner)
       stats[(size_t)(h0 + my_head) * ldu + j0 + jj] =
-          make_double2(am1 * mu[0], am1 * sqrt(fmax(s2[0], 0.0)));
+          ok[t] ? make_double2(am1 * mu[0], am1 * sqrt(fmax(s2[0], 0.0)))
+                : make_double2(-DBL_MAX, 0.0);
   }
 }
 

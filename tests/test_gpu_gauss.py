@@ -164,3 +164,37 @@ def test_gauss_select_then_decode():
             ref = O.decode_sparse(inp, b, h, alpha, sel[b, h])
             check_decode(ref, out[b, h], tau[b, h], sup[b, h], w.kv_dtype, alpha,
                          f"gauss decode b{b} h{h}")
+
+
+def test_gauss_select_full_size_128k():
+    """The Gaussian selection at the 128K workload's full size (the report's
+    configuration: cap 82 and no cap, margin 3): every head's row is a valid
+    ascending selection, and sampled heads match the oracle (moments of the
+    sampled sequences' pages computed by the oracle itself)."""
+    w = synth.WORKLOADS["long_128k"]
+    announce("gauss full size long_128k: generate")
+    inp = synth.generate(w, synth.WORKLOAD_SEEDS["long_128k"])
+    dev = Dev(inp)
+    announce("gauss full size long_128k: moments/select")
+    mom = build_moments(dev)
+    rng = np.random.default_rng(17)
+    heads = sorted({(int(rng.integers(0, w.batch)), int(rng.integers(0, w.num_q_heads)))
+                    for _ in range(6)})
+    # oracle moments only for the sampled sequences' pages
+    bs = sorted({b for b, _ in heads})
+    sub_bt = inp["block_table"][bs]
+    sub_lens = inp["seq_lens"][bs]
+    moments = GO.page_moments(inp["k_pool"], sub_bt, sub_lens, w.page_size, w.kv_dtype)
+    P = O.num_pages(int(inp["seq_lens"][0]), w.page_size)
+    for cap in (82, P):
+        sel, tau_hat = _run_select(dev, mom, 1.5, 3.0, cap)
+        n = (sel >= 0).sum(axis=2)
+        for b in range(w.batch):
+            for h in range(w.num_q_heads):
+                row = sel[b, h]
+                kept = row[:n[b, h]]
+                assert (row[n[b, h]:] == -1).all() and (np.diff(kept) > 0).all()
+        assert np.isfinite(tau_hat).all()
+        for b, h in heads:
+            announce(f"gauss full size long_128k: oracle b{b} h{h} cap {cap}")
+            _check_head(inp, b, h, 1.5, 3.0, cap, moments, sel[b, h], tau_hat[b, h])
