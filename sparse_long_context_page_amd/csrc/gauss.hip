@@ -257,6 +257,44 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
   // n (E[A] - a)^M >= 1 by Jensen), f < 1 at the right end
   double a = mx - 1.0, z = fmax(hx, a + 1.0);
 
+  // Starting point: the root for one Gaussian pooled over the head's tokens
+  // (mean and variance of the page mixture, taken about mx), i.e.
+  // N sbar^M E[(Y - c)_+^M] = 1 solved for c by Newton steps on the log of
+  // the left side (concave and decreasing in c), then t0 = mubar + c sbar.
+  double s1 = 0.0, s2 = 0.0;
+  for (int j = tid; j < P; j += NT) {
+    const double mu = in_lds ? smu[j] : row[j].x;
+    const double sd = in_lds ? ss[j] : row[j].y;
+    if (mu > -DBL_MAX) {
+      const double n = rows_of(j), d = mu - mx;
+      s1 += n * d;
+      s2 += n * (sd * sd + d * d);
+    }
+  }
+  block2(s1, s2, false);
+  double t0 = a;
+  {
+    const double N = (double)L;
+    const double m1 = s1 / N;
+    const double var = s2 / N - m1 * m1;
+    if (var > 0.0) {
+      const double sbar = sqrt(var);
+      const double target = -log(N) - (double)M * log(sbar);  // ln E[(Y - c)_+^M] at the root
+      double c = 0.0;
+      for (int it = 0; it < 12; ++it) {
+        double pm, pm1;
+        normal_partial_moments<M>(c, pm, pm1);
+        if (!(pm > 0.0)) break;
+        const double h = log(pm) - target;
+        const double dh = -(double)M * pm1 / pm;
+        const double step = -h / dh;
+        c += step;
+        if (fabs(step) <= 1e-6 * fmax(1.0, fabs(c))) break;
+      }
+      t0 = fmin(fmax(mx + m1 + c * sbar, a), z);
+    }
+  }
+
   // f(t) = sum_p n_p E[(A_p - t)_+^M] and g(t) = -f'(t) / M, over the pages
   // that can reach t (a page with mu + 9 s below the bracket's left end adds
   // less than 1e-19 n s^M). sums64 in float64; sums32 entirely in float32, a
@@ -337,12 +375,16 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
   };
   // Newton steps on ln f (nearly quadratic for Gaussian tails, so few steps)
   // inside a bracket [lo, hi] that every step shrinks; a step that would
-  // leave it bisects instead. First in float32, to about 1e-4 of f (on a
-  // bracket of its own: float32 may misjudge which side of the root a point
-  // is on), then in float64 from there on the float64 bracket: from that
-  // start Newton's quadratic convergence reaches the sum's rounding level
-  // (|f - 1| <= 1e-13) within three steps.
-  auto newton = [&](auto f32, double t, double lo, double hi, double tol, int iters) {
+  // leave it bisects instead. First in float32 from the pooled start, to
+  // about 1e-4 of f (on a bracket of its own: float32 may misjudge which side
+  // of the root a point is on), then in float64 from there on the float64
+  // bracket: from that start Newton's quadratic convergence reaches the
+  // sum's rounding level in two steps.
+  // tol: stop when |f - 1| <= tol; last: when |f - 1| <= last, take that
+  // step and stop (from there one quadratic step reaches the rounding
+  // level); rel: stop when a step or the bracket is below rel of t.
+  auto newton = [&](auto f32, double t, double lo, double hi, double tol, double last,
+                    double rel, int iters) {
     for (int it = 0; it < iters; ++it) {
       double f, g;
       sums(f32, t, f, g);
@@ -355,7 +397,7 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
         if (tt > lo && tt < hi) tn = tt;
       }
       const double scale = fmax(1.0, fabs(t));
-      if (fabs(tn - t) <= 1e-14 * scale || hi - lo <= 1e-14 * scale) {
+      if (fabs(f - 1.0) <= last || fabs(tn - t) <= rel * scale || hi - lo <= rel * scale) {
         t = tn;
         break;
       }
@@ -363,8 +405,8 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
     }
     return t;
   };
-  double t = newton(std::true_type{}, a, a, z, 1e-4, kGaussIters);
-  t = newton(std::false_type{}, fmin(fmax(t, a), z), a, z, 1e-13, kGaussIters);
+  double t = newton(std::true_type{}, t0, a, z, 1e-4, 0.0, 1e-6, kGaussIters);
+  t = newton(std::false_type{}, fmin(fmax(t, a), z), a, z, 1e-13, 1e-7, 1e-14, kGaussIters);
 
   // one key per page: the estimated maximum, or -inf off the rule
   const double cut = t - delta;
