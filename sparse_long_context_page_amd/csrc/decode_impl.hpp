@@ -14,19 +14,24 @@
 //   every token with p > 0 has z > max(z) - 1/(alpha-1) (at
 //   tau = (alpha-1) max z - 1 the top token alone has weight 1), and a
 //   running maximum can only underestimate max(z), so filtering against it
-//   keeps a superset. Survivors go to per-wave LDS lists, are filtered again
-//   against the workgroup maximum and written, in a fixed order, as this
-//   split's candidate region (z, token index) with its count and maximum.
+//   keeps a superset (the four waves share their running maxima through
+//   LDS, so each filters against the largest). Survivors go to per-wave LDS
+//   lists, are filtered again against the workgroup maximum and written, in
+//   a fixed order, as this split's candidate region (z, token index) with its
+//   count and maximum.
 //   Sparse: the split is a slice of the union of the G heads' selected pages
 //   (each page read once), built from a bitmap in LDS.
-// tau_pv_kernel (one workgroup per (sequence, query head)):
+// tau_pv_kernel (one workgroup per (sequence, query head); one kernel for the
+// budgeted and the full-cache decode):
 //   Takes the global maximum over the regions, gathers the candidates inside
 //   the window into a list (tightened first by a lower bound on tau when
 //   there are many), solves tau on f(tau) = sum [a_i - tau]_+^m = 1 -- by
 //   the sort-based closed form for m = 1, 2 on short lists, else by a
 //   safeguarded Newton iteration bracketed by [a_max - 1, a_max] with
 //   bisection when a step leaves the bracket -- then reads V rows only for
-//   the tokens with p > 0 and writes o = sum p v / sum p.
+//   the tokens with p > 0 (for short lists they are requested before the
+//   solve) and writes o = sum p v / sum p. The rarely taken steps are
+//   out-of-line functions, which keeps the common path's code compact.
 #pragma once
 
 #include <float.h>
