@@ -72,7 +72,7 @@ float window_of(float alpha) {
 int score_lds_ok(const LaunchShape& s, const SplitPlan& p, bool sparse, int budget) {
   const size_t total = score_lds_layout(s.group, s.page_size, p.pages_per_split, sparse,
                                         s.max_pages, budget, score_bytes(s.bf16),
-                                        score_kbuf_bytes(s.bf16, s.page_size, s.head_dim, sparse),
+                                        score_kbuf_bytes(s.bf16, s.group, s.page_size, s.head_dim, sparse),
                                         s.head_dim)
                            .total;
   return total <= kMaxScoreLds ? ENTMAXKV_OK : ENTMAXKV_ERR_UNSUPPORTED;
@@ -95,7 +95,7 @@ namespace ekv {
 static int fit_pps(const LaunchShape& s, int pps, bool sparse, int budget) {
   while (pps > 1 && score_lds_layout(s.group, s.page_size, pps, sparse, s.max_pages, budget,
                                      score_bytes(s.bf16),
-                                     score_kbuf_bytes(s.bf16, s.page_size, s.head_dim, sparse),
+                                     score_kbuf_bytes(s.bf16, s.group, s.page_size, s.head_dim, sparse),
                                      s.head_dim)
                             .total > kMaxScoreLds)
     pps /= 2;

@@ -594,7 +594,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
   };
 
   const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc),
-                                        score_kbuf_bytes(sizeof(KV) == 2, PS, D, SPARSE), D);
+                                        score_kbuf_bytes(sizeof(KV) == 2, G, PS, D, SPARSE), D);
   // The waves' running maxima per head: a static LDS array, so the compiler
   // can tell it apart from the page buffers that direct-to-LDS loads fill
   // (reads of it then need not wait for those loads).
@@ -660,7 +660,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     static_assert(NI >= 1 && NI * 1024 == PB && CPR * 16 == RB, "page tiling");
     auto swz = [](int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & (CPR - 1)); };
     const int kgrp = lane >> 4, tok = lane & 15;
-    constexpr int NBUF = score_kbuf_pages(SPARSE);
+    constexpr int NBUF = score_kbuf_pages(SPARSE, G, PS, D);
     unsigned char* kbuf = smem + lay.kbuf + (size_t)wave * NBUF * PB;
 
     // q split exactly into three bf16 parts, staged in LDS as rows
@@ -1647,7 +1647,7 @@ hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float*
   using ZT = typename KvTraits<KV>::Acc;
   const int U = s.batch * s.num_kv_heads;
   const ScoreLds lay = score_lds_layout(G, PS, p.pages_per_split, SPARSE, s.max_pages, budget,
-                                        sizeof(ZT), score_kbuf_bytes(s.bf16, PS, D, SPARSE), D);
+                                        sizeof(ZT), score_kbuf_bytes(s.bf16, G, PS, D, SPARSE), D);
   auto kern = score_kernel<KV, D, G, PS, SPARSE>;
   // The LDS limit is a kernel attribute: raised once, to the most any plan
   // asks for (a function-local static is initialised exactly once, also when

@@ -59,11 +59,21 @@ __host__ __device__ constexpr int qtab_pitch(int k) { return k + 8; }
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 // Pages of K staged per wave on the matrix-core path: two (double-buffered)
-// for the long full-cache slices, one for the short sparse ones.
-__host__ __device__ constexpr int score_kbuf_pages(bool sparse) { return sparse ? 1 : 2; }
+// for the long full-cache slices, one for the short sparse ones, and one
+// where two would leave no room for the rest of the workgroup's LDS (the
+// split-q table and the G heads' candidate lists, plus 4 KiB for the slice
+// tables): 8 heads of 128-dim keys in 64-token pages.
+__host__ __device__ constexpr int score_kbuf_pages(bool sparse, int G, int ps, int head_dim) {
+  return (sparse || (size_t)kNW * 2 * ps * head_dim * 2 + (size_t)G * 3 * qtab_pitch(head_dim) * 2 +
+                            (size_t)kNW * G * kListSlots * 8 + 4096 > kMaxScoreLdsBytes)
+             ? 1
+             : 2;
+}
 // Bytes of K staging per wave on the matrix-core path, else 0.
-__host__ __device__ inline int score_kbuf_bytes(bool bf16, int ps, int head_dim, bool sparse) {
-  return (kMfmaScores && bf16) ? score_kbuf_pages(sparse) * ps * head_dim * 2 : 0;
+__host__ __device__ inline int score_kbuf_bytes(bool bf16, int G, int ps, int head_dim,
+                                                bool sparse) {
+  return (kMfmaScores && bf16) ? score_kbuf_pages(sparse, G, ps, head_dim) * ps * head_dim * 2
+                               : 0;
 }
 
 // zbytes: bytes of one score (4 for bf16 caches, 8 for float32 caches);
