@@ -116,7 +116,9 @@ enum {
  * wise min and max of its valid keys (rows t < seq_lens[b]) for each KV head
  * to meta[block_table[b, j]]. min/max is exact, so meta holds stored key
  * values (a zero may come out as -0 or +0). Pages not referenced are left
- * untouched. Kernels launched: 1.
+ * untouched. A physical page listed by several sequences (a shared prefix)
+ * must hold the same valid rows in each; otherwise the box it ends up with
+ * is one of theirs. Kernels launched: 1.
  */
 int entmaxkv_build_page_meta(const entmaxkv_shape* shape, const void* k_pool,
                              const int32_t* block_table, const int32_t* seq_lens,
