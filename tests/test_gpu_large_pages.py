@@ -60,3 +60,29 @@ def test_more_pages_than_staged_on_chip():
         diff = set(got[:n]) ^ {j for j in ref if j >= 0}
         if diff:
             assert diff <= GO.gauss_near_threshold(est, tau_ref, 3.0, cap), sorted(diff)
+
+
+def test_budget_beyond_the_sequence():
+    """A budget of more pages than the sequence has (25000 for 20000): every
+    page is kept (then -1), the selection no longer fits the score kernel's
+    LDS copy, and the sparse decode equals the full-cache one."""
+    ps, P = 16, 20000
+    lens = (P * ps - 9,)
+    w = synth.Workload("many_pages_all", 1, 2, 1, 128, ps, lens[0], "bf16", (1.5,), (25000,),
+                       4.0 / np.sqrt(128), plant="group_mean", n_planted=16, seq_lens=lens)
+    inp = synth.generate(w, 78)
+    dev = Dev(inp)
+    budget, alpha = 25000, 1.5
+    announce("budget beyond the sequence: select/sparse/full")
+    sel, _ = dev.select(budget)
+    sp = dev.sparse(sel, budget, alpha)
+    fu = dev.full(alpha)
+    torch.cuda.synchronize()
+    s = sel.cpu().numpy()
+    assert (s[:, :, :P] == np.arange(P)).all() and (s[:, :, P:] == -1).all()
+    so, st, ss = (x.cpu().numpy() for x in sp)
+    fo, ft, fs = (x.cpu().numpy() for x in fu)
+    for h in range(2):
+        ref = O.decode_full(inp, 0, h, alpha)
+        check_decode(ref, so[0, h], st[0, h], ss[0, h], "bf16", alpha, f"sparse (all pages) h{h}")
+        check_decode(ref, fo[0, h], ft[0, h], fs[0, h], "bf16", alpha, f"full h{h}")
