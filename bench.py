@@ -422,7 +422,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(collectives and sharding are out of scope; see DESIGN.md).", file=sys.stderr)
+              "(collectives and sharding are out of scope).", file=sys.stderr)
         sys.exit(2)
 
     if args.report == "containment":

@@ -25,7 +25,7 @@ standard Tsallis alpha-entmax of Peters, Niculae & Martins (ACL 2019):
 equivalently p = argmax_{p in simplex} p.z + H_alpha(p) with the Tsallis
 entropy H_alpha(p) = sum_j (p_j - p_j^alpha) / (alpha (alpha-1)).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   - the box bound is the maximum of q.k over the box:
     sum_d max(q_d kmin_d, q_d kmax_d);
   - scores are z = q.k on the stored values (no 1/sqrt(d) inside);

@@ -15,7 +15,7 @@ per l'Attention Entmax" (gist.science, paper 2605.21649), [EntmaxKV page]:
     estimated maximum score exceeds the estimate (less a safety margin Delta)
     are selected, so the number of pages follows the query's scores.
 The pages state neither the equation, nor the estimator of a page's maximum,
-nor Delta. The readings taken here (each listed in the design doc):
+nor Delta. The readings taken here:
   G1  moments: per coordinate, the mean and the population variance (1/n) of
       the page's valid keys, computed in float64 and stored in the cache's
       dtype, rounded through float32 (float64 -> float32 -> bf16, each round
