@@ -323,7 +323,10 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
     if (s > 0.0f) {
       if (mu + (float)kGaussReach * s <= a32) return;
       float pm, pm1;
-      normal_partial_moments_f<M>((t - mu) * __frcp_rn(s), pm, pm1);
+      // (clamped so that its powers stay finite in float32; only the float64
+      // steps that follow decide tau_hat)
+      const float c = fminf(fmaxf((t - mu) * __frcp_rn(s), -1.0e4f), 1.0e4f);
+      normal_partial_moments_f<M>(c, pm, pm1);
       float sm1 = 1.0f;
 #pragma unroll
       for (int i = 0; i < M - 1; ++i) sm1 *= s;

@@ -138,6 +138,22 @@ def test_gauss_edge_cases():
                     _check_head(inp, b, h, alpha, 0.25, cap, moments, sel[b, h], tau_hat[b, h])
 
 
+def test_gauss_tiny_query():
+    """A query scaled to 1e-12: every page's score spread is tiny against
+    the bracket (|c| ~ 1e12 in the first, float32 phase of the solve); tau_hat
+    and the selection still match the oracle."""
+    inp = synth.generate(_workload("bf16", 128, 16, 2, (300, 77), q_scale=1e-12), 43)
+    dev = Dev(inp)
+    announce("gauss tiny query")
+    mom = build_moments(dev)
+    moments = GO.page_moments(inp["k_pool"], inp["block_table"], inp["seq_lens"], 16, "bf16")
+    for alpha in ALPHAS:
+        sel, tau_hat = _run_select(dev, mom, alpha, 0.0, 19)
+        for b in range(2):
+            for h in range(dev.w.num_q_heads):
+                _check_head(inp, b, h, alpha, 0.0, 19, moments, sel[b, h], tau_hat[b, h])
+
+
 def test_gauss_select_then_decode():
     """The GPU's Gaussian selection fed to the sparse decode: the decode over
     those pages equals the oracle's decode over the same pages."""
