@@ -342,6 +342,16 @@ def gauss_report(args):
         E.entmaxkv_build_page_moments(shape, k, bt, lens, mom, events=list(ev)[:2])
         torch.cuda.synchronize()
         mom_us.append(ev.elapsed_ms(0, 1) * 1e3)
+    # a decode step's moment maintenance: one appended token per sequence
+    # (the touched pages are recomputed to the bits they already hold)
+    old_lens = (lens - 1).clamp(min=0)
+    mom_app_us = []
+    for i in range(5):
+        flush.fill_(i)
+        E.entmaxkv_append_page_moments(shape, k, bt, old_lens, lens, 1, mom,
+                                       events=list(ev)[:2])
+        torch.cuda.synchronize()
+        mom_app_us.append(ev.elapsed_ms(0, 1) * 1e3)
     rng = np.random.default_rng(0)
     alphas = (args.alpha,) if args.alpha else w.alphas
     budget = args.budget or w.budgets[0]
@@ -391,6 +401,7 @@ def gauss_report(args):
                     f"contained {c.mean():.4f} select {us:.1f} us")
     print(json.dumps({"report": "gauss", "workload": w.name, "data": "synthetic",
                       "page_moments_us": round(float(np.median(mom_us[1:])), 2),
+                      "page_moments_append_us": round(float(np.median(mom_app_us[1:])), 2),
                       "trial": "one (sequence, query head) decode",
                       "criterion": "kept pages contain the full-cache support (GPU: equal "
                                    "support size and tau within 1e-6; sampled trials re-checked "

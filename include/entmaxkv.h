@@ -166,6 +166,26 @@ int entmaxkv_build_page_moments(const entmaxkv_shape* shape, const void* k_pool,
                                 void* moments, hipStream_t stream, hipEvent_t* events);
 
 /*
+ * Page key moments after an append (the statistics of [EntmaxKV page]
+ * section 2.A kept current by a decode loop, like the boxes). The caller has
+ * written the keys of tokens old_lens[b] <= t < new_lens[b] into k_pool. Every
+ * page holding such a token is recomputed from all its valid rows t <
+ * new_lens[b] (stored moments are rounded, so they are not updated in
+ * place): the result on those pages is bit for bit that of
+ * entmaxkv_build_page_moments with seq_lens = new_lens, and no other page is
+ * touched. Arguments as for entmaxkv_append_page_meta (max_new_tokens >= 1,
+ * at least every new_lens[b] - old_lens[b]; pages beyond
+ * ceil(max_new_tokens / page_size) + 1 per sequence are not updated; a
+ * sequence with new_lens[b] <= old_lens[b] is left as it is). Returns
+ * ENTMAXKV_ERR_INVALID for a null or misaligned pointer or max_new_tokens < 1.
+ * Kernels launched: 1.
+ */
+int entmaxkv_append_page_moments(const entmaxkv_shape* shape, const void* k_pool,
+                                 const int32_t* block_table, const int32_t* old_lens,
+                                 const int32_t* new_lens, int32_t max_new_tokens, void* moments,
+                                 hipStream_t stream, hipEvent_t* events);
+
+/*
  * Gaussian-aware entmax page selection ([EntmaxKV page] section 2.B, policy
  * 2). The page states the policy, not its formulas; this is one reading. For
  * each (b, h), with m = 1/(alpha-1), pages j < P_b and n_j their valid rows:

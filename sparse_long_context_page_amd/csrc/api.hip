@@ -302,7 +302,27 @@ int entmaxkv_build_page_moments(const entmaxkv_shape* shape, const void* k_pool,
   if (!aligned(k_pool, 16) || !aligned(moments, 16)) return ENTMAXKV_ERR_INVALID;
   const Events ev{events, stream};
   if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
-  if (launch_moments(s, k_pool, block_table, seq_lens, moments, stream) != hipSuccess)
+  if (launch_moments(s, k_pool, block_table, nullptr, seq_lens, 0, moments, stream) !=
+      hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(0)) return ENTMAXKV_ERR_HIP;
+  return ENTMAXKV_OK;
+}
+
+int entmaxkv_append_page_moments(const entmaxkv_shape* shape, const void* k_pool,
+                                 const int32_t* block_table, const int32_t* old_lens,
+                                 const int32_t* new_lens, int32_t max_new_tokens, void* moments,
+                                 hipStream_t stream, hipEvent_t* events) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  if (!k_pool || !block_table || !old_lens || !new_lens || !moments) return ENTMAXKV_ERR_INVALID;
+  if (max_new_tokens <= 0) return ENTMAXKV_ERR_INVALID;
+  if (!aligned(k_pool, 16) || !aligned(moments, 16)) return ENTMAXKV_ERR_INVALID;
+  const Events ev{events, stream};
+  if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
+  if (launch_moments(s, k_pool, block_table, old_lens, new_lens, max_new_tokens, moments,
+                     stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(0)) return ENTMAXKV_ERR_HIP;
   return ENTMAXKV_OK;

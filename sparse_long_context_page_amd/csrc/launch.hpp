@@ -148,8 +148,11 @@ hipError_t launch_select(const LaunchShape& s, const float* ub, const int32_t* l
                          int budget, int32_t* sel, float* sel_ub, bool drop_neg_inf,
                          hipStream_t st);
 
+// Page key moments of every page (old_lens == nullptr), or, after an append,
+// of the pages the tokens [old_lens, lens) touch (at most max_new per sequence).
 hipError_t launch_moments(const LaunchShape& s, const void* k_pool, const int32_t* bt,
-                          const int32_t* lens, void* moments, hipStream_t st);
+                          const int32_t* old_lens, const int32_t* lens, int max_new,
+                          void* moments, hipStream_t st);
 
 // Gaussian-aware selection, before the top-cap select: per-page score
 // statistics (mu_a, s_a) into `stats` ([B*H, ub_ld] double2), then per head

@@ -106,11 +106,17 @@ meta_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_tab
 // s2/n - (s1/n)^2 does not cancel; for bf16 keys every d, d^2 and sum of a
 // page is exact. Results are rounded to float32 and then, for bf16 caches,
 // to bf16 (each to nearest even).
-template <typename KV, int D>
+// kAppend: after tokens [L0, L1) were appended (seq_lens holds L1), items are
+// (sequence, KV head, i-th page those tokens touch) as in append_meta_kernel,
+// and each touched page is recomputed from all its valid rows: the stored,
+// rounded moments cannot be updated in place, and a page's result is the
+// same bits as a full build at L1.
+template <typename KV, int D, bool kAppend>
 __global__ void __launch_bounds__(256)
 moments_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_table,
-               const int32_t* __restrict__ seq_lens, KV* __restrict__ moments, int B, int Hkv,
-               int ps, int max_pages, int num_phys) {
+               const int32_t* __restrict__ old_lens, const int32_t* __restrict__ seq_lens,
+               KV* __restrict__ moments, int B, int Hkv, int ps, int max_pages, int num_phys,
+               int slots) {
   constexpr int VPC = 16 / sizeof(KV);
   constexpr int CPR = D / VPC;
   constexpr int IPW = kWave / CPR;
@@ -120,11 +126,17 @@ moments_kernel(const KV* __restrict__ k_pool, const int32_t* __restrict__ block_
   const int c = lane % CPR;
   const long long item = ((long long)blockIdx.x * (256 / kWave) + wave) * IPW + lane / CPR;
   const int g = (int)(item % Hkv);
-  const long long bj = item / Hkv;
-  const int j = (int)(bj % max_pages);
-  const int b = (int)(bj / max_pages);
+  const long long rest = item / Hkv;
+  const int per_seq = kAppend ? slots : max_pages;
+  const int b = (int)(rest / per_seq);
   if (b >= B) return;
   const int L = clamp_len(seq_lens[b], max_pages * ps);
+  int j = (int)(rest % per_seq);
+  if constexpr (kAppend) {
+    const int L0 = min(clamp_len(old_lens[b], max_pages * ps), L);
+    if (L0 == L) return;
+    j += L0 / ps;
+  }
   if (j * ps >= L) return;
   const int phys = block_table[(size_t)b * max_pages + j];
   if (phys < 0 || phys >= num_phys) return;
@@ -333,26 +345,45 @@ static hipError_t launch_meta_t(const LaunchShape& s, const void* k_pool, const 
   return hipGetLastError();
 }
 
+// old_lens == nullptr: every page of every sequence; else only the pages the
+// tokens [old_lens, lens) touch, at most max_new tokens per sequence.
 template <typename KV, int D>
 static hipError_t launch_moments_t(const LaunchShape& s, const void* k_pool, const int32_t* bt,
-                                   const int32_t* lens, void* moments, hipStream_t st) {
+                                   const int32_t* old_lens, const int32_t* lens, int max_new,
+                                   void* moments, hipStream_t st) {
   constexpr int IPB = (256 / kWave) * (kWave / (D / (16 / sizeof(KV))));  // items per block
-  const long long items = (long long)s.batch * s.max_pages * s.num_kv_heads;
+  long long slots = s.max_pages;
+  if (old_lens) {
+    // the partly filled last page plus ceil(max_new / ps) more
+    slots = ((long long)max_new + s.page_size - 1) / s.page_size + 1;
+    if (slots > s.max_pages) slots = s.max_pages;
+  }
+  const long long items = (long long)s.batch * slots * s.num_kv_heads;
   const long long blocks = (items + IPB - 1) / IPB;
-  hipLaunchKernelGGL((moments_kernel<KV, D>), dim3((unsigned)blocks), dim3(256), 0, st,
-                     static_cast<const KV*>(k_pool), bt, lens, static_cast<KV*>(moments),
-                     s.batch, s.num_kv_heads, s.page_size, s.max_pages, s.num_phys);
+  if (old_lens)
+    hipLaunchKernelGGL((moments_kernel<KV, D, true>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const KV*>(k_pool), bt, old_lens, lens,
+                       static_cast<KV*>(moments), s.batch, s.num_kv_heads, s.page_size,
+                       s.max_pages, s.num_phys, (int)slots);
+  else
+    hipLaunchKernelGGL((moments_kernel<KV, D, false>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const KV*>(k_pool), bt, nullptr, lens,
+                       static_cast<KV*>(moments), s.batch, s.num_kv_heads, s.page_size,
+                       s.max_pages, s.num_phys, (int)slots);
   return hipGetLastError();
 }
 
 hipError_t launch_moments(const LaunchShape& s, const void* k_pool, const int32_t* bt,
-                          const int32_t* lens, void* moments, hipStream_t st) {
+                          const int32_t* old_lens, const int32_t* lens, int max_new,
+                          void* moments, hipStream_t st) {
   if (s.bf16) {
-    if (s.head_dim == 64) return launch_moments_t<bf16_t, 64>(s, k_pool, bt, lens, moments, st);
-    return launch_moments_t<bf16_t, 128>(s, k_pool, bt, lens, moments, st);
+    if (s.head_dim == 64)
+      return launch_moments_t<bf16_t, 64>(s, k_pool, bt, old_lens, lens, max_new, moments, st);
+    return launch_moments_t<bf16_t, 128>(s, k_pool, bt, old_lens, lens, max_new, moments, st);
   }
-  if (s.head_dim == 64) return launch_moments_t<float, 64>(s, k_pool, bt, lens, moments, st);
-  return launch_moments_t<float, 128>(s, k_pool, bt, lens, moments, st);
+  if (s.head_dim == 64)
+    return launch_moments_t<float, 64>(s, k_pool, bt, old_lens, lens, max_new, moments, st);
+  return launch_moments_t<float, 128>(s, k_pool, bt, old_lens, lens, max_new, moments, st);
 }
 
 hipError_t launch_meta(const LaunchShape& s, const void* k_pool, const int32_t* bt,

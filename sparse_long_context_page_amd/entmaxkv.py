@@ -8,7 +8,8 @@ built (there is no fallback path).
 The function names match the C ABI:
     entmaxkv_build_page_meta, entmaxkv_append_page_meta, entmaxkv_score_select,
     entmaxkv_decode_sparse, entmaxkv_decode_full, entmaxkv_build_page_moments,
-    entmaxkv_gauss_select, entmaxkv_workspace_bytes, entmaxkv_strerror
+    entmaxkv_append_page_moments, entmaxkv_gauss_select, entmaxkv_workspace_bytes,
+    entmaxkv_strerror
 """
 from __future__ import annotations
 
@@ -35,7 +36,8 @@ ENTMAXKV_WS_GAUSS = 3
 
 # kernels each entry point launches (for per-kernel event timing)
 KERNELS = {"build_page_meta": 1, "append_page_meta": 1, "score_select": 2, "decode_sparse": 2,
-           "decode_full": 2, "build_page_moments": 1, "gauss_select": 3}
+           "decode_full": 2, "build_page_moments": 1, "append_page_moments": 1,
+           "gauss_select": 3}
 
 
 class Shape(ctypes.Structure):
@@ -70,6 +72,7 @@ def _load() -> ctypes.CDLL:
     lib.entmaxkv_decode_sparse.argtypes = [SP, P, P, P, P, P, P, I32, F32, P, P, P, P, SZ, P, P]
     lib.entmaxkv_decode_full.argtypes = [SP, P, P, P, P, P, F32, P, P, P, P, SZ, P, P]
     lib.entmaxkv_build_page_moments.argtypes = [SP, P, P, P, P, P, P]
+    lib.entmaxkv_append_page_moments.argtypes = [SP, P, P, P, P, I32, P, P, P]
     lib.entmaxkv_gauss_select.argtypes = [SP, P, P, P, P, F32, F32, I32, P, P, P, SZ, P, P]
     lib.entmaxkv_workspace_bytes.argtypes = [SP, I32, I32, ctypes.POINTER(SZ)]
     lib.entmaxkv_strerror.argtypes = [ctypes.c_int]
@@ -77,8 +80,8 @@ def _load() -> ctypes.CDLL:
     lib.entmaxkv_version.argtypes = []
     for name in ("entmaxkv_build_page_meta", "entmaxkv_append_page_meta",
                  "entmaxkv_score_select", "entmaxkv_decode_sparse", "entmaxkv_decode_full",
-                 "entmaxkv_build_page_moments", "entmaxkv_gauss_select",
-                 "entmaxkv_workspace_bytes", "entmaxkv_version"):
+                 "entmaxkv_build_page_moments", "entmaxkv_append_page_moments",
+                 "entmaxkv_gauss_select", "entmaxkv_workspace_bytes", "entmaxkv_version"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -174,6 +177,15 @@ def _args_append_page_meta(shape: Shape, k_pool, block_table, old_lens, new_lens
         _ptr(meta, "meta", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
 
 
+def _args_append_page_moments(shape: Shape, k_pool, block_table, old_lens, new_lens,
+                              max_new_tokens, moments, stream=None):
+    return lib.entmaxkv_append_page_moments, [
+        ctypes.byref(shape), _ptr(k_pool, "k_pool", _kv_dtypes(shape)),
+        _ptr(block_table, "block_table", (torch.int32,)), _ptr(old_lens, "old_lens", (torch.int32,)),
+        _ptr(new_lens, "new_lens", (torch.int32,)), int(max_new_tokens),
+        _ptr(moments, "moments", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
+
+
 def _args_build_page_moments(shape: Shape, k_pool, block_table, seq_lens, moments, stream=None):
     return lib.entmaxkv_build_page_moments, [
         ctypes.byref(shape), _ptr(k_pool, "k_pool", _kv_dtypes(shape)),
@@ -261,6 +273,13 @@ def entmaxkv_build_page_moments(shape: Shape, k_pool, block_table, seq_lens, mom
     _run("entmaxkv_build_page_moments", fn, args, events)
 
 
+def entmaxkv_append_page_moments(shape: Shape, k_pool, block_table, old_lens, new_lens,
+                                 max_new_tokens, moments, stream=None, events=None):
+    fn, args = _args_append_page_moments(shape, k_pool, block_table, old_lens, new_lens,
+                                         max_new_tokens, moments, stream)
+    _run("entmaxkv_append_page_moments", fn, args, events)
+
+
 def entmaxkv_gauss_select(shape: Shape, q, moments, block_table, seq_lens, alpha, delta,
                           cap_pages, sel, tau_hat=None, ws=None, stream=None, events=None):
     fn, args, _ = _args_gauss_select(shape, q, moments, block_table, seq_lens, alpha, delta,
@@ -302,6 +321,7 @@ class Prepared:
                "append_page_meta": _args_append_page_meta, "score_select": _args_score_select,
                "decode_sparse": _args_decode_sparse, "decode_full": _args_decode_full,
                "build_page_moments": _args_build_page_moments,
+               "append_page_moments": _args_append_page_moments,
                "gauss_select": _args_gauss_select}
 
     def __init__(self, name: str, *args, **kwargs):

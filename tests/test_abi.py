@@ -229,3 +229,23 @@ def test_gauss_select_validation(ek):
     odd = ctypes.c_void_p(256 + 8)
     assert f(ctypes.byref(s), odd, d, d, d, 1.5, 0.0, 64, d, None, d, big, None, None) == -1
     assert f(ctypes.byref(s), d, odd, d, d, 1.5, 0.0, 64, d, None, d, big, None, None) == -1
+
+
+def test_append_page_moments_validation(ek):
+    """The moments append entry point rejects null pointers, a non-positive
+    max_new_tokens, misaligned buffers and unsupported shapes before any HIP
+    call."""
+    s = shape(ek)
+    d = ctypes.c_void_p(256)
+    f = ek.lib.entmaxkv_append_page_moments
+    assert f(None, d, d, d, d, 1, d, None, None) == -1
+    for i in range(5):
+        args = [d, d, d, d, d]
+        args[i] = None
+        assert f(ctypes.byref(s), *args[:4], 1, args[4], None, None) == -1
+    for m in (0, -1):
+        assert f(ctypes.byref(s), d, d, d, d, m, d, None, None) == -1
+    odd = ctypes.c_void_p(256 + 8)
+    assert f(ctypes.byref(s), odd, d, d, d, 1, d, None, None) == -1
+    assert f(ctypes.byref(s), d, d, d, d, 1, odd, None, None) == -1
+    assert f(ctypes.byref(shape(ek, head_dim=96)), d, d, d, d, 1, d, None, None) == -2

@@ -1,11 +1,16 @@
-"""Page boxes kept current by appends: boxes built for shorter sequences and
-then updated with entmaxkv_append_page_meta equal the oracle's boxes of the
-longer sequences (value for value), for one-token decode steps and for
-multi-token appends that start pages, fill pages and cross page ends."""
+"""Page boxes and page key moments kept current by appends: boxes built for
+shorter sequences and then updated with entmaxkv_append_page_meta equal the
+oracle's boxes of the longer sequences (value for value), for one-token
+decode steps and for multi-token appends that start pages, fill pages and
+cross page ends; moments updated with entmaxkv_append_page_moments equal a
+full rebuild bit for bit and the oracle's moments within one unit in the
+last place."""
 import numpy as np
 import pytest
 import torch
 
+from oracle import entmax_oracle as O
+from oracle import gauss_oracle as GO
 from sparse_long_context_page_amd import synth
 from parity_util import Dev, announce, check_meta_sequence, meta_to_f64
 
@@ -67,3 +72,82 @@ def test_decode_loop_one_token_per_step():
     torch.cuda.synchronize()
     assert torch.equal(cur.cpu(), dev.lens.cpu())
     _check_all(inp, meta)
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu()
+
+
+def _check_moments(inp, mom):
+    """Every referenced page's moments against the oracle: within one unit
+    in the last place of the stored dtype (bf16: float32 spacing x 2^16)."""
+    w = inp["workload"]
+    mean, var = GO.page_moments(inp["k_pool"], inp["block_table"], inp["seq_lens"],
+                                w.page_size, w.kv_dtype)
+    got = meta_to_f64(mom, w.kv_dtype)
+    used = sorted({int(inp["block_table"][b, j]) for b in range(w.batch)
+                   for j in range(O.num_pages(int(inp["seq_lens"][b]), w.page_size))})
+    for side, ref in ((0, mean), (1, var)):
+        g, r = got[used, :, side], ref[used]
+        sp = np.spacing(np.maximum(np.abs(r), 1e-30).astype(np.float32)).astype(np.float64)
+        if w.kv_dtype == "bf16":
+            sp *= 65536.0
+        assert (np.abs(g - r) <= sp).all(), f"moments side {side}"
+
+
+@pytest.mark.parametrize("kv_dtype,D,ps,Hkv", [
+    ("bf16", 128, 32, 2), ("f32", 64, 16, 1), ("bf16", 64, 64, 4), ("f32", 128, 32, 2)])
+def test_append_moments_matches_rebuild(kv_dtype, D, ps, Hkv):
+    from sparse_long_context_page_amd import entmaxkv as E
+    new = (1, ps, ps + 1, 3 * ps - 1, 5 * ps + 7, 40, 2 * ps)
+    added = (1, 1, ps, 2, ps + 9, 40, 0)
+    inp = synth.generate(_workload(kv_dtype, D, ps, Hkv, new), 23)
+    dev = Dev(inp)
+    announce(f"append moments {kv_dtype} D{D} ps{ps} Hkv{Hkv}")
+    old = torch.from_numpy(np.maximum(np.asarray(new) - np.asarray(added), 0)
+                           .astype(np.int32)).cuda()
+    shape = (inp["num_phys_pages"], Hkv, 2, D)
+    mom = torch.full(shape, float("nan"), dtype=dev.kv_torch, device="cuda")
+    ref = torch.full(shape, float("nan"), dtype=dev.kv_torch, device="cuda")
+    E.entmaxkv_build_page_moments(dev.shape, dev.k, dev.bt, old, mom)
+    E.entmaxkv_append_page_moments(dev.shape, dev.k, dev.bt, old, dev.lens, max(added), mom)
+    E.entmaxkv_build_page_moments(dev.shape, dev.k, dev.bt, dev.lens, ref)
+    torch.cuda.synchronize()
+    # unreferenced pages stay NaN in both: the whole buffer agrees bit for bit
+    assert torch.equal(_bits(mom), _bits(ref))
+    _check_moments(inp, mom)
+
+
+def test_decode_loop_moments_then_gauss_select():
+    """A decode loop keeping boxes and moments current one token per step,
+    then the Gaussian selection on the maintained moments equals the one on
+    rebuilt moments."""
+    from sparse_long_context_page_amd import entmaxkv as E
+    ps = 16
+    final = (3 * ps + 5, 2 * ps, ps + 1, 9)
+    steps = ps + 6
+    inp = synth.generate(_workload("bf16", 128, ps, 2, final), 24)
+    dev = Dev(inp)
+    announce("append moments decode loop")
+    cur = torch.from_numpy(np.maximum(np.asarray(final) - steps, 0).astype(np.int32)).cuda()
+    shape = (inp["num_phys_pages"], 2, 2, 128)
+    mom = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    E.entmaxkv_build_page_moments(dev.shape, dev.k, dev.bt, cur, mom)
+    for _ in range(steps):
+        nxt = torch.minimum(cur + 1, dev.lens)
+        E.entmaxkv_append_page_moments(dev.shape, dev.k, dev.bt, cur, nxt, 1, mom)
+        cur = nxt
+    ref = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    E.entmaxkv_build_page_moments(dev.shape, dev.k, dev.bt, dev.lens, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(mom), _bits(ref))
+    _check_moments(inp, mom)
+    B, H = len(final), dev.w.num_q_heads
+    outs = []
+    for m in (mom, ref):
+        sel = torch.empty((B, H, 4), dtype=torch.int32, device="cuda")
+        tau_hat = torch.empty((B, H), device="cuda")
+        E.entmaxkv_gauss_select(dev.shape, dev.q, m, dev.bt, dev.lens, 1.5, 1.0, 4, sel, tau_hat)
+        outs.append((sel.cpu(), tau_hat.cpu()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
