@@ -108,7 +108,8 @@ def meta_to_f64(meta: torch.Tensor, kv_dtype: str) -> np.ndarray:
 
 
 def check_meta_sequence(inp, meta64: np.ndarray, b: int, g: int):
-    """GPU machines of every page of (b, g) equal the oracle's, value for value."""
+    """The page boxes the GPU built for every page of (b, g) equal the oracle's, value for
+    value."""
     w = inp["workload"]
     kmin, kmax = O.sequence_metadata(inp["k_pool"], inp["block_table"][b], inp["seq_lens"][b],
                                      w.page_size, g, w.kv_dtype)
