@@ -151,3 +151,36 @@ def test_decode_loop_moments_then_gauss_select():
         outs.append((sel.cpu(), tau_hat.cpu()))
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_append_without_growth_leaves_pages_alone(kv_dtype):
+    """Sequences whose new length is not above the old one (equal, or
+    shorter) are left as they are by both append entry points, bit for bit;
+    the one sequence that grows is updated."""
+    from sparse_long_context_page_amd import entmaxkv as E
+    ps, D, Hkv = 16, 64, 2
+    lens = (3 * ps + 5, 2 * ps, ps + 1, 9)
+    inp = synth.generate(_workload(kv_dtype, D, ps, Hkv, lens), 25)
+    dev = Dev(inp)
+    announce(f"append without growth {kv_dtype}")
+    shape = (inp["num_phys_pages"], Hkv, 2, D)
+    meta = torch.full(shape, float("nan"), dtype=dev.kv_torch, device="cuda")
+    mom = torch.full(shape, float("nan"), dtype=dev.kv_torch, device="cuda")
+    E.entmaxkv_build_page_meta(dev.shape, dev.k, dev.bt, dev.lens, meta)
+    E.entmaxkv_build_page_moments(dev.shape, dev.k, dev.bt, dev.lens, mom)
+    torch.cuda.synchronize()
+    meta0, mom0 = _bits(meta), _bits(mom)
+    old = dev.lens.clone()
+    new = torch.tensor([lens[0], lens[1] - 3, 0, lens[3] - 1], dtype=torch.int32, device="cuda")
+    E.entmaxkv_append_page_meta(dev.shape, dev.k, dev.bt, old, new, 4, meta)
+    E.entmaxkv_append_page_moments(dev.shape, dev.k, dev.bt, old, new, 4, mom)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(meta), meta0) and torch.equal(_bits(mom), mom0)
+    # growing back to the built lengths (3, 17 and 1 rows) recomputes the
+    # touched pages to the same bits
+    E.entmaxkv_append_page_moments(dev.shape, dev.k, dev.bt, new, dev.lens, lens[2], mom)
+    E.entmaxkv_append_page_meta(dev.shape, dev.k, dev.bt, new, dev.lens, lens[2], meta)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(mom), mom0)
+    _check_all(inp, meta)
