@@ -541,26 +541,38 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed pass: K steps; events only at call boundaries (start, after the
-    # sparse path, after the full path).
+    # Timed pass: K steps, an event before and after each step only (an event
+    # between the two paths holds the next launch back by a few us).
     K = args.steps
-    ev_step = E.HipEvents(3 * K)
+    ev_step = E.HipEvents(2 * K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         flush(i)
-        ev_step.record(3 * i, stream)
+        ev_step.record(2 * i, stream)
         call_sel()
         call_sp()
-        ev_step.record(3 * i + 1, stream)
         call_fu()
-        ev_step.record(3 * i + 2, stream)
+        ev_step.record(2 * i + 1, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = np.array([ev_step.elapsed_ms(3 * i, 3 * i + 2) for i in range(K)])
-    sparse_ms = np.array([ev_step.elapsed_ms(3 * i, 3 * i + 1) for i in range(K)])
-    full_ms = np.array([ev_step.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(K)])
+    step_ms = np.array([ev_step.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)])
     ms_per_step = float(step_ms.mean())
+
+    # Path pass: the same steps with an event between the sparse and the
+    # full path as well, for the per-path times.
+    ev_path = E.HipEvents(3 * K)
+    for i in range(K):
+        flush(i)
+        ev_path.record(3 * i, stream)
+        call_sel()
+        call_sp()
+        ev_path.record(3 * i + 1, stream)
+        call_fu()
+        ev_path.record(3 * i + 2, stream)
+    torch.cuda.synchronize()
+    sparse_ms = np.array([ev_path.elapsed_ms(3 * i, 3 * i + 1) for i in range(K)])
+    full_ms = np.array([ev_path.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(K)])
 
     # Kernel pass: the same steps with events around every kernel (the library
     # records them on the launch stream), for per-kernel durations.
