@@ -327,13 +327,19 @@ def gauss_report(args):
     ev = E.HipEvents(6)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
+    stream = torch.cuda.current_stream(dev)
+
     def timed(call, n=7):
+        # events at the call's ends only (events between its kernels hold
+        # each next launch back)
         ts = []
         for i in range(n):
             flush.fill_(i & 255)
-            call(list(ev))
+            ev.record(0, stream)
+            call()
+            ev.record(1, stream)
             torch.cuda.synchronize()
-            ts.append(ev.elapsed_ms(0, len(ev) - 1 if len(ev) > 2 else 1) * 1e3)
+            ts.append(ev.elapsed_ms(0, 1) * 1e3)
         return float(np.median(ts[2:]))
 
     mom_us = []
