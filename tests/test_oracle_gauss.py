@@ -100,12 +100,78 @@ def test_integer_m_rejects_other_alphas():
     assert [GO.integer_m(a) for a in ALPHAS] == [1, 2, 3, 4]
 
 
-def test_estimated_max_growth():
-    """sqrt(2 ln n) growth; a single token is its own maximum."""
-    est = GO.estimated_max([1.0, 1.0, 0.0], [0.5, 0.5, 2.0], [1, 64, 16])
-    assert est[0] == 1.0
-    assert est[1] == pytest.approx(1.0 + 0.5 * math.sqrt(2 * math.log(64)), rel=1e-15)
-    assert est[2] == pytest.approx(2.0 * math.sqrt(2 * math.log(16)), rel=1e-15)
+def test_estimated_max_single_token_and_monotone():
+    """A page of one token is its own maximum (no spread); the estimate grows
+    with the page's token count and is affine in (mu, s)."""
+    est = GO.estimated_max([1.0, -2.0], [0.5, 3.0], [1, 1])
+    assert est[0] == 1.0 and est[1] == -2.0
+    ns = np.array([1, 2, 4, 16, 64, 1024])
+    e = GO.estimated_max(np.zeros(len(ns)), np.ones(len(ns)), ns)
+    assert np.all(np.diff(e) > 0)
+    a = GO.estimated_max([0.3], [0.7], [64])[0]
+    b = GO.estimated_max([0.0], [1.0], [64])[0]
+    assert a == pytest.approx(0.3 + 0.7 * b, rel=1e-15)
+
+
+def _expected_max_std_normal(n):
+    """E[max of n iid N(0,1)] by quadrature of x n phi(x) Phi(x)^(n-1)."""
+    from scipy import stats
+    f = lambda x: x * n * stats.norm.pdf(x) * stats.norm.cdf(x) ** (n - 1)
+    val, _ = integrate.quad(f, -12.0, 12.0, limit=400, points=[0.0, 2.0, 4.0])
+    return val
+
+
+def test_expected_max_quadrature_textbook():
+    """The quadrature used below gives the textbook E[max of 2 N(0,1)] =
+    1/sqrt(pi)."""
+    assert _expected_max_std_normal(2) == pytest.approx(1.0 / math.sqrt(math.pi), rel=1e-9)
+
+
+@pytest.mark.parametrize("n", [16, 32, 64])
+def test_estimated_max_against_simulated_maximum(n):
+    """Reading G4 takes a page's estimated maximum as the usual growth of the
+    largest of n Gaussian draws. Checked against the maximum itself,
+    simulated (seeded Monte Carlo, 100000 pages of n draws from N(mu, s^2)):
+    the estimate lies above the simulated mean maximum (sqrt(2 ln n) bounds
+    E[max] of n standard normals), by less than s times the classical
+    second-order term (ln ln n + ln 4 pi) / (2 sqrt(2 ln n)) of the
+    maximum's growth, and the simulated mean agrees with the quadrature of
+    E[max]. A dropped factor, a wrong logarithm, s^2 for s or a sign error
+    in mu each breaks one of these."""
+    mu, s = 0.7, 0.3
+    rng = np.random.default_rng(100 + n)
+    N = 100_000
+    mx = rng.normal(mu, s, (N, n)).max(axis=1)
+    m_hat, se = float(mx.mean()), float(mx.std() / math.sqrt(N))
+    assert abs(m_hat - (mu + s * _expected_max_std_normal(n))) <= 5 * se
+    est = float(GO.estimated_max([mu], [s], [n])[0])
+    r = math.sqrt(2.0 * math.log(n))
+    second = (math.log(math.log(n)) + math.log(4.0 * math.pi)) / (2.0 * r)
+    assert est > m_hat + 5 * se
+    assert est - m_hat < s * second - 5 * se
+    # and it is a high quantile of the simulated maximum, not its median
+    frac_below = float((mx <= est).mean())
+    assert 0.80 < frac_below < 0.95
+
+
+def test_near_threshold_hand_cases():
+    """Hand-computed near-threshold sets (reading G5's excusal band)."""
+    # cut = tau_hat - delta = 1.5; band 1e-9 * max(1, |tau_hat|) = 2e-9
+    est = [1.0, 2.0, 1.5 + 5e-10, 1.5 - 5e-10, 1.5 + 1e-8, 3.0]
+    assert GO.gauss_near_threshold(est, 2.0, 0.5, 6) == {2, 3}
+    # cap 2 binds (pages 1..5 pass): float32 keys 3, 2, 1.5, 1.5, 1.5; the
+    # cap-th key is 2.0 and page 1 sits on it
+    assert GO.gauss_near_threshold(est, 2.0, 0.5, 2) == {1, 2, 3}
+    # cap boundary among float32 ties: 4 +- 1e-7 both round to 4.0
+    est2 = [5.0, 4.0, 4.0 + 1e-7, 4.0 - 1e-7, 1.0]
+    assert GO.gauss_near_threshold(est2, 0.0, 0.0, 2) == {1, 2, 3}
+    # nothing near when every estimate is far from the cut and the cap does
+    # not bind
+    assert GO.gauss_near_threshold([0.0, 1.0, 2.0], 0.5, 0.0, 3) == set()
+    # a wider band (relative to |tau_hat| = 10) takes in more pages
+    est3 = [10.0 + 5e-9, 10.0 + 5e-8, 9.0]
+    assert GO.gauss_near_threshold(est3, 10.0, 0.0, 3) == {0}
+    assert GO.gauss_near_threshold(est3, 10.0, 0.0, 3, rel=1e-8) == {0, 1}
 
 
 def test_selection_of_point_pages_is_the_support():
