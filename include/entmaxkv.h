@@ -216,10 +216,15 @@ int entmaxkv_gauss_select(const entmaxkv_shape* shape, const float* q, const voi
  * policy 1). For each (b, h) and logical page j < P_b = ceil(seq_lens[b] /
  * page_size):
  *     ub[j] = fp32( sum_d max(q_d * kmin_d, q_d * kmax_d) )   (then -0 -> +0)
- * the maximum of q.k over the page's box, summed in float64 from exact
- * products and rounded once to float32. Selects the budget_pages pages with
- * the largest ub, ties to the lower j, written ascending to sel[b, h, :]; if
- * P_b <= budget_pages every page is kept. Unused slots are -1.
+ * the maximum of q.k over the page's box. Every product is exact; the sum is
+ * taken in float64 and rounded once to float32 for F32 boxes, and
+ * accumulated in float32 on the matrix cores for BF16 boxes (q split exactly
+ * into three bf16 parts; the bound then differs from the exactly rounded
+ * sum by float32 accumulation error, about 1e-7 relative). A page whose
+ * block-table entry is outside [0, num_phys_pages) gets ub = -inf. Selects
+ * the budget_pages pages with the largest ub, ties to the lower j, written
+ * ascending to sel[b, h, :]; if P_b <= budget_pages every page is kept.
+ * Unused slots are -1.
  * sel_ub (nullable, float32 [batch, num_q_heads, budget_pages]) receives the
  * ub of each kept page (-inf in unused slots).
  * Workspace: entmaxkv_workspace_bytes(..., ENTMAXKV_WS_SELECT).

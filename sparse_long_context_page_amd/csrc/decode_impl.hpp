@@ -460,14 +460,15 @@ __device__ double solve_tau_ranked(double a, int n, int mcode, double amax) {
 }
 
 // One wave solves tau over a window list held K entries per lane in
-// registers (a_i = am1 * z_i), then compacts the support (V row, p) to the
-// front of the list in list order; returns the support size, the wave's
-// sum of p and tau (every lane). Lists of up to 64 entries at m = 1, 2 take
-// the rank-based closed form.
+// registers (a_i = am1 * z_i), then (when `compact`) compacts the support
+// (V row, p) to the front of the list in list order; returns the support
+// size, the wave's sum of p and tau (every lane). Lists of up to 64 entries
+// at m = 1, 2 take the rank-based closed form. Without `compact` li and sp
+// are left as they are: other waves may still be reading li.
 template <int K, bool GEN, typename ZT>
 __device__ __forceinline__ void wave_solve_list(const ZT* lz, int* li, float* sp, int n_list, double am1, double m,
-                                int mcode, double amax, int lane, uint64_t ltm, int& n_sup,
-                                double& psum, double& tau) {
+                                int mcode, double amax, int lane, uint64_t ltm, bool compact,
+                                int& n_sup, double& psum, double& tau) {
   double a[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -484,13 +485,15 @@ __device__ __forceinline__ void wave_solve_list(const ZT* lz, int* li, float* sp
     const int e = k * kWave + lane;
     const double d = a[k] - t;
     const bool f = e < n_list && d > 0.0;
-    const int ix = f ? li[e] : 0;
+    const int ix = (f && compact) ? li[e] : 0;
     const uint64_t bal = __ballot(f);
     if (f) {
       const double pv = d * pow_m1_t<GEN>(d, m, mcode);
       ps += pv;
-      li[o + __popcll(bal & ltm)] = ix;
-      sp[o + __popcll(bal & ltm)] = (float)pv;
+      if (compact) {
+        li[o + __popcll(bal & ltm)] = ix;
+        sp[o + __popcll(bal & ltm)] = (float)pv;
+      }
     }
     o += __popcll(bal);
   }
@@ -1496,8 +1499,11 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
     if (wave == 0) {
       int o;
       double t;
-      wave_solve_list<kRegList, true>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm, o, psum,
-                                      t);
+      // With the V rows requested up front the P.V step weights them from
+      // lz, and the other waves' reads of li may still be in flight, so the
+      // support is not compacted into li.
+      wave_solve_list<kRegList, true>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm, !vpre,
+                                      o, psum, t);
       if (lane == 0) {
         nb[1] = o;
         red[0] = psum;
@@ -1514,8 +1520,8 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
     if (wave == 0) {
       int o;
       double t;
-      wave_solve_list<kRegListLong, false>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm, o,
-                                           psum, t);
+      wave_solve_list<kRegListLong, false>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm,
+                                           true, o, psum, t);
       if (lane == 0) {
         nb[1] = o;
         red[0] = psum;

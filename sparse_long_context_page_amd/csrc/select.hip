@@ -125,7 +125,10 @@ bounds_kernel(const float* __restrict__ q, const KV* __restrict__ meta,
     }
     BF::reduce(acc, lane);
     const int jj = t * PPB + threadIdx.x / LP;
-    if (ok[t] && owner) ub[(size_t)(h0 + my_head) * ldu + j0 + jj] = (float)acc[0] + 0.0f;
+    // a page whose block-table entry is out of range gets -inf (never kept
+    // ahead of a valid page), so no bound of the row is left unwritten
+    if (jj < n && owner)
+      ub[(size_t)(h0 + my_head) * ldu + j0 + jj] = ok[t] ? (float)acc[0] + 0.0f : -__builtin_inff();
   }
 }
 

@@ -105,20 +105,51 @@ def make_shape(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_
 # marshalling helpers
 
 
-def _ptr(t, name, dtypes=None, nullable=False):
+def _ptr(t, name, dtypes=None, nullable=False, numel=None):
+    """Pointer of tensor `t` after host-side checks: its dtype, at least
+    `numel` elements (the count the shape implies: a shorter tensor would
+    make the kernels read or write past its end) and contiguity. Raises
+    TypeError / ValueError before any library call. That every tensor lives
+    on the GPU is checked afterwards, for all arguments at once
+    (_on_device)."""
     if t is None:
         if nullable:
             return None
         raise ValueError(f"{name} is required")
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtypes is not None and t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements; the shape needs {numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _on_device(**tensors):
+    """Every given tensor (None allowed) must be a device tensor."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
+class _Sizes:
+    """Element counts the shape implies for each array argument."""
+
+    def __init__(self, shape: Shape):
+        B, H, Hkv = shape.batch, shape.num_q_heads, shape.num_kv_heads
+        D, ps = shape.head_dim, shape.page_size
+        self.q = B * H * D
+        self.out = B * H * D
+        self.heads = B * H
+        self.pool = shape.num_phys_pages * Hkv * ps * D
+        self.meta = shape.num_phys_pages * Hkv * 2 * D
+        self.block_table = B * shape.max_pages_per_seq
+        self.batch = B
+
+    def sel(self, budget):
+        return self.heads * max(int(budget), 0)
 
 
 def _kv_dtypes(shape: Shape):
@@ -162,88 +193,132 @@ def workspace(shape: Shape, budget_pages: int, which: int, device) -> torch.Tens
 
 
 def _args_build_page_meta(shape: Shape, k_pool, block_table, seq_lens, meta, stream=None):
-    return lib.entmaxkv_build_page_meta, [
-        ctypes.byref(shape), _ptr(k_pool, "k_pool", _kv_dtypes(shape)),
-        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
-        _ptr(meta, "meta", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
+    n = _Sizes(shape)
+    ptrs = [_ptr(k_pool, "k_pool", _kv_dtypes(shape), numel=n.pool),
+            _ptr(block_table, "block_table", (torch.int32,), numel=n.block_table),
+            _ptr(seq_lens, "seq_lens", (torch.int32,), numel=n.batch),
+            _ptr(meta, "meta", _kv_dtypes(shape), numel=n.meta)]
+    _on_device(k_pool=k_pool, block_table=block_table, seq_lens=seq_lens, meta=meta)
+    return lib.entmaxkv_build_page_meta, [ctypes.byref(shape), *ptrs,
+                                          _stream(stream, k_pool.device), None]
+
+
+def _args_append(fn, what, shape: Shape, k_pool, block_table, old_lens, new_lens,
+                 max_new_tokens, meta, stream=None):
+    n = _Sizes(shape)
+    ptrs = [_ptr(k_pool, "k_pool", _kv_dtypes(shape), numel=n.pool),
+            _ptr(block_table, "block_table", (torch.int32,), numel=n.block_table),
+            _ptr(old_lens, "old_lens", (torch.int32,), numel=n.batch),
+            _ptr(new_lens, "new_lens", (torch.int32,), numel=n.batch)]
+    mp = _ptr(meta, what, _kv_dtypes(shape), numel=n.meta)
+    _on_device(k_pool=k_pool, block_table=block_table, old_lens=old_lens, new_lens=new_lens,
+               **{what: meta})
+    return fn, [ctypes.byref(shape), *ptrs, int(max_new_tokens), mp,
+                _stream(stream, k_pool.device), None]
 
 
 def _args_append_page_meta(shape: Shape, k_pool, block_table, old_lens, new_lens,
                            max_new_tokens, meta, stream=None):
-    return lib.entmaxkv_append_page_meta, [
-        ctypes.byref(shape), _ptr(k_pool, "k_pool", _kv_dtypes(shape)),
-        _ptr(block_table, "block_table", (torch.int32,)), _ptr(old_lens, "old_lens", (torch.int32,)),
-        _ptr(new_lens, "new_lens", (torch.int32,)), int(max_new_tokens),
-        _ptr(meta, "meta", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
+    return _args_append(lib.entmaxkv_append_page_meta, "meta", shape, k_pool, block_table,
+                        old_lens, new_lens, max_new_tokens, meta, stream)
 
 
 def _args_append_page_moments(shape: Shape, k_pool, block_table, old_lens, new_lens,
                               max_new_tokens, moments, stream=None):
-    return lib.entmaxkv_append_page_moments, [
-        ctypes.byref(shape), _ptr(k_pool, "k_pool", _kv_dtypes(shape)),
-        _ptr(block_table, "block_table", (torch.int32,)), _ptr(old_lens, "old_lens", (torch.int32,)),
-        _ptr(new_lens, "new_lens", (torch.int32,)), int(max_new_tokens),
-        _ptr(moments, "moments", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
+    return _args_append(lib.entmaxkv_append_page_moments, "moments", shape, k_pool,
+                        block_table, old_lens, new_lens, max_new_tokens, moments, stream)
 
 
 def _args_build_page_moments(shape: Shape, k_pool, block_table, seq_lens, moments, stream=None):
-    return lib.entmaxkv_build_page_moments, [
-        ctypes.byref(shape), _ptr(k_pool, "k_pool", _kv_dtypes(shape)),
-        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
-        _ptr(moments, "moments", _kv_dtypes(shape)), _stream(stream, k_pool.device), None]
+    n = _Sizes(shape)
+    ptrs = [_ptr(k_pool, "k_pool", _kv_dtypes(shape), numel=n.pool),
+            _ptr(block_table, "block_table", (torch.int32,), numel=n.block_table),
+            _ptr(seq_lens, "seq_lens", (torch.int32,), numel=n.batch),
+            _ptr(moments, "moments", _kv_dtypes(shape), numel=n.meta)]
+    _on_device(k_pool=k_pool, block_table=block_table, seq_lens=seq_lens, moments=moments)
+    return lib.entmaxkv_build_page_moments, [ctypes.byref(shape), *ptrs,
+                                             _stream(stream, k_pool.device), None]
+
+
+def _ws_args(ws, shape, budget, which, device):
+    """(pointer, bytes, tensor) of the workspace, allocated when not given."""
+    if ws is None:
+        ws = workspace(shape, budget, which, device)
+    else:
+        _ptr(ws, "ws")
+        _on_device(ws=ws)
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), ws
 
 
 def _args_gauss_select(shape: Shape, q, moments, block_table, seq_lens, alpha, delta, cap_pages,
                        sel, tau_hat=None, ws=None, stream=None):
-    if ws is None:
-        ws = workspace(shape, cap_pages, ENTMAXKV_WS_GAUSS, q.device)
+    n = _Sizes(shape)
+    pq = _ptr(q, "q", (torch.float32,), numel=n.q)
+    pm = _ptr(moments, "moments", _kv_dtypes(shape), numel=n.meta)
+    pbt = _ptr(block_table, "block_table", (torch.int32,), numel=n.block_table)
+    pl = _ptr(seq_lens, "seq_lens", (torch.int32,), numel=n.batch)
+    ps_ = _ptr(sel, "sel", (torch.int32,), numel=n.sel(cap_pages))
+    pt = _ptr(tau_hat, "tau_hat", (torch.float32,), nullable=True, numel=n.heads)
+    _on_device(q=q, moments=moments, block_table=block_table, seq_lens=seq_lens, sel=sel,
+               tau_hat=tau_hat)
+    pw, nw, ws = _ws_args(ws, shape, cap_pages, ENTMAXKV_WS_GAUSS, q.device)
     return lib.entmaxkv_gauss_select, [
-        ctypes.byref(shape), _ptr(q, "q", (torch.float32,)),
-        _ptr(moments, "moments", _kv_dtypes(shape)),
-        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
-        float(alpha), float(delta), int(cap_pages), _ptr(sel, "sel", (torch.int32,)),
-        _ptr(tau_hat, "tau_hat", (torch.float32,), nullable=True), _ptr(ws, "ws"),
-        ws.numel() * ws.element_size(), _stream(stream, q.device), None], ws
+        ctypes.byref(shape), pq, pm, pbt, pl, float(alpha), float(delta), int(cap_pages), ps_,
+        pt, pw, nw, _stream(stream, q.device), None], ws
 
 
 def _args_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_pages, sel,
                        sel_ub=None, ws=None, stream=None):
-    if ws is None:
-        ws = workspace(shape, budget_pages, ENTMAXKV_WS_SELECT, q.device)
+    n = _Sizes(shape)
+    pq = _ptr(q, "q", (torch.float32,), numel=n.q)
+    pm = _ptr(meta, "meta", _kv_dtypes(shape), numel=n.meta)
+    pbt = _ptr(block_table, "block_table", (torch.int32,), numel=n.block_table)
+    pl = _ptr(seq_lens, "seq_lens", (torch.int32,), numel=n.batch)
+    ps_ = _ptr(sel, "sel", (torch.int32,), numel=n.sel(budget_pages))
+    pu = _ptr(sel_ub, "sel_ub", (torch.float32,), nullable=True, numel=n.sel(budget_pages))
+    _on_device(q=q, meta=meta, block_table=block_table, seq_lens=seq_lens, sel=sel,
+               sel_ub=sel_ub)
+    pw, nw, ws = _ws_args(ws, shape, budget_pages, ENTMAXKV_WS_SELECT, q.device)
     return lib.entmaxkv_score_select, [
-        ctypes.byref(shape), _ptr(q, "q", (torch.float32,)), _ptr(meta, "meta", _kv_dtypes(shape)),
-        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
-        int(budget_pages), _ptr(sel, "sel", (torch.int32,)),
-        _ptr(sel_ub, "sel_ub", (torch.float32,), nullable=True), _ptr(ws, "ws"),
-        ws.numel() * ws.element_size(), _stream(stream, q.device), None], ws
+        ctypes.byref(shape), pq, pm, pbt, pl, int(budget_pages), ps_, pu, pw, nw,
+        _stream(stream, q.device), None], ws
+
+
+def _decode_ptrs(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, out, tau, support):
+    n = _Sizes(shape)
+    return (_ptr(q, "q", (torch.float32,), numel=n.q),
+            _ptr(k_pool, "k_pool", _kv_dtypes(shape), numel=n.pool),
+            _ptr(v_pool, "v_pool", _kv_dtypes(shape), numel=n.pool),
+            _ptr(block_table, "block_table", (torch.int32,), numel=n.block_table),
+            _ptr(seq_lens, "seq_lens", (torch.int32,), numel=n.batch),
+            _ptr(out, "out", (torch.float32,), numel=n.out),
+            _ptr(tau, "tau", (torch.float32,), nullable=True, numel=n.heads),
+            _ptr(support, "support", (torch.int32,), nullable=True, numel=n.heads))
 
 
 def _args_decode_sparse(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, sel,
                         budget_pages, alpha, out, tau=None, support=None, ws=None, stream=None):
-    if ws is None:
-        ws = workspace(shape, budget_pages, ENTMAXKV_WS_SPARSE, q.device)
+    pq, pk, pv, pbt, pl, po, pt, psu = _decode_ptrs(shape, q, k_pool, v_pool, block_table,
+                                                     seq_lens, out, tau, support)
+    ps_ = _ptr(sel, "sel", (torch.int32,), numel=_Sizes(shape).sel(budget_pages))
+    _on_device(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table, seq_lens=seq_lens,
+               sel=sel, out=out, tau=tau, support=support)
+    pw, nw, ws = _ws_args(ws, shape, budget_pages, ENTMAXKV_WS_SPARSE, q.device)
     return lib.entmaxkv_decode_sparse, [
-        ctypes.byref(shape), _ptr(q, "q", (torch.float32,)),
-        _ptr(k_pool, "k_pool", _kv_dtypes(shape)), _ptr(v_pool, "v_pool", _kv_dtypes(shape)),
-        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
-        _ptr(sel, "sel", (torch.int32,)), int(budget_pages), float(alpha),
-        _ptr(out, "out", (torch.float32,)), _ptr(tau, "tau", (torch.float32,), nullable=True),
-        _ptr(support, "support", (torch.int32,), nullable=True), _ptr(ws, "ws"),
-        ws.numel() * ws.element_size(), _stream(stream, q.device), None], ws
+        ctypes.byref(shape), pq, pk, pv, pbt, pl, ps_, int(budget_pages), float(alpha), po, pt,
+        psu, pw, nw, _stream(stream, q.device), None], ws
 
 
 def _args_decode_full(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, alpha, out,
                       tau=None, support=None, ws=None, stream=None):
-    if ws is None:
-        ws = workspace(shape, 0, ENTMAXKV_WS_FULL, q.device)
+    pq, pk, pv, pbt, pl, po, pt, psu = _decode_ptrs(shape, q, k_pool, v_pool, block_table,
+                                                     seq_lens, out, tau, support)
+    _on_device(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table, seq_lens=seq_lens,
+               out=out, tau=tau, support=support)
+    pw, nw, ws = _ws_args(ws, shape, 0, ENTMAXKV_WS_FULL, q.device)
     return lib.entmaxkv_decode_full, [
-        ctypes.byref(shape), _ptr(q, "q", (torch.float32,)),
-        _ptr(k_pool, "k_pool", _kv_dtypes(shape)), _ptr(v_pool, "v_pool", _kv_dtypes(shape)),
-        _ptr(block_table, "block_table", (torch.int32,)), _ptr(seq_lens, "seq_lens", (torch.int32,)),
-        float(alpha), _ptr(out, "out", (torch.float32,)),
-        _ptr(tau, "tau", (torch.float32,), nullable=True),
-        _ptr(support, "support", (torch.int32,), nullable=True), _ptr(ws, "ws"),
-        ws.numel() * ws.element_size(), _stream(stream, q.device), None], ws
+        ctypes.byref(shape), pq, pk, pv, pbt, pl, float(alpha), po, pt, psu, pw, nw,
+        _stream(stream, q.device), None], ws
 
 
 def _run(name, fn, args, events):

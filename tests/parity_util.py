@@ -119,9 +119,19 @@ def check_meta_sequence(inp, meta64: np.ndarray, b: int, g: int):
     return kmin, kmax
 
 
+# Near ties of the top-k selection over the test session: per checked head,
+# the pages other than the budget-th whose key lies within NEAR_TIE_REL of
+# the budget-th key, and the pages on which the GPU selection and the
+# oracle's differ (allowed only among those). Printed at the end of the run.
+TALLY = {"heads": 0, "near_tie_pages": 0, "heads_with_near_ties": 0, "differing_pages": 0,
+         "heads_differing": 0}
+
+
 def check_selection(inp, b, h, budget, sel_row, ub_row, seq_meta=None):
-    """GPU selection of one head vs the oracle's. Returns the number of
-    near-tie pages on which they differ (0 when identical)."""
+    """GPU selection of one head vs the oracle's. Returns (near-tie pages
+    other than the budget-th, pages on which the two selections differ);
+    the second is 0 when they are identical, and every differing page must
+    be a near tie."""
     ub, key, ref = O.select_for_head(inp, b, h, budget, seq_meta=seq_meta)
     gpu = [int(x) for x in sel_row]
     P = len(key)
@@ -130,8 +140,14 @@ def check_selection(inp, b, h, budget, sel_row, ub_row, seq_meta=None):
     kept = gpu[:n_keep]
     assert kept == sorted(kept) and len(set(kept)) == n_keep and all(0 <= j < P for j in kept)
     diff = set(kept) ^ set(j for j in ref if j >= 0)
+    nt = O.near_tie_pages(key, budget, NEAR_TIE_REL)
+    n_near = max(0, len(nt) - 1)  # the budget-th page itself is always in the band
+    TALLY["heads"] += 1
+    TALLY["near_tie_pages"] += n_near
+    TALLY["heads_with_near_ties"] += int(n_near > 0)
+    TALLY["differing_pages"] += len(diff)
+    TALLY["heads_differing"] += int(bool(diff))
     if diff:
-        nt = O.near_tie_pages(key, budget)
         assert diff <= nt, f"selection differs outside near ties: {sorted(diff)[:10]}"
     # bounds the GPU reports for the kept pages vs the float32 key of the exact bound
     gk = np.asarray(ub_row[:n_keep], dtype=np.float32)
@@ -149,7 +165,7 @@ def check_selection(inp, b, h, budget, sel_row, ub_row, seq_meta=None):
         err = np.abs(gk.astype(np.float64) - rk.astype(np.float64))
         assert (err <= NEAR_TIE_REL * np.abs(rk.astype(np.float64)) + 1e-30).all(), \
             f"sel_ub off by {err.max():.3e}"
-    return len(diff)
+    return n_near, len(diff)
 
 
 def marginal_tokens(res: O.DecodeResult, alpha: float, eps: float) -> int:

@@ -249,3 +249,45 @@ def test_append_page_moments_validation(ek):
     assert f(ctypes.byref(s), odd, d, d, d, 1, d, None, None) == -1
     assert f(ctypes.byref(s), d, d, d, d, 1, odd, None, None) == -1
     assert f(ctypes.byref(shape(ek, head_dim=96)), d, d, d, d, 1, d, None, None) == -2
+
+
+def test_binding_rejects_short_tensors(ek):
+    """Every array argument shorter than the shape implies is rejected on the
+    host (ValueError naming it) before the library is called; at the right
+    size the same host tensors fail only for not being on the GPU."""
+    import torch
+    B, H, Hkv, D, ps, mp, nphys, budget = 2, 4, 2, 64, 16, 8, 16, 3
+    s = shape(ek, batch=B, num_q_heads=H, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+              max_pages_per_seq=mp, num_phys_pages=nphys)
+    bf = torch.bfloat16
+    full = dict(q=torch.zeros(B, H, D), k=torch.zeros(nphys, Hkv, ps, D, dtype=bf),
+                v=torch.zeros(nphys, Hkv, ps, D, dtype=bf),
+                bt=torch.zeros(B, mp, dtype=torch.int32), lens=torch.zeros(B, dtype=torch.int32),
+                meta=torch.zeros(nphys, Hkv, 2, D, dtype=bf),
+                sel=torch.zeros(B, H, budget, dtype=torch.int32), out=torch.zeros(B, H, D),
+                tau=torch.zeros(B, H), sup=torch.zeros(B, H, dtype=torch.int32))
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    calls = {
+        "build_page_meta": lambda a: ek.entmaxkv_build_page_meta(
+            s, a["k"], a["bt"], a["lens"], a["meta"], stream=0),
+        "score_select": lambda a: ek.entmaxkv_score_select(
+            s, a["q"], a["meta"], a["bt"], a["lens"], budget, a["sel"], ws=ws, stream=0),
+        "decode_sparse": lambda a: ek.entmaxkv_decode_sparse(
+            s, a["q"], a["k"], a["v"], a["bt"], a["lens"], a["sel"], budget, 1.5, a["out"],
+            a["tau"], a["sup"], ws=ws, stream=0),
+        "decode_full": lambda a: ek.entmaxkv_decode_full(
+            s, a["q"], a["k"], a["v"], a["bt"], a["lens"], 1.5, a["out"], a["tau"], a["sup"],
+            ws=ws, stream=0),
+    }
+    uses = {"build_page_meta": ("k", "bt", "lens", "meta"),
+            "score_select": ("q", "meta", "bt", "lens", "sel"),
+            "decode_sparse": ("q", "k", "v", "bt", "lens", "sel", "out", "tau", "sup"),
+            "decode_full": ("q", "k", "v", "bt", "lens", "out", "tau", "sup")}
+    for name, call in calls.items():
+        with pytest.raises(ValueError, match="device tensor"):
+            call(full)
+        for arg in uses[name]:
+            short = dict(full)
+            short[arg] = full[arg].reshape(-1)[:-1]
+            with pytest.raises(ValueError, match="elements"):
+                call(short)

@@ -59,13 +59,18 @@ def test_full_size_workload(name):
     so, st, ss = (x.cpu().numpy() for x in sp)
     fo, ft, fs = (x.cpu().numpy() for x in fu)
     G = w.num_q_heads // w.num_kv_heads
+    near = differing = 0
     for b, h in sample_heads(w, N_SAMPLES, 7):
         seq_meta = check_meta_sequence(inp, meta64, b, h // G)
-        check_selection(inp, b, h, budget, sel_np[b, h], ub_np[b, h], seq_meta)
+        n_near, n_diff = check_selection(inp, b, h, budget, sel_np[b, h], ub_np[b, h], seq_meta)
+        near += n_near
+        differing += n_diff
         check_decode(O.decode_sparse(inp, b, h, alpha, sel_np[b, h]), so[b, h], st[b, h],
                      ss[b, h], w.kv_dtype, alpha, f"{name} sparse b{b} h{h}")
         check_decode(O.decode_full(inp, b, h, alpha), fo[b, h], ft[b, h], fs[b, h],
                      w.kv_dtype, alpha, f"{name} full b{b} h{h}")
+    announce(f"full size {name}: near-tie pages {near}, pages where the selections "
+             f"differ {differing}")
 
 
 def test_full_size_alpha_sweep():
@@ -91,7 +96,10 @@ def test_full_size_alpha_sweep():
         for b, h in heads:
             if (b, h // G) not in seq_meta:
                 seq_meta[(b, h // G)] = check_meta_sequence(inp, meta64, b, h // G)
-            check_selection(inp, b, h, budget, sel_np[b, h], ub_np[b, h], seq_meta[(b, h // G)])
+            n_near, n_diff = check_selection(inp, b, h, budget, sel_np[b, h], ub_np[b, h],
+                                             seq_meta[(b, h // G)])
+            announce(f"full size {name}: budget {budget} b{b} h{h}: near-tie pages {n_near}, "
+                     f"differing {n_diff}")
         for alpha in w.alphas:
             announce(f"full size {name}: decode budget={budget} alpha={alpha}")
             sp = dev.sparse(sel, budget, alpha)

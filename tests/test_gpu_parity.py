@@ -32,17 +32,22 @@ def full_compare(inp, budget, alpha, heads=None, check_full=True):
     G = w.num_q_heads // w.num_kv_heads
     heads = heads or [(b, h) for b in range(w.batch) for h in range(w.num_q_heads)]
     seq_meta = {}
-    near = 0
+    near = differing = 0
     for b, h in heads:
         g = h // G
         if (b, g) not in seq_meta:
             seq_meta[(b, g)] = check_meta_sequence(inp, meta64, b, g)
-        near += check_selection(inp, b, h, budget, sel_np[b, h], ub_np[b, h], seq_meta[(b, g)])
+        n_near, n_diff = check_selection(inp, b, h, budget, sel_np[b, h], ub_np[b, h],
+                                         seq_meta[(b, g)])
+        near += n_near
+        differing += n_diff
         ref = O.decode_sparse(inp, b, h, alpha, sel_np[b, h])
         check_decode(ref, o_s[b, h], t_s[b, h], s_s[b, h], w.kv_dtype, alpha, f"sparse b{b} h{h}")
         if check_full:
             ref = O.decode_full(inp, b, h, alpha)
             check_decode(ref, o_f[b, h], t_f[b, h], s_f[b, h], w.kv_dtype, alpha, f"full b{b} h{h}")
+    announce(f"{w.name}: {len(heads)} heads, near-tie pages {near}, pages where the "
+             f"selections differ {differing}")
     return dev, near
 
 

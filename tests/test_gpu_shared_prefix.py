@@ -48,6 +48,11 @@ def test_shared_prefix_pages(kv_dtype):
     meta64 = meta_to_f64(meta, kv_dtype)
     moments = GO.page_moments(inp["k_pool"], bt, inp["seq_lens"], ps, kv_dtype)
     mom64 = meta_to_f64(mom, kv_dtype)
+    # the Gaussian selection is compared with the oracle run on the GPU's
+    # moments (themselves checked against the oracle's within one unit in
+    # the last place below): a one-ulp moment difference would otherwise
+    # move tau_hat by far more than the float64 summation-order band
+    gpu_moments = (mom64[:, :, 0], mom64[:, :, 1])
     sel_np, ub_np = sel.cpu().numpy(), sel_ub.cpu().numpy()
     so, st, ss = (x.cpu().numpy() for x in sp)
     fo, ft, fs = (x.cpu().numpy() for x in fu)
@@ -70,10 +75,10 @@ def test_shared_prefix_pages(kv_dtype):
                 check_decode(O.decode_full(inp, b, h, alpha), fo[b, h], ft[b, h], fs[b, h],
                              kv_dtype, alpha, "full " + what)
                 tau_ref, est, ref = GO.gauss_select_for_head(inp, b, h, alpha, delta, P0,
-                                                             moments=moments)
+                                                             moments=gpu_moments)
                 assert abs(float(gtau_np[b, h]) - tau_ref) <= 1e-6 * max(1.0, abs(tau_ref))
                 got_sel = {int(j) for j in gsel_np[b, h] if j >= 0}
                 diff = got_sel ^ {j for j in ref if j >= 0}
                 if diff:
-                    near = GO.gauss_near_threshold(est, tau_ref, delta, P0, rel=1e-6)
+                    near = GO.gauss_near_threshold(est, tau_ref, delta, P0)
                     assert diff <= near, f"gauss {what}: {sorted(diff)}"
