@@ -236,6 +236,25 @@ int entmaxkv_score_select(const entmaxkv_shape* shape, const float* q, const voi
                           size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
 
 /*
+ * entmaxkv_score_select without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Same kernels, arguments and
+ * results as entmaxkv_score_select (bit for bit); the per-head bounds go to
+ * a file-scope device array of 16 MiB that the library holds on every GPU
+ * it runs on until the process ends. The call allocates and frees nothing.
+ * Limit: batch * num_q_heads * (max_pages_per_seq rounded up to a multiple
+ * of 4) * 4 bytes <= 16 MiB (e.g. 128 heads x 32768 pages); beyond it the
+ * call returns ENTMAXKV_ERR_WORKSPACE before any HIP call. All calls on one
+ * GPU share that array: calls that overlap in time on one GPU (several
+ * streams or host threads) race and must be serialized by the caller.
+ * Kernels launched: 2 (bounds, select).
+ */
+int entmaxkv_score_select_noalloc(const entmaxkv_shape* shape, const float* q, const void* meta,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  int32_t budget_pages, int32_t* sel, float* sel_ub,
+                                  hipStream_t stream, hipEvent_t* events);
+
+/*
  * Sparse alpha-entmax decode ([EntmaxKV page] section 2.C). For each (b, h),
  * gathers the valid tokens of the pages listed in sel[b, h, :] (entries < 0
  * or >= P_b are ignored), computes z = q . k in float32 (float64 for F32

@@ -3,12 +3,41 @@
 // HIP call, so a rejected call enqueues nothing.
 #include <math.h>
 
+#include <mutex>
+
 #include "entmaxkv.h"
 #include "launch.hpp"
 
 using namespace ekv;
 
 namespace {
+
+// Scratch memory of entmaxkv_score_select_noalloc: the per-head page bounds
+// that entmaxkv_score_select keeps in the caller's workspace. A file-scope
+// device array, so the call allocates nothing; every GPU the library runs on
+// holds its own copy until the process ends. Host code uses the address
+// hipGetSymbolAddress reports for the current device, never the array's
+// name (a host-side stand-in).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ENTMAXKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return ENTMAXKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ENTMAXKV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ENTMAXKV_OK;
+}
 
 constexpr int kMaxPagesPerSeq = 262144;
 constexpr size_t kMaxScoreLds = kMaxScoreLdsBytes;
@@ -396,6 +425,33 @@ int entmaxkv_score_select(const entmaxkv_shape* shape, const float* q, const voi
   if (!aligned(q, 16) || !aligned(meta, 16)) return ENTMAXKV_ERR_INVALID;
   if (!ws || ws_bytes < select_ws_bytes(s)) return ENTMAXKV_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return ENTMAXKV_ERR_INVALID;
+  float* ub = static_cast<float*>(ws);
+  const Events ev{events, stream};
+  if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
+  if (launch_bounds(s, q, meta, block_table, seq_lens, ub, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
+  if (launch_select(s, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
+  return ENTMAXKV_OK;
+}
+
+int entmaxkv_score_select_noalloc(const entmaxkv_shape* shape, const float* q, const void* meta,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  int32_t budget_pages, int32_t* sel, float* sel_ub,
+                                  hipStream_t stream, hipEvent_t* events) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  if ((rc = check_budget(budget_pages))) return rc;
+  if (!q || !meta || !block_table || !seq_lens || !sel) return ENTMAXKV_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(meta, 16)) return ENTMAXKV_ERR_INVALID;
+  if (select_ws_bytes(s) > kNoAllocScratchBytes) return ENTMAXKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  // the same kernels as entmaxkv_score_select, with the bounds in `scratch`
+  // (every bound the select reads is written first: nothing to clear)
   float* ub = static_cast<float*>(ws);
   const Events ev{events, stream};
   if (!ev.before(0)) return ENTMAXKV_ERR_HIP;

@@ -7,7 +7,7 @@ built (there is no fallback path).
 
 The function names match the C ABI:
     entmaxkv_build_page_meta, entmaxkv_append_page_meta, entmaxkv_score_select,
-    entmaxkv_decode_sparse, entmaxkv_decode_full, entmaxkv_build_page_moments,
+    entmaxkv_score_select_noalloc, entmaxkv_decode_sparse, entmaxkv_decode_full, entmaxkv_build_page_moments,
     entmaxkv_append_page_moments, entmaxkv_gauss_select, entmaxkv_workspace_bytes,
     entmaxkv_strerror
 """
@@ -35,7 +35,8 @@ ENTMAXKV_WS_FULL = 2
 ENTMAXKV_WS_GAUSS = 3
 
 # kernels each entry point launches (for per-kernel event timing)
-KERNELS = {"build_page_meta": 1, "append_page_meta": 1, "score_select": 2, "decode_sparse": 2,
+KERNELS = {"build_page_meta": 1, "append_page_meta": 1, "score_select": 2,
+           "score_select_noalloc": 2, "decode_sparse": 2,
            "decode_full": 2, "build_page_moments": 1, "append_page_moments": 1,
            "gauss_select": 3}
 
@@ -69,6 +70,7 @@ def _load() -> ctypes.CDLL:
     lib.entmaxkv_build_page_meta.argtypes = [SP, P, P, P, P, P, P]
     lib.entmaxkv_append_page_meta.argtypes = [SP, P, P, P, P, I32, P, P, P]
     lib.entmaxkv_score_select.argtypes = [SP, P, P, P, P, I32, P, P, P, SZ, P, P]
+    lib.entmaxkv_score_select_noalloc.argtypes = [SP, P, P, P, P, I32, P, P, P, P]
     lib.entmaxkv_decode_sparse.argtypes = [SP, P, P, P, P, P, P, I32, F32, P, P, P, P, SZ, P, P]
     lib.entmaxkv_decode_full.argtypes = [SP, P, P, P, P, P, F32, P, P, P, P, SZ, P, P]
     lib.entmaxkv_build_page_moments.argtypes = [SP, P, P, P, P, P, P]
@@ -79,7 +81,8 @@ def _load() -> ctypes.CDLL:
     lib.entmaxkv_strerror.restype = ctypes.c_char_p
     lib.entmaxkv_version.argtypes = []
     for name in ("entmaxkv_build_page_meta", "entmaxkv_append_page_meta",
-                 "entmaxkv_score_select", "entmaxkv_decode_sparse", "entmaxkv_decode_full",
+                 "entmaxkv_score_select", "entmaxkv_score_select_noalloc",
+                 "entmaxkv_decode_sparse", "entmaxkv_decode_full",
                  "entmaxkv_build_page_moments", "entmaxkv_append_page_moments",
                  "entmaxkv_gauss_select", "entmaxkv_workspace_bytes", "entmaxkv_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -284,6 +287,22 @@ def _args_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_page
         _stream(stream, q.device), None], ws
 
 
+def _args_score_select_noalloc(shape: Shape, q, meta, block_table, seq_lens, budget_pages, sel,
+                               sel_ub=None, stream=None):
+    n = _Sizes(shape)
+    pq = _ptr(q, "q", (torch.float32,), numel=n.q)
+    pm = _ptr(meta, "meta", _kv_dtypes(shape), numel=n.meta)
+    pbt = _ptr(block_table, "block_table", (torch.int32,), numel=n.block_table)
+    pl = _ptr(seq_lens, "seq_lens", (torch.int32,), numel=n.batch)
+    ps_ = _ptr(sel, "sel", (torch.int32,), numel=n.sel(budget_pages))
+    pu = _ptr(sel_ub, "sel_ub", (torch.float32,), nullable=True, numel=n.sel(budget_pages))
+    _on_device(q=q, meta=meta, block_table=block_table, seq_lens=seq_lens, sel=sel,
+               sel_ub=sel_ub)
+    return lib.entmaxkv_score_select_noalloc, [
+        ctypes.byref(shape), pq, pm, pbt, pl, int(budget_pages), ps_, pu,
+        _stream(stream, q.device), None]
+
+
 def _decode_ptrs(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, out, tau, support):
     n = _Sizes(shape)
     return (_ptr(q, "q", (torch.float32,), numel=n.q),
@@ -367,6 +386,15 @@ def entmaxkv_score_select(shape: Shape, q, meta, block_table, seq_lens, budget_p
     fn, args, _ = _args_score_select(shape, q, meta, block_table, seq_lens, budget_pages, sel,
                                      sel_ub, ws, stream)
     _run("entmaxkv_score_select", fn, args, events)
+
+
+def entmaxkv_score_select_noalloc(shape: Shape, q, meta, block_table, seq_lens, budget_pages,
+                                  sel, sel_ub=None, stream=None, events=None):
+    """entmaxkv_score_select with the library's static scratch in place of a
+    workspace (allocates nothing; calls overlapping on one GPU race)."""
+    fn, args = _args_score_select_noalloc(shape, q, meta, block_table, seq_lens, budget_pages,
+                                          sel, sel_ub, stream)
+    _run("entmaxkv_score_select_noalloc", fn, args, events)
 
 
 def entmaxkv_decode_sparse(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, sel,

@@ -291,3 +291,21 @@ def test_binding_rejects_short_tensors(ek):
             short[arg] = full[arg].reshape(-1)[:-1]
             with pytest.raises(ValueError, match="elements"):
                 call(short)
+
+
+def test_noalloc_select_rejects_oversize_before_any_hip_call(ek):
+    """The no-allocation select holds its bounds in a 16 MiB static array:
+    a shape needing more is rejected with ENTMAXKV_ERR_WORKSPACE (before any
+    HIP call, so no GPU is needed), as are the usual bad arguments."""
+    d = ctypes.c_void_p(256)
+    f = ek.lib.entmaxkv_score_select_noalloc
+    # 32 heads x 4 sequences x 32768 pages x 4 bytes = 16 MiB: the limit itself
+    # is accepted by validation (not called here); one more page row is not
+    big = shape(ek, batch=4, max_pages_per_seq=32772, num_phys_pages=1 << 20, page_size=16)
+    assert f(ctypes.byref(big), d, d, d, d, 82, d, None, None, None) == -3
+    s = shape(ek)
+    assert f(ctypes.byref(s), d, d, d, d, 0, d, None, None, None) == -1
+    assert f(ctypes.byref(s), None, d, d, d, 82, d, None, None, None) == -1
+    assert f(ctypes.byref(s), d, d, d, d, 82, None, None, None, None) == -1
+    assert f(ctypes.byref(s), ctypes.c_void_p(256 + 8), d, d, d, 82, d, None, None, None) == -1
+    assert f(ctypes.byref(shape(ek, head_dim=96)), d, d, d, d, 82, d, None, None, None) == -2
