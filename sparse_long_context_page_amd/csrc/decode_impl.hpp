@@ -79,44 +79,6 @@ struct alignas(2 * sizeof(ZT)) Cand {
   int idx;
 };
 
-// Stores and loads of data that one workgroup hands to another within a
-// launch (selections, candidate regions, their counts and maxima): made at
-// device scope, so they bypass this XCD's L2 for the memory side that the
-// other XCDs see, and no cache-wide write-back or invalidate is needed. A
-// writer waits for its stores to complete before it announces them.
-template <typename T>
-__device__ __forceinline__ void st_dev(T* p, T v) {
-  if constexpr (sizeof(T) == 4) {
-    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    static_assert(sizeof(T) == 8, "4- or 8-byte values");
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-template <typename T>
-__device__ __forceinline__ T ld_dev(const T* p) {
-  if constexpr (sizeof(T) == 4) {
-    return __builtin_bit_cast(T, __hip_atomic_load(reinterpret_cast<const uint32_t*>(p),
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  } else {
-    static_assert(sizeof(T) == 8, "4- or 8-byte values");
-    return __builtin_bit_cast(T, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p),
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  }
-}
-template <typename ZT>
-__device__ __forceinline__ void st_dev_cand(Cand<ZT>* p, ZT z, int idx) {
-  if constexpr (sizeof(ZT) == 4) {
-    st_dev(reinterpret_cast<uint64_t*>(p),
-           (uint64_t)__builtin_bit_cast(uint32_t, z) | ((uint64_t)(uint32_t)idx << 32));
-  } else {
-    st_dev(&p->z, z);
-    st_dev(&p->idx, idx);
-  }
-}
-
 // A candidate read through a pointer into global memory, addressed as such
 // (a global load even where the compiler cannot see the pointer's origin).
 template <typename ZT>
@@ -129,20 +91,6 @@ __device__ __forceinline__ Cand<ZT> ld_global_cand(const Cand<ZT>* p) {
   } else {
     c.z = *(const __attribute__((address_space(1))) double*)&p->z;
     c.idx = *(const __attribute__((address_space(1))) int*)&p->idx;
-  }
-  return c;
-}
-
-template <typename ZT>
-__device__ __forceinline__ Cand<ZT> ld_dev_cand(const Cand<ZT>* p) {
-  Cand<ZT> c;
-  if constexpr (sizeof(ZT) == 4) {
-    const uint64_t v = ld_dev(reinterpret_cast<const uint64_t*>(p));
-    c.z = __builtin_bit_cast(float, (uint32_t)v);
-    c.idx = (int)(uint32_t)(v >> 32);
-  } else {
-    c.z = ld_dev(&p->z);
-    c.idx = ld_dev(&p->idx);
   }
   return c;
 }
@@ -183,7 +131,7 @@ __device__ __forceinline__ int find_slot(const int32_t* row, int n, int key) {
 // did not select it) and `sphys` (physical page ids, fetched with one
 // coalesced load per page). Returns the number of pages; ends with a barrier
 // (every thread of the block must call it).
-template <int G, bool SPARSE, bool DEV = false>
+template <int G, bool SPARSE>
 __device__ int build_slice(const int32_t* __restrict__ sel, const int32_t* __restrict__ block_table,
                            int b, int bh0, int budget, int P, int max_pages, int split, int pps,
                            unsigned* bm, int32_t* ssel, int* slice, int* slots, int* sphys,
@@ -196,7 +144,7 @@ __device__ int build_slice(const int32_t* __restrict__ sel, const int32_t* __res
     const int nwords = (P + 31) >> 5;
     for (int i = tid; i < nwords; i += kNT) bm[i] = 0u;
     if (staged)
-      for (int i = tid; i < G * budget; i += kNT) ssel[i] = DEV ? ld_dev(selrow + i) : selrow[i];
+      for (int i = tid; i < G * budget; i += kNT) ssel[i] = selrow[i];
     __syncthreads();
     const int32_t* srow = staged ? ssel : selrow;
     for (int i = tid; i < G * budget; i += kNT) {
@@ -566,10 +514,8 @@ struct ScoreArgs {
   Cand<typename KvTraits<KV>::Acc>* spill;
 };
 
-// One split of one (sequence, KV head) unit, by the whole workgroup. DEV:
-// the selection is read, and the candidate region written, at device scope
-// (handed between workgroups of one launch).
-template <typename KV, int D, int G, int PS, bool SPARSE, bool DEV>
+// One split of one (sequence, KV head) unit, by the whole workgroup.
+template <typename KV, int D, int G, int PS, bool SPARSE>
 __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split, int u, unsigned char* smem) {
   using Tr = KvTraits<KV>;
   using Acc = typename Tr::Acc;  // also the score type
@@ -587,13 +533,8 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
   Cand<Acc>* __restrict__ spill = args.spill;
   const Acc window = (Acc)args.window_d;
   auto put_count = [&](size_t r, int n, Acc mval) {
-    if constexpr (DEV) {
-      st_dev(&counts[r], n);
-      st_dev(&maxima[r], mval);
-    } else {
-      counts[r] = n;
-      maxima[r] = mval;
-    }
+    counts[r] = n;
+    maxima[r] = mval;
   };
 
   const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc),
@@ -631,7 +572,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     }
   }
 
-  const int n_slice = build_slice<G, SPARSE, DEV>(
+  const int n_slice = build_slice<G, SPARSE>(
       sel, block_table, b, bh0, budget, P, max_pages, split, pps,
       reinterpret_cast<unsigned*>(smem + lay.bitmap), reinterpret_cast<int32_t*>(smem + lay.ssel),
       slice, slots, sphys, tmp);
@@ -1042,14 +983,10 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
         const bool f = base + k * kWave + lane < ntot && zr[k] >= thr;
         const uint64_t bal = __ballot(f);
         if (f) {
-          if constexpr (DEV) {
-            st_dev_cand(dst + o + __popcll(bal & ltm), zr[k], ir[k]);
-          } else {
-            Cand<Acc> cv;
-            cv.z = zr[k];
-            cv.idx = ir[k];
-            dst[o + __popcll(bal & ltm)] = cv;
-          }
+          Cand<Acc> cv;
+          cv.z = zr[k];
+          cv.idx = ir[k];
+          dst[o + __popcll(bal & ltm)] = cv;
         }
         o += __popcll(bal);
       }
@@ -1062,7 +999,7 @@ template <typename KV, int D, int G, int PS, bool SPARSE>
 __global__ void __launch_bounds__(kNT)
 score_kernel(ScoreArgs<KV> args) {
   extern __shared__ __align__(16) unsigned char smem[];
-  score_split<KV, D, G, PS, SPARSE, false>(args, blockIdx.x / args.U, blockIdx.x % args.U, smem);
+  score_split<KV, D, G, PS, SPARSE>(args, blockIdx.x / args.U, blockIdx.x % args.U, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1084,7 +1021,7 @@ struct GatherArgs {
   int lcap;
   int* tmp;
 };
-template <int R, bool DEV, typename ZT>
+template <int R, typename ZT>
 __device__ __forceinline__ int gather_batch(const GatherArgs<ZT>& a, int bbase, int nb, int n_list) {
   const int tid = threadIdx.x;
   const int per = (nb + kNT - 1) / kNT;
@@ -1115,7 +1052,7 @@ __device__ __forceinline__ int gather_batch(const GatherArgs<ZT>& a, int bbase, 
   }
   Cand<ZT> v[R];
 #pragma unroll
-  for (int k = 0; k < R; ++k) v[k] = DEV ? ld_dev_cand(a.creg + off[k]) : ld_global_cand(a.creg + off[k]);
+  for (int k = 0; k < R; ++k) v[k] = ld_global_cand(a.creg + off[k]);
   int keep = 0;
 #pragma unroll
   for (int k = 0; k < R; ++k) keep += (e0 + k < e1 && v[k].z >= a.thr) ? 1 : 0;
@@ -1183,7 +1120,7 @@ __device__ __forceinline__ T* lds_view(T* p) {
 // Gather runs of more than 8 entries per thread (batches of over 2048
 // candidates). The arguments come one by one (an aggregate argument would
 // pass through scratch memory).
-template <int R, bool DEV, typename ZT>
+template <int R, typename ZT>
 __device__ __attribute__((noinline)) int gather_batch_wide(const int* roff, const Cand<ZT>* creg,
                                                            int splits, int cap, ZT thr, ZT* lz,
                                                            int* li, ZT* gz, int* gi, int lcap,
@@ -1191,7 +1128,7 @@ __device__ __attribute__((noinline)) int gather_batch_wide(const int* roff, cons
                                                            int n_list) {
   const GatherArgs<ZT> a{lds_view(roff), creg, splits, cap, thr, lds_view(lz), lds_view(li),
                          gz, gi, lcap, lds_view(tmp)};
-  return gather_batch<R, DEV>(a, bbase, nb, n_list);
+  return gather_batch<R>(a, bbase, nb, n_list);
 }
 
 // Lower bound on tau from a subset of the head's tokens. The threshold t_S of
@@ -1347,8 +1284,7 @@ struct TauArgs {
 };
 
 // One query head (unit u, head hh of its group), by the whole workgroup.
-// DEV: the candidate regions are read at device scope.
-template <typename KV, int D, bool DEV>
+template <typename KV, int D>
 __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh, unsigned char* smem) {
   using ZT = typename KvTraits<KV>::Acc;
   const KV* __restrict__ v_pool = args.v_pool;
@@ -1400,10 +1336,10 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
   int s = 0;
   ZT mloc = neg_inf<ZT>();
   for (int r = r0; r < r1; ++r) {
-    const int c = DEV ? ld_dev(cn + r) : cn[r];
+    const int c = cn[r];
     roff[r] = c;
     s += c;
-    mloc = max(mloc, DEV ? ld_dev(mx + r) : mx[r]);
+    mloc = max(mloc, mx[r]);
   }
   const ZT M = block_reduce<kNT>(mloc, fred, [](ZT a, ZT c) { return max(a, c); });
   int n_cand;
@@ -1445,10 +1381,10 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
     const int nb_ = min(kNT * KB, n_cand - bbase);
     const int per = (nb_ + kNT - 1) / kNT;
     const GatherArgs<ZT> ga{roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp};
-    if (per <= 2) n_list = gather_batch<2, DEV>(ga, bbase, nb_, n_list);
-    else if (per <= 8) n_list = gather_batch<8, DEV>(ga, bbase, nb_, n_list);
+    if (per <= 2) n_list = gather_batch<2>(ga, bbase, nb_, n_list);
+    else if (per <= 8) n_list = gather_batch<8>(ga, bbase, nb_, n_list);
     else
-      n_list = gather_batch_wide<KB, DEV>(roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp,
+      n_list = gather_batch_wide<KB>(roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp,
                                           bbase, nb_, n_list);
   }
   __syncthreads();
@@ -1609,7 +1545,7 @@ template <typename KV, int D>
 __global__ void __launch_bounds__(kNT)
 tau_pv_kernel(TauArgs<KV> args) {
   extern __shared__ __align__(16) unsigned char smem[];
-  tau_head<KV, D, false>(args, blockIdx.x % args.U, blockIdx.x / args.U, smem);
+  tau_head<KV, D>(args, blockIdx.x % args.U, blockIdx.x / args.U, smem);
 }
 
 // ---------------------------------------------------------------------------
