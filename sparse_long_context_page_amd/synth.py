@@ -102,11 +102,21 @@ WORKLOADS = {
     "extreme_1m": Workload(
         "extreme_1m", 1, 32, 8, 128, 64, 1048576, "bf16", (1.5,), (64,), 4.0 * _S128,
         plant="group_mean", n_planted=256),
+    # Extra, not one of the sizing workloads above: long_128k with planted runs
+    # of magnitude 32 instead of 3, so a planted key's coordinates (about 2.8
+    # each) leave the random keys' per-page range and its score (about 64)
+    # tops the random maximum (about 17): the peaked attention regime of a
+    # trained model, where the entmax support sits in a few pages the box
+    # bound can find. Used by the discarded-mass report.
+    "long_128k_peaked": Workload(
+        "long_128k_peaked", 4, 32, 8, 128, 32, 131072, "bf16", (1.5,), (82,), 4.0 * _S128,
+        plant="group_mean", n_planted=128, run_len=8, plant_magnitude=32.0),
 }
 
 # Seeds: each workload has a fixed seed so every run sees the same data.
 WORKLOAD_SEEDS = {"tiny_4k_f32": 1, "gqa_32k": 2, "long_128k": 3,
-                  "alpha_sweep_64k": 4, "extreme_512k": 5, "extreme_1m": 6}
+                  "alpha_sweep_64k": 4, "extreme_512k": 5, "extreme_1m": 6,
+                  "long_128k_peaked": 7}
 
 
 def shrink(w: Workload, context: int | None = None, batch: int | None = None,

@@ -21,6 +21,14 @@ def test_union_pages_and_bytes():
     assert nb["score_full"] == 2 * 4096 * 8 * 128 * 2 + 2 * 32 * 128 * 4 + 2 * P * 4
     assert nb["score_sparse"] == 6 * 32 * 128 * 2 + 2 * 32 * 128 * 4 + 2 * 32 * 4 * 4 + 2 * P * 4
     assert nb["tau_pv_full"] == 64 * 3 * 128 * 2 + 2 * 32 * 128 * 4
+    # the all-K+V view: the union pages' K and V (plus boxes), or all of K and V
+    meta_b = 2 * P * 8 * 2 * 128 * 2
+    k_sel = 6 * 32 * 128 * 2
+    q_b = out_b = 2 * 32 * 128 * 4
+    sel_b, bt_b = 2 * 32 * 4 * 4, 2 * P * 4
+    # q and the block table are read by the bound and the score kernels
+    assert nb["_sparse_all_kv"] == meta_b + 2 * k_sel + 2 * q_b + out_b + sel_b + 2 * bt_b
+    assert nb["_full_all_kv"] == 2 * 2 * 4096 * 8 * 128 * 2 + q_b + out_b + bt_b
 
 
 def test_cpu_baseline_runs_and_matches_oracle_selection():
@@ -29,8 +37,10 @@ def test_cpu_baseline_runs_and_matches_oracle_selection():
     cb = bench.cpu_baseline(inp, 8, 1.5, n_heads=4)
     assert cb["value"] > 0 and cb["cores"] >= 1 and cb["kind"] == "oracle"
     assert len(cb["_results"]) == 4
-    for b, h, dt, sel, rs, rf in cb["_results"]:
+    for b, h, dt, sel, rs, rf, near in cb["_results"]:
         assert len(sel) == 8 and rs.shape == (128,) and rf.shape == (128,)
+        # the near-tie band always holds the budget-th page itself
+        assert len(near) >= 1 and all(0 <= j < 2048 // 32 for j in near)
 
 
 def test_multi_gpu_request_exits(monkeypatch, capsys):
