@@ -281,7 +281,7 @@ int entmaxkv_workspace_bytes(const entmaxkv_shape* shape, int32_t budget_pages, 
   switch (which) {
     case ENTMAXKV_WS_SELECT:
       if ((rc = check_budget(budget_pages))) return rc;
-      *bytes = align256(select_ws_bytes(s));
+      *bytes = align256(select_ws_bytes(s, budget_pages));
       return ENTMAXKV_OK;
     case ENTMAXKV_WS_SPARSE: {
       if ((rc = check_budget(budget_pages))) return rc;
@@ -388,7 +388,8 @@ int entmaxkv_gauss_select(const entmaxkv_shape* shape, const float* q, const voi
       hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(1) || !ev.before(2)) return ENTMAXKV_ERR_HIP;
-  if (launch_select(s, keys, seq_lens, cap_pages, sel, nullptr, true, stream) != hipSuccess)
+  if (launch_select(s, SelectPlan(), keys, seq_lens, cap_pages, sel, nullptr, true, stream) !=
+      hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(2)) return ENTMAXKV_ERR_HIP;
   return ENTMAXKV_OK;
@@ -423,15 +424,16 @@ int entmaxkv_score_select(const entmaxkv_shape* shape, const float* q, const voi
   if ((rc = check_budget(budget_pages))) return rc;
   if (!q || !meta || !block_table || !seq_lens || !sel) return ENTMAXKV_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(meta, 16)) return ENTMAXKV_ERR_INVALID;
-  if (!ws || ws_bytes < select_ws_bytes(s)) return ENTMAXKV_ERR_WORKSPACE;
+  if (!ws || ws_bytes < select_ws_bytes(s, budget_pages)) return ENTMAXKV_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return ENTMAXKV_ERR_INVALID;
   float* ub = static_cast<float*>(ws);
+  const SelectPlan sp = plan_select(s, budget_pages);
   const Events ev{events, stream};
   if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
-  if (launch_bounds(s, q, meta, block_table, seq_lens, ub, stream) != hipSuccess)
+  if (launch_bounds(s, sp, q, meta, block_table, seq_lens, ub, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
-  if (launch_select(s, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
+  if (launch_select(s, sp, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
   return ENTMAXKV_OK;
@@ -447,18 +449,19 @@ int entmaxkv_score_select_noalloc(const entmaxkv_shape* shape, const float* q, c
   if ((rc = check_budget(budget_pages))) return rc;
   if (!q || !meta || !block_table || !seq_lens || !sel) return ENTMAXKV_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(meta, 16)) return ENTMAXKV_ERR_INVALID;
-  if (select_ws_bytes(s) > kNoAllocScratchBytes) return ENTMAXKV_ERR_WORKSPACE;
+  if (select_ws_bytes(s, budget_pages) > kNoAllocScratchBytes) return ENTMAXKV_ERR_WORKSPACE;
   void* ws = nullptr;
   if ((rc = scratch_of_current_device(&ws))) return rc;
   // the same kernels as entmaxkv_score_select, with the bounds in `scratch`
   // (every bound the select reads is written first: nothing to clear)
   float* ub = static_cast<float*>(ws);
+  const SelectPlan sp = plan_select(s, budget_pages);
   const Events ev{events, stream};
   if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
-  if (launch_bounds(s, q, meta, block_table, seq_lens, ub, stream) != hipSuccess)
+  if (launch_bounds(s, sp, q, meta, block_table, seq_lens, ub, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
-  if (launch_select(s, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
+  if (launch_select(s, sp, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
   return ENTMAXKV_OK;

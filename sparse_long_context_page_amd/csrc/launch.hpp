@@ -9,6 +9,8 @@
 
 namespace ekv {
 
+constexpr int kNumCUs = 256;  // compute units of the MI355X
+
 struct LaunchShape {
   int batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages, num_phys;
   int group;  // num_q_heads / num_kv_heads
@@ -130,7 +132,15 @@ DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p);
 // Row stride (floats) of the per-head page bounds in the select workspace:
 // padded to a multiple of 4 so every row starts 16-byte aligned.
 inline int ub_ld(int max_pages) { return (max_pages + 3) & ~3; }
-size_t select_ws_bytes(const LaunchShape& s);
+// Top-k plan: the bounds kernel's chunk of cp pages (nchunks per sequence)
+// and, when chunked, each head's top keepc pages of a chunk as the select's
+// candidates instead of every page's bound.
+struct SelectPlan {
+  bool chunked = false;
+  int nt = 1, cp = 64, nchunks = 0, keepc = 0;
+};
+SelectPlan plan_select(const LaunchShape& s, int budget);
+size_t select_ws_bytes(const LaunchShape& s, int budget);
 
 hipError_t launch_append_meta(const LaunchShape& s, const void* k_pool, const int32_t* bt,
                               const int32_t* old_lens, const int32_t* new_lens, int max_new,
@@ -138,15 +148,16 @@ hipError_t launch_append_meta(const LaunchShape& s, const void* k_pool, const in
 hipError_t launch_meta(const LaunchShape& s, const void* k_pool, const int32_t* bt,
                        const int32_t* lens, void* meta, hipStream_t st);
 
-hipError_t launch_bounds(const LaunchShape& s, const float* q, const void* meta,
-                         const int32_t* bt, const int32_t* lens, float* ub, hipStream_t st);
+hipError_t launch_bounds(const LaunchShape& s, const SelectPlan& p, const float* q,
+                         const void* meta, const int32_t* bt, const int32_t* lens, float* ub,
+                         hipStream_t st);
 
 // drop_neg_inf: pages whose key is -inf are not candidates (the Gaussian
 // selection marks the pages that fail its rule that way); when no more than
 // `budget` candidates remain, all are kept and the rest of the row is -1.
-hipError_t launch_select(const LaunchShape& s, const float* ub, const int32_t* lens,
-                         int budget, int32_t* sel, float* sel_ub, bool drop_neg_inf,
-                         hipStream_t st);
+hipError_t launch_select(const LaunchShape& s, const SelectPlan& p, const float* ub,
+                         const int32_t* lens, int budget, int32_t* sel, float* sel_ub,
+                         bool drop_neg_inf, hipStream_t st);
 
 // Page key moments of every page (old_lens == nullptr), or, after an append,
 // of the pages the tokens [old_lens, lens) touch (at most max_new per sequence).

@@ -23,6 +23,14 @@
 //   8 bits per pass, stopping as soon as the boundary digit is taken whole.
 //   Ties on the full 32 bits go to the lower page index. The kept pages are
 //   written in ascending order with two block scans.
+// Chunked selection (bf16 boxes, budget at most half a bounds chunk): each
+//   bounds workgroup keeps, per head, the top min(budget, chunk) pages of its
+//   chunk (a wave-level radix select on the same keys, ties to the lower
+//   page) and writes them in page order in place of its bound rows; the
+//   select kernel then takes the budget largest of those candidates. The
+//   result is the same selection: every page of the global top-k is in its
+//   chunk's top-k, and the candidates stay in ascending page order, so ties
+//   still go to the lower page.
 #include <type_traits>
 
 #include "launch.hpp"
@@ -36,6 +44,117 @@ namespace ekv {
 constexpr int kSelWideFrom = 256;
 constexpr int kSelLds = 16384;  // bounds staged in LDS when the sequence has at most this many pages
 constexpr int kBoundPages = 32;  // pages per workgroup of the bounds kernel
+
+// The k largest of n 32-bit keys, ties to the lower index, by one wave
+// (k < n <= 64 * KPL): lane l holds keys l, l + 64, ... in kr[0..KPL). Radix
+// select, 8 bits per pass from the highest bit where the keys differ, until
+// the boundary digit is taken whole; the keys stay in registers. The
+// histogram has kHistCopies interleaved copies (bin b, copy c at word
+// b * kHistCopies + c, lane l adding to copy l % kHistCopies), so keys that
+// share a digit, common in the first pass, spread their LDS atomics over
+// that many banks. hist: 256 * kHistCopies ints of LDS owned by the wave.
+// On return key i is kept iff (key & pmask) > prefix, or it equals prefix
+// and fewer than keq equal keys precede it.
+constexpr int kHistCopies = 4;
+template <int KPL>
+__device__ void wave_topk(const uint32_t (&kr)[KPL], int n, int k, int* hist, int lane,
+                          uint32_t& prefix, uint32_t& pmask, int& keq) {
+  static_assert(kHistCopies == 4, "one 16-byte access per bin");
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    if (r * kWave + lane < n) {
+      mn = min(mn, kr[r]);
+      mx = max(mx, kr[r]);
+    }
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (mn == mx) {
+    prefix = mx;
+    pmask = 0xffffffffu;
+    keq = k;
+    return;
+  }
+  int hb = 31 - __clz(mn ^ mx);
+  pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+  prefix = mx & pmask;
+  int kk = k;
+  uint4* mine = reinterpret_cast<uint4*>(hist) + 4 * lane;  // bins 4 lane .. 4 lane + 3
+  int* slot = hist + (lane & (kHistCopies - 1));
+  for (int pass = 0; pass < 8; ++pass) {
+    const int lo = hb >= 7 ? hb - 7 : 0;
+    const uint32_t dmask = (1u << (hb - lo + 1)) - 1u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mine[i] = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) {
+      const uint32_t o = kr[r];
+      if (r * kWave + lane < n && (o & pmask) == prefix)
+        atomicAdd(slot + ((o >> lo) & dmask) * kHistCopies, 1);
+    }
+    __builtin_amdgcn_wave_barrier();
+    int c4[4];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = mine[i];
+      c4[i] = (int)(v.x + v.y + v.z + v.w);
+      sum += c4[i];
+    }
+    const int incl = wave_incl_scan(sum, lane);
+    int above = lane_value(incl, kWave - 1) - incl;  // keys in higher lanes' bins
+    int d = -1, ab = 0, cd = 0;
+    if (above < kk && kk <= above + sum) {
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (above < kk && kk <= above + c4[i]) {
+          d = 4 * lane + i;
+          ab = above;
+          cd = c4[i];
+        }
+        above += c4[i];
+      }
+    }
+    const uint64_t bal = __ballot(d >= 0);
+    __builtin_amdgcn_wave_barrier();
+    if (bal == 0ull) break;  // (cannot happen: kk <= keys matching the prefix)
+    const int src = __ffsll((unsigned long long)bal) - 1;
+    d = __builtin_amdgcn_readlane(d, src);
+    ab = __builtin_amdgcn_readlane(ab, src);
+    cd = __builtin_amdgcn_readlane(cd, src);
+    kk -= ab;
+    prefix |= ((uint32_t)d) << lo;
+    pmask |= dmask << lo;
+    if (cd == kk || lo == 0) break;
+    hb = lo - 1;
+  }
+  keq = kk;
+}
+
+// Calls emit(i, key, pos) for every kept key i (held as in wave_topk) in
+// ascending i, pos = its rank among the kept. One wave.
+template <int KPL, typename Emit>
+__device__ void wave_emit_kept(const uint32_t (&kr)[KPL], int n, uint32_t prefix, uint32_t pmask,
+                               int keq, int lane, Emit emit) {
+  const uint64_t ltm = lanemask_below(lane);
+  int eq_before = 0, pos0 = 0;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    if (r * kWave >= n) break;
+    const int i = r * kWave + lane;
+    const uint32_t m = kr[r] & pmask;
+    const bool gt = i < n && m > prefix;
+    const bool eq = i < n && m == prefix;
+    const uint64_t beq = __ballot(eq);
+    const bool take = gt || (eq && eq_before + __popcll(beq & ltm) < keq);
+    const uint64_t btk = __ballot(take);
+    if (take) emit(i, kr[r], pos0 + __popcll(btk & ltm));
+    eq_before += __popcll(beq);
+    pos0 += __popcll(btk);
+  }
+}
 
 template <typename KV, int D, int G>
 __global__ void __launch_bounds__(256)
@@ -149,22 +268,26 @@ bounds_kernel(const float* __restrict__ q, const KV* __restrict__ meta,
 // Workgroups of the matrix-core bounds kernel: about 256 in all (one per CU,
 // a single round; on the 32K-512K workloads this beat 512-4096 shorter ones),
 // each wave taking `nt` tiles of 16 pages.
-constexpr long long kBoundsGrid = 256;
+constexpr long long kBoundsGrid = kNumCUs;
 constexpr int kBoundsMaxTiles = 16;
 constexpr int kBoundsBufs = 2;  // tile buffers per wave
 
 // LDS of the matrix-core bounds kernel: kBoundsBufs 16-record tiles per wave, the
-// chunk's physical page ids, then the split q table.
-__host__ __device__ constexpr size_t bounds_lds_bytes(int D, int G, int cp) {
-  return (size_t)kNW * kBoundsBufs * 16 * 4 * D + (size_t)cp * 4 + (size_t)G * 3 * (2 * D + 8) * 2;
+// chunk's physical page ids, then the split q table; chunked (LOCAL) runs
+// add the chunk's bounds [G][cp].
+__host__ __device__ constexpr size_t bounds_lds_bytes(int D, int G, int cp, bool local = false) {
+  return (size_t)kNW * kBoundsBufs * 16 * 4 * D + (size_t)cp * 4 + (size_t)G * 3 * (2 * D + 8) * 2 +
+         (local ? (size_t)G * cp * 4 : 0);
 }
 
-template <int D, int G>
+// LOCAL: instead of the bound rows, each head's top keepc pages of the chunk
+// go to cand[(head * nchunks + chunk) * keepc + ...] as (order key | page << 32).
+template <int D, int G, bool LOCAL>
 __global__ void __launch_bounds__(256)
 bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
                    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
                    float* __restrict__ ub, int H, int Hkv, int ps, int max_pages, int num_phys,
-                   int U, int ldu, int nt) {
+                   int U, int ldu, int nt, int keepc, int nchunks) {
   constexpr int K2 = 2 * D;        // values per record
   constexpr int RB = K2 * 2;       // bytes per record
   constexpr int TP = 16;           // records (pages) per tile
@@ -175,6 +298,7 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
   constexpr int KS = K2 / 32;      // k-steps of 32 values
   constexpr int NMB = (G + 3) / 4; // blocks of 4 heads
   static_assert(NI * 1024 == PB && RPI * RB == 1024 && D % 32 == 0, "tiling");
+  static_assert(!LOCAL || kBoundsBufs * PB >= 256 * kHistCopies * 4, "histogram fits a wave's tiles");
   extern __shared__ __align__(16) unsigned char smem[];
   int* sphys = reinterpret_cast<int*>(smem + kNW * kBoundsBufs * PB);
 
@@ -182,6 +306,9 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
   const int u = blockIdx.x % U, chunk = blockIdx.x / U;
   const int b = u / Hkv, g = u % Hkv;
   const int cp = kNW * TP * nt;
+  // LOCAL: the chunk's bounds, past the split q table
+  float* lub = reinterpret_cast<float*>(smem + kNW * kBoundsBufs * PB + (size_t)cp * 4 +
+                                        (size_t)G * 3 * (K2 + 8) * 2);
   const int j0 = chunk * cp;
   // the chunk's block-table entries (up to kBoundsMaxTiles * 64, four per
   // thread) are read together with the length, not after it
@@ -283,9 +410,11 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
       for (int ks = 0; ks < KS; ++ks)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[blk][ks], kv[ks], acc, 0, 0, 0);
       const int h = blk * 4 + kgrp;
-      if (h < G && p < n)
-        ub[(size_t)(h0 + h) * ldu + j0 + p] =
-            ok ? ((acc[0] + acc[1]) + acc[2]) + 0.0f : -__builtin_inff();
+      const float bound = ok ? ((acc[0] + acc[1]) + acc[2]) + 0.0f : -__builtin_inff();
+      if (h < G && p < n) {
+        if constexpr (LOCAL) lub[h * cp + p] = bound;
+        else ub[(size_t)(h0 + h) * ldu + j0 + p] = bound;
+      }
     }
   };
   // A operand, read before any load into LDS is in flight: lane l holds row
@@ -315,6 +444,29 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
     k = k + 1 == kBoundsBufs ? 0 : k + 1;
   }
   wait_vmcnt<0>();  // no load into LDS is left in flight
+  if constexpr (LOCAL) {
+    // each head's top keepc pages of the chunk, in page order
+    __syncthreads();
+    constexpr int KPL = kNW * 16 * kBoundsMaxTiles / kWave;  // keys per lane, cp <= 64 KPL
+    for (int h = wave; h < G; h += kNW) {
+      const float* row = lub + h * cp;
+      uint32_t kr[KPL];
+#pragma unroll
+      for (int r = 0; r < KPL; ++r) {
+        const int i = r * kWave + lane;
+        kr[r] = i < n ? float_order(row[i]) : 0u;
+      }
+      uint32_t prefix = 0u, pmask = 0u;
+      int keq = n;
+      // the histogram lives in the wave's own tile buffers, idle now
+      if (n > keepc)
+        wave_topk<KPL>(kr, n, keepc, reinterpret_cast<int*>(kbuf), lane, prefix, pmask, keq);
+      uint64_t* dst = reinterpret_cast<uint64_t*>(ub) + ((size_t)(h0 + h) * nchunks + chunk) * keepc;
+      wave_emit_kept<KPL>(kr, n, prefix, pmask, keq, lane, [&](int i, uint32_t key, int pos) {
+        dst[pos] = (uint64_t)key | ((uint64_t)(uint32_t)(j0 + i) << 32);
+      });
+    }
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -322,11 +474,18 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
 // kDrop: keys at or below the order value of -inf are not candidates (the
 // Gaussian selection marks the pages that fail its rule that way); when no
 // more than `budget` candidates remain all are kept and the row is -1 padded.
-template <int kSelNT, bool kDrop>
+// kCand: the keys are the chunked candidates of bounds_mfma_kernel<..., true>
+// (order key | page << 32, keepc per chunk of cp pages, nchunks per head),
+// at most kSelCand of them per head; the kept candidates' pages are written.
+constexpr int kSelCand = kSelLds / 2;
+constexpr long long kSelChunkedMinPages = 8192;
+template <int kSelNT, bool kDrop, bool kCand>
 __global__ void __launch_bounds__(kSelNT)
 select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens, int H, int G,
               int Hkv, int U, int ps, int max_pages, int ldu, int budget,
-              int32_t* __restrict__ sel, float* __restrict__ sel_ub) {
+              int32_t* __restrict__ sel, float* __restrict__ sel_ub, int cp, int keepc,
+              int nchunks) {
+  static_assert(!(kDrop && kCand), "the Gaussian keys are not chunked");
   constexpr uint32_t drop_below = 0x007fffffu;  // float_order(-inf)
   constexpr int NW = kSelNT / kWave;
   constexpr int UNR = 4;  // 16-byte loads in flight per thread
@@ -342,15 +501,24 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   const int b = u / Hkv, g = u % Hkv;
   const int bh = b * H + g * G + hh;
   const int L = clamp_len(seq_lens[b], max_pages * ps);
-  const int P = (L + ps - 1) / ps;
+  int P = (L + ps - 1) / ps;
   const float* row = ub + (size_t)bh * ldu;
   int32_t* out = sel + (size_t)bh * budget;
   float* out_ub = sel_ub ? sel_ub + (size_t)bh * budget : nullptr;
 
+  // chunked candidates: nk of them (every chunk but the last holds keepc)
+  const uint64_t* crow = reinterpret_cast<const uint64_t*>(ub) + (size_t)bh * nchunks * keepc;
+  const int nc = kCand ? (P + cp - 1) / cp : 0;
+  const int nk = kCand ? (nc == 0 ? 0 : (nc - 1) * keepc + min(keepc, P - (nc - 1) * cp)) : P;
+  int* sj = reinterpret_cast<int*>(sord + kSelCand);  // kCand: candidates' pages
+
   if (!kDrop && P <= budget) {
+    // every page kept (kCand: then one chunk holds them all, in page order)
     for (int i = tid; i < budget; i += kSelNT) {
       out[i] = i < P ? i : -1;
-      if (out_ub) out_ub[i] = i < P ? row[i] + 0.0f : -__builtin_inff();
+      if (out_ub)
+        out_ub[i] = i >= P ? -__builtin_inff()
+                           : (kCand ? order_float((uint32_t)crow[i]) : row[i] + 0.0f);
     }
     return;
   }
@@ -358,7 +526,9 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   // Order-preserving 32-bit keys, handled four at a time (rows are padded to
   // a multiple of 4 floats; a quad's entries at or past P are masked). They
   // are staged in LDS when they fit, else re-read from the bounds row.
-  const bool staged = P <= kSelLds;
+  // kCand: the candidates' keys (always staged) take the place of the pages'.
+  if constexpr (kCand) P = nk;
+  const bool staged = kCand || P <= kSelLds;
   const int n4 = (P + 3) >> 2;
   const float4* row4 = reinterpret_cast<const float4*>(row);
   auto from_global = [&](int i4) -> uint4 {
@@ -377,7 +547,31 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   auto valid = [&](int j, uint32_t o) { return j < P && (!kDrop || o > drop_below); };
   uint32_t mn = 0xffffffffu, mx = 0u;
   int nvalid = 0;
-  for (int base = 0; base < n4; base += UNR * kSelNT) {
+  if constexpr (kCand) {
+    // stage the candidates' keys and pages, every load of a batch issued
+    // before the first is used
+    constexpr int CU = 8;
+    for (int base = 0; base < P; base += CU * kSelNT) {
+      uint64_t v[CU];
+#pragma unroll
+      for (int r = 0; r < CU; ++r) {
+        const int i = base + r * kSelNT + tid;
+        v[r] = i < P ? crow[i] : 0ull;
+      }
+#pragma unroll
+      for (int r = 0; r < CU; ++r) {
+        const int i = base + r * kSelNT + tid;
+        if (i < P) {
+          const uint32_t o = (uint32_t)v[r];
+          sord[i] = o;
+          sj[i] = (int)(uint32_t)(v[r] >> 32);
+          mn = min(mn, o);
+          mx = max(mx, o);
+        }
+      }
+    }
+  }
+  for (int base = 0; !kCand && base < n4; base += UNR * kSelNT) {
     uint4 v[UNR] = {};
 #pragma unroll
     for (int r = 0; r < UNR; ++r) {
@@ -533,7 +727,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
       eqc += eq ? 1 : 0;
       if (take) {
         if (pos < budget) {
-          out[pos] = 4 * i4 + e;
+          out[pos] = kCand ? sj[4 * i4 + e] : 4 * i4 + e;
           if (out_ub) out_ub[pos] = order_float(at(v, e));
         }
         ++pos;
@@ -542,29 +736,48 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   }
 }
 
-template <int D, int G>
-static hipError_t launch_bounds_mfma(const LaunchShape& s, const float* q, const void* meta,
-                                     const int32_t* bt, const int32_t* lens, float* ub,
-                                     hipStream_t st) {
+SelectPlan plan_select(const LaunchShape& s, int budget) {
+  SelectPlan p;
   const int U = s.batch * s.num_kv_heads;
   const long long tiles = (long long)U * ((s.max_pages + 15) / 16);
   long long nt = (tiles + kBoundsGrid * kNW - 1) / (kBoundsGrid * kNW);
   nt = nt < 1 ? 1 : (nt > kBoundsMaxTiles ? kBoundsMaxTiles : nt);
-  const int cp = kNW * 16 * (int)nt;
-  const long long chunks = (s.max_pages + cp - 1) / cp;
-  const size_t lds = bounds_lds_bytes(D, G, cp);
-  auto kern = bounds_mfma_kernel<D, G>;
+  p.nt = (int)nt;
+  p.cp = kNW * 16 * p.nt;
+  p.nchunks = (s.max_pages + p.cp - 1) / p.cp;
+  p.keepc = budget < p.cp ? budget : p.cp;
+  // Chunked when it leaves at most half the keys, they fit the select's LDS
+  // staging (bf16 boxes, where the bounds kernel covers cp-page chunks), and
+  // the one-workgroup-per-row select would scan at least kSelChunkedMinPages
+  // pages per CU: the chunk-local top-k adds about 3.5 us to the bounds kernel
+  // (its tail runs with one wave per SIMD), which the shorter select repays
+  // only there (measured: 32K x 256 rows and 128K x 128 rows lose 2 us,
+  // 64K x 512 rows, 512K and 1M x 32 rows gain 2-8 us).
+  const long long rows = (long long)s.batch * s.num_q_heads;
+  const long long per_cu = (rows + kNumCUs - 1) / kNumCUs * s.max_pages;
+  p.chunked = s.bf16 && budget > 0 && 2 * (long long)p.keepc <= p.cp &&
+              (long long)p.nchunks * p.keepc <= kSelCand && per_cu >= kSelChunkedMinPages;
+  return p;
+}
+
+template <int D, int G, bool LOCAL>
+static hipError_t launch_bounds_mfma(const LaunchShape& s, const SelectPlan& p, const float* q,
+                                     const void* meta, const int32_t* bt, const int32_t* lens,
+                                     float* ub, hipStream_t st) {
+  const int U = s.batch * s.num_kv_heads;
+  const size_t lds = bounds_lds_bytes(D, G, p.cp, LOCAL);
+  auto kern = bounds_mfma_kernel<D, G, LOCAL>;
   // The LDS limit is a kernel attribute: raised once, to the most any plan
   // asks for (a function-local static is initialised exactly once, also when
   // several host threads launch).
   static const hipError_t lds_raised = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)bounds_lds_bytes(D, 8, kNW * 16 * kBoundsMaxTiles));
+      (int)bounds_lds_bytes(D, 8, kNW * 16 * kBoundsMaxTiles, LOCAL));
   if (lds_raised != hipSuccess) return lds_raised;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(U * chunks)), dim3(256), lds, st, q,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(U * p.nchunks)), dim3(256), lds, st, q,
                      static_cast<const bf16_t*>(meta), bt, lens, ub, s.num_q_heads,
                      s.num_kv_heads, s.page_size, s.max_pages, s.num_phys, U,
-                     ub_ld(s.max_pages), (int)nt);
+                     ub_ld(s.max_pages), p.nt, p.keepc, p.nchunks);
   return hipGetLastError();
 }
 
@@ -580,16 +793,24 @@ static hipError_t launch_bounds_t(const LaunchShape& s, const float* q, const vo
   return hipGetLastError();
 }
 
+template <int D, int G>
+static hipError_t launch_bounds_mfma_any(const LaunchShape& s, const SelectPlan& p,
+                                         const float* q, const void* meta, const int32_t* bt,
+                                         const int32_t* lens, float* ub, hipStream_t st) {
+  return p.chunked ? launch_bounds_mfma<D, G, true>(s, p, q, meta, bt, lens, ub, st)
+                   : launch_bounds_mfma<D, G, false>(s, p, q, meta, bt, lens, ub, st);
+}
+
 template <typename KV, int D>
-static hipError_t launch_bounds_d(const LaunchShape& s, const float* q, const void* meta,
-                                  const int32_t* bt, const int32_t* lens, float* ub,
-                                  hipStream_t st) {
+static hipError_t launch_bounds_d(const LaunchShape& s, const SelectPlan& p, const float* q,
+                                  const void* meta, const int32_t* bt, const int32_t* lens,
+                                  float* ub, hipStream_t st) {
   if constexpr (sizeof(KV) == 2) {
     switch (s.group) {
-      case 1: return launch_bounds_mfma<D, 1>(s, q, meta, bt, lens, ub, st);
-      case 2: return launch_bounds_mfma<D, 2>(s, q, meta, bt, lens, ub, st);
-      case 4: return launch_bounds_mfma<D, 4>(s, q, meta, bt, lens, ub, st);
-      default: return launch_bounds_mfma<D, 8>(s, q, meta, bt, lens, ub, st);
+      case 1: return launch_bounds_mfma_any<D, 1>(s, p, q, meta, bt, lens, ub, st);
+      case 2: return launch_bounds_mfma_any<D, 2>(s, p, q, meta, bt, lens, ub, st);
+      case 4: return launch_bounds_mfma_any<D, 4>(s, p, q, meta, bt, lens, ub, st);
+      default: return launch_bounds_mfma_any<D, 8>(s, p, q, meta, bt, lens, ub, st);
     }
   } else {
     switch (s.group) {
@@ -601,30 +822,41 @@ static hipError_t launch_bounds_d(const LaunchShape& s, const float* q, const vo
   }
 }
 
-hipError_t launch_bounds(const LaunchShape& s, const float* q, const void* meta,
-                         const int32_t* bt, const int32_t* lens, float* ub, hipStream_t st) {
+hipError_t launch_bounds(const LaunchShape& s, const SelectPlan& p, const float* q,
+                         const void* meta, const int32_t* bt, const int32_t* lens, float* ub,
+                         hipStream_t st) {
   if (s.bf16) {
-    if (s.head_dim == 64) return launch_bounds_d<bf16_t, 64>(s, q, meta, bt, lens, ub, st);
-    return launch_bounds_d<bf16_t, 128>(s, q, meta, bt, lens, ub, st);
+    if (s.head_dim == 64) return launch_bounds_d<bf16_t, 64>(s, p, q, meta, bt, lens, ub, st);
+    return launch_bounds_d<bf16_t, 128>(s, p, q, meta, bt, lens, ub, st);
   }
-  if (s.head_dim == 64) return launch_bounds_d<float, 64>(s, q, meta, bt, lens, ub, st);
-  return launch_bounds_d<float, 128>(s, q, meta, bt, lens, ub, st);
+  if (s.head_dim == 64) return launch_bounds_d<float, 64>(s, p, q, meta, bt, lens, ub, st);
+  return launch_bounds_d<float, 128>(s, p, q, meta, bt, lens, ub, st);
 }
 
-hipError_t launch_select(const LaunchShape& s, const float* ub, const int32_t* lens, int budget,
-                         int32_t* sel, float* sel_ub, bool drop_neg_inf, hipStream_t st) {
+hipError_t launch_select(const LaunchShape& s, const SelectPlan& p, const float* ub,
+                         const int32_t* lens, int budget, int32_t* sel, float* sel_ub,
+                         bool drop_neg_inf, hipStream_t st) {
   const int U = s.batch * s.num_kv_heads;
   const bool wide = U * s.group >= kSelWideFrom;
   const dim3 grid(U * s.group), block(wide ? 256 : 512);
-  auto kern = wide ? (drop_neg_inf ? select_kernel<256, true> : select_kernel<256, false>)
-                   : (drop_neg_inf ? select_kernel<512, true> : select_kernel<512, false>);
+  const bool cand = p.chunked && !drop_neg_inf;
+  auto kern = wide ? (drop_neg_inf ? select_kernel<256, true, false>
+                                   : (cand ? select_kernel<256, false, true>
+                                           : select_kernel<256, false, false>))
+                   : (drop_neg_inf ? select_kernel<512, true, false>
+                                   : (cand ? select_kernel<512, false, true>
+                                           : select_kernel<512, false, false>));
   hipLaunchKernelGGL(kern, grid, block, 0, st, ub, lens, s.num_q_heads, s.group, s.num_kv_heads,
-                     U, s.page_size, s.max_pages, ub_ld(s.max_pages), budget, sel, sel_ub);
+                     U, s.page_size, s.max_pages, ub_ld(s.max_pages), budget, sel, sel_ub, p.cp,
+                     p.keepc, p.nchunks);
   return hipGetLastError();
 }
 
-size_t select_ws_bytes(const LaunchShape& s) {
-  return (size_t)s.batch * s.num_q_heads * ub_ld(s.max_pages) * sizeof(float);
+size_t select_ws_bytes(const LaunchShape& s, int budget) {
+  const size_t rows = (size_t)s.batch * s.num_q_heads * ub_ld(s.max_pages) * sizeof(float);
+  const SelectPlan p = plan_select(s, budget);
+  const size_t cand = p.chunked ? (size_t)s.batch * s.num_q_heads * p.nchunks * p.keepc * 8 : 0;
+  return rows > cand ? rows : cand;
 }
 
 }  // namespace ekv
