@@ -195,6 +195,10 @@ DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p) {
   const size_t wcap = (size_t)((p.pages_per_split + kNW - 1) / kNW) * s.page_size;
   w.spill = o;
   o = align256(o + bh * p.splits * (size_t)kNW * wcap * cand_bytes(s.bf16));
+  // the score step's shared maxima, one order key per head, kMaxStride
+  // words apart
+  w.gmax = o;
+  o = align256(o + bh * kMaxStride * 4);
   w.total = o;
   return w;
 }
@@ -202,6 +206,13 @@ DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p) {
 }  // namespace ekv
 
 namespace {
+
+// Sets the n order keys m[i * kMaxStride] to that of -inf: the start of the
+// score step's shared maxima.
+__global__ void reset_maxima_kernel(uint32_t* m, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) m[(size_t)i * kMaxStride] = 0x007fffffu;
+}
 
 hipError_t launch_score(const LaunchShape& s, const SplitPlan& p, const float* q,
                         const void* k_pool, const int32_t* bt, const int32_t* lens,
@@ -244,6 +255,12 @@ int decode_common(const entmaxkv_shape* shape, const float* q, const void* k_poo
   const float window = window_of(alpha);
   const Events ev{events, stream};
   if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
+  if (score_mode(s, p, sparse, budget, window).share) {
+    const int bh = s.batch * s.num_q_heads;
+    hipLaunchKernelGGL(reset_maxima_kernel, dim3((unsigned)((bh + 255) / 256)), dim3(256), 0,
+                       stream, reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.gmax), bh);
+    if (hipGetLastError() != hipSuccess) return ENTMAXKV_ERR_HIP;
+  }
   if (launch_score(s, p, q, k_pool, block_table, seq_lens, sel, budget, alpha, window, ws, L,
                    stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;

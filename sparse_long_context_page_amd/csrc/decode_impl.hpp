@@ -451,17 +451,18 @@ __device__ __forceinline__ void wave_solve_list(const ZT* lz, int* li, float* sp
 }
 
 // Candidate lists of the score kernel: a wave appends the survivors of each
-// head in page order; the first kListSlots of them stay in LDS, the rest go
+// head in page order; the first `slots` of them stay in LDS, the rest go
 // to the wave's spill area in global memory (only when scores are nearly
-// uniform does a wave keep more).
+// uniform, or the window is wide, does a wave keep more).
 template <typename Acc>
 struct CandLists {
-  Acc* rz;              // LDS scores  [wave][head][kListSlots]
-  int* ri;              // LDS indices [wave][head][kListSlots]
+  Acc* rz;              // LDS scores  [wave][head][slots]
+  int* ri;              // LDS indices [wave][head][slots]
   Cand<Acc>* spill;     // this workgroup's spill areas [wave][head][wcap]
   int wcap;
+  int slots;
   __device__ __forceinline__ void put_lds(int wave, int h, int G, int pos, Acc z, int idx) const {
-    const int o = (wave * G + h) * kListSlots + pos;
+    const int o = (wave * G + h) * slots + pos;
     rz[o] = z;
     ri[o] = idx;
   }
@@ -470,27 +471,27 @@ struct CandLists {
     Cand<Acc> cv;
     cv.z = z;
     cv.idx = idx;
-    spill[(size_t)(wave * G + h) * wcap + (pos - kListSlots)] = cv;
+    spill[(size_t)(wave * G + h) * wcap + (pos - slots)] = cv;
   }
   __device__ __forceinline__ void put(int wave, int h, int G, int pos, Acc z, int idx) const {
-    if (pos < kListSlots) {
-      const int o = (wave * G + h) * kListSlots + pos;
+    if (pos < slots) {
+      const int o = (wave * G + h) * slots + pos;
       rz[o] = z;
       ri[o] = idx;
     } else {
       Cand<Acc> cv;
       cv.z = z;
       cv.idx = idx;
-      spill[(size_t)(wave * G + h) * wcap + (pos - kListSlots)] = cv;
+      spill[(size_t)(wave * G + h) * wcap + (pos - slots)] = cv;
     }
   }
   __device__ __forceinline__ void get(int wave, int h, int G, int pos, Acc& z, int& idx) const {
-    if (pos < kListSlots) {
-      const int o = (wave * G + h) * kListSlots + pos;
+    if (pos < slots) {
+      const int o = (wave * G + h) * slots + pos;
       z = rz[o];
       idx = ri[o];
     } else {
-      const Cand<Acc> cv = spill[(size_t)(wave * G + h) * wcap + (pos - kListSlots)];
+      const Cand<Acc> cv = spill[(size_t)(wave * G + h) * wcap + (pos - slots)];
       z = cv.z;
       idx = cv.idx;
     }
@@ -512,6 +513,11 @@ struct ScoreArgs {
   int* counts;
   typename KvTraits<KV>::Acc* maxima;
   Cand<typename KvTraits<KV>::Acc>* spill;
+  // full cache on the matrix cores with a wide window: each head's maximum
+  // shared by every workgroup of the call (order keys kMaxStride apart,
+  // reset to that of -inf before the launch), else null
+  uint32_t* gmax;
+  int slots;  // LDS candidate slots per (wave, head)
 };
 
 // One split of one (sequence, KV head) unit, by the whole workgroup.
@@ -538,14 +544,15 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
   };
 
   const ScoreLds lay = score_lds_layout(G, PS, pps, SPARSE, max_pages, budget, sizeof(Acc),
-                                        score_kbuf_bytes(sizeof(KV) == 2, G, PS, D, SPARSE), D);
+                                        score_kbuf_bytes(sizeof(KV) == 2, G, PS, D, SPARSE), D, args.slots);
   // The waves' running maxima per head: a static LDS array, so the compiler
   // can tell it apart from the page buffers that direct-to-LDS loads fill
   // (reads of it then need not wait for those loads).
   __shared__ Acc wmax[kNW * G];
+  __shared__ Acc wfloor[G];
   int* wcnt = reinterpret_cast<int*>(smem + lay.wcnt);
   int* slice = reinterpret_cast<int*>(smem + lay.slice);
-  int* slots = reinterpret_cast<int*>(smem + lay.slots);
+  int* slots = reinterpret_cast<int*>(smem + lay.slot);
   int* sphys = reinterpret_cast<int*>(smem + lay.phys);
   int* tmp = reinterpret_cast<int*>(smem + lay.tmp);
 
@@ -558,18 +565,24 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
                              reinterpret_cast<int*>(smem + lay.ri),
                              spill + (size_t)(b * Hkv + g) * splits * kNW * G * lay.wcap +
                                  (size_t)split * kNW * G * lay.wcap,
-                             lay.wcap};
+                             lay.wcap, lay.slots};
 
   // Matrix-core path: this thread's q values of the group, read now so that
   // their latency overlaps the slice set-up.
   constexpr int QPT = (G * D + kNT - 1) / kNT;
   float qx[QPT];
+  // and, full cache, the call's shared maxima of the group's heads (thread
+  // t < kNW * G: head t % G), the waves' starting maxima
+  uint32_t gstart = 0x007fffffu;  // the order key of -inf
   if constexpr (MFMA) {
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
       const int i = k * kNT + tid;
       qx[k] = i < G * D ? q[(size_t)bh0 * D + i] : 0.0f;
     }
+    if (!SPARSE && args.gmax && tid < kNW * G)
+      gstart = __hip_atomic_load(args.gmax + (size_t)(bh0 + tid % G) * kMaxStride, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
   }
 
   const int n_slice = build_slice<G, SPARSE>(
@@ -582,6 +595,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
   }
 
   const uint64_t ltm = lanemask_below(lane);
+  uint32_t gkey = 0u;  // full cache on the matrix cores: a shared maximum (see below)
   if constexpr (MFMA) {
     // Matrix-core scores. Each wave streams its pages into its own two LDS
     // page buffers with direct-to-LDS 16-byte loads: every load instruction
@@ -595,6 +609,14 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     // part sums for token l%16 and adds them.
     constexpr int KS = D / 32;        // k-steps of 32 dims
     constexpr int NMB = (G + 3) / 4;  // blocks of 4 heads
+    // Full cache: each head's maximum shared by every workgroup of the call
+    // (raised by each workgroup to its split's maximum when it ends, read
+    // when one starts and again before its final pass). Every value there
+    // is the score of one of the head's tokens, so at most the head's
+    // maximum: filtering against it still keeps every token within the
+    // window of that maximum, and far fewer others once earlier workgroups
+    // have seen large scores.
+    uint32_t* const gm = SPARSE ? nullptr : args.gmax;
     constexpr int TILES = PS / 16;    // 16-token tiles per page
     constexpr int RB = D * 2;         // bytes per K row
     constexpr int PB = PS * RB;       // bytes per page
@@ -614,6 +636,10 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     constexpr int QP = qtab_pitch(D);
     uint16_t* qtab = reinterpret_cast<uint16_t*>(smem + lay.qtab);
     if (tid < kNW * G) wmax[tid] = neg_inf<Acc>();  // the waves' shared running maxima
+    // the call's shared maxima at the start, a floor under the filter level
+    // (never a split maximum: those stay the maxima of the split's own
+    // tokens, which the threshold step takes as distinct token scores)
+    if (tid < G) wfloor[tid] = gm ? order_float(gstart) : neg_inf<Acc>();
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
       const int i = k * kNT + tid;
@@ -652,10 +678,15 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     const uint64_t gmask = 0xffffull << (16 * kgrp);
     Acc M[NMB];
     int mycnt[NMB];
+    // The filter level starts from the call's shared maxima (gfl, read
+    // into wfloor before the barrier above).
+    Acc gfl[NMB];
 #pragma unroll
     for (int blk = 0; blk < NMB; ++blk) {
+      const int h = blk * 4 + kgrp;
       M[blk] = neg_inf<Acc>();
       mycnt[blk] = 0;
+      gfl[blk] = h < G ? wfloor[h] : neg_inf<Acc>();
     }
     // Page pp into buffer `bsel` (an invalid physical page, or a page past
     // the slice, reads page 0 of the pool; its scores are dropped). The loads
@@ -708,7 +739,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
 #pragma unroll
         for (int w = 0; w < kNW; ++w)
           if (h < G) v = max(v, wmax[w * G + h]);
-        om[blk] = v;
+        om[blk] = max(v, gfl[blk]);
       }
       const unsigned char* src = kbuf + bsel * PB;
       Acc zz[TILES][NMB];
@@ -751,11 +782,11 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
           const uint64_t bal = __ballot(f);
           const int pos = mycnt[blk] + __popcll(bal & gmask & ltm);
           const int ix = phys * PS + t * 16 + tok;
-          if (f && pos < kListSlots) lists.put_lds(wave, h, G, pos, z, ix);
+          if (f && pos < lists.slots) lists.put_lds(wave, h, G, pos, z, ix);
           // spilled entries: one store instruction for the wave, counted
-          if (__ballot(f && pos >= kListSlots) != 0ull) {
+          if (__ballot(f && pos >= lists.slots) != 0ull) {
             ++nst;
-            if (f && pos >= kListSlots) lists.put_spill(wave, h, G, pos, z, ix);
+            if (f && pos >= lists.slots) lists.put_spill(wave, h, G, pos, z, ix);
           }
           mycnt[blk] += __popcll(bal & gmask);
         }
@@ -780,6 +811,11 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
         nst = score_page(p + kNW, 1);
         issue(p + 3 * kNW, 1);
       }
+      // the shared maxima once more, for the workgroup pass below (lane h
+      // of every wave holds head h's), waited for with the page loads
+      if (gm && lane < G)
+        gkey = __hip_atomic_load(gm + (size_t)(bh0 + lane) * kMaxStride, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
       wait_vmcnt<0>();  // no load into LDS is left in flight
     } else {
       // One buffer: short slices (the sparse path) keep more workgroups
@@ -932,11 +968,17 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
 
   // Workgroup pass: keep the candidates within the window of the workgroup
   // maximum, in (wave, page) order, as this split's region of each head.
+  const bool shared = !SPARSE && MFMA && args.gmax != nullptr;
   for (int h = wave; h < G; h += kNW) {
     Acc mg = neg_inf<Acc>();
 #pragma unroll
     for (int w = 0; w < kNW; ++w) mg = max(mg, wmax[w * G + h]);
-    const Acc thr = mg - window;
+    Acc mf = mg;  // filter level: this split's maximum or the call's, if larger
+    if (shared) {
+      const uint32_t key = lane_value(gkey, h);
+      if (key > float_order((float)mg)) mf = (Acc)order_float(key);
+    }
+    const Acc thr = mf - window;
     const size_t r = (size_t)(bh0 + h) * splits + split;
     Cand<Acc>* dst = cand + r * (size_t)cap;
     // The waves' lists, concatenated in wave order, are read kWave *
@@ -950,7 +992,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     for (int w = 0; w < kNW; ++w) {
       const int n = wcnt[w * G + h];
       nb[w + 1] = nb[w] + n;
-      nsp += max(0, n - kListSlots);
+      nsp += max(0, n - lists.slots);
     }
     const int ntot = nb[kNW];
     int o = 0;
@@ -966,17 +1008,17 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
         for (int v = 1; v < kNW; ++v) w += (t >= nb[v]) ? 1 : 0;
         const int pos = t - nb[w];
         pr[k] = pos;
-        const int lo = (w * G + h) * kListSlots + min(pos, kListSlots - 1);
+        const int lo = (w * G + h) * lists.slots + min(pos, lists.slots - 1);
         zr[k] = lists.rz[lo];
         ir[k] = lists.ri[lo];
         if (nsp > 0)  // (uniform) the spill slot, or the area's first slot
-          cs[k] = lists.spill[pos >= kListSlots
-                                  ? (size_t)(w * G + h) * lists.wcap + (pos - kListSlots)
+          cs[k] = lists.spill[pos >= lists.slots
+                                  ? (size_t)(w * G + h) * lists.wcap + (pos - lists.slots)
                                   : 0];
       }
 #pragma unroll
       for (int k = 0; k < kPassRegs; ++k) {
-        if (nsp > 0 && pr[k] >= kListSlots) {
+        if (nsp > 0 && pr[k] >= lists.slots) {
           zr[k] = cs[k].z;
           ir[k] = cs[k].idx;
         }
@@ -992,6 +1034,11 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
       }
     }
     if (lane == 0) put_count(r, o, mg);
+    // raise the call's shared maximum of the head to this split's, last
+    // (nothing waits for the atomic: later workgroups see it when it lands)
+    if (shared && lane == 0 && mg > neg_inf<Acc>())
+      __hip_atomic_fetch_max(args.gmax + (size_t)(bh0 + h) * kMaxStride, float_order((float)mg),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1578,6 +1625,9 @@ ScoreArgs<KV> score_args(const LaunchShape& s, const SplitPlan& p, const float* 
   a.counts = reinterpret_cast<int*>(w + L.counts);
   a.maxima = reinterpret_cast<ZT*>(w + L.maxima);
   a.spill = reinterpret_cast<Cand<ZT>*>(w + L.spill);
+  const ScoreMode mode = score_mode(s, p, sel != nullptr, budget, window);
+  a.gmax = mode.share ? reinterpret_cast<uint32_t*>(w + L.gmax) : nullptr;
+  a.slots = mode.slots;
   return a;
 }
 
@@ -1589,7 +1639,8 @@ hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float*
   using ZT = typename KvTraits<KV>::Acc;
   const int U = s.batch * s.num_kv_heads;
   const ScoreLds lay = score_lds_layout(G, PS, p.pages_per_split, SPARSE, s.max_pages, budget,
-                                        sizeof(ZT), score_kbuf_bytes(s.bf16, G, PS, D, SPARSE), D);
+                                        sizeof(ZT), score_kbuf_bytes(s.bf16, G, PS, D, SPARSE), D,
+                                        score_mode(s, p, SPARSE, budget, window).slots);
   auto kern = score_kernel<KV, D, G, PS, SPARSE>;
   // The LDS limit is a kernel attribute: raised once, to the most any plan
   // asks for (a function-local static is initialised exactly once, also when

@@ -45,13 +45,28 @@ constexpr int kSelCopy = 8192;  // selection ints staged in LDS by the sparse sc
 
 
 constexpr int kListSlots = 64;  // LDS candidate slots per (wave, head) in the score kernel
+// Full cache with a window of at least kWideWindow score units (alpha of
+// 4/3 or less): on flat scores about a tenth of a split's tokens survive a
+// workgroup's own running maximum. The lists then get kListSlotsWide slots
+// where that keeps as many workgroups on a CU, and where at least
+// kShareMinWgs workgroups share a CU (enough to hide two more memory round
+// trips per workgroup) and the grid takes two or more rounds of them (so
+// that later workgroups start from earlier ones' maxima) each head's
+// maximum is shared across the call's workgroups, one entry per kMaxStride
+// words (its own 128-byte line).
+constexpr int kListSlotsWide = 128;
+constexpr float kWideWindow = 3.0f;
+constexpr int kMaxStride = 32;
+constexpr int kShareMinWgs = 3;
+constexpr size_t kLdsPerCU = 160 * 1024;
 constexpr int kPassRegs = 4;    // candidates per lane read at once by the score kernel's final pass
 constexpr size_t kMaxScoreLdsBytes = 150 * 1024;  // most LDS a score-kernel plan may use
 
 // LDS layout of the score kernel (bytes), shared by host sizing and device carving.
 struct ScoreLds {
   int wcap;  // candidates one wave can produce per head: every token of its pages
-  size_t kbuf, qtab, rz, ri, wcnt, slice, slots, phys, tmp, bitmap, ssel, total;
+  int slots;  // LDS candidate slots per (wave, head)
+  size_t kbuf, qtab, rz, ri, wcnt, slice, slot, phys, tmp, bitmap, ssel, total;
 };
 
 // Row pitch (bf16 values) of the split-q table of the matrix-core kernels:
@@ -82,19 +97,24 @@ __host__ __device__ inline int score_kbuf_bytes(bool bf16, int G, int ps, int he
 // kbuf_wave: score_kbuf_bytes (the matrix-core path when > 0).
 __host__ __device__ inline ScoreLds score_lds_layout(int G, int ps, int pps, bool sparse,
                                                      int max_pages, int budget, int zbytes,
-                                                     int kbuf_wave, int head_dim) {
+                                                     int kbuf_wave, int head_dim,
+                                                     int slots = kListSlots) {
   ScoreLds l;
   l.wcap = ((pps + kNW - 1) / kNW) * ps;
+  l.slots = slots;
   size_t o = 0;
   l.kbuf = o; o = align16(o + (size_t)kNW * kbuf_wave);
   l.qtab = o;
   if (kbuf_wave > 0) o = align16(o + (size_t)G * 3 * qtab_pitch(head_dim) * 2);
-  const size_t nreg = (size_t)kNW * G * kListSlots;
+  const size_t nreg = (size_t)kNW * G * slots;
   l.rz = o; o = align16(o + nreg * zbytes);
   l.ri = o; o = align16(o + nreg * 4);
   l.wcnt = o; o = align16(o + (size_t)kNW * G * 4);
-  l.slice = o; o = align16(o + (size_t)pps * 4);
-  l.slots = o; o = align16(o + (size_t)pps * G * 4);
+  // the page slice and per-head slots exist on the sparse path only
+  l.slice = o;
+  if (sparse) o = align16(o + (size_t)pps * 4);
+  l.slot = o;
+  if (sparse) o = align16(o + (size_t)pps * G * 4);
   l.phys = o; o = align16(o + (size_t)pps * 4);
   l.tmp = o; o = align16(o + (kNW + 2) * 4);
   l.bitmap = o;
@@ -122,12 +142,38 @@ SplitPlan plan_full(const LaunchShape& s);
 
 // Workspace carve-up of the decode calls (byte offsets, 256-aligned).
 struct DecodeWs {
-  size_t cand, counts, maxima, list, spill, total;
+  size_t cand, counts, maxima, list, spill, gmax, total;
 };
 // Scores are kept in the accumulation precision: float for bf16 caches,
 // double for float32 caches. A candidate is (score, token index).
 __host__ __device__ inline int score_bytes(bool bf16) { return bf16 ? 4 : 8; }
 __host__ __device__ inline int cand_bytes(bool bf16) { return bf16 ? 8 : 16; }
+// Candidate-list slots per (wave, head) of a score launch, and whether it
+// shares each head's maximum across its workgroups (the decode then resets
+// the workspace's per-head maxima before the launch); see kWideWindow.
+struct ScoreMode {
+  int slots = kListSlots;
+  bool share = false;
+};
+inline ScoreMode score_mode(const LaunchShape& s, const SplitPlan& p, bool sparse, int budget,
+                            float window) {
+  ScoreMode m;
+  if (sparse || window < kWideWindow || !(s.bf16 && kMfmaScores)) return m;
+  auto lds = [&](int slots) {
+    return score_lds_layout(s.group, s.page_size, p.pages_per_split, sparse, s.max_pages, budget,
+                            score_bytes(s.bf16),
+                            score_kbuf_bytes(s.bf16, s.group, s.page_size, s.head_dim, sparse),
+                            s.head_dim, slots)
+        .total;
+  };
+  const size_t narrow = lds(kListSlots), wide = lds(kListSlotsWide);
+  if (wide <= kMaxScoreLdsBytes && kLdsPerCU / wide == kLdsPerCU / narrow)
+    m.slots = kListSlotsWide;
+  const long long per_cu = (long long)(kLdsPerCU / lds(m.slots));
+  const long long grid = (long long)s.batch * s.num_kv_heads * p.splits;
+  m.share = per_cu >= kShareMinWgs && grid >= 2 * per_cu * kNumCUs;
+  return m;
+}
 DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p);
 // Row stride (floats) of the per-head page bounds in the select workspace:
 // padded to a multiple of 4 so every row starts 16-byte aligned.
