@@ -36,6 +36,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 #include "launch.hpp"
 #include "mfma.hpp"
 
@@ -274,37 +276,72 @@ __device__ __forceinline__ double pow_m(double d, double m, int mcode) {
   return d * pow_m1(d, m, mcode);
 }
 
-// pow_m1 / pow_m for a caller that only sees integer m (mcode 1..4): no call
-// to pow_general, so a caller holding many values in registers spills none
-// around it.
-template <bool GEN>
+// The exponent of the threshold equation as a compile-time value: MC = m for
+// the integer m = 1..4 (alpha = 2, 3/2, 4/3, 5/4), MC = 0 for any other m
+// (taken at run time through pow_m1). With MC > 0 the Newton sums below are
+// branch-free: no call to pow_general (a caller holding many values in
+// registers spills none around it) and no per-term branch on mcode or on
+// the sign of d.
+template <int MC>
 __device__ __forceinline__ double pow_m1_t(double d, double m, int mcode) {
-  if constexpr (GEN) {
+  if constexpr (MC == 0) {
     return pow_m1(d, m, mcode);
   } else {
     (void)m;
-    return mcode == 1 ? 1.0 : (mcode == 2 ? d : (mcode == 3 ? d * d : d * d * d));
+    (void)mcode;
+    if constexpr (MC == 1) return 1.0;
+    else if constexpr (MC == 2) return d;
+    else if constexpr (MC == 3) return d * d;
+    else return d * d * d;
+  }
+}
+
+// Adds [d]_+^(m-1) to fp and [d]_+^m to f: the terms of f(t) = sum [a_i -
+// t]_+^m and of f'(t) / -m, the same values (and so the same sums) whether
+// a term is skipped or added as zero.
+template <int MC>
+__device__ __forceinline__ void add_terms(double d, double m, int mcode, double& f, double& fp) {
+  if constexpr (MC == 0) {
+    if (d > 0.0) {
+      const double pm1 = pow_m1(d, m, mcode);
+      fp += pm1;
+      f += pm1 * d;
+    }
+  } else {
+    const double dd = fmax(d, 0.0);
+    const double pm1 = MC == 1 ? (d > 0.0 ? 1.0 : 0.0) : pow_m1_t<MC>(dd, m, mcode);
+    fp += pm1;
+    f += pm1 * dd;
+  }
+}
+
+// Calls fn(std::integral_constant<int, MC>) with MC = mcode for mcode 1..4,
+// else MC = 0 (INT_ONLY: the caller has checked that m is an integer 1..4,
+// and only those four are instantiated).
+template <bool INT_ONLY = false, typename Fn>
+__device__ __forceinline__ auto with_mcode(int mcode, Fn fn) {
+  switch (mcode) {
+    case 1: return fn(std::integral_constant<int, 1>());
+    case 2: return fn(std::integral_constant<int, 2>());
+    case 3: return fn(std::integral_constant<int, 3>());
+    default:
+      if constexpr (INT_ONLY) return fn(std::integral_constant<int, 4>());
+      else if (mcode == 4) return fn(std::integral_constant<int, 4>());
+      else return fn(std::integral_constant<int, 0>());
   }
 }
 
 // The same safeguarded Newton iteration for the whole workgroup, each thread
 // holding K of the a_i in registers (-DBL_MAX marks an empty slot); every
 // thread of the block must call it and gets the same result.
-template <int K>
+template <int K, int MC>
 __device__ double solve_tau_block(const double (&a)[K], double m, int mcode, double amax,
                                   double* red) {
   double lo = amax - 1.0, hi = amax, t = lo;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fp = 0.0;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const double d = a[k] - t;
-      if (d > 0.0) {
-        const double pm1 = pow_m1(d, m, mcode);
-        fp += pm1;
-        f += pm1 * d;
-      }
-    }
+    for (int k = 0; k < K; ++k) add_terms<MC>(a[k] - t, m, mcode, f, fp);
     scope_sum2<kNT>(f, fp, red);
     fp *= m;
     if (f >= 1.0) lo = t;
@@ -329,7 +366,7 @@ __device__ double solve_tau_block(const double (&a)[K], double m, int mcode, dou
 // The safeguarded Newton iteration of solve_tau for one wave whose lanes
 // hold the list's a_i = am1 * z_i in registers (K per lane; -DBL_MAX marks an
 // empty slot), so an iteration reads no memory. Same steps and stopping rules.
-template <int K, bool GEN = true>
+template <int K, int MC>
 __device__ double solve_tau_regs(const double (&a)[K], double am1, double m, int mcode,
                                  double amax) {
   (void)am1;
@@ -337,14 +374,7 @@ __device__ double solve_tau_regs(const double (&a)[K], double am1, double m, int
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fp = 0.0;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const double d = a[k] - t;
-      if (d > 0.0) {
-        const double pm1 = pow_m1_t<GEN>(d, m, mcode);
-        fp += pm1;
-        f += pm1 * d;
-      }
-    }
+    for (int k = 0; k < K; ++k) add_terms<MC>(a[k] - t, m, mcode, f, fp);
     f = wave_allsum(f);
     fp = wave_allsum(fp) * m;
     if (f >= 1.0) lo = t;
@@ -413,7 +443,7 @@ __device__ double solve_tau_ranked(double a, int n, int mcode, double amax) {
 // size, the wave's sum of p and tau (every lane). Lists of up to 64 entries
 // at m = 1, 2 take the rank-based closed form. Without `compact` li and sp
 // are left as they are: other waves may still be reading li.
-template <int K, bool GEN, typename ZT>
+template <int K, int MC, typename ZT>
 __device__ __forceinline__ void wave_solve_list(const ZT* lz, int* li, float* sp, int n_list, double am1, double m,
                                 int mcode, double amax, int lane, uint64_t ltm, bool compact,
                                 int& n_sup, double& psum, double& tau) {
@@ -425,7 +455,7 @@ __device__ __forceinline__ void wave_solve_list(const ZT* lz, int* li, float* sp
   }
   const double t = (n_list <= kWave && (mcode == 1 || mcode == 2))
                        ? solve_tau_ranked(a[0], n_list, mcode, amax)
-                       : solve_tau_regs<K, GEN>(a, am1, m, mcode, amax);
+                       : solve_tau_regs<K, MC>(a, am1, m, mcode, amax);
   int o = 0;
   double ps = 0.0;
 #pragma unroll
@@ -436,7 +466,7 @@ __device__ __forceinline__ void wave_solve_list(const ZT* lz, int* li, float* sp
     const int ix = (f && compact) ? li[e] : 0;
     const uint64_t bal = __ballot(f);
     if (f) {
-      const double pv = d * pow_m1_t<GEN>(d, m, mcode);
+      const double pv = d * pow_m1_t<MC>(d, m, mcode);
       ps += pv;
       if (compact) {
         li[o + __popcll(bal & ltm)] = ix;
@@ -1197,7 +1227,9 @@ __device__ __attribute__((noinline)) ZT tau_window_bound(ZT mloc, double* rmax, 
     double a[kRegList];
 #pragma unroll
     for (int k = 0; k < kRegList; ++k) a[k] = rmax[k * kWave + lane];
-    const double ts = solve_tau_regs<kRegList>(a, am1, m, mcode, amax);
+    const double ts = with_mcode(mcode, [&](auto mc) {
+      return solve_tau_regs<kRegList, decltype(mc)::value>(a, am1, m, mcode, amax);
+    });
     if (lane == 0) *tau_b = ts;
   }
   __syncthreads();
@@ -1226,7 +1258,9 @@ __device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int
   double a[KB];
 #pragma unroll
   for (int k = 0; k < KB; ++k) a[k] = (e0 + k < e1) ? am1 * (double)lz[e0 + k] : -DBL_MAX;
-  const double tau = solve_tau_block<KB>(a, m, mcode, amax, red);
+  const double tau = with_mcode(mcode, [&](auto mc) {
+    return solve_tau_block<KB, decltype(mc)::value>(a, m, mcode, amax, red);
+  });
   int ns = 0;
 #pragma unroll
   for (int k = 0; k < KB; ++k) ns += (a[k] - tau > 0.0) ? 1 : 0;
@@ -1485,8 +1519,10 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
       // With the V rows requested up front the P.V step weights them from
       // lz, and the other waves' reads of li may still be in flight, so the
       // support is not compacted into li.
-      wave_solve_list<kRegList, true>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm, !vpre,
-                                      o, psum, t);
+      with_mcode(mcode, [&](auto mc) {
+        wave_solve_list<kRegList, decltype(mc)::value>(lz, li, sp, n_list, am1, m, mcode, amax,
+                                                       lane, ltm, !vpre, o, psum, t);
+      });
       if (lane == 0) {
         nb[1] = o;
         red[0] = psum;
@@ -1503,8 +1539,10 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
     if (wave == 0) {
       int o;
       double t;
-      wave_solve_list<kRegListLong, false>(lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm,
-                                           true, o, psum, t);
+      with_mcode<true>(mcode, [&](auto mc) {
+        wave_solve_list<kRegListLong, decltype(mc)::value>(lz, li, sp, n_list, am1, m, mcode,
+                                                           amax, lane, ltm, true, o, psum, t);
+      });
       if (lane == 0) {
         nb[1] = o;
         red[0] = psum;
