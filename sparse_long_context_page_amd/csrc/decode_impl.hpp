@@ -332,16 +332,18 @@ __device__ __forceinline__ auto with_mcode(int mcode, Fn fn) {
 }
 
 // The same safeguarded Newton iteration for the whole workgroup, each thread
-// holding K of the a_i in registers (-DBL_MAX marks an empty slot); every
-// thread of the block must call it and gets the same result.
+// holding K of the a_i in registers (-DBL_MAX marks an empty slot), of
+// which only the first `used` (uniform) can be occupied; every thread of the
+// block must call it and gets the same result.
 template <int K, int MC>
-__device__ double solve_tau_block(const double (&a)[K], double m, int mcode, double amax,
-                                  double* red) {
+__device__ double solve_tau_block(const double (&a)[K], int used, double m, int mcode,
+                                  double amax, double* red) {
   double lo = amax - 1.0, hi = amax, t = lo;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fp = 0.0;
 #pragma unroll
-    for (int k = 0; k < K; ++k) add_terms<MC>(a[k] - t, m, mcode, f, fp);
+    for (int k = 0; k < K; ++k)
+      if (k < used) add_terms<MC>(a[k] - t, m, mcode, f, fp);
     scope_sum2<kNT>(f, fp, red);
     fp *= m;
     if (f >= 1.0) lo = t;
@@ -364,17 +366,20 @@ __device__ double solve_tau_block(const double (&a)[K], double m, int mcode, dou
 }
 
 // The safeguarded Newton iteration of solve_tau for one wave whose lanes
-// hold the list's a_i = am1 * z_i in registers (K per lane; -DBL_MAX marks an
-// empty slot), so an iteration reads no memory. Same steps and stopping rules.
+// hold the list's a_i = am1 * z_i in registers (K per lane, entry e in slot
+// e / 64 of lane e % 64; -DBL_MAX marks an empty slot), so an iteration reads
+// no memory; only the slots below n (uniform) entries are summed. Same steps
+// and stopping rules.
 template <int K, int MC>
-__device__ double solve_tau_regs(const double (&a)[K], double am1, double m, int mcode,
+__device__ double solve_tau_regs(const double (&a)[K], int n, double am1, double m, int mcode,
                                  double amax) {
   (void)am1;
   double lo = amax - 1.0, hi = amax, t = lo;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fp = 0.0;
 #pragma unroll
-    for (int k = 0; k < K; ++k) add_terms<MC>(a[k] - t, m, mcode, f, fp);
+    for (int k = 0; k < K; ++k)
+      if (k * kWave < n) add_terms<MC>(a[k] - t, m, mcode, f, fp);
     f = wave_allsum(f);
     fp = wave_allsum(fp) * m;
     if (f >= 1.0) lo = t;
@@ -455,7 +460,7 @@ __device__ __forceinline__ void wave_solve_list(const ZT* lz, int* li, float* sp
   }
   const double t = (n_list <= kWave && (mcode == 1 || mcode == 2))
                        ? solve_tau_ranked(a[0], n_list, mcode, amax)
-                       : solve_tau_regs<K, MC>(a, am1, m, mcode, amax);
+                       : solve_tau_regs<K, MC>(a, n_list, am1, m, mcode, amax);
   int o = 0;
   double ps = 0.0;
 #pragma unroll
@@ -1228,7 +1233,8 @@ __device__ __attribute__((noinline)) ZT tau_window_bound(ZT mloc, double* rmax, 
 #pragma unroll
     for (int k = 0; k < kRegList; ++k) a[k] = rmax[k * kWave + lane];
     const double ts = with_mcode(mcode, [&](auto mc) {
-      return solve_tau_regs<kRegList, decltype(mc)::value>(a, am1, m, mcode, amax);
+      return solve_tau_regs<kRegList, decltype(mc)::value>(a, kRegList * kWave, am1, m, mcode,
+                                                           amax);
     });
     if (lane == 0) *tau_b = ts;
   }
@@ -1259,7 +1265,7 @@ __device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int
 #pragma unroll
   for (int k = 0; k < KB; ++k) a[k] = (e0 + k < e1) ? am1 * (double)lz[e0 + k] : -DBL_MAX;
   const double tau = with_mcode(mcode, [&](auto mc) {
-    return solve_tau_block<KB, decltype(mc)::value>(a, m, mcode, amax, red);
+    return solve_tau_block<KB, decltype(mc)::value>(a, per, m, mcode, amax, red);
   });
   int ns = 0;
 #pragma unroll
