@@ -107,7 +107,8 @@ enum {
   ENTMAXKV_WS_SELECT = 0,
   ENTMAXKV_WS_SPARSE = 1,
   ENTMAXKV_WS_FULL = 2,
-  ENTMAXKV_WS_GAUSS = 3
+  ENTMAXKV_WS_GAUSS = 3,
+  ENTMAXKV_WS_TOPK = 4
 };
 
 /*
@@ -273,6 +274,36 @@ int entmaxkv_decode_sparse(const entmaxkv_shape* shape, const float* q, const vo
                            const int32_t* seq_lens, const int32_t* sel, int32_t budget_pages,
                            float alpha, float* out, float* tau, int32_t* support, void* ws,
                            size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
+
+/*
+ * Page bounds, top-k selection and sparse decode in one call ([EntmaxKV page]
+ * sections 2.A, 2.B policy 1 and 2.C): the same results as
+ * entmaxkv_score_select (sel, sel_ub) followed by entmaxkv_decode_sparse on
+ * that selection (out, tau, support; every score and sum computed the same
+ * way, so equal up to the order of the threshold solve's float64 sums).
+ * sel is required; sel_ub, tau and support are nullable.
+ * With bf16 caches, at least 128 query heads in the batch (batch *
+ * num_q_heads) and budget_pages <= 1024, it runs two kernels: the bounds,
+ * then one workgroup per query head that selects the head's pages, gathers
+ * and scores them, solves tau and writes the output (no candidate crosses a
+ * workgroup). Otherwise the four kernels of the two calls run.
+ * Workspace: entmaxkv_workspace_bytes(..., ENTMAXKV_WS_TOPK) for the same
+ * budget_pages. events (nullable): 2*4 handles; pairs 0 and 1 enclose the
+ * bounds and the select (or the per-head kernel), pairs 2 and 3 the sparse
+ * decode's two kernels (empty intervals on the per-head path).
+ */
+int entmaxkv_decode_topk(const entmaxkv_shape* shape, const float* q, const void* meta,
+                         const void* k_pool, const void* v_pool, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t budget_pages, float alpha,
+                         int32_t* sel, float* sel_ub, float* out, float* tau, int32_t* support,
+                         void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
+
+/*
+ * Number of kernels entmaxkv_decode_topk launches at this shape and budget:
+ * 2 on the per-head path, 4 otherwise. Writes *kernels; returns an error
+ * code for an invalid or unsupported shape or budget.
+ */
+int entmaxkv_topk_kernels(const entmaxkv_shape* shape, int32_t budget_pages, int32_t* kernels);
 
 /*
  * Full-cache alpha-entmax decode ([EntmaxKV page] section 4, the full-cache

@@ -272,6 +272,30 @@ int decode_common(const entmaxkv_shape* shape, const float* q, const void* k_poo
   return ENTMAXKV_OK;
 }
 
+// Workspace of entmaxkv_decode_topk: the per-head path (bounds, then the
+// per-head kernel's spill areas and lists), or the select workspace followed
+// by the sparse decode's.
+struct TopkWs {
+  HeadPlan head;
+  SplitPlan split;
+  DecodeWs dec;
+  size_t dec_off = 0, total = 0;
+};
+int topk_ws(const LaunchShape& s, int budget, TopkWs* w) {
+  const size_t sel_bytes = align256(select_ws_bytes(s, budget));
+  w->head = plan_head(s, budget, sel_bytes);
+  if (w->head.use) {
+    w->total = w->head.total;
+    return ENTMAXKV_OK;
+  }
+  w->split = plan_sparse(s, budget);
+  if (int rc = score_lds_ok(s, w->split, true, budget)) return rc;
+  w->dec = decode_ws_layout(s, w->split);
+  w->dec_off = sel_bytes;
+  w->total = sel_bytes + w->dec.total;
+  return ENTMAXKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -317,6 +341,13 @@ int entmaxkv_workspace_bytes(const entmaxkv_shape* shape, int32_t budget_pages, 
       if ((rc = check_budget(budget_pages))) return rc;
       *bytes = align256(gauss_ws_bytes(s));
       return ENTMAXKV_OK;
+    case ENTMAXKV_WS_TOPK: {
+      if ((rc = check_budget(budget_pages))) return rc;
+      TopkWs w;
+      if ((rc = topk_ws(s, budget_pages, &w))) return rc;
+      *bytes = w.total;
+      return ENTMAXKV_OK;
+    }
     default:
       return ENTMAXKV_ERR_INVALID;
   }
@@ -492,6 +523,63 @@ int entmaxkv_decode_sparse(const entmaxkv_shape* shape, const float* q, const vo
   if (!sel) return ENTMAXKV_ERR_INVALID;
   return decode_common(shape, q, k_pool, v_pool, block_table, seq_lens, sel, budget_pages, alpha,
                        out, tau, support, ws, ws_bytes, stream, events);
+}
+
+int entmaxkv_decode_topk(const entmaxkv_shape* shape, const float* q, const void* meta,
+                         const void* k_pool, const void* v_pool, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t budget_pages, float alpha,
+                         int32_t* sel, float* sel_ub, float* out, float* tau, int32_t* support,
+                         void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  if ((rc = check_budget(budget_pages))) return rc;
+  if ((rc = check_alpha(alpha))) return rc;
+  if (!q || !meta || !k_pool || !v_pool || !block_table || !seq_lens || !sel || !out)
+    return ENTMAXKV_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(meta, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return ENTMAXKV_ERR_INVALID;
+  TopkWs w;
+  if ((rc = topk_ws(s, budget_pages, &w))) return rc;
+  if (!ws || ws_bytes < w.total) return ENTMAXKV_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return ENTMAXKV_ERR_INVALID;
+  float* ub = static_cast<float*>(ws);
+  const SelectPlan sp = plan_select(s, budget_pages);
+  const float window = window_of(alpha);
+  const Events ev{events, stream};
+  if (!ev.before(0)) return ENTMAXKV_ERR_HIP;
+  if (launch_bounds(s, sp, q, meta, block_table, seq_lens, ub, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
+  if (w.head.use) {
+    const bool bt_lds = s.max_pages % 4 == 0 && aligned(block_table, 16);
+    if (launch_head_decode(s, sp, w.head, q, k_pool, v_pool, block_table, seq_lens, budget_pages,
+                           alpha, window, sel, sel_ub, out, tau, support, ws, bt_lds,
+                           stream) != hipSuccess)
+      return ENTMAXKV_ERR_HIP;
+    // pairs 2 and 3 enclose nothing on this path
+    if (!ev.after(1) || !ev.before(2) || !ev.after(2) || !ev.before(3) || !ev.after(3))
+      return ENTMAXKV_ERR_HIP;
+    return ENTMAXKV_OK;
+  }
+  if (launch_select(s, sp, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
+    return ENTMAXKV_ERR_HIP;
+  if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
+  return decode_common(shape, q, k_pool, v_pool, block_table, seq_lens, sel, budget_pages, alpha,
+                       out, tau, support, static_cast<char*>(ws) + w.dec_off,
+                       ws_bytes - w.dec_off, stream, events ? events + 4 : nullptr);
+}
+
+int entmaxkv_topk_kernels(const entmaxkv_shape* shape, int32_t budget_pages, int32_t* kernels) {
+  LaunchShape s;
+  int rc = check_shape(shape, &s);
+  if (rc) return rc;
+  if ((rc = check_budget(budget_pages))) return rc;
+  if (!kernels) return ENTMAXKV_ERR_INVALID;
+  TopkWs w;
+  if ((rc = topk_ws(s, budget_pages, &w))) return rc;
+  *kernels = w.head.use ? 2 : 4;
+  return ENTMAXKV_OK;
 }
 
 int entmaxkv_decode_full(const entmaxkv_shape* shape, const float* q, const void* k_pool,

@@ -335,7 +335,7 @@ __device__ __forceinline__ auto with_mcode(int mcode, Fn fn) {
 // holding K of the a_i in registers (-DBL_MAX marks an empty slot), of
 // which only the first `used` (uniform) can be occupied; every thread of the
 // block must call it and gets the same result.
-template <int K, int MC>
+template <int K, int MC, int NT>
 __device__ double solve_tau_block(const double (&a)[K], int used, double m, int mcode,
                                   double amax, double* red) {
   double lo = amax - 1.0, hi = amax, t = lo;
@@ -344,7 +344,7 @@ __device__ double solve_tau_block(const double (&a)[K], int used, double m, int 
 #pragma unroll
     for (int k = 0; k < K; ++k)
       if (k < used) add_terms<MC>(a[k] - t, m, mcode, f, fp);
-    scope_sum2<kNT>(f, fp, red);
+    scope_sum2<NT>(f, fp, red);
     fp *= m;
     if (f >= 1.0) lo = t;
     else hi = t;
@@ -1247,7 +1247,7 @@ __device__ __attribute__((noinline)) ZT tau_window_bound(ZT mloc, double* rmax, 
 // entries [t*per, t*per + per) (per <= KB) in registers for the whole solve,
 // and one block scan compacts the support's (V row, p) to the front of
 // (li, sp) in list order. Every thread of the workgroup calls it.
-template <typename ZT, int KB>
+template <typename ZT, int KB, int NT>
 __device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int* li, float* sp,
                                                                int n_list, double am1, double m,
                                                                int mcode, double amax, double* red,
@@ -1259,13 +1259,13 @@ __device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int
   red = lds_view(red);
   tmp = lds_view(tmp);
   TauSolution r;
-  const int per = (n_list + kNT - 1) / kNT;
+  const int per = (n_list + NT - 1) / NT;
   const int e0 = min(n_list, tid * per), e1 = min(n_list, e0 + per);
   double a[KB];
 #pragma unroll
   for (int k = 0; k < KB; ++k) a[k] = (e0 + k < e1) ? am1 * (double)lz[e0 + k] : -DBL_MAX;
   const double tau = with_mcode(mcode, [&](auto mc) {
-    return solve_tau_block<KB, decltype(mc)::value>(a, per, m, mcode, amax, red);
+    return solve_tau_block<KB, decltype(mc)::value, NT>(a, per, m, mcode, amax, red);
   });
   int ns = 0;
 #pragma unroll
@@ -1273,7 +1273,7 @@ __device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int
   int ix[KB];
 #pragma unroll
   for (int k = 0; k < KB; ++k) ix[k] = (e0 + k < e1) ? li[e0 + k] : 0;
-  int base = block_excl_scan<kNT>(ns, tmp, &r.n_sup);  // (its barriers order the reads above)
+  int base = block_excl_scan<NT>(ns, tmp, &r.n_sup);  // (its barriers order the reads above)
   double psum = 0.0;
 #pragma unroll
   for (int k = 0; k < KB; ++k) {
@@ -1287,7 +1287,7 @@ __device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int
     }
   }
   double zero = 0.0;
-  scope_sum2<kNT>(psum, zero, red);
+  scope_sum2<NT>(psum, zero, red);
   r.tau = tau;
   r.psum = psum;
   return r;
@@ -1295,17 +1295,17 @@ __device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int
 
 // A window list in global memory (longer than the LDS capacity): the
 // block-wide Newton solve over it, the support size and the sum of p.
-template <typename ZT>
+template <typename ZT, int NT>
 __device__ __attribute__((noinline)) TauSolution tau_global_list(const ZT* dz, int n_list,
                                                                  double am1, double m, int mcode,
                                                                  double amax, double* red) {
   const int tid = threadIdx.x;
   red = lds_view(red);
   TauSolution r;
-  r.tau = solve_tau<kNT>(dz, n_list, am1, m, mcode, amax, tid, red);
+  r.tau = solve_tau<NT>(dz, n_list, am1, m, mcode, amax, tid, red);
   int ns = 0;
   double psum = 0.0;
-  for (int i = tid; i < n_list; i += kNT) {
+  for (int i = tid; i < n_list; i += NT) {
     const double d = am1 * (double)dz[i] - r.tau;
     if (d > 0.0) {
       ++ns;
@@ -1313,7 +1313,7 @@ __device__ __attribute__((noinline)) TauSolution tau_global_list(const ZT* dz, i
     }
   }
   double nsd = (double)ns;
-  scope_sum2<kNT>(psum, nsd, red);
+  scope_sum2<NT>(psum, nsd, red);
   r.psum = psum;
   r.n_sup = (int)nsd;
   return r;
@@ -1322,7 +1322,7 @@ __device__ __attribute__((noinline)) TauSolution tau_global_list(const ZT* dz, i
 // P.V over a global-memory window list: thread (grp, c) accumulates the
 // weighted 16-byte slice c of every grp-th support row and writes its partial
 // sums to prow.
-template <typename KV, int D>
+template <typename KV, int D, int NT>
 __device__ __attribute__((noinline)) void pv_global_list(const KV* v_pool, int Hkv, int g, int PS,
                                                          const typename KvTraits<KV>::Acc* dz,
                                                          const int* di, int n_list, double am1,
@@ -1330,7 +1330,7 @@ __device__ __attribute__((noinline)) void pv_global_list(const KV* v_pool, int H
                                                          float* prow) {
   constexpr int VPC = 16 / sizeof(KV);
   constexpr int LR = D / VPC;
-  constexpr int NG = kNT / LR;
+  constexpr int NG = NT / LR;
   const int grp = threadIdx.x / LR, c = threadIdx.x % LR;
   float acc[VPC];
 #pragma unroll
@@ -1354,132 +1354,42 @@ __device__ __attribute__((noinline)) void pv_global_list(const KV* v_pool, int H
   for (int e = 0; e < VPC; ++e) prow[e] = acc[e];
 }
 
-template <typename KV>
-struct TauArgs {
-  const KV* v_pool;
-  int H, Hkv, G, U, PS, splits, cap, list_cap, lcap;
-  float alpha;
-  double window_d;
-  const Cand<typename KvTraits<KV>::Acc>* cand;
-  const int* counts;
-  const typename KvTraits<KV>::Acc* maxima;
-  typename KvTraits<KV>::Acc* list_z;
-  int* list_i;
-  float* out;
-  float* tau_out;
-  int32_t* sup_out;
+// The window list's threshold, support and output for one head, by a
+// workgroup of NT threads (every thread calls it, after a barrier that
+// orders the list's writes): the list is (lz, li) in LDS, n_list entries
+// (score, V row); when n_list > lcap the first lcap entries are in LDS and
+// the rest already in (gz, gi) at the same positions, and the whole list
+// moves there. Solves tau (one wave in registers for up to 256 entries, or
+// 1024 at integer m; the workgroup beyond), then o = sum p v / sum p from
+// the support's V rows, written to out_row[0, D); tau and the support size
+// to *tau_p and *sup_p when not null. pvbase: NT / (D / VPC) rows of D
+// floats of LDS.
+template <int NT>
+struct TauShared {
+  double red[2 * (NT / kWave)];
+  int tmp[NT / kWave + 2];
+  double tau_b;
+  int nb[2];
 };
-
-// One query head (unit u, head hh of its group), by the whole workgroup.
-template <typename KV, int D>
-__device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh, unsigned char* smem) {
+template <typename KV, int D, int NT>
+__device__ __forceinline__ void tau_solve_pv(
+    const KV* __restrict__ v_pool, int Hkv, int g, int PS, typename KvTraits<KV>::Acc* lz,
+    int* li, float* sp, float* pvbase, int n_list, int lcap, typename KvTraits<KV>::Acc* gz,
+    int* gi, double am1, double m, int mcode, double amax, TauShared<NT>& sh,
+    float* __restrict__ out_row, float* tau_p, int32_t* sup_p) {
   using ZT = typename KvTraits<KV>::Acc;
-  const KV* __restrict__ v_pool = args.v_pool;
-  const int H = args.H, Hkv = args.Hkv, G = args.G, PS = args.PS, splits = args.splits;
-  const int cap = args.cap, list_cap = args.list_cap, lcap = args.lcap;
-  const float alpha = args.alpha;
-  const Cand<ZT>* __restrict__ cand = args.cand;
-  const int* __restrict__ counts = args.counts;
-  const ZT* __restrict__ maxima = args.maxima;
-  ZT* __restrict__ list_z = args.list_z;
-  int* __restrict__ list_i = args.list_i;
-  float* __restrict__ out = args.out;
-  float* __restrict__ tau_out = args.tau_out;
-  int32_t* __restrict__ sup_out = args.sup_out;
-  const ZT window = (ZT)args.window_d;
   constexpr int VPC = 16 / sizeof(KV);
   constexpr int LR = D / VPC;     // lanes per V row
-  constexpr int NG = kNT / LR;    // rows in flight per pass
-  constexpr int KB = kTauMaxList / kNT;  // most list entries per thread in block-wide steps
-  const TauLds lay = tau_lds_layout(splits, lcap, sizeof(ZT), NG, D);
-  int* roff = reinterpret_cast<int*>(smem);  // region offsets
-  ZT* lz = reinterpret_cast<ZT*>(smem + lay.lz);
-  int* li = reinterpret_cast<int*>(smem + lay.li);
-  float* sp = reinterpret_cast<float*>(smem + lay.sp);
-  float (*pvacc)[D] = reinterpret_cast<float (*)[D]>(smem + lay.pv);
-  double* rmax = reinterpret_cast<double*>(smem + lay.rmax);  // kNT doubles
-  __shared__ double red[2 * kNW];
-  __shared__ ZT fred[kNW];
-  __shared__ int tmp[kNW + 2];
-  __shared__ double tau_b;
-  __shared__ int nb[2];
-
+  constexpr int NG = NT / LR;     // rows in flight per pass
+  constexpr int KB = kTauMaxList / NT;  // most list entries per thread in block-wide steps
+  float (*pvacc)[D] = reinterpret_cast<float (*)[D]>(pvbase);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int b = u / Hkv, g = u % Hkv;
-  const int h = g * G + hh;
-  const int bh = b * H + h;
-  const ZT* mx = maxima + (size_t)bh * splits;
-  const int* cn = counts + (size_t)bh * splits;
-  const Cand<ZT>* creg = cand + (size_t)bh * splits * cap;
   const uint64_t ltm = lanemask_below(lane);
-  const double am1 = (double)alpha - 1.0;
-  const double m = 1.0 / am1;
-  const int mcode = (m == 1.0) ? 1 : (m == 2.0) ? 2 : (m == 3.0) ? 3 : (m == 4.0) ? 4 : 0;
-
-  // Region counts and maxima: every thread loads its contiguous block of
-  // regions at once; one block scan turns counts into offsets.
-  const int cpt = (splits + kNT - 1) / kNT;
-  const int r0 = min(splits, tid * cpt), r1 = min(splits, r0 + cpt);
-  int s = 0;
-  ZT mloc = neg_inf<ZT>();
-  for (int r = r0; r < r1; ++r) {
-    const int c = cn[r];
-    roff[r] = c;
-    s += c;
-    mloc = max(mloc, mx[r]);
-  }
-  const ZT M = block_reduce<kNT>(mloc, fred, [](ZT a, ZT c) { return max(a, c); });
-  int n_cand;
-  {
-    int base = block_excl_scan<kNT>(s, tmp, &n_cand);
-    for (int r = r0; r < r1; ++r) {
-      const int v = roff[r];
-      roff[r] = base;
-      base += v;
-    }
-    if (tid == 0) roff[splits] = n_cand;
-  }
-  __syncthreads();
-  if (M == neg_inf<ZT>()) {
-    for (int d = tid; d < D; d += kNT) out[(size_t)bh * D + d] = 0.0f;
-    if (tid == 0) {
-      if (tau_out) tau_out[bh] = __builtin_nanf("");
-      if (sup_out) sup_out[bh] = 0;
-    }
-    return;
-  }
-  const double amax = am1 * (double)M;
-  ZT thr = M - window;
-  if (n_cand > kTauBoundFrom) {
-    // Many candidates: tighten the window with a lower bound on tau.
-    const ZT lb = tau_window_bound(mloc, rmax, &tau_b, am1, m, mcode, amax);
-    if (lb > thr) thr = lb;
-  }
-
-  // Gather and window filter, in batches of up to kNT * KB entries: thread t
-  // takes a contiguous run of the batch (all of its loads in flight
-  // together), keeps those with z >= thr, and one block scan places them in
-  // order; members beyond the LDS capacity go to the head's global list. The
-  // run length is a compile-time 2, 8 or KB, picked from the batch size.
-  ZT* gz = list_z + (size_t)bh * list_cap;
-  int* gi = list_i + (size_t)bh * list_cap;
-  int n_list = 0;
-  for (int bbase = 0; bbase < n_cand; bbase += kNT * KB) {
-    const int nb_ = min(kNT * KB, n_cand - bbase);
-    const int per = (nb_ + kNT - 1) / kNT;
-    const GatherArgs<ZT> ga{roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp};
-    if (per <= 2) n_list = gather_batch<2>(ga, bbase, nb_, n_list);
-    else if (per <= 8) n_list = gather_batch<8>(ga, bbase, nb_, n_list);
-    else
-      n_list = gather_batch_wide<KB>(roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp,
-                                          bbase, nb_, n_list);
-  }
-  __syncthreads();
   ZT* dz = lz;
   int* di = li;
   if (n_list > lcap) {
     // the whole list goes to global memory
-    for (int i = tid; i < lcap; i += kNT) {
+    for (int i = tid; i < lcap; i += NT) {
       gz[i] = lz[i];
       gi[i] = li[i];
     }
@@ -1530,15 +1440,15 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
                                                        lane, ltm, !vpre, o, psum, t);
       });
       if (lane == 0) {
-        nb[1] = o;
-        red[0] = psum;
-        tau_b = t;
+        sh.nb[1] = o;
+        sh.red[0] = psum;
+        sh.tau_b = t;
       }
     }
     __syncthreads();
-    tau = tau_b;
-    n_sup = nb[1];
-    psum = red[0];
+    tau = sh.tau_b;
+    n_sup = sh.nb[1];
+    psum = sh.red[0];
   } else if (list_lds && n_list <= kWave * kRegListLong && mcode != 0) {
     // Up to 1024 entries at integer m: the same by wave 0 with 16 entries
     // per lane (no call to the general power).
@@ -1550,21 +1460,21 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
                                                            amax, lane, ltm, true, o, psum, t);
       });
       if (lane == 0) {
-        nb[1] = o;
-        red[0] = psum;
-        tau_b = t;
+        sh.nb[1] = o;
+        sh.red[0] = psum;
+        sh.tau_b = t;
       }
     }
     __syncthreads();
-    tau = tau_b;
-    n_sup = nb[1];
-    psum = red[0];
+    tau = sh.tau_b;
+    n_sup = sh.nb[1];
+    psum = sh.red[0];
   } else {
     // Longer lists, out of line: up to the LDS capacity by the workgroup,
     // beyond it from global memory.
-    const TauSolution r = list_lds ? tau_long_list<ZT, KB>(lz, li, sp, n_list, am1, m, mcode, amax,
-                                                          red, tmp)
-                                   : tau_global_list<ZT>(dz, n_list, am1, m, mcode, amax, red);
+    const TauSolution r = list_lds ? tau_long_list<ZT, KB, NT>(lz, li, sp, n_list, am1, m, mcode, amax,
+                                                          sh.red, sh.tmp)
+                                   : tau_global_list<ZT, NT>(dz, n_list, am1, m, mcode, amax, sh.red);
     tau = r.tau;
     n_sup = r.n_sup;
     psum = r.psum;
@@ -1612,21 +1522,145 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
 #pragma unroll
     for (int e = 0; e < VPC; ++e) pvacc[grp][c * VPC + e] = acc[e];
   } else {
-    pv_global_list<KV, D>(v_pool, Hkv, g, PS, dz, di, n_list, am1, m, mcode, tau,
+    pv_global_list<KV, D, NT>(v_pool, Hkv, g, PS, dz, di, n_list, am1, m, mcode, tau,
                           &pvacc[grp][c * VPC]);
   }
   __syncthreads();
   const double inv = psum > 0.0 ? 1.0 / psum : 0.0;
-  for (int d = tid; d < D; d += kNT) {
+  for (int d = tid; d < D; d += NT) {
     float sacc = 0.0f;
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) sacc += pvacc[gg][d];
-    out[(size_t)bh * D + d] = (float)((double)sacc * inv);
+    out_row[d] = (float)((double)sacc * inv);
   }
   if (tid == 0) {
-    if (tau_out) tau_out[bh] = (float)tau;
-    if (sup_out) sup_out[bh] = n_sup;
+    if (tau_p) *tau_p = (float)tau;
+    if (sup_p) *sup_p = n_sup;
   }
+}
+
+
+template <typename KV>
+struct TauArgs {
+  const KV* v_pool;
+  int H, Hkv, G, U, PS, splits, cap, list_cap, lcap;
+  float alpha;
+  double window_d;
+  const Cand<typename KvTraits<KV>::Acc>* cand;
+  const int* counts;
+  const typename KvTraits<KV>::Acc* maxima;
+  typename KvTraits<KV>::Acc* list_z;
+  int* list_i;
+  float* out;
+  float* tau_out;
+  int32_t* sup_out;
+};
+
+// One query head (unit u, head hh of its group), by the whole workgroup.
+template <typename KV, int D>
+__device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh, unsigned char* smem) {
+  using ZT = typename KvTraits<KV>::Acc;
+  const KV* __restrict__ v_pool = args.v_pool;
+  const int H = args.H, Hkv = args.Hkv, G = args.G, PS = args.PS, splits = args.splits;
+  const int cap = args.cap, list_cap = args.list_cap, lcap = args.lcap;
+  const float alpha = args.alpha;
+  const Cand<ZT>* __restrict__ cand = args.cand;
+  const int* __restrict__ counts = args.counts;
+  const ZT* __restrict__ maxima = args.maxima;
+  ZT* __restrict__ list_z = args.list_z;
+  int* __restrict__ list_i = args.list_i;
+  float* __restrict__ out = args.out;
+  float* __restrict__ tau_out = args.tau_out;
+  int32_t* __restrict__ sup_out = args.sup_out;
+  const ZT window = (ZT)args.window_d;
+  constexpr int VPC = 16 / sizeof(KV);
+  constexpr int LR = D / VPC;     // lanes per V row
+  constexpr int NG = kNT / LR;    // rows in flight per pass
+  constexpr int KB = kTauMaxList / kNT;  // most entries per thread in a gather batch
+  const TauLds lay = tau_lds_layout(splits, lcap, sizeof(ZT), NG, D);
+  int* roff = reinterpret_cast<int*>(smem);  // region offsets
+  ZT* lz = reinterpret_cast<ZT*>(smem + lay.lz);
+  int* li = reinterpret_cast<int*>(smem + lay.li);
+  float* sp = reinterpret_cast<float*>(smem + lay.sp);
+  float (*pvacc)[D] = reinterpret_cast<float (*)[D]>(smem + lay.pv);
+  double* rmax = reinterpret_cast<double*>(smem + lay.rmax);  // kNT doubles
+  __shared__ ZT fred[kNW];
+  __shared__ TauShared<kNT> tsh;
+  int* tmp = tsh.tmp;
+
+  const int tid = threadIdx.x;
+  const int b = u / Hkv, g = u % Hkv;
+  const int h = g * G + hh;
+  const int bh = b * H + h;
+  const ZT* mx = maxima + (size_t)bh * splits;
+  const int* cn = counts + (size_t)bh * splits;
+  const Cand<ZT>* creg = cand + (size_t)bh * splits * cap;
+  const double am1 = (double)alpha - 1.0;
+  const double m = 1.0 / am1;
+  const int mcode = (m == 1.0) ? 1 : (m == 2.0) ? 2 : (m == 3.0) ? 3 : (m == 4.0) ? 4 : 0;
+
+  // Region counts and maxima: every thread loads its contiguous block of
+  // regions at once; one block scan turns counts into offsets.
+  const int cpt = (splits + kNT - 1) / kNT;
+  const int r0 = min(splits, tid * cpt), r1 = min(splits, r0 + cpt);
+  int s = 0;
+  ZT mloc = neg_inf<ZT>();
+  for (int r = r0; r < r1; ++r) {
+    const int c = cn[r];
+    roff[r] = c;
+    s += c;
+    mloc = max(mloc, mx[r]);
+  }
+  const ZT M = block_reduce<kNT>(mloc, fred, [](ZT a, ZT c) { return max(a, c); });
+  int n_cand;
+  {
+    int base = block_excl_scan<kNT>(s, tmp, &n_cand);
+    for (int r = r0; r < r1; ++r) {
+      const int v = roff[r];
+      roff[r] = base;
+      base += v;
+    }
+    if (tid == 0) roff[splits] = n_cand;
+  }
+  __syncthreads();
+  if (M == neg_inf<ZT>()) {
+    for (int d = tid; d < D; d += kNT) out[(size_t)bh * D + d] = 0.0f;
+    if (tid == 0) {
+      if (tau_out) tau_out[bh] = __builtin_nanf("");
+      if (sup_out) sup_out[bh] = 0;
+    }
+    return;
+  }
+  const double amax = am1 * (double)M;
+  ZT thr = M - window;
+  if (n_cand > kTauBoundFrom) {
+    // Many candidates: tighten the window with a lower bound on tau.
+    const ZT lb = tau_window_bound(mloc, rmax, &tsh.tau_b, am1, m, mcode, amax);
+    if (lb > thr) thr = lb;
+  }
+
+  // Gather and window filter, in batches of up to kNT * KB entries: thread t
+  // takes a contiguous run of the batch (all of its loads in flight
+  // together), keeps those with z >= thr, and one block scan places them in
+  // order; members beyond the LDS capacity go to the head's global list. The
+  // run length is a compile-time 2, 8 or KB, picked from the batch size.
+  ZT* gz = list_z + (size_t)bh * list_cap;
+  int* gi = list_i + (size_t)bh * list_cap;
+  int n_list = 0;
+  for (int bbase = 0; bbase < n_cand; bbase += kNT * KB) {
+    const int nb_ = min(kNT * KB, n_cand - bbase);
+    const int per = (nb_ + kNT - 1) / kNT;
+    const GatherArgs<ZT> ga{roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp};
+    if (per <= 2) n_list = gather_batch<2>(ga, bbase, nb_, n_list);
+    else if (per <= 8) n_list = gather_batch<8>(ga, bbase, nb_, n_list);
+    else
+      n_list = gather_batch_wide<KB>(roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp,
+                                          bbase, nb_, n_list);
+  }
+  __syncthreads();
+  tau_solve_pv<KV, D, kNT>(v_pool, Hkv, g, PS, lz, li, sp, &pvacc[0][0], n_list, lcap, gz, gi,
+                           am1, m, mcode, amax, tsh, out + (size_t)bh * D,
+                           tau_out ? tau_out + bh : nullptr, sup_out ? sup_out + bh : nullptr);
 }
 
 // One kernel serves the budgeted and the full-cache decode (the step is the

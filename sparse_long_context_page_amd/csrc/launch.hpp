@@ -222,6 +222,32 @@ hipError_t launch_gauss_solve(const LaunchShape& s, const void* stats, const int
                               double delta, float* keys, float* tau_hat, hipStream_t st);
 size_t gauss_ws_bytes(const LaunchShape& s);
 
+// Per-head select-and-decode (bf16 caches): one workgroup per query head
+// selects its pages from the bounds in the select workspace and decodes
+// them. Used when there are at least kHeadMinHeads heads (enough workgroups
+// to stream at full rate), the budget is at most kHeadMaxBudget pages, a
+// head's selected K is at most kHeadMaxBytes (beyond it re-reading pages
+// that the heads of a KV head share costs more than the launches it saves:
+// measured 343 -> 415 us at 4 MiB per head) and the kernel's LDS fits. Workspace: the select's bounds, then per (head,
+// wave) spill areas of wcap candidates, then per head list_cap window-list
+// entries (scores, then V rows).
+constexpr long long kHeadMinHeads = 128;
+constexpr long long kHeadMaxBytes = 2 << 20;
+constexpr size_t kHeadMaxLds = 150 * 1024;
+struct HeadPlan {
+  bool use = false;
+  int wcap = 0, list_cap = 0;
+  size_t spill = 0, list = 0, total = 0;
+};
+HeadPlan plan_head(const LaunchShape& s, int budget, size_t select_bytes);
+// bt_lds: block_table is 16-byte aligned and max_pages a multiple of 4 (the
+// kernel may then stage a block-table row in LDS with 16-byte loads).
+hipError_t launch_head_decode(const LaunchShape& s, const SelectPlan& sp, const HeadPlan& hp,
+                              const float* q, const void* k_pool, const void* v_pool,
+                              const int32_t* bt, const int32_t* lens, int budget, float alpha,
+                              float window, int32_t* sel, float* sel_ub, float* out, float* tau,
+                              int32_t* support, void* ws, bool bt_lds, hipStream_t st);
+
 // Per-dtype instantiations (decode_bf16.hip, decode_f32.hip).
 hipError_t launch_score_bf16(const LaunchShape& s, const SplitPlan& p, const float* q,
                              const void* k_pool, const int32_t* bt, const int32_t* lens,

@@ -35,6 +35,7 @@
 
 #include "launch.hpp"
 #include "mfma.hpp"
+#include "select_impl.hpp"
 
 namespace ekv {
 
@@ -42,7 +43,6 @@ namespace ekv {
 // per thread shorten each pass), 256 from kSelWideFrom heads on (the grid
 // then fills the chip and smaller workgroups pack better).
 constexpr int kSelWideFrom = 256;
-constexpr int kSelLds = 16384;  // bounds staged in LDS when the sequence has at most this many pages
 constexpr int kBoundPages = 32;  // pages per workgroup of the bounds kernel
 
 // The k largest of n 32-bit keys, ties to the lower index, by one wave
@@ -477,7 +477,6 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
 // kCand: the keys are the chunked candidates of bounds_mfma_kernel<..., true>
 // (order key | page << 32, keepc per chunk of cp pages, nchunks per head),
 // at most kSelCand of them per head; the kept candidates' pages are written.
-constexpr int kSelCand = kSelLds / 2;
 constexpr long long kSelChunkedMinPages = 8192;
 template <int kSelNT, bool kDrop, bool kCand>
 __global__ void __launch_bounds__(kSelNT)
@@ -485,254 +484,26 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
               int Hkv, int U, int ps, int max_pages, int ldu, int budget,
               int32_t* __restrict__ sel, float* __restrict__ sel_ub, int cp, int keepc,
               int nchunks) {
-  static_assert(!(kDrop && kCand), "the Gaussian keys are not chunked");
-  constexpr uint32_t drop_below = 0x007fffffu;  // float_order(-inf)
-  constexpr int NW = kSelNT / kWave;
-  constexpr int UNR = 4;  // 16-byte loads in flight per thread
   __shared__ __align__(16) uint32_t sord[kSelLds];
-  __shared__ __align__(16) int hist[2][256];
-  __shared__ unsigned int ured[NW][2];
-  __shared__ int wcnt[NW][2];
-  __shared__ int vcnt[NW];
-  __shared__ int bc[3];
-
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  __shared__ SelectScratch<kSelNT> sh;
+  const int tid = threadIdx.x;
   const int u = blockIdx.x % U, hh = blockIdx.x / U;
   const int b = u / Hkv, g = u % Hkv;
   const int bh = b * H + g * G + hh;
   const int L = clamp_len(seq_lens[b], max_pages * ps);
-  int P = (L + ps - 1) / ps;
-  const float* row = ub + (size_t)bh * ldu;
+  const int P = (L + ps - 1) / ps;
   int32_t* out = sel + (size_t)bh * budget;
   float* out_ub = sel_ub ? sel_ub + (size_t)bh * budget : nullptr;
-
-  // chunked candidates: nk of them (every chunk but the last holds keepc)
-  const uint64_t* crow = reinterpret_cast<const uint64_t*>(ub) + (size_t)bh * nchunks * keepc;
-  const int nc = kCand ? (P + cp - 1) / cp : 0;
-  const int nk = kCand ? (nc == 0 ? 0 : (nc - 1) * keepc + min(keepc, P - (nc - 1) * cp)) : P;
-  int* sj = reinterpret_cast<int*>(sord + kSelCand);  // kCand: candidates' pages
-
-  if (!kDrop && P <= budget) {
-    // every page kept (kCand: then one chunk holds them all, in page order)
-    for (int i = tid; i < budget; i += kSelNT) {
-      out[i] = i < P ? i : -1;
-      if (out_ub)
-        out_ub[i] = i >= P ? -__builtin_inff()
-                           : (kCand ? order_float((uint32_t)crow[i]) : row[i] + 0.0f);
-    }
-    return;
-  }
-
-  // Order-preserving 32-bit keys, handled four at a time (rows are padded to
-  // a multiple of 4 floats; a quad's entries at or past P are masked). They
-  // are staged in LDS when they fit, else re-read from the bounds row.
-  // kCand: the candidates' keys (always staged) take the place of the pages'.
-  if constexpr (kCand) P = nk;
-  const bool staged = kCand || P <= kSelLds;
-  const int n4 = (P + 3) >> 2;
-  const float4* row4 = reinterpret_cast<const float4*>(row);
-  auto from_global = [&](int i4) -> uint4 {
-    const float4 f = row4[i4];
-    return make_uint4(float_order(f.x + 0.0f), float_order(f.y + 0.0f), float_order(f.z + 0.0f),
-                      float_order(f.w + 0.0f));
-  };
-  auto quad = [&](int i4) -> uint4 {
-    return staged ? *reinterpret_cast<const uint4*>(&sord[4 * i4]) : from_global(i4);
-  };
-  auto at = [](const uint4& v, int e) -> uint32_t {
-    return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
-  };
-
-  // A key counts when its page is below P (and, with kDrop, it is above -inf).
-  auto valid = [&](int j, uint32_t o) { return j < P && (!kDrop || o > drop_below); };
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  int nvalid = 0;
-  if constexpr (kCand) {
-    // stage the candidates' keys and pages, every load of a batch issued
-    // before the first is used
-    constexpr int CU = 8;
-    for (int base = 0; base < P; base += CU * kSelNT) {
-      uint64_t v[CU];
-#pragma unroll
-      for (int r = 0; r < CU; ++r) {
-        const int i = base + r * kSelNT + tid;
-        v[r] = i < P ? crow[i] : 0ull;
-      }
-#pragma unroll
-      for (int r = 0; r < CU; ++r) {
-        const int i = base + r * kSelNT + tid;
-        if (i < P) {
-          const uint32_t o = (uint32_t)v[r];
-          sord[i] = o;
-          sj[i] = (int)(uint32_t)(v[r] >> 32);
-          mn = min(mn, o);
-          mx = max(mx, o);
-        }
-      }
-    }
-  }
-  for (int base = 0; !kCand && base < n4; base += UNR * kSelNT) {
-    uint4 v[UNR] = {};
-#pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      const int i4 = base + r * kSelNT + tid;
-      if (i4 < n4) v[r] = from_global(i4);
-    }
-#pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      const int i4 = base + r * kSelNT + tid;
-      if (i4 < n4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (valid(4 * i4 + e, at(v[r], e))) {
-            mn = min(mn, at(v[r], e));
-            mx = max(mx, at(v[r], e));
-            if constexpr (kDrop) ++nvalid;
-          }
-        }
-        if (staged) *reinterpret_cast<uint4*>(&sord[4 * i4]) = v[r];
-      }
-    }
-  }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
-  if constexpr (kDrop) nvalid = wave_sum(nvalid);
-  if (lane == 0) {
-    ured[wave][0] = mn;
-    ured[wave][1] = mx;
-    if constexpr (kDrop) vcnt[wave] = nvalid;
-  }
-  if (tid < 256) hist[0][tid] = 0;
-  __syncthreads();
-  nvalid = kDrop ? 0 : P;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    mn = min(mn, ured[w][0]);
-    mx = max(mx, ured[w][1]);
-    if constexpr (kDrop) nvalid += vcnt[w];
-  }
-
-  // Radix select of the budget-th largest key, 8 bits per pass from the
-  // highest bit where keys differ; stop once the boundary digit is taken
-  // whole. Two histograms alternate so that a pass needs two barriers.
-  uint32_t prefix, pmask;
-  int k = budget;  // rank still to place among keys matching the prefix
-  if (kDrop && nvalid <= budget) {
-    // every counted key is kept: all of them "equal" an empty prefix
-    prefix = 0u;
-    pmask = 0u;
-    k = nvalid;
-    for (int i = nvalid + tid; i < budget; i += kSelNT) {
-      out[i] = -1;
-      if (out_ub) out_ub[i] = -__builtin_inff();
-    }
-  } else if (mn == mx) {
-    prefix = mx;
-    pmask = 0xffffffffu;
-  } else {
-    int hb = 31 - __clz(mn ^ mx);
-    pmask = ~((2u << hb) - 1u);
-    prefix = mx & pmask;
-    int cur = 0;
-    while (true) {
-      const int lo = hb >= 7 ? hb - 7 : 0;
-      const int width = hb - lo + 1;
-      const uint32_t dmask = (1u << width) - 1u;
-      if (tid < 256) hist[cur ^ 1][tid] = 0;
-      for (int base = 0; base < n4; base += UNR * kSelNT) {
-        uint4 v[UNR] = {};
-#pragma unroll
-        for (int r = 0; r < UNR; ++r) {
-          const int i4 = base + r * kSelNT + tid;
-          if (i4 < n4) v[r] = quad(i4);
-        }
-#pragma unroll
-        for (int r = 0; r < UNR; ++r) {
-          const int i4 = base + r * kSelNT + tid;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t o = at(v[r], e);
-            if (i4 < n4 && valid(4 * i4 + e, o) && (o & pmask) == prefix)
-              atomicAdd(&hist[cur][(o >> lo) & dmask], 1);
-          }
-        }
-      }
-      __syncthreads();
-      if (wave == 0) {
-        int c4[4];
-        int s = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          c4[i] = hist[cur][4 * lane + i];
-          s += c4[i];
-        }
-        // keys in this lane's bins and above: the total less the keys in
-        // lower lanes' bins
-        const int incl = wave_incl_scan(s, lane);
-        const int suf = lane_value(incl, kWave - 1) - incl + s;
-        int above = suf - s;
-        if (above < k && k <= suf) {
-#pragma unroll
-          for (int i = 3; i >= 0; --i) {
-            if (above < k && k <= above + c4[i]) {
-              bc[0] = 4 * lane + i;
-              bc[1] = above;
-              bc[2] = c4[i];
-            }
-            above += c4[i];
-          }
-        }
-      }
-      __syncthreads();
-      const int d = bc[0];
-      const int cnt_d = bc[2];
-      k -= bc[1];
-      prefix |= ((uint32_t)d) << lo;
-      pmask |= dmask << lo;
-      if (cnt_d == k || lo == 0) break;
-      hb = lo - 1;
-      cur ^= 1;
-    }
-  }
-
-  // Keep keys above the prefix and the first k (by page index) equal to it,
-  // written in ascending page order: thread t owns a contiguous run of quads,
-  // one block scan of the runs' (above, equal) counts places each run, and
-  // the thread writes its kept pages in order.
-  const int qpt = (n4 + kSelNT - 1) / kSelNT;
-  const int q0 = min(n4, tid * qpt), q1 = min(n4, q0 + qpt);
-  int n_gt = 0, n_eq = 0;
-  for (int i4 = q0; i4 < q1; ++i4) {
-    const uint4 v = quad(i4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool ok = valid(4 * i4 + e, at(v, e));
-      const uint32_t m = at(v, e) & pmask;
-      n_eq += (ok && m == prefix) ? 1 : 0;
-      n_gt += (ok && m > prefix) ? 1 : 0;
-    }
-  }
-  int gt_base, eq_base;
-  block_excl_scan2<kSelNT>(n_gt, n_eq, &wcnt[0][0], &gt_base, &eq_base);
-  int pos = gt_base + min(eq_base, k);
-  int eqc = eq_base;  // equal keys on lower pages
-  for (int i4 = q0; i4 < q1 && pos < budget; ++i4) {
-    const uint4 v = quad(i4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool ok = valid(4 * i4 + e, at(v, e));
-      const uint32_t m = at(v, e) & pmask;
-      const bool eq = ok && m == prefix;
-      const bool take = (ok && m > prefix) || (eq && eqc < k);
-      eqc += eq ? 1 : 0;
-      if (take) {
-        if (pos < budget) {
-          out[pos] = kCand ? sj[4 * i4 + e] : 4 * i4 + e;
-          if (out_ub) out_ub[pos] = order_float(at(v, e));
-        }
-        ++pos;
-      }
-    }
+  const int kept = select_row<kSelNT, kDrop, kCand>(
+      ub + (size_t)bh * ldu, reinterpret_cast<const uint64_t*>(ub) + (size_t)bh * nchunks * keepc,
+      P, budget, cp, keepc, sord, sh, [](int, int) {},
+      [&](int pos, int page, uint32_t key) {
+        out[pos] = page;
+        if (out_ub) out_ub[pos] = order_float(key);
+      });
+  for (int i = kept + tid; i < budget; i += kSelNT) {
+    out[i] = -1;
+    if (out_ub) out_ub[i] = -__builtin_inff();
   }
 }
 

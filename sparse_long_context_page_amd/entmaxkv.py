@@ -7,9 +7,10 @@ built (there is no fallback path).
 
 The function names match the C ABI:
     entmaxkv_build_page_meta, entmaxkv_append_page_meta, entmaxkv_score_select,
-    entmaxkv_score_select_noalloc, entmaxkv_decode_sparse, entmaxkv_decode_full, entmaxkv_build_page_moments,
+    entmaxkv_score_select_noalloc, entmaxkv_decode_sparse, entmaxkv_decode_topk,
+    entmaxkv_decode_full, entmaxkv_build_page_moments,
     entmaxkv_append_page_moments, entmaxkv_gauss_select, entmaxkv_workspace_bytes,
-    entmaxkv_strerror
+    entmaxkv_topk_kernels, entmaxkv_strerror
 """
 from __future__ import annotations
 
@@ -33,10 +34,11 @@ ENTMAXKV_WS_SELECT = 0
 ENTMAXKV_WS_SPARSE = 1
 ENTMAXKV_WS_FULL = 2
 ENTMAXKV_WS_GAUSS = 3
+ENTMAXKV_WS_TOPK = 4
 
 # kernels each entry point launches (for per-kernel event timing)
 KERNELS = {"build_page_meta": 1, "append_page_meta": 1, "score_select": 2,
-           "score_select_noalloc": 2, "decode_sparse": 2,
+           "score_select_noalloc": 2, "decode_sparse": 2, "decode_topk": 4,
            "decode_full": 2, "build_page_moments": 1, "append_page_moments": 1,
            "gauss_select": 3}
 
@@ -72,19 +74,23 @@ def _load() -> ctypes.CDLL:
     lib.entmaxkv_score_select.argtypes = [SP, P, P, P, P, I32, P, P, P, SZ, P, P]
     lib.entmaxkv_score_select_noalloc.argtypes = [SP, P, P, P, P, I32, P, P, P, P]
     lib.entmaxkv_decode_sparse.argtypes = [SP, P, P, P, P, P, P, I32, F32, P, P, P, P, SZ, P, P]
+    lib.entmaxkv_decode_topk.argtypes = [SP, P, P, P, P, P, P, I32, F32, P, P, P, P, P, P, SZ,
+                                         P, P]
     lib.entmaxkv_decode_full.argtypes = [SP, P, P, P, P, P, F32, P, P, P, P, SZ, P, P]
     lib.entmaxkv_build_page_moments.argtypes = [SP, P, P, P, P, P, P]
     lib.entmaxkv_append_page_moments.argtypes = [SP, P, P, P, P, I32, P, P, P]
     lib.entmaxkv_gauss_select.argtypes = [SP, P, P, P, P, F32, F32, I32, P, P, P, SZ, P, P]
     lib.entmaxkv_workspace_bytes.argtypes = [SP, I32, I32, ctypes.POINTER(SZ)]
+    lib.entmaxkv_topk_kernels.argtypes = [SP, I32, ctypes.POINTER(I32)]
     lib.entmaxkv_strerror.argtypes = [ctypes.c_int]
     lib.entmaxkv_strerror.restype = ctypes.c_char_p
     lib.entmaxkv_version.argtypes = []
     for name in ("entmaxkv_build_page_meta", "entmaxkv_append_page_meta",
                  "entmaxkv_score_select", "entmaxkv_score_select_noalloc",
-                 "entmaxkv_decode_sparse", "entmaxkv_decode_full",
+                 "entmaxkv_decode_sparse", "entmaxkv_decode_topk", "entmaxkv_decode_full",
                  "entmaxkv_build_page_moments", "entmaxkv_append_page_moments",
-                 "entmaxkv_gauss_select", "entmaxkv_workspace_bytes", "entmaxkv_version"):
+                 "entmaxkv_gauss_select", "entmaxkv_workspace_bytes", "entmaxkv_topk_kernels",
+                 "entmaxkv_version"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -182,6 +188,14 @@ def entmaxkv_workspace_bytes(shape: Shape, budget_pages: int, which: int) -> int
     out = ctypes.c_size_t(0)
     _check(lib.entmaxkv_workspace_bytes(ctypes.byref(shape), int(budget_pages), int(which),
                                         ctypes.byref(out)), "entmaxkv_workspace_bytes")
+    return int(out.value)
+
+
+def entmaxkv_topk_kernels(shape: Shape, budget_pages: int) -> int:
+    """Kernels entmaxkv_decode_topk launches here: 2 (per-head path) or 4."""
+    out = ctypes.c_int32(0)
+    _check(lib.entmaxkv_topk_kernels(ctypes.byref(shape), int(budget_pages), ctypes.byref(out)),
+           "entmaxkv_topk_kernels")
     return int(out.value)
 
 
@@ -328,6 +342,23 @@ def _args_decode_sparse(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, 
         psu, pw, nw, _stream(stream, q.device), None], ws
 
 
+def _args_decode_topk(shape: Shape, q, meta, k_pool, v_pool, block_table, seq_lens,
+                      budget_pages, alpha, sel, out, sel_ub=None, tau=None, support=None,
+                      ws=None, stream=None):
+    pq, pk, pv, pbt, pl, po, pt, psu = _decode_ptrs(shape, q, k_pool, v_pool, block_table,
+                                                     seq_lens, out, tau, support)
+    n = _Sizes(shape)
+    pm = _ptr(meta, "meta", _kv_dtypes(shape), numel=n.meta)
+    ps_ = _ptr(sel, "sel", (torch.int32,), numel=n.sel(budget_pages))
+    pu = _ptr(sel_ub, "sel_ub", (torch.float32,), nullable=True, numel=n.sel(budget_pages))
+    _on_device(q=q, meta=meta, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
+               seq_lens=seq_lens, sel=sel, sel_ub=sel_ub, out=out, tau=tau, support=support)
+    pw, nw, ws = _ws_args(ws, shape, budget_pages, ENTMAXKV_WS_TOPK, q.device)
+    return lib.entmaxkv_decode_topk, [
+        ctypes.byref(shape), pq, pm, pk, pv, pbt, pl, int(budget_pages), float(alpha), ps_, pu,
+        po, pt, psu, pw, nw, _stream(stream, q.device), None], ws
+
+
 def _args_decode_full(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, alpha, out,
                       tau=None, support=None, ws=None, stream=None):
     pq, pk, pv, pbt, pl, po, pt, psu = _decode_ptrs(shape, q, k_pool, v_pool, block_table,
@@ -405,6 +436,16 @@ def entmaxkv_decode_sparse(shape: Shape, q, k_pool, v_pool, block_table, seq_len
     _run("entmaxkv_decode_sparse", fn, args, events)
 
 
+def entmaxkv_decode_topk(shape: Shape, q, meta, k_pool, v_pool, block_table, seq_lens,
+                         budget_pages, alpha, sel, out, sel_ub=None, tau=None, support=None,
+                         ws=None, stream=None, events=None):
+    """Bounds, top-k selection and sparse decode in one call (sel is written)."""
+    fn, args, _ = _args_decode_topk(shape, q, meta, k_pool, v_pool, block_table, seq_lens,
+                                    budget_pages, alpha, sel, out, sel_ub, tau, support, ws,
+                                    stream)
+    _run("entmaxkv_decode_topk", fn, args, events)
+
+
 def entmaxkv_decode_full(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, alpha, out,
                          tau=None, support=None, ws=None, stream=None, events=None):
     fn, args, _ = _args_decode_full(shape, q, k_pool, v_pool, block_table, seq_lens, alpha, out,
@@ -422,7 +463,8 @@ class Prepared:
 
     _makers = {"build_page_meta": _args_build_page_meta,
                "append_page_meta": _args_append_page_meta, "score_select": _args_score_select,
-               "decode_sparse": _args_decode_sparse, "decode_full": _args_decode_full,
+               "decode_sparse": _args_decode_sparse, "decode_topk": _args_decode_topk,
+               "decode_full": _args_decode_full,
                "build_page_moments": _args_build_page_moments,
                "append_page_moments": _args_append_page_moments,
                "gauss_select": _args_gauss_select}

@@ -309,3 +309,47 @@ def test_noalloc_select_rejects_oversize_before_any_hip_call(ek):
     assert f(ctypes.byref(s), d, d, d, d, 82, None, None, None, None) == -1
     assert f(ctypes.byref(s), ctypes.c_void_p(256 + 8), d, d, d, 82, d, None, None, None) == -1
     assert f(ctypes.byref(shape(ek, head_dim=96)), d, d, d, d, 82, d, None, None, None) == -2
+
+
+def test_decode_topk_validation(ek):
+    """entmaxkv_decode_topk rejects null or misaligned pointers, bad budgets
+    and alphas and a short workspace before any HIP call; the kernel count
+    and workspace size follow the path it takes."""
+    s = shape(ek)
+    d = ctypes.c_void_p(256)
+    mis8 = ctypes.c_void_p(256 + 8)
+    big = 1 << 40
+    f = ek.lib.entmaxkv_decode_topk
+
+    def call(q=d, meta=d, k=d, v=d, bt=d, lens=d, budget=82, alpha=1.5, sel=d, out=d, ws=d,
+             nws=big, sh=None):
+        return f(ctypes.byref(sh or s), q, meta, k, v, bt, lens, budget, alpha, sel, None, out,
+                 None, None, ws, nws, None, None)
+
+    for name in ("q", "meta", "k", "v", "bt", "lens", "sel", "out"):
+        assert call(**{name: None}) == -1, name
+    for name in ("q", "meta", "k", "v"):
+        assert call(**{name: mis8}) == -1, name
+    assert call(ws=ctypes.c_void_p(256 + 16)) == -1
+    for alpha in (1.0, math.nan, -1.0):
+        assert call(alpha=alpha) == -1
+    assert call(budget=0) == -1
+    assert call(budget=(1 << 22) + 1) == -2
+    rc, need = ws_rc(ek, s, 82, ek.ENTMAXKV_WS_TOPK)
+    assert rc == 0 and need > 0
+    assert call(nws=need - 1) == -3
+    assert call(ws=None) == -3
+
+    n = ctypes.c_int32(0)
+    # 128 query heads, bf16, budget 82: the per-head path (bounds + one kernel)
+    assert ek.lib.entmaxkv_topk_kernels(ctypes.byref(s), 82, ctypes.byref(n)) == 0
+    assert n.value == 2 and ek.entmaxkv_topk_kernels(s, 82) == 2
+    # fewer heads, float32 caches or a budget past the per-head limit: four kernels
+    for sh, budget in ((shape(ek, batch=1), 64), (shape(ek, kv_dtype="f32"), 82), (s, 1025)):
+        assert ek.entmaxkv_topk_kernels(sh, budget) == 4
+        rc, need4 = ws_rc(ek, sh, budget, ek.ENTMAXKV_WS_TOPK)
+        _, sel_b = ws_rc(ek, sh, budget, ek.ENTMAXKV_WS_SELECT)
+        _, sp_b = ws_rc(ek, sh, budget, ek.ENTMAXKV_WS_SPARSE)
+        assert rc == 0 and need4 >= sel_b + sp_b
+    assert ek.lib.entmaxkv_topk_kernels(ctypes.byref(s), 0, ctypes.byref(n)) == -1
+    assert ek.lib.entmaxkv_topk_kernels(ctypes.byref(s), 82, None) == -1
