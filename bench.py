@@ -45,9 +45,20 @@ from sparse_long_context_page_amd import synth  # noqa: E402
 METRIC = ("decode steps/s + achieved HBM GB/s (% of peak), sparse vs full entmax, "
           "32K–512K")
 PEAK_HBM_GBPS = 8000.0
-KERNEL_NAMES = ["bounds", "select", "score_sparse", "tau_pv_sparse", "score_full", "tau_pv_full"]
-KERNEL_SOURCES = ["common.hpp", "launch.hpp", "mfma.hpp", "select.hip", "decode_impl.hpp", "decode_bf16.hip",
-                  "decode_f32.hip", "meta.hip", "api.hip"]
+# kernels of the sparse path (entmaxkv_decode_topk) on its per-head path and
+# on its four-kernel path, then those of the full-cache path
+SPARSE_KERNELS_HEAD = ["bounds", "select_decode"]
+SPARSE_KERNELS_SPLIT = ["bounds", "select", "score_sparse", "tau_pv_sparse"]
+FULL_KERNELS = ["score_full", "tau_pv_full"]
+KERNEL_SOURCES = ["common.hpp", "launch.hpp", "mfma.hpp", "select.hip", "select_impl.hpp",
+                  "decode_impl.hpp", "decode_bf16.hip", "decode_f32.hip", "head_impl.hpp",
+                  "head_bf16.hip", "meta.hip", "api.hip"]
+
+
+def sparse_kernels(E, shape, budget) -> list:
+    """Names of the kernels entmaxkv_decode_topk runs at this shape and budget."""
+    return SPARSE_KERNELS_HEAD if E.entmaxkv_topk_kernels(shape, budget) == 2 \
+        else SPARSE_KERNELS_SPLIT
 
 
 # ---------------------------------------------------------------------------
@@ -92,6 +103,11 @@ def algorithmic_bytes(w, lens: np.ndarray, budget: int, sel: np.ndarray, sup_spa
         "select": sel_b,
         "score_sparse": k_sel_b + q_b + sel_b + bt_b,
         "tau_pv_sparse": v_sup_sparse + out_b,
+        # the per-head kernel: selection written, K of the union pages (each
+        # page counted once per KV head, as above), V of the support, outputs
+        "select_decode": sel_b + k_sel_b + q_b + bt_b + v_sup_sparse + out_b,
+        # what the per-head kernel requests: each selected page once per head
+        "_k_per_head": int((sel >= 0).sum()) * ps * D * s,
         "score_full": k_full_b + q_b + bt_b,
         "tau_pv_full": v_sup_full + out_b,
         "_meta_build": int(lens.sum()) * Hkv * D * s + meta_b,
@@ -307,7 +323,7 @@ def containment_report(args):
 
 def sweep_report(args):
     """Times every (alpha, budget) cell of the workload: the sparse path
-    (score_select + decode_sparse) per cell and the full-cache path per
+    (entmaxkv_decode_topk) per cell and the full-cache path per
     alpha, each step after the cache eviction, median of K steps; bytes
     touched and all-K+V bytes against 8 TB/s; per-kernel times from a second
     pass with events around every kernel."""
@@ -390,25 +406,22 @@ def sweep_report(args):
         log(f"full alpha {alpha}: {ms * 1e3:.1f} us")
     for budget in w.budgets:
         sel = torch.empty((B, H, budget), dtype=torch.int32, device=dev)
-        ws_sel = E.workspace(shape, budget, E.ENTMAXKV_WS_SELECT, dev)
-        ws_sp = E.workspace(shape, budget, E.ENTMAXKV_WS_SPARSE, dev)
-        c_sel = E.Prepared("score_select", shape, q, meta, bt, lens, budget, sel, None,
-                           ws=ws_sel, stream=stream)
+        ws_tk = E.workspace(shape, budget, E.ENTMAXKV_WS_TOPK, dev)
+        names = sparse_kernels(E, shape, budget)
         for alpha in w.alphas:
-            c_sp = E.Prepared("decode_sparse", shape, q, k, v, bt, lens, sel, budget, alpha, out,
-                              tau, sup, ws=ws_sp, stream=stream)
-            ms, kk = timed([c_sel, c_sp], [2, 2])
+            c_tk = E.Prepared("decode_topk", shape, q, meta, k, v, bt, lens, budget, alpha, sel,
+                              out, None, tau, sup, ws=ws_tk, stream=stream)
+            ms, kk = timed([c_tk], [4])
             sup_np = sup.cpu().numpy()
             nb = algorithmic_bytes(w, inp["seq_lens"], budget, sel.cpu().numpy(), sup_np, sup_np)
-            by = sum(nb[n] for n in KERNEL_NAMES[:4])
+            by = sum(nb[n] for n in names)
             cells.append({"alpha": alpha, "budget_pages": budget, "median_us": round(ms * 1e3, 2),
                           "bytes": by, "frac": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                           "bytes_all_kv": nb["_sparse_all_kv"],
                           "frac_all_kv": round(nb["_sparse_all_kv"] / (ms * 1e-3) / 1e9 /
                                                PEAK_HBM_GBPS, 4),
                           "union_fraction": round(nb["_union_fraction"], 4),
-                          "kernels_us": {n: round(float(x), 2)
-                                         for n, x in zip(KERNEL_NAMES[:4], kk)},
+                          "kernels_us": {n: round(float(x), 2) for n, x in zip(names, kk)},
                           "mean_support": float(sup_np.mean())})
             log(f"sparse alpha {alpha} budget {budget}: {ms * 1e3:.1f} us")
     print(json.dumps({"report": "sweep", "workload": w.name, "data": "synthetic", "steps": K,
@@ -771,9 +784,9 @@ def main():
     tau_f = torch.empty((B, H), device=dev)
     sup_s = torch.empty((B, H), dtype=torch.int32, device=dev)
     sup_f = torch.empty((B, H), dtype=torch.int32, device=dev)
-    ws_sel = E.workspace(shape, budget, E.ENTMAXKV_WS_SELECT, dev)
-    ws_sp = E.workspace(shape, budget, E.ENTMAXKV_WS_SPARSE, dev)
+    ws_tk = E.workspace(shape, budget, E.ENTMAXKV_WS_TOPK, dev)
     ws_fu = E.workspace(shape, budget, E.ENTMAXKV_WS_FULL, dev)
+    sp_names = sparse_kernels(E, shape, budget)
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     read_buf = (torch.ones(1 << 28, dtype=torch.int32, device=dev)
                 if args.flush == "write_read" else None)
@@ -806,21 +819,17 @@ def main():
     torch.cuda.synchronize()
     append_us = float(np.mean([ev_app.elapsed_ms(2 * i, 2 * i + 1) for i in range(n_meta)])) * 1e3
 
-    call_sel = E.Prepared("score_select", shape, q, meta, bt, lens, budget, sel, sel_ub, ws=ws_sel,
-                          stream=stream)
-    call_sp = E.Prepared("decode_sparse", shape, q, k, v, bt, lens, sel, budget, alpha, out_s,
-                         tau_s, sup_s, ws=ws_sp, stream=stream)
+    call_tk = E.Prepared("decode_topk", shape, q, meta, k, v, bt, lens, budget, alpha, sel, out_s,
+                         sel_ub, tau_s, sup_s, ws=ws_tk, stream=stream)
     call_fu = E.Prepared("decode_full", shape, q, k, v, bt, lens, alpha, out_f, tau_f, sup_f,
                          ws=ws_fu, stream=stream)
 
     def step(kev=None):
         if kev is None:
-            call_sel()
-            call_sp()
+            call_tk()
             call_fu()
         else:
-            call_sel(kev[0:4])
-            call_sp(kev[4:8])
+            call_tk(kev[0:8])
             call_fu(kev[8:12])
 
     for i in range(args.warmup):
@@ -837,8 +846,7 @@ def main():
     for i in range(K):
         flush(i)
         ev_step.record(2 * i, stream)
-        call_sel()
-        call_sp()
+        call_tk()
         call_fu()
         ev_step.record(2 * i + 1, stream)
     torch.cuda.synchronize()
@@ -852,8 +860,7 @@ def main():
     for i in range(K):
         flush(i)
         ev_path.record(3 * i, stream)
-        call_sel()
-        call_sp()
+        call_tk()
         ev_path.record(3 * i + 1, stream)
         call_fu()
         ev_path.record(3 * i + 2, stream)
@@ -869,8 +876,12 @@ def main():
         flush(i)
         step(hk[12 * i:12 * (i + 1)])
     torch.cuda.synchronize()
-    kern_ms = np.array([[ev_kern.elapsed_ms(12 * i + 2 * j, 12 * i + 2 * j + 1) for j in range(6)]
+    # event pairs of the step: four for decode_topk (the per-head path fills
+    # the first two), two for decode_full
+    pairs = list(range(len(sp_names))) + [4, 5]
+    kern_ms = np.array([[ev_kern.elapsed_ms(12 * i + 2 * j, 12 * i + 2 * j + 1) for j in pairs]
                         for i in range(K)])
+    kernel_names = sp_names + FULL_KERNELS
 
     # Graph pass: the same step captured once as a HIP graph (on a stream of
     # its own, default priority) and replayed K times, the flush still outside
@@ -878,10 +889,8 @@ def main():
     eager = [x.clone() for x in (sel, out_s, out_f, tau_s, tau_f)]
     gstream = torch.cuda.Stream(dev)
     g_calls = [
-        E.Prepared("score_select", shape, q, meta, bt, lens, budget, sel, sel_ub, ws=ws_sel,
-                   stream=gstream),
-        E.Prepared("decode_sparse", shape, q, k, v, bt, lens, sel, budget, alpha, out_s, tau_s,
-                   sup_s, ws=ws_sp, stream=gstream),
+        E.Prepared("decode_topk", shape, q, meta, k, v, bt, lens, budget, alpha, sel, out_s,
+                   sel_ub, tau_s, sup_s, ws=ws_tk, stream=gstream),
         E.Prepared("decode_full", shape, q, k, v, bt, lens, alpha, out_f, tau_f, sup_f, ws=ws_fu,
                    stream=gstream)]
     torch.cuda.synchronize()
@@ -911,12 +920,12 @@ def main():
                                sup_f.cpu().numpy())
     kmean = kern_ms.mean(axis=0)
     kernels = {}
-    for j, name in enumerate(KERNEL_NAMES):
+    for j, name in enumerate(kernel_names):
         gbps = nbytes[name] / (kmean[j] * 1e-3) / 1e9
         kernels[name] = {"us": round(kmean[j] * 1e3, 2), "bytes": nbytes[name],
                          "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
-    sparse_bytes = sum(nbytes[n] for n in KERNEL_NAMES[:4])
-    full_bytes = sum(nbytes[n] for n in KERNEL_NAMES[4:])
+    sparse_bytes = sum(nbytes[n] for n in sp_names)
+    full_bytes = sum(nbytes[n] for n in FULL_KERNELS)
     paths = {}
     for name, ms, by, by_all in (("sparse", sparse_ms, sparse_bytes, nbytes["_sparse_all_kv"]),
                                  ("full", full_ms, full_bytes, nbytes["_full_all_kv"])):
@@ -944,7 +953,7 @@ def main():
                                   "note": "box update for one appended token per sequence "
                                           "(a decode step's box maintenance), outside the step"}
     dom = int(np.argmax(kmean))
-    dname = KERNEL_NAMES[dom]
+    dname = kernel_names[dom]
     achieved = nbytes[dname] / (kmean[dom] * 1e-3) / 1e9
     traffic = counter_traffic(dname, profile_name(w, alpha, budget))
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
@@ -1001,13 +1010,15 @@ def main():
                    "head_dim": D, "context": int(w.context), "page_size": w.page_size,
                    "budget_pages": budget, "alpha": alpha, "kv_dtype": w.kv_dtype,
                    "parallelism": "single GPU", "cache_flush": (args.flush if not args.no_flush else None),
-                   "step": "score_select + decode_sparse + decode_full"},
+                   "step": "decode_topk (bounds, top-k, sparse decode) + decode_full",
+                   "sparse_kernels": sp_names},
         "paths": paths,
         "kernels": kernels,
         "roofline": roofline,
         "roofline_paths": roofline_paths,
         "cpu_baseline": cpu_line,
         "diagnostics": {"union_fraction": round(nbytes["_union_fraction"], 4),
+                        "k_bytes_per_head_reads": nbytes["_k_per_head"],
                         "mean_support_sparse": float(sup_s.float().mean()),
                         "mean_support_full": float(sup_f.float().mean()),
                         "wall_s_timed_region": round(wall, 3),

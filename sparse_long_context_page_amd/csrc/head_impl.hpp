@@ -139,15 +139,17 @@ head_decode_kernel(HeadArgs a) {
   float* pmax = reinterpret_cast<float*>(smem + lay.pmax);
   const int32_t* bt_row = a.block_table + (size_t)b * max_pages;
 
-  // 1. The block-table row (its first P entries, rounded up to 4) into LDS
-  // past the select's keys, with direct-to-LDS loads in flight during the
-  // select; entries are read once the select's barriers have passed.
+  // 1. The block-table row into LDS past the select's keys, with
+  // direct-to-LDS loads in flight during the select (issued before the
+  // sequence length is known: the whole row when it fits); entries are read
+  // once the select's barriers have passed.
   int32_t* bt_l = reinterpret_cast<int32_t*>(smem + lay.bt);
-  const bool bt_staged = a.bt_lds && P <= kHeadMaxBt;
+  const bool bt_staged = a.bt_lds && max_pages <= kHeadMaxBt;
   if (bt_staged) {
-    // wave w loads 1 KiB pieces w, w + 8, ... (256 entries each); a piece
-    // past the row's end reads its last valid piece again
-    const int npc = (P + 255) / 256;
+    // wave w loads 1 KiB pieces w, w + 8, ... (256 entries each); lanes past
+    // the row's end re-read its last four entries (max_pages is a multiple
+    // of 4, so every other lane reads whole entries of the row)
+    const int npc = (max_pages + 255) / 256;
     for (int pc = wave; pc < npc; pc += kHNW) {
       const int e0 = pc * 256 + lane * 4;
       const int es = e0 + 4 <= max_pages ? e0 : max_pages - 4;
@@ -157,7 +159,7 @@ head_decode_kernel(HeadArgs a) {
   const int n_sel = select_row<kHNT, false, CAND>(
       a.ub + (size_t)bh * a.ldu,
       reinterpret_cast<const uint64_t*>(a.ub) + (size_t)bh * a.nchunks * a.keepc, P, budget,
-      a.cp, a.keepc, reinterpret_cast<uint32_t*>(smem), ssh, [](int, int) {},
+      a.cp, a.keepc, CAND ? a.nchunks * a.keepc : a.ldu, reinterpret_cast<uint32_t*>(smem), ssh,
       [&](int pos, int page, uint32_t key) {
         sel_l[pos] = page;
         a.sel[(size_t)bh * budget + pos] = page;

@@ -496,7 +496,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   float* out_ub = sel_ub ? sel_ub + (size_t)bh * budget : nullptr;
   const int kept = select_row<kSelNT, kDrop, kCand>(
       ub + (size_t)bh * ldu, reinterpret_cast<const uint64_t*>(ub) + (size_t)bh * nchunks * keepc,
-      P, budget, cp, keepc, sord, sh, [](int, int) {},
+      P, budget, cp, keepc, kCand ? nchunks * keepc : ldu, sord, sh,
       [&](int pos, int page, uint32_t key) {
         out[pos] = page;
         if (out_ub) out_ub[pos] = order_float(key);

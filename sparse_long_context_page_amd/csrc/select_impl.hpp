@@ -38,19 +38,35 @@ struct SelectScratch {
 // more than `budget` remain all are kept. Calls emit(pos, page, key) for
 // every kept page (pos its rank in ascending page order; key its order key)
 // and returns the number kept (at most budget; the caller pads the rest).
-// `pre(i4_first, i4_end)` is called once per thread, before the first key is
-// loaded, with the quads [i4_first, i4_end) whose pages this thread will emit
-// (its run in the final pass), so a caller can start loads for them early;
-// kCand and the every-page-kept case emit from other threads and skip it.
-template <int NT, bool kDrop, bool kCand, typename Pre, typename Emit>
-__device__ int select_row(const float* __restrict__ row, const uint64_t* __restrict__ crow, int P,
-                          int budget, int cp, int keepc, uint32_t* sord, SelectScratch<NT>& sh,
-                          Pre pre, Emit emit) {
+// `row_cap` (>= 1): keys of the row (candidates with kCand) that are
+// readable memory, at least P; the first batch of loads is issued from it
+// before anything depends on P, so a caller may pass a P whose load is still
+// in flight.
+template <int NT, bool kDrop, bool kCand, typename Emit>
+__device__ __forceinline__ int select_row(const float* __restrict__ row,
+                                          const uint64_t* __restrict__ crow, int P, int budget,
+                                          int cp, int keepc, int row_cap, uint32_t* sord,
+                                          SelectScratch<NT>& sh, Emit emit) {
   static_assert(!(kDrop && kCand), "the Gaussian keys are not chunked");
   constexpr uint32_t drop_below = 0x007fffffu;  // float_order(-inf)
   constexpr int NW = NT / kWave;
   constexpr int UNR = 4;  // 16-byte loads in flight per thread
+  constexpr int CU = 8;   // 8-byte candidate loads in flight per thread
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const float4* row4 = reinterpret_cast<const float4*>(row);
+
+  // The first batch of keys, from the readable part of the row (slots past
+  // it re-read its last entry); the staging loop below uses it for its first
+  // pass.
+  float4 f0[UNR];
+  uint64_t c0[CU];
+  if constexpr (kCand) {
+#pragma unroll
+    for (int r = 0; r < CU; ++r) c0[r] = crow[min(r * NT + tid, row_cap - 1)];
+  } else {
+#pragma unroll
+    for (int r = 0; r < UNR; ++r) f0[r] = row4[min(r * NT + tid, (row_cap >> 2) - 1)];
+  }
 
   // chunked candidates: nk of them (every chunk but the last holds keepc)
   const int nc = kCand ? (P + cp - 1) / cp : 0;
@@ -73,8 +89,6 @@ __device__ int select_row(const float* __restrict__ row, const uint64_t* __restr
   const int n4 = (P + 3) >> 2;
   const int qpt = (n4 + NT - 1) / NT;
   const int q0 = min(n4, tid * qpt), q1 = min(n4, q0 + qpt);
-  if constexpr (!kCand) pre(q0, q1);
-  const float4* row4 = reinterpret_cast<const float4*>(row);
   auto from_global = [&](int i4) -> uint4 {
     const float4 f = row4[i4];
     return make_uint4(float_order(f.x + 0.0f), float_order(f.y + 0.0f), float_order(f.z + 0.0f),
@@ -94,14 +108,13 @@ __device__ int select_row(const float* __restrict__ row, const uint64_t* __restr
   if constexpr (kCand) {
     // stage the candidates' keys and pages, every load of a batch issued
     // before the first is used
-    constexpr int CU = 8;
     for (int base = 0; base < P; base += CU * NT) {
+      // unconditional loads (slots past the row re-read its last entry), so
+      // that all of them are issued before the first wait
       uint64_t v[CU];
 #pragma unroll
-      for (int r = 0; r < CU; ++r) {
-        const int i = base + r * NT + tid;
-        v[r] = i < P ? crow[i] : 0ull;
-      }
+      for (int r = 0; r < CU; ++r)
+        v[r] = base == 0 ? c0[r] : crow[min(base + r * NT + tid, P - 1)];
 #pragma unroll
       for (int r = 0; r < CU; ++r) {
         const int i = base + r * NT + tid;
@@ -116,12 +129,17 @@ __device__ int select_row(const float* __restrict__ row, const uint64_t* __restr
     }
   }
   for (int base = 0; !kCand && base < n4; base += UNR * NT) {
-    uint4 v[UNR] = {};
+    // unconditional loads (slots past the row re-read its last quad), all
+    // issued before the first is converted
+    float4 f[UNR];
 #pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      const int i4 = base + r * NT + tid;
-      if (i4 < n4) v[r] = from_global(i4);
-    }
+    for (int r = 0; r < UNR; ++r)
+      f[r] = base == 0 ? f0[r] : row4[min(base + r * NT + tid, n4 - 1)];
+    uint4 v[UNR];
+#pragma unroll
+    for (int r = 0; r < UNR; ++r)
+      v[r] = make_uint4(float_order(f[r].x + 0.0f), float_order(f[r].y + 0.0f),
+                        float_order(f[r].z + 0.0f), float_order(f[r].w + 0.0f));
 #pragma unroll
     for (int r = 0; r < UNR; ++r) {
       const int i4 = base + r * NT + tid;
@@ -180,12 +198,9 @@ __device__ int select_row(const float* __restrict__ row, const uint64_t* __restr
       const uint32_t dmask = (1u << width) - 1u;
       if (tid < 256) sh.hist[cur ^ 1][tid] = 0;
       for (int base = 0; base < n4; base += UNR * NT) {
-        uint4 v[UNR] = {};
+        uint4 v[UNR];
 #pragma unroll
-        for (int r = 0; r < UNR; ++r) {
-          const int i4 = base + r * NT + tid;
-          if (i4 < n4) v[r] = quad(i4);
-        }
+        for (int r = 0; r < UNR; ++r) v[r] = quad(min(base + r * NT + tid, n4 - 1));
 #pragma unroll
         for (int r = 0; r < UNR; ++r) {
           const int i4 = base + r * NT + tid;
