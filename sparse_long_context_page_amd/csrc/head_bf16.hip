@@ -11,8 +11,9 @@ HeadPlan plan_head(const LaunchShape& s, int budget, size_t select_bytes) {
   const long long heads = (long long)s.batch * s.num_q_heads;
   const int keep = budget < s.max_pages ? budget : s.max_pages;
   const long long head_bytes = (long long)keep * s.page_size * s.head_dim * 2;
+  const long long max_bytes = heads > kNumCUs ? kHeadMaxBytesRounds : kHeadMaxBytes;
   p.use = s.bf16 && kMfmaScores && budget <= kHeadMaxBudget && heads >= kHeadMinHeads &&
-          head_bytes <= kHeadMaxBytes && head_lds_layout(budget, s.head_dim).total <= kHeadMaxLds;
+          head_bytes <= max_bytes && head_lds_layout(budget, s.head_dim).total <= kHeadMaxLds;
   p.wcap = ((keep + kHNW - 1) / kHNW) * s.page_size;
   p.list_cap = keep * s.page_size;
   p.spill = align256(select_bytes);

@@ -228,11 +228,15 @@ size_t gauss_ws_bytes(const LaunchShape& s);
 // to stream at full rate), the budget is at most kHeadMaxBudget pages, a
 // head's selected K is at most kHeadMaxBytes (beyond it re-reading pages
 // that the heads of a KV head share costs more than the launches it saves:
-// measured 343 -> 415 us at 4 MiB per head) and the kernel's LDS fits. Workspace: the select's bounds, then per (head,
+// measured 343 -> 415 us at 4 MiB per head), or kHeadMaxBytesRounds when
+// the grid takes more than one round of workgroups (one per CU; measured
+// with 512 heads: 256 KiB per head 111 -> 107 us, 1 MiB 178 -> 186 us), and
+// the kernel's LDS fits. Workspace: the select's bounds, then per (head,
 // wave) spill areas of wcap candidates, then per head list_cap window-list
 // entries (scores, then V rows).
 constexpr long long kHeadMinHeads = 128;
 constexpr long long kHeadMaxBytes = 2 << 20;
+constexpr long long kHeadMaxBytesRounds = 512 << 10;
 constexpr size_t kHeadMaxLds = 150 * 1024;
 struct HeadPlan {
   bool use = false;
