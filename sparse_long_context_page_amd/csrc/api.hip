@@ -207,11 +207,15 @@ DecodeWs decode_ws_layout(const LaunchShape& s, const SplitPlan& p) {
 
 namespace {
 
-// Sets the n order keys m[i * kMaxStride] to that of -inf: the start of the
-// score step's shared maxima.
+// Sets the order keys m[i * kMaxStride] and m[i * kMaxStride + 1], i < n, to
+// that of -inf: the start of the score step's shared maxima and shared lower
+// bounds on tau.
 __global__ void reset_maxima_kernel(uint32_t* m, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) m[(size_t)i * kMaxStride] = 0x007fffffu;
+  if (i < n) {
+    m[(size_t)i * kMaxStride] = 0x007fffffu;
+    m[(size_t)i * kMaxStride + 1] = 0x007fffffu;
+  }
 }
 
 hipError_t launch_score(const LaunchShape& s, const SplitPlan& p, const float* q,

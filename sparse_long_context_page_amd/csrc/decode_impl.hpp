@@ -236,11 +236,14 @@ __device__ __forceinline__ void scope_sum2(double& a, double& c, double* red) {
 
 // Safeguarded Newton for sum_i [a_i - t]_+^m = 1 with a_i = am1 * z_i. The
 // root lies in [a_max - 1, a_max): f(a_max - 1) >= 1 (top term is 1) and
-// f(a_max) = 0. Called by the SNT threads t0 = 0..SNT-1 of the scope.
+// f(a_max) = 0. tlo, when given, is a known lower bound on the root (the
+// threshold of a subset of the tokens, less a margin): the bracket and the
+// first step start at max(a_max - 1, tlo). Called by the SNT threads
+// t0 = 0..SNT-1 of the scope.
 template <int SNT, typename ZT>
 __device__ double solve_tau(const ZT* z, int n, double am1, double m, int mcode, double amax,
-                            int t0, double* red) {
-  double lo = amax - 1.0, hi = amax, t = lo;
+                            int t0, double* red, double tlo = -DBL_MAX) {
+  double lo = fmax(amax - 1.0, tlo), hi = amax, t = lo;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fp = 0.0;
     for (int i = t0; i < n; i += SNT) {
@@ -337,8 +340,8 @@ __device__ __forceinline__ auto with_mcode(int mcode, Fn fn) {
 // block must call it and gets the same result.
 template <int K, int MC, int NT>
 __device__ double solve_tau_block(const double (&a)[K], int used, double m, int mcode,
-                                  double amax, double* red) {
-  double lo = amax - 1.0, hi = amax, t = lo;
+                                  double amax, double* red, double tlo = -DBL_MAX) {
+  double lo = fmax(amax - 1.0, tlo), hi = amax, t = lo;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fp = 0.0;
 #pragma unroll
@@ -372,9 +375,9 @@ __device__ double solve_tau_block(const double (&a)[K], int used, double m, int 
 // and stopping rules.
 template <int K, int MC>
 __device__ double solve_tau_regs(const double (&a)[K], int n, double am1, double m, int mcode,
-                                 double amax) {
+                                 double amax, double tlo = -DBL_MAX) {
   (void)am1;
-  double lo = amax - 1.0, hi = amax, t = lo;
+  double lo = fmax(amax - 1.0, tlo), hi = amax, t = lo;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fp = 0.0;
 #pragma unroll
@@ -451,7 +454,7 @@ __device__ double solve_tau_ranked(double a, int n, int mcode, double amax) {
 template <int K, int MC, typename ZT>
 __device__ __forceinline__ void wave_solve_list(const ZT* lz, int* li, float* sp, int n_list, double am1, double m,
                                 int mcode, double amax, int lane, uint64_t ltm, bool compact,
-                                int& n_sup, double& psum, double& tau) {
+                                int& n_sup, double& psum, double& tau, double tlo) {
   double a[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -460,7 +463,7 @@ __device__ __forceinline__ void wave_solve_list(const ZT* lz, int* li, float* sp
   }
   const double t = (n_list <= kWave && (mcode == 1 || mcode == 2))
                        ? solve_tau_ranked(a[0], n_list, mcode, amax)
-                       : solve_tau_regs<K, MC>(a, n_list, am1, m, mcode, amax);
+                       : solve_tau_regs<K, MC>(a, n_list, am1, m, mcode, amax, tlo);
   int o = 0;
   double ps = 0.0;
 #pragma unroll
@@ -553,6 +556,12 @@ struct ScoreArgs {
   // reset to that of -inf before the launch), else null
   uint32_t* gmax;
   int slots;  // LDS candidate slots per (wave, head)
+  // wide windows on the matrix cores: each workgroup solves the threshold of
+  // its own first candidates (a lower bound on tau) and keeps only those
+  // above it; with shared maxima the bound is shared too (word 1 of each
+  // head's gmax line)
+  int local_bound;
+  float alpha;
 };
 
 // One split of one (sequence, KV head) unit, by the whole workgroup.
@@ -585,6 +594,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
   // (reads of it then need not wait for those loads).
   __shared__ Acc wmax[kNW * G];
   __shared__ Acc wfloor[G];
+  __shared__ Acc wlb[G];
   int* wcnt = reinterpret_cast<int*>(smem + lay.wcnt);
   int* slice = reinterpret_cast<int*>(smem + lay.slice);
   int* slots = reinterpret_cast<int*>(smem + lay.slot);
@@ -608,16 +618,20 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
   float qx[QPT];
   // and, full cache, the call's shared maxima of the group's heads (thread
   // t < kNW * G: head t % G), the waves' starting maxima
-  uint32_t gstart = 0x007fffffu;  // the order key of -inf
+  uint32_t gstart = 0x007fffffu;    // the order key of -inf
+  uint32_t gstartlb = 0x007fffffu;  // and the shared lower bound on tau (z units)
   if constexpr (MFMA) {
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
       const int i = k * kNT + tid;
       qx[k] = i < G * D ? q[(size_t)bh0 * D + i] : 0.0f;
     }
-    if (!SPARSE && args.gmax && tid < kNW * G)
+    if (!SPARSE && args.gmax && tid < kNW * G) {
       gstart = __hip_atomic_load(args.gmax + (size_t)(bh0 + tid % G) * kMaxStride, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
+      gstartlb = __hip_atomic_load(args.gmax + (size_t)(bh0 + tid % G) * kMaxStride + 1,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   const int n_slice = build_slice<G, SPARSE>(
@@ -631,6 +645,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
 
   const uint64_t ltm = lanemask_below(lane);
   uint32_t gkey = 0u;  // full cache on the matrix cores: a shared maximum (see below)
+  uint32_t gkeylb = 0x007fffffu;  // and the shared lower bound on tau (order key of -inf)
   if constexpr (MFMA) {
     // Matrix-core scores. Each wave streams its pages into its own two LDS
     // page buffers with direct-to-LDS 16-byte loads: every load instruction
@@ -674,7 +689,10 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     // the call's shared maxima at the start, a floor under the filter level
     // (never a split maximum: those stay the maxima of the split's own
     // tokens, which the threshold step takes as distinct token scores)
-    if (tid < G) wfloor[tid] = gm ? order_float(gstart) : neg_inf<Acc>();
+    if (tid < G) {
+      wfloor[tid] = gm ? order_float(gstart) : neg_inf<Acc>();
+      wlb[tid] = gm ? order_float(gstartlb) : neg_inf<Acc>();
+    }
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
       const int i = k * kNT + tid;
@@ -714,14 +732,16 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
     Acc M[NMB];
     int mycnt[NMB];
     // The filter level starts from the call's shared maxima (gfl, read
-    // into wfloor before the barrier above).
-    Acc gfl[NMB];
+    // into wfloor before the barrier above) and never drops below the
+    // call's shared lower bound on tau (glb, from wlb).
+    Acc gfl[NMB], glb[NMB];
 #pragma unroll
     for (int blk = 0; blk < NMB; ++blk) {
       const int h = blk * 4 + kgrp;
       M[blk] = neg_inf<Acc>();
       mycnt[blk] = 0;
       gfl[blk] = h < G ? wfloor[h] : neg_inf<Acc>();
+      glb[blk] = h < G ? wlb[h] : neg_inf<Acc>();
     }
     // Page pp into buffer `bsel` (an invalid physical page, or a page past
     // the slice, reads page 0 of the pool; its scores are dropped). The loads
@@ -807,7 +827,7 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
         pm = max(pm, partner<4>(pm));
         pm = max(pm, partner<8>(pm));
         M[blk] = max(M[blk], pm);
-        const Acc thr = max(M[blk], om[blk]) - window;
+        const Acc thr = max(max(M[blk], om[blk]) - window, glb[blk]);
         const int h = blk * 4 + kgrp;
         if (tok == 0 && h < G) wmax[wave * G + h] = M[blk];
 #pragma unroll
@@ -848,9 +868,12 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
       }
       // the shared maxima once more, for the workgroup pass below (lane h
       // of every wave holds head h's), waited for with the page loads
-      if (gm && lane < G)
+      if (gm && lane < G) {
         gkey = __hip_atomic_load(gm + (size_t)(bh0 + lane) * kMaxStride, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
+        gkeylb = __hip_atomic_load(gm + (size_t)(bh0 + lane) * kMaxStride + 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+      }
       wait_vmcnt<0>();  // no load into LDS is left in flight
     } else {
       // One buffer: short slices (the sparse path) keep more workgroups
@@ -1013,7 +1036,8 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
       const uint32_t key = lane_value(gkey, h);
       if (key > float_order((float)mg)) mf = (Acc)order_float(key);
     }
-    const Acc thr = mf - window;
+    Acc thr = mf - window;
+    if (shared) thr = max(thr, (Acc)order_float(lane_value(gkeylb, h)));
     const size_t r = (size_t)(bh0 + h) * splits + split;
     Cand<Acc>* dst = cand + r * (size_t)cap;
     // The waves' lists, concatenated in wave order, are read kWave *
@@ -1030,10 +1054,10 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
       nsp += max(0, n - lists.slots);
     }
     const int ntot = nb[kNW];
-    int o = 0;
-    for (int base = 0; base < ntot; base += kWave * kPassRegs) {
-      Acc zr[kPassRegs];
-      int ir[kPassRegs], pr[kPassRegs];
+    // entries base + k * 64 + lane of the concatenation (past the end: its
+    // last entry) into zr / ir
+    auto load_batch = [&](int base, Acc (&zr)[kPassRegs], int (&ir)[kPassRegs]) {
+      int pr[kPassRegs];
       Cand<Acc> cs[kPassRegs];
 #pragma unroll
       for (int k = 0; k < kPassRegs; ++k) {
@@ -1057,6 +1081,55 @@ __device__ __forceinline__ void score_split(const ScoreArgs<KV>& args, int split
           zr[k] = cs[k].z;
           ir[k] = cs[k].idx;
         }
+      }
+    };
+    if constexpr (MFMA) {
+      if (args.local_bound && ntot > 0) {
+        // The threshold t_S of any set S of the head's tokens is at most tau
+        // (the left side of the threshold equation only grows with more
+        // tokens), so every support token has a = (alpha-1) z > t_S. S = the
+        // first kWave * kPassRegs candidates above the filter level, solved
+        // in this wave's registers; the filter level rises to t_S (less a
+        // relative 1e-6 for rounding) and, with shared maxima, so does the
+        // call's shared bound of the head.
+        Acc zr[kPassRegs];
+        int ir[kPassRegs];
+        load_batch(0, zr, ir);
+        const double am1 = (double)args.alpha - 1.0;
+        const double m = 1.0 / am1;
+        const int mcode = (m == 1.0) ? 1 : (m == 2.0) ? 2 : (m == 3.0) ? 3 : (m == 4.0) ? 4 : 0;
+        double av[kPassRegs];
+        double amx = -DBL_MAX;
+#pragma unroll
+        for (int k = 0; k < kPassRegs; ++k) {
+          const bool ok = k * kWave + lane < ntot && zr[k] >= thr;
+          av[k] = ok ? am1 * (double)zr[k] : -DBL_MAX;
+          amx = fmax(amx, av[k]);
+        }
+        amx = wave_max(amx);
+        if (amx > -DBL_MAX) {
+          const double ts = with_mcode(mcode, [&](auto mc) {
+            return solve_tau_regs<kPassRegs, decltype(mc)::value>(
+                av, min(ntot, kWave * kPassRegs), am1, m, mcode, amx);
+          });
+          const Acc lbz = (Acc)((ts - 1e-6 * fmax(1.0, fabs(ts))) / am1);
+          if (lbz > thr) {
+            thr = lbz;
+            if (shared && lane == 0)
+              __hip_atomic_fetch_max(args.gmax + (size_t)(bh0 + h) * kMaxStride + 1,
+                                     float_order((float)lbz), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    }
+    int o = 0;
+    for (int base = 0; base < ntot; base += kWave * kPassRegs) {
+      Acc zr[kPassRegs];
+      int ir[kPassRegs];
+      load_batch(base, zr, ir);
+#pragma unroll
+      for (int k = 0; k < kPassRegs; ++k) {
         const bool f = base + k * kWave + lane < ntot && zr[k] >= thr;
         const uint64_t bal = __ballot(f);
         if (f) {
@@ -1251,7 +1324,7 @@ template <typename ZT, int KB, int NT>
 __device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int* li, float* sp,
                                                                int n_list, double am1, double m,
                                                                int mcode, double amax, double* red,
-                                                               int* tmp) {
+                                                               int* tmp, double tlo) {
   const int tid = threadIdx.x;
   lz = lds_view(lz);
   li = lds_view(li);
@@ -1265,7 +1338,7 @@ __device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int
 #pragma unroll
   for (int k = 0; k < KB; ++k) a[k] = (e0 + k < e1) ? am1 * (double)lz[e0 + k] : -DBL_MAX;
   const double tau = with_mcode(mcode, [&](auto mc) {
-    return solve_tau_block<KB, decltype(mc)::value, NT>(a, per, m, mcode, amax, red);
+    return solve_tau_block<KB, decltype(mc)::value, NT>(a, per, m, mcode, amax, red, tlo);
   });
   int ns = 0;
 #pragma unroll
@@ -1293,16 +1366,91 @@ __device__ __attribute__((noinline)) TauSolution tau_long_list(const ZT* lz, int
   return r;
 }
 
+// A window list in LDS longer than one wave's registers hold (integer m):
+// a few block-wide Newton steps from the left raise the lower bound on tau
+// (each iterate with f(t) >= 1 is at most tau), then the entries at or below
+// it, which take no part in the threshold or the output, are dropped and the
+// rest compacted to the front in list order. Repeated while the list is
+// longer than kWave * kRegListLong and the steps make progress. Returns the
+// new length; *tlo gets the bound. Every thread of the workgroup calls it.
+template <typename ZT, int KB, int NT>
+__device__ __attribute__((noinline)) int tau_prune_list(ZT* lz, int* li, int n_list, double am1,
+                                                        double m, int mcode, double amax,
+                                                        double* red, int* tmp, double* tlo) {
+  const int tid = threadIdx.x;
+  lz = lds_view(lz);
+  li = lds_view(li);
+  red = lds_view(red);
+  tmp = lds_view(tmp);
+  constexpr int kSteps = 3;
+  double lo = fmax(amax - 1.0, *tlo);
+  for (int round = 0; round < 4 && n_list > kWave * kRegListLong; ++round) {
+    const int per = (n_list + NT - 1) / NT;
+    const int e0 = min(n_list, tid * per), e1 = min(n_list, e0 + per);
+    const double lo0 = lo;
+    int ns = 0;
+    {
+      double a[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) a[k] = e0 + k < e1 ? am1 * (double)lz[e0 + k] : -DBL_MAX;
+      double t = lo;
+      for (int it = 0; it < kSteps; ++it) {
+        double f = 0.0, fp = 0.0;
+        with_mcode<true>(mcode, [&](auto mc) {
+#pragma unroll
+          for (int k = 0; k < KB; ++k)
+            if (k < per) add_terms<decltype(mc)::value>(a[k] - t, m, mcode, f, fp);
+        });
+        scope_sum2<NT>(f, fp, red);
+        fp *= m;
+        if (!(f >= 1.0) || !(fp > 0.0)) break;  // (not left of the root)
+        lo = t;
+        if (f == 1.0) break;
+        t = t + (f - 1.0) / fp;
+        if (!(t < amax)) break;
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) ns += (a[k] > lo) ? 1 : 0;
+    }
+    int kept;
+    int base = block_excl_scan<NT>(ns, tmp, &kept);
+    // every thread reads its run before any is overwritten
+    ZT zv[KB];
+    int iv[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      zv[k] = e0 + k < e1 ? lz[e0 + k] : (ZT)0;
+      iv[k] = e0 + k < e1 ? li[e0 + k] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      if (e0 + k < e1 && am1 * (double)zv[k] > lo) {
+        lz[base] = zv[k];
+        li[base] = iv[k];
+        ++base;
+      }
+    }
+    __syncthreads();
+    const bool progress = kept < n_list && lo > lo0;
+    n_list = kept;
+    if (!progress) break;
+  }
+  *tlo = lo;
+  return n_list;
+}
+
 // A window list in global memory (longer than the LDS capacity): the
 // block-wide Newton solve over it, the support size and the sum of p.
 template <typename ZT, int NT>
 __device__ __attribute__((noinline)) TauSolution tau_global_list(const ZT* dz, int n_list,
                                                                  double am1, double m, int mcode,
-                                                                 double amax, double* red) {
+                                                                 double amax, double* red,
+                                                                 double tlo) {
   const int tid = threadIdx.x;
   red = lds_view(red);
   TauSolution r;
-  r.tau = solve_tau<NT>(dz, n_list, am1, m, mcode, amax, tid, red);
+  r.tau = solve_tau<NT>(dz, n_list, am1, m, mcode, amax, tid, red, tlo);
   int ns = 0;
   double psum = 0.0;
   for (int i = tid; i < n_list; i += NT) {
@@ -1376,7 +1524,7 @@ __device__ __forceinline__ void tau_solve_pv(
     const KV* __restrict__ v_pool, int Hkv, int g, int PS, typename KvTraits<KV>::Acc* lz,
     int* li, float* sp, float* pvbase, int n_list, int lcap, typename KvTraits<KV>::Acc* gz,
     int* gi, double am1, double m, int mcode, double amax, TauShared<NT>& sh,
-    float* __restrict__ out_row, float* tau_p, int32_t* sup_p) {
+    float* __restrict__ out_row, float* tau_p, int32_t* sup_p, double tlo) {
   using ZT = typename KvTraits<KV>::Acc;
   constexpr int VPC = 16 / sizeof(KV);
   constexpr int LR = D / VPC;     // lanes per V row
@@ -1425,6 +1573,9 @@ __device__ __forceinline__ void tau_solve_pv(
   double tau;
   int n_sup;
   double psum = 0.0;
+  if (list_lds && mcode != 0 && n_list > kWave * kRegListLong)
+    n_list = tau_prune_list<ZT, KB, NT>(lz, li, n_list, am1, m, mcode, amax, sh.red, sh.tmp, &tlo);
+
   if (list_lds && n_list <= kWave * kRegList) {
     // Short lists (up to 256): wave 0 holds a_i = am1 * z_i in registers for
     // the whole solve (no barrier per iteration), then compacts (V row, p)
@@ -1437,7 +1588,7 @@ __device__ __forceinline__ void tau_solve_pv(
       // support is not compacted into li.
       with_mcode(mcode, [&](auto mc) {
         wave_solve_list<kRegList, decltype(mc)::value>(lz, li, sp, n_list, am1, m, mcode, amax,
-                                                       lane, ltm, !vpre, o, psum, t);
+                                                       lane, ltm, !vpre, o, psum, t, tlo);
       });
       if (lane == 0) {
         sh.nb[1] = o;
@@ -1457,7 +1608,7 @@ __device__ __forceinline__ void tau_solve_pv(
       double t;
       with_mcode<true>(mcode, [&](auto mc) {
         wave_solve_list<kRegListLong, decltype(mc)::value>(lz, li, sp, n_list, am1, m, mcode,
-                                                           amax, lane, ltm, true, o, psum, t);
+                                                           amax, lane, ltm, true, o, psum, t, tlo);
       });
       if (lane == 0) {
         sh.nb[1] = o;
@@ -1473,8 +1624,9 @@ __device__ __forceinline__ void tau_solve_pv(
     // Longer lists, out of line: up to the LDS capacity by the workgroup,
     // beyond it from global memory.
     const TauSolution r = list_lds ? tau_long_list<ZT, KB, NT>(lz, li, sp, n_list, am1, m, mcode, amax,
-                                                          sh.red, sh.tmp)
-                                   : tau_global_list<ZT, NT>(dz, n_list, am1, m, mcode, amax, sh.red);
+                                                          sh.red, sh.tmp, tlo)
+                                   : tau_global_list<ZT, NT>(dz, n_list, am1, m, mcode, amax, sh.red,
+                                                             tlo);
     tau = r.tau;
     n_sup = r.n_sup;
     psum = r.psum;
@@ -1490,9 +1642,6 @@ __device__ __forceinline__ void tau_solve_pv(
 #pragma unroll
     for (int e = 0; e < VPC; ++e) acc[e] = fmaf(pk, (float)f[e], acc[e]);
   };
-  auto accumulate = [&](const KV* vp, float pk) {
-    accumulate_x(*reinterpret_cast<const uint4*>(vp), pk);
-  };
   if (vpre) {
     // p from the list's scores (z is not moved by the support compaction),
     // by the same expression the solve summed
@@ -1507,18 +1656,24 @@ __device__ __forceinline__ void tau_solve_pv(
 #pragma unroll
     for (int e = 0; e < VPC; ++e) pvacc[grp][c * VPC + e] = acc[e];
   } else if (list_lds) {
-    int k = grp;
-    for (; k + 3 * NG < n_sup; k += 4 * NG) {
-      const KV* p0 = row_ptr(li[k]);
-      const KV* p1 = row_ptr(li[k + NG]);
-      const KV* p2 = row_ptr(li[k + 2 * NG]);
-      const KV* p3 = row_ptr(li[k + 3 * NG]);
-      accumulate(p0, sp[k]);
-      accumulate(p1, sp[k + NG]);
-      accumulate(p2, sp[k + 2 * NG]);
-      accumulate(p3, sp[k + 3 * NG]);
+    // the support's rows in batches of RPT per thread (rows grp, grp + NG,
+    // ...), every load of a batch issued before the first is used (slots
+    // past the support re-read its last row with weight 0; every use is
+    // unconditional, so no load is moved into a branch), so a support of up
+    // to RPT * NG rows costs one round trip
+    constexpr int RPT = 4096 / NT;
+    for (int k0 = grp; k0 < n_sup; k0 += RPT * NG) {
+      uint4 x[RPT];
+      float pk[RPT];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int k = min(k0 + i * NG, n_sup - 1);
+        x[i] = *reinterpret_cast<const uint4*>(row_ptr(li[k]));
+        pk[i] = k0 + i * NG < n_sup ? sp[k] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) accumulate_x(x[i], pk[i]);
     }
-    for (; k < n_sup; k += NG) accumulate(row_ptr(li[k]), sp[k]);
 #pragma unroll
     for (int e = 0; e < VPC; ++e) pvacc[grp][c * VPC + e] = acc[e];
   } else {
@@ -1554,6 +1709,9 @@ struct TauArgs {
   float* out;
   float* tau_out;
   int32_t* sup_out;
+  // the score step's per-head lines of shared maxima (word 1: its shared
+  // lower bound on tau), or null when it shares none
+  const uint32_t* glb;
 };
 
 // One query head (unit u, head hh of its group), by the whole workgroup.
@@ -1595,6 +1753,8 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
   const ZT* mx = maxima + (size_t)bh * splits;
   const int* cn = counts + (size_t)bh * splits;
   const Cand<ZT>* creg = cand + (size_t)bh * splits * cap;
+  // the score step's shared lower bound on tau (order key; -inf without one)
+  const uint32_t glb_key = args.glb ? args.glb[(size_t)bh * kMaxStride + 1] : 0x007fffffu;
   const double am1 = (double)alpha - 1.0;
   const double m = 1.0 / am1;
   const int mcode = (m == 1.0) ? 1 : (m == 2.0) ? 2 : (m == 3.0) ? 3 : (m == 4.0) ? 4 : 0;
@@ -1633,6 +1793,8 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
   }
   const double amax = am1 * (double)M;
   ZT thr = M - window;
+  // the score step's shared lower bound on tau of this head (wide windows)
+  if (glb_key != 0x007fffffu && (ZT)order_float(glb_key) > thr) thr = (ZT)order_float(glb_key);
   if (n_cand > kTauBoundFrom) {
     // Many candidates: tighten the window with a lower bound on tau.
     const ZT lb = tau_window_bound(mloc, rmax, &tsh.tau_b, am1, m, mcode, amax);
@@ -1658,9 +1820,11 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
                                           bbase, nb_, n_list);
   }
   __syncthreads();
+  // (every bound that raised thr is at most tau, so Newton may start there)
   tau_solve_pv<KV, D, kNT>(v_pool, Hkv, g, PS, lz, li, sp, &pvacc[0][0], n_list, lcap, gz, gi,
                            am1, m, mcode, amax, tsh, out + (size_t)bh * D,
-                           tau_out ? tau_out + bh : nullptr, sup_out ? sup_out + bh : nullptr);
+                           tau_out ? tau_out + bh : nullptr, sup_out ? sup_out + bh : nullptr,
+                           am1 * (double)thr);
 }
 
 // One kernel serves the budgeted and the full-cache decode (the step is the
@@ -1679,7 +1843,7 @@ tau_pv_kernel(TauArgs<KV> args) {
 template <typename KV>
 ScoreArgs<KV> score_args(const LaunchShape& s, const SplitPlan& p, const float* q,
                          const void* k_pool, const int32_t* bt, const int32_t* lens,
-                         const int32_t* sel, int budget, float window, void* ws,
+                         const int32_t* sel, int budget, float alpha, float window, void* ws,
                          const DecodeWs& L) {
   using ZT = typename KvTraits<KV>::Acc;
   char* w = static_cast<char*>(ws);
@@ -1706,6 +1870,8 @@ ScoreArgs<KV> score_args(const LaunchShape& s, const SplitPlan& p, const float* 
   const ScoreMode mode = score_mode(s, p, sel != nullptr, budget, window);
   a.gmax = mode.share ? reinterpret_cast<uint32_t*>(w + L.gmax) : nullptr;
   a.slots = mode.slots;
+  a.local_bound = s.bf16 && kMfmaScores && window >= kWideWindow;
+  a.alpha = alpha;
   return a;
 }
 
@@ -1728,7 +1894,8 @@ hipError_t launch_score_t(const LaunchShape& s, const SplitPlan& p, const float*
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxScoreLdsBytes);
   if (lds_raised != hipSuccess) return lds_raised;
   char* w = static_cast<char*>(ws);
-  const ScoreArgs<KV> args = score_args<KV>(s, p, q, k_pool, bt, lens, sel, budget, window, ws, L);
+  const ScoreArgs<KV> args =
+      score_args<KV>(s, p, q, k_pool, bt, lens, sel, budget, alpha, window, ws, L);
   hipLaunchKernelGGL(kern, dim3(U * p.splits), dim3(kNT), lay.total, st, args);
   return hipGetLastError();
 }
@@ -1774,7 +1941,7 @@ hipError_t launch_score_kv(const LaunchShape& s, const SplitPlan& p, const float
 template <typename KV>
 TauArgs<KV> tau_args(const LaunchShape& s, const SplitPlan& p, const void* v_pool, float alpha,
                      float window, float* out, float* tau, int32_t* support, void* ws,
-                     const DecodeWs& L, int lcap) {
+                     const DecodeWs& L, int lcap, bool share) {
   using ZT = typename KvTraits<KV>::Acc;
   char* w = static_cast<char*>(ws);
   TauArgs<KV> a;
@@ -1798,6 +1965,7 @@ TauArgs<KV> tau_args(const LaunchShape& s, const SplitPlan& p, const void* v_poo
   a.out = out;
   a.tau_out = tau;
   a.sup_out = support;
+  a.glb = share ? reinterpret_cast<const uint32_t*>(w + L.gmax) : nullptr;
   return a;
 }
 
@@ -1806,7 +1974,7 @@ hipError_t launch_tau_pv_t(const LaunchShape& s, const SplitPlan& p, const void*
                            const int32_t* bt, const int32_t* lens, const int32_t* sel, int budget,
                            float alpha, float window, float* out, float* tau, int32_t* support,
                            void* ws, const DecodeWs& L, hipStream_t st) {
-  (void)bt; (void)lens; (void)sel; (void)budget;
+  (void)bt; (void)lens; (void)sel;
   using ZT = typename KvTraits<KV>::Acc;
   constexpr int NG = kNT / (D / (16 / (int)sizeof(KV)));
   const int U = s.batch * s.num_kv_heads;
@@ -1823,7 +1991,8 @@ hipError_t launch_tau_pv_t(const LaunchShape& s, const SplitPlan& p, const void*
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)tau_lds_layout(kMaxSplits, kTauMaxList, 8, NG, D).total);
   if (lds_raised != hipSuccess) return lds_raised;
-  const TauArgs<KV> args = tau_args<KV>(s, p, v_pool, alpha, window, out, tau, support, ws, L, lcap);
+  const TauArgs<KV> args = tau_args<KV>(s, p, v_pool, alpha, window, out, tau, support, ws, L,
+                                        lcap, score_mode(s, p, SPARSE, budget, window).share);
   hipLaunchKernelGGL(kern, dim3(U * s.group), dim3(kNT), lds, st, args);
   return hipGetLastError();
 }

@@ -445,7 +445,7 @@ head_decode_kernel(HeadArgs a) {
                                 reinterpret_cast<float*>(smem + lay.pv), n_list, kHeadLcap, gz,
                                 gi, am1, m, mcode, amax, tsh, out_row,
                                 a.tau_out ? a.tau_out + bh : nullptr,
-                                a.sup_out ? a.sup_out + bh : nullptr);
+                                a.sup_out ? a.sup_out + bh : nullptr, am1 * (double)thr);
 }
 
 }  // namespace ekv
