@@ -48,6 +48,7 @@ PEAK_HBM_GBPS = 8000.0
 # kernels of the sparse path (entmaxkv_decode_topk) on its per-head path and
 # on its four-kernel path, then those of the full-cache path
 SPARSE_KERNELS_HEAD = ["bounds", "select_decode"]
+SPARSE_KERNELS_HEAD_SPLIT = ["bounds", "select_score", "tau_pv_sparse"]
 SPARSE_KERNELS_SPLIT = ["bounds", "select", "score_sparse", "tau_pv_sparse"]
 FULL_KERNELS = ["score_full", "tau_pv_full"]
 KERNEL_SOURCES = ["common.hpp", "launch.hpp", "mfma.hpp", "select.hip", "select_impl.hpp",
@@ -57,8 +58,8 @@ KERNEL_SOURCES = ["common.hpp", "launch.hpp", "mfma.hpp", "select.hip", "select_
 
 def sparse_kernels(E, shape, budget) -> list:
     """Names of the kernels entmaxkv_decode_topk runs at this shape and budget."""
-    return SPARSE_KERNELS_HEAD if E.entmaxkv_topk_kernels(shape, budget) == 2 \
-        else SPARSE_KERNELS_SPLIT
+    n = E.entmaxkv_topk_kernels(shape, budget)
+    return {2: SPARSE_KERNELS_HEAD, 3: SPARSE_KERNELS_HEAD_SPLIT}.get(n, SPARSE_KERNELS_SPLIT)
 
 
 # ---------------------------------------------------------------------------
@@ -106,6 +107,9 @@ def algorithmic_bytes(w, lens: np.ndarray, budget: int, sel: np.ndarray, sup_spa
         # the per-head kernel: selection written, K of the union pages (each
         # page counted once per KV head, as above), V of the support, outputs
         "select_decode": sel_b + k_sel_b + q_b + bt_b + v_sup_sparse + out_b,
+        # its split form: selection, K of the union pages (the threshold
+        # kernel then reads the V rows)
+        "select_score": sel_b + k_sel_b + q_b + bt_b,
         # what the per-head kernel requests: each selected page once per head
         "_k_per_head": int((sel >= 0).sum()) * ps * D * s,
         "score_full": k_full_b + q_b + bt_b,

@@ -283,14 +283,19 @@ int entmaxkv_decode_sparse(const entmaxkv_shape* shape, const float* q, const vo
  * way, so equal up to the order of the threshold solve's float64 sums).
  * sel is required; sel_ub, tau and support are nullable.
  * With bf16 caches, at least 128 query heads in the batch (batch *
- * num_q_heads) and budget_pages <= 1024, it runs two kernels: the bounds,
- * then one workgroup per query head that selects the head's pages, gathers
- * and scores them, solves tau and writes the output (no candidate crosses a
- * workgroup). Otherwise the four kernels of the two calls run.
+ * num_q_heads), budget_pages <= 1024 and at most 2 MiB of selected keys per
+ * head (512 KiB beyond 256 heads), it runs two kernels: the bounds, then one
+ * workgroup per query head that selects the head's pages, gathers and
+ * scores them, solves tau and writes the output (no candidate crosses a
+ * workgroup). With bf16 caches, fewer than 128 heads and budget_pages <=
+ * 1024, it runs three: the bounds, several workgroups per head that each
+ * select the head's pages and gather and score a share of them, and the
+ * threshold kernel. Otherwise the four kernels of the two calls run.
  * Workspace: entmaxkv_workspace_bytes(..., ENTMAXKV_WS_TOPK) for the same
  * budget_pages. events (nullable): 2*4 handles; pairs 0 and 1 enclose the
  * bounds and the select (or the per-head kernel), pairs 2 and 3 the sparse
- * decode's two kernels (empty intervals on the per-head path).
+ * decode's two kernels (on the per-head path pair 2 encloses the threshold
+ * kernel of the split form, else nothing, and pair 3 nothing).
  */
 int entmaxkv_decode_topk(const entmaxkv_shape* shape, const float* q, const void* meta,
                          const void* k_pool, const void* v_pool, const int32_t* block_table,
@@ -300,8 +305,9 @@ int entmaxkv_decode_topk(const entmaxkv_shape* shape, const float* q, const void
 
 /*
  * Number of kernels entmaxkv_decode_topk launches at this shape and budget:
- * 2 on the per-head path, 4 otherwise. Writes *kernels; returns an error
- * code for an invalid or unsupported shape or budget.
+ * 2 on the per-head path, 3 on its split form, 4 otherwise. Writes
+ * *kernels; returns an error code for an invalid or unsupported shape or
+ * budget.
  */
 int entmaxkv_topk_kernels(const entmaxkv_shape* shape, int32_t budget_pages, int32_t* kernels);
 

@@ -561,9 +561,14 @@ int entmaxkv_decode_topk(const entmaxkv_shape* shape, const float* q, const void
                            alpha, window, sel, sel_ub, out, tau, support, ws, bt_lds,
                            stream) != hipSuccess)
       return ENTMAXKV_ERR_HIP;
-    // pairs 2 and 3 enclose nothing on this path
-    if (!ev.after(1) || !ev.before(2) || !ev.after(2) || !ev.before(3) || !ev.after(3))
+    if (!ev.after(1) || !ev.before(2)) return ENTMAXKV_ERR_HIP;
+    if (w.head.splits > 1 &&
+        launch_tau_pv(s, w.head.tp, v_pool, block_table, seq_lens, sel, budget_pages, alpha,
+                      window, out, tau, support, static_cast<char*>(ws) + w.head.dec, w.head.tws,
+                      stream) != hipSuccess)
       return ENTMAXKV_ERR_HIP;
+    // pair 3 (and pair 2 without splits) encloses nothing on this path
+    if (!ev.after(2) || !ev.before(3) || !ev.after(3)) return ENTMAXKV_ERR_HIP;
     return ENTMAXKV_OK;
   }
   if (launch_select(s, sp, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
@@ -582,7 +587,7 @@ int entmaxkv_topk_kernels(const entmaxkv_shape* shape, int32_t budget_pages, int
   if (!kernels) return ENTMAXKV_ERR_INVALID;
   TopkWs w;
   if ((rc = topk_ws(s, budget_pages, &w))) return rc;
-  *kernels = w.head.use ? 2 : 4;
+  *kernels = w.head.use ? (w.head.splits > 1 ? 3 : 2) : 4;
   return ENTMAXKV_OK;
 }
 

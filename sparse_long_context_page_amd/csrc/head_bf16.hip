@@ -12,20 +12,46 @@ HeadPlan plan_head(const LaunchShape& s, int budget, size_t select_bytes) {
   const int keep = budget < s.max_pages ? budget : s.max_pages;
   const long long head_bytes = (long long)keep * s.page_size * s.head_dim * 2;
   const long long max_bytes = heads > kNumCUs ? kHeadMaxBytesRounds : kHeadMaxBytes;
-  p.use = s.bf16 && kMfmaScores && budget <= kHeadMaxBudget && heads >= kHeadMinHeads &&
-          head_bytes <= max_bytes && head_lds_layout(budget, s.head_dim).total <= kHeadMaxLds;
-  p.wcap = ((keep + kHNW - 1) / kHNW) * s.page_size;
+  const bool fits = s.bf16 && kMfmaScores && budget <= kHeadMaxBudget &&
+                    head_lds_layout(budget, s.head_dim).total <= kHeadMaxLds;
+  if (fits && heads >= kHeadMinHeads && head_bytes <= max_bytes) {
+    p.use = true;
+  } else if (fits && heads < kHeadMinHeads) {
+    // split form: about kHeadSplitTarget workgroups in all
+    long long sp = (kHeadSplitTarget + heads - 1) / heads;
+    if (sp > keep) sp = keep;
+    if (sp < 1) sp = 1;
+    p.pps = (int)((keep + sp - 1) / sp);
+    p.splits = (keep + p.pps - 1) / p.pps;
+    p.use = (long long)p.pps * s.page_size <= kHeadLcap;
+  }
   p.list_cap = keep * s.page_size;
   p.spill = align256(select_bytes);
-  p.list = align256(p.spill + (size_t)heads * kHNW * p.wcap * sizeof(Cand<float>));
-  p.total = align256(p.list + (size_t)heads * p.list_cap * 8);
+  if (p.splits > 1) {
+    p.wcap = ((p.pps + kHNW - 1) / kHNW) * s.page_size;
+    p.tp.pages_per_split = p.pps;
+    p.tp.splits = p.splits;
+    p.tp.cap = p.pps * s.page_size;
+    p.tp.regions = p.splits;
+    p.tp.rcap = p.tp.cap;
+    p.tp.list_cap = p.list_cap;
+    p.tws = decode_ws_layout(s, p.tp);
+    p.dec = align256(p.spill + (size_t)heads * p.splits * kHNW * p.wcap * sizeof(Cand<float>));
+    p.list = p.dec;
+    p.total = align256(p.dec + p.tws.total);
+  } else {
+    p.pps = keep;
+    p.wcap = ((keep + kHNW - 1) / kHNW) * s.page_size;
+    p.list = align256(p.spill + (size_t)heads * kHNW * p.wcap * sizeof(Cand<float>));
+    p.total = align256(p.list + (size_t)heads * p.list_cap * 8);
+  }
   return p;
 }
 
-template <int D, int PS, bool CAND>
+template <int D, int PS, bool CAND, bool SPLIT>
 static hipError_t launch_head_t(const LaunchShape& s, const SelectPlan& sp, const HeadPlan& hp,
                                 const HeadArgs& a, hipStream_t st) {
-  auto kern = head_decode_kernel<D, PS, CAND>;
+  auto kern = head_decode_kernel<D, PS, CAND, SPLIT>;
   // The LDS limit is a kernel attribute: raised once, to the most any plan
   // asks for (a function-local static is initialised exactly once, also when
   // several host threads launch).
@@ -36,18 +62,26 @@ static hipError_t launch_head_t(const LaunchShape& s, const SelectPlan& sp, cons
   (void)sp;
   (void)hp;
   const size_t lds = head_lds_layout(a.budget, D).total;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(s.batch * s.num_q_heads)), dim3(kHNT), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(s.batch * s.num_q_heads * hp.splits)), dim3(kHNT), lds,
+                     st, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAND>
+template <int D, bool CAND, bool SPLIT>
 static hipError_t launch_head_ps(const LaunchShape& s, const SelectPlan& sp, const HeadPlan& hp,
                                  const HeadArgs& a, hipStream_t st) {
   switch (s.page_size) {
-    case 16: return launch_head_t<D, 16, CAND>(s, sp, hp, a, st);
-    case 32: return launch_head_t<D, 32, CAND>(s, sp, hp, a, st);
-    default: return launch_head_t<D, 64, CAND>(s, sp, hp, a, st);
+    case 16: return launch_head_t<D, 16, CAND, SPLIT>(s, sp, hp, a, st);
+    case 32: return launch_head_t<D, 32, CAND, SPLIT>(s, sp, hp, a, st);
+    default: return launch_head_t<D, 64, CAND, SPLIT>(s, sp, hp, a, st);
   }
+}
+
+template <int D, bool CAND>
+static hipError_t launch_head_sp(const LaunchShape& s, const SelectPlan& sp, const HeadPlan& hp,
+                                 const HeadArgs& a, hipStream_t st) {
+  return hp.splits > 1 ? launch_head_ps<D, CAND, true>(s, sp, hp, a, st)
+                       : launch_head_ps<D, CAND, false>(s, sp, hp, a, st);
 }
 
 hipError_t launch_head_decode(const LaunchShape& s, const SelectPlan& sp, const HeadPlan& hp,
@@ -87,11 +121,17 @@ hipError_t launch_head_decode(const LaunchShape& s, const SelectPlan& sp, const 
   a.out = out;
   a.tau_out = tau;
   a.sup_out = support;
+  a.splits = hp.splits;
+  a.pps = hp.pps;
+  a.rcap = hp.tp.rcap;
+  a.cand = hp.splits > 1 ? reinterpret_cast<Cand<float>*>(w + hp.dec + hp.tws.cand) : nullptr;
+  a.counts = hp.splits > 1 ? reinterpret_cast<int*>(w + hp.dec + hp.tws.counts) : nullptr;
+  a.maxima = hp.splits > 1 ? reinterpret_cast<float*>(w + hp.dec + hp.tws.maxima) : nullptr;
   if (s.head_dim == 64)
-    return sp.chunked ? launch_head_ps<64, true>(s, sp, hp, a, st)
-                      : launch_head_ps<64, false>(s, sp, hp, a, st);
-  return sp.chunked ? launch_head_ps<128, true>(s, sp, hp, a, st)
-                    : launch_head_ps<128, false>(s, sp, hp, a, st);
+    return sp.chunked ? launch_head_sp<64, true>(s, sp, hp, a, st)
+                      : launch_head_sp<64, false>(s, sp, hp, a, st);
+  return sp.chunked ? launch_head_sp<128, true>(s, sp, hp, a, st)
+                    : launch_head_sp<128, false>(s, sp, hp, a, st);
 }
 
 }  // namespace ekv

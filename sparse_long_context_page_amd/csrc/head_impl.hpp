@@ -98,9 +98,16 @@ struct HeadArgs {
   float* out;
   float* tau_out;
   int32_t* sup_out;
+  // split form: workgroup (head, split) takes selection slots [split * pps,
+  // (split + 1) * pps) and writes its candidate region (window members of
+  // its own maximum; count and maximum) for the threshold kernel
+  int splits, pps, rcap;
+  Cand<float>* cand;
+  int* counts;
+  float* maxima;
 };
 
-template <int D, int PS, bool CAND>
+template <int D, int PS, bool CAND, bool SPLIT>
 __global__ void __launch_bounds__(kHNT)
 head_decode_kernel(HeadArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -125,7 +132,10 @@ head_decode_kernel(HeadArgs a) {
   const HeadLds lay = head_lds_layout(a.budget, D);
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int u = blockIdx.x % a.U, hh = blockIdx.x / a.U;
+  const int nheads = a.U * a.G;
+  const int hid = SPLIT ? (int)(blockIdx.x % nheads) : (int)blockIdx.x;
+  const int split = SPLIT ? (int)(blockIdx.x / nheads) : 0;
+  const int u = hid % a.U, hh = hid / a.U;
   const int b = u / a.Hkv, g = u % a.Hkv;
   const int bh = b * a.H + g * a.G + hh;
   const int budget = a.budget, max_pages = a.max_pages, num_phys = a.num_phys;
@@ -162,10 +172,12 @@ head_decode_kernel(HeadArgs a) {
       a.cp, a.keepc, CAND ? a.nchunks * a.keepc : a.ldu, reinterpret_cast<uint32_t*>(smem), ssh,
       [&](int pos, int page, uint32_t key) {
         sel_l[pos] = page;
-        a.sel[(size_t)bh * budget + pos] = page;
-        if (a.sel_ub) a.sel_ub[(size_t)bh * budget + pos] = order_float(key);
+        if (split == 0) {  // (every split selects; the first writes the selection)
+          a.sel[(size_t)bh * budget + pos] = page;
+          if (a.sel_ub) a.sel_ub[(size_t)bh * budget + pos] = order_float(key);
+        }
       });
-  for (int i = n_sel + tid; i < budget; i += kHNT) {
+  for (int i = n_sel + tid; i < budget && split == 0; i += kHNT) {
     a.sel[(size_t)bh * budget + i] = -1;
     if (a.sel_ub) a.sel_ub[(size_t)bh * budget + i] = -__builtin_inff();
   }
@@ -215,14 +227,17 @@ head_decode_kernel(HeadArgs a) {
   unsigned char* kbuf = smem + (size_t)wave * kHeadKbufWave;
   float* rz = reinterpret_cast<float*>(smem + lay.rz) + wave * kHeadSlots;
   int* ri = reinterpret_cast<int*>(smem + lay.ri) + wave * kHeadSlots;
-  Cand<float>* wspill = a.spill + ((size_t)bh * kHNW + wave) * a.wcap;
+  Cand<float>* wspill = a.spill + (((size_t)bh * a.splits + split) * kHNW + wave) * a.wcap;
+  // this workgroup's selection slots (all of them unless split)
+  const int s_lo = SPLIT ? split * a.pps : 0;
+  const int s_hi = SPLIT ? min(n_sel, s_lo + a.pps) : n_sel;
   const float window = (float)a.window_d;
   const uint64_t ltm = lanemask_below(lane);
   // Slot s (page sel_l[s]) into buffer k; a slot past the selection or an
   // invalid physical page reads page 0 of the pool (its scores are dropped).
   // The loads are issued on every path, so the waits count them exactly.
   auto issue = [&](int s, int k) {
-    const int ph = s < n_sel ? phys_l[s] : 0;
+    const int ph = s < s_hi ? phys_l[s] : 0;
     const bool okp = ph >= 0 && ph < num_phys;
     const unsigned char* base = reinterpret_cast<const unsigned char*>(
         a.k_pool + ((size_t)(okp ? ph : 0) * a.Hkv + g) * (size_t)PS * D);
@@ -306,14 +321,14 @@ head_decode_kernel(HeadArgs a) {
   int since[NBUF];
 #pragma unroll
   for (int k = 0; k < NBUF; ++k) {
-    issue(wave + k * kHNW, k);
+    issue(s_lo + wave + k * kHNW, k);
     since[k] = 0;
   }
-  for (int s0 = wave; s0 < n_sel; s0 += NBUF * kHNW) {
+  for (int s0 = s_lo + wave; s0 < s_hi; s0 += NBUF * kHNW) {
 #pragma unroll
     for (int k = 0; k < NBUF; ++k) {
       const int s = s0 + k * kHNW;
-      if (s < n_sel) {
+      if (s < s_hi) {
         wait_vmcnt_plus<(NBUF - 1) * NI>(since[k]);
         const int nst = score_page(s, k);
 #pragma unroll
@@ -344,6 +359,14 @@ head_decode_kernel(HeadArgs a) {
     n_cand += wcnt[w];
   }
   float* out_row = a.out + (size_t)bh * D;
+  const size_t reg = (size_t)bh * a.splits + split;  // split form: this region
+  if (SPLIT && Mg == -__builtin_inff()) {
+    if (tid == 0) {
+      a.counts[reg] = 0;
+      a.maxima[reg] = -__builtin_inff();
+    }
+    return;
+  }
   if (Mg == -__builtin_inff()) {
     for (int d = tid; d < D; d += kHNT) out_row[d] = 0.0f;
     if (tid == 0) {
@@ -361,7 +384,7 @@ head_decode_kernel(HeadArgs a) {
     // support token has a > t_S.
     if (tid < kRegList * kWave) {
       float v = -__builtin_inff();
-      for (int s = tid; s < n_sel; s += kRegList * kWave) v = max(v, pmax[s]);
+      for (int s = s_lo + tid; s < s_hi; s += kRegList * kWave) v = max(v, pmax[s]);
       reinterpret_cast<float*>(smem + lay.lz)[tid] = v;  // region A is idle here
     }
     __syncthreads();
@@ -439,6 +462,22 @@ head_decode_kernel(HeadArgs a) {
   }
   __syncthreads();
 
+  if constexpr (SPLIT) {
+    // the region for the threshold kernel: the window list in order, its
+    // length and this split's maximum (at most rcap <= LCAP entries)
+    Cand<float>* dst = a.cand + reg * a.rcap;
+    for (int i = tid; i < n_list; i += kHNT) {
+      Cand<float> cv;
+      cv.z = lz[i];
+      cv.idx = li[i];
+      dst[i] = cv;
+    }
+    if (tid == 0) {
+      a.counts[reg] = n_list;
+      a.maxima[reg] = Mg;
+    }
+    return;
+  }
   // 4. Threshold, support and output.
   tau_solve_pv<bf16_t, D, kHNT>(a.v_pool, a.Hkv, g, PS, lz, li,
                                 reinterpret_cast<float*>(smem + lay.sp),

@@ -238,10 +238,18 @@ constexpr long long kHeadMinHeads = 128;
 constexpr long long kHeadMaxBytes = 2 << 20;
 constexpr long long kHeadMaxBytesRounds = 512 << 10;
 constexpr size_t kHeadMaxLds = 150 * 1024;
+// With fewer than kHeadMinHeads heads, each head's selection is split over
+// `splits` workgroups (enough for about one per CU) that write candidate
+// regions, and the threshold kernel finishes the step (its plan `tp`, its
+// workspace `tws` at offset `dec`).
 struct HeadPlan {
   bool use = false;
+  int splits = 1, pps = 0;
   int wcap = 0, list_cap = 0;
   size_t spill = 0, list = 0, total = 0;
+  SplitPlan tp;
+  DecodeWs tws;
+  size_t dec = 0;
 };
 HeadPlan plan_head(const LaunchShape& s, int budget, size_t select_bytes);
 // bt_lds: block_table is 16-byte aligned and max_pages a multiple of 4 (the
@@ -251,6 +259,7 @@ hipError_t launch_head_decode(const LaunchShape& s, const SelectPlan& sp, const 
                               const int32_t* bt, const int32_t* lens, int budget, float alpha,
                               float window, int32_t* sel, float* sel_ub, float* out, float* tau,
                               int32_t* support, void* ws, bool bt_lds, hipStream_t st);
+constexpr long long kHeadSplitTarget = kNumCUs;  // workgroups the split form aims at
 
 // Per-dtype instantiations (decode_bf16.hip, decode_f32.hip).
 hipError_t launch_score_bf16(const LaunchShape& s, const SplitPlan& p, const float* q,

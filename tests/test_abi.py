@@ -344,8 +344,13 @@ def test_decode_topk_validation(ek):
     # 128 query heads, bf16, budget 82: the per-head path (bounds + one kernel)
     assert ek.lib.entmaxkv_topk_kernels(ctypes.byref(s), 82, ctypes.byref(n)) == 0
     assert n.value == 2 and ek.entmaxkv_topk_kernels(s, 82) == 2
-    # fewer heads, float32 caches or a budget past the per-head limit: four kernels
-    for sh, budget in ((shape(ek, batch=1), 64), (shape(ek, kv_dtype="f32"), 82), (s, 1025)):
+    # fewer heads: the split form (bounds, split per-head kernel, threshold)
+    few = shape(ek, batch=1)
+    assert ek.entmaxkv_topk_kernels(few, 64) == 3
+    rc, need3 = ws_rc(ek, few, 64, ek.ENTMAXKV_WS_TOPK)
+    assert rc == 0 and need3 >= ws_rc(ek, few, 64, ek.ENTMAXKV_WS_SELECT)[1]
+    # float32 caches or a budget past the per-head limit: four kernels
+    for sh, budget in ((shape(ek, kv_dtype="f32"), 82), (s, 1025), (few, 1025)):
         assert ek.entmaxkv_topk_kernels(sh, budget) == 4
         rc, need4 = ws_rc(ek, sh, budget, ek.ENTMAXKV_WS_TOPK)
         _, sel_b = ws_rc(ek, sh, budget, ek.ENTMAXKV_WS_SELECT)

@@ -2,8 +2,10 @@
 one call) against the oracle and against the two-call path.
 
 With bf16 caches and at least 128 query heads the call runs the per-head
-select-and-decode kernel; otherwise the four kernels of entmaxkv_score_select
-and entmaxkv_decode_sparse. In both cases the selection must equal
+select-and-decode kernel; with fewer heads its split form (several
+workgroups per head, each selecting the head's pages and scoring a share,
+then the threshold kernel); with float32 caches the four kernels of
+entmaxkv_score_select and entmaxkv_decode_sparse. In both cases the selection must equal
 entmaxkv_score_select's bit for bit (same bounds, same radix select), the
 outputs must match the oracle run on that selection at the tolerances of the
 other parity tests, and the two paths' outputs must agree. Shapes cover both
@@ -144,11 +146,41 @@ def test_all_equal_scores_spill_and_global_list():
     compare(inp, 1024, 1.5, sample(w, 6, 3))
 
 
-def test_fallback_path_matches():
-    """Fewer than 128 heads: the four-kernel path behind the same call."""
+def test_split_form_few_heads():
+    """Fewer than 128 heads: the split form (bounds, several workgroups per
+    head writing candidate regions, the threshold kernel)."""
     w = synth.shrink(synth.WORKLOADS["extreme_512k"], context=9000, n_planted=32)
     inp = synth.generate(w, synth.WORKLOAD_SEEDS["extreme_512k"])
-    compare(inp, 20, 1.5)
+    dev = None
+    for budget, alpha in ((20, 1.5), (64, 1.25), (200, 2.0)):
+        dev = compare(inp, budget, alpha, dev=dev)
+
+
+@pytest.mark.parametrize("D,ps,H,Hkv,lens", [
+    (128, 16, 8, 2, (3000, 1, 0, 2500)),
+    (64, 32, 16, 16, (900, 4000)),
+    (128, 64, 4, 1, (7000,)),
+])
+def test_split_form_shapes_ragged(D, ps, H, Hkv, lens):
+    w = synth.Workload("topk_split", len(lens), H, Hkv, D, ps, max(lens), "bf16", (1.5,), (9,),
+                       4.0 / np.sqrt(D), plant="group_mean", n_planted=16, seq_lens=lens)
+    inp = synth.generate(w, 43)
+    dev = None
+    for budget in (3, 37):
+        dev = compare(inp, budget, 1.5, dev=dev)
+
+
+def test_split_form_chunked_selection():
+    """32 rows of 8192+ pages: chunk candidates selected by every split."""
+    lens = (8192 * 16 + 33,)
+    w = synth.Workload("topk_split_chunked", 1, 32, 8, 64, 16, max(lens), "bf16", (1.5,), (64,),
+                       4.0 / 8.0, plant="group_mean", n_planted=64, run_len=4, seq_lens=lens)
+    inp = synth.generate(w, 47)
+    compare(inp, 64, 1.5)
+
+
+def test_fallback_path_matches():
+    """float32 caches: the four-kernel path behind the same call."""
     w = synth.WORKLOADS["tiny_4k_f32"]
     inp = synth.generate(w, synth.WORKLOAD_SEEDS["tiny_4k_f32"])
     compare(inp, 32, 1.5)
