@@ -92,6 +92,21 @@ class Dev:
                                  budget, alpha, out, tau, sup)
         return out, tau, sup
 
+    def topk(self, budget, alpha):
+        """entmaxkv_decode_topk: bounds, top-k and sparse decode in one call
+        (the sparse path the benchmark times)."""
+        E = ek()
+        if self.meta is None:
+            self.build_meta()
+        sel = torch.full((self.w.batch, self.w.num_q_heads, budget), -7, dtype=torch.int32,
+                         device=self.device)
+        sel_ub = torch.empty((self.w.batch, self.w.num_q_heads, budget), dtype=torch.float32,
+                             device=self.device)
+        out, tau, sup = self._outs()
+        E.entmaxkv_decode_topk(self.shape, self.q, self.meta, self.k, self.v, self.bt, self.lens,
+                               budget, alpha, sel, out, sel_ub=sel_ub, tau=tau, support=sup)
+        return sel, sel_ub, out, tau, sup
+
     def full(self, alpha):
         E = ek()
         out, tau, sup = self._outs()

@@ -1,6 +1,9 @@
 """Parity at the workloads' full sizes (the configuration the benchmark
-times), on sampled (sequence, head) outputs the oracle computes one by one,
-plus properties that hold at any size for every head."""
+times: entmaxkv_decode_topk for the sparse path, entmaxkv_decode_full), on
+sampled (sequence, head) outputs the oracle computes one by one, plus
+properties that hold at any size for every head. The two-call sparse path
+(entmaxkv_score_select, entmaxkv_decode_sparse) is checked beside it, and the
+one-call path must select the same pages bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -46,14 +49,19 @@ def test_full_size_workload(name):
     inp = synth.generate(w, synth.WORKLOAD_SEEDS[name])
     dev = Dev(inp)
     alpha, budget = w.alphas[0], w.budgets[0]
-    announce(f"full size {name}: meta/select/sparse/full")
+    announce(f"full size {name}: meta/select/sparse/full/topk")
     meta = dev.build_meta()
     sel, sel_ub = dev.select(budget)
     sp = dev.sparse(sel, budget, alpha)
     fu = dev.full(alpha)
+    tk_sel, tk_ub, *tk = dev.topk(budget, alpha)
     torch.cuda.synchronize()
     whole_batch_properties(w, sel, sel_ub, *sp, budget, inp["seq_lens"])
     whole_batch_properties(w, sel, sel_ub, *fu, budget, inp["seq_lens"])
+    # the one-call sparse path selects the same pages bit for bit
+    assert torch.equal(tk_sel, sel) and torch.equal(tk_ub, sel_ub)
+    whole_batch_properties(w, sel, sel_ub, *tk, budget, inp["seq_lens"])
+    to, tt, ts = (x.cpu().numpy() for x in tk)
     meta64 = meta_to_f64(meta, w.kv_dtype)
     sel_np, ub_np = sel.cpu().numpy(), sel_ub.cpu().numpy()
     so, st, ss = (x.cpu().numpy() for x in sp)
@@ -65,8 +73,9 @@ def test_full_size_workload(name):
         n_near, n_diff = check_selection(inp, b, h, budget, sel_np[b, h], ub_np[b, h], seq_meta)
         near += n_near
         differing += n_diff
-        check_decode(O.decode_sparse(inp, b, h, alpha, sel_np[b, h]), so[b, h], st[b, h],
-                     ss[b, h], w.kv_dtype, alpha, f"{name} sparse b{b} h{h}")
+        ref = O.decode_sparse(inp, b, h, alpha, sel_np[b, h])
+        check_decode(ref, so[b, h], st[b, h], ss[b, h], w.kv_dtype, alpha, f"{name} sparse b{b} h{h}")
+        check_decode(ref, to[b, h], tt[b, h], ts[b, h], w.kv_dtype, alpha, f"{name} topk b{b} h{h}")
         check_decode(O.decode_full(inp, b, h, alpha), fo[b, h], ft[b, h], fs[b, h],
                      w.kv_dtype, alpha, f"{name} full b{b} h{h}")
     announce(f"full size {name}: near-tie pages {near}, pages where the selections "
@@ -104,12 +113,19 @@ def test_full_size_alpha_sweep():
             announce(f"full size {name}: decode budget={budget} alpha={alpha}")
             sp = dev.sparse(sel, budget, alpha)
             fu = dev.full(alpha) if budget == w.budgets[0] else None
+            tk_sel, tk_ub, *tk = dev.topk(budget, alpha)
             torch.cuda.synchronize()
             whole_batch_properties(w, sel, sel_ub, *sp, budget, inp["seq_lens"])
+            assert torch.equal(tk_sel, sel) and torch.equal(tk_ub, sel_ub)
+            whole_batch_properties(w, sel, sel_ub, *tk, budget, inp["seq_lens"])
             so, st, ss = (x.cpu().numpy() for x in sp)
+            to, tt, ts = (x.cpu().numpy() for x in tk)
             for b, h in heads:
-                check_decode(O.decode_sparse(inp, b, h, alpha, sel_np[b, h]), so[b, h], st[b, h],
-                             ss[b, h], w.kv_dtype, alpha, f"sweep sparse a{alpha} B{budget} b{b} h{h}")
+                ref = O.decode_sparse(inp, b, h, alpha, sel_np[b, h])
+                check_decode(ref, so[b, h], st[b, h], ss[b, h], w.kv_dtype, alpha,
+                             f"sweep sparse a{alpha} B{budget} b{b} h{h}")
+                check_decode(ref, to[b, h], tt[b, h], ts[b, h], w.kv_dtype, alpha,
+                             f"sweep topk a{alpha} B{budget} b{b} h{h}")
             if fu is not None:
                 fo, ft, fs = (x.cpu().numpy() for x in fu)
                 for b, h in heads:

@@ -21,21 +21,9 @@ import torch
 from oracle import entmax_oracle as O
 from sparse_long_context_page_amd import synth
 from parity_util import Dev, announce, check_decode, check_meta_sequence, check_selection, \
-    meta_to_f64, ek
+    meta_to_f64
 
 pytestmark = pytest.mark.gpu
-
-
-def topk(dev: Dev, budget: int, alpha: float):
-    E = ek()
-    w = dev.w
-    sel = torch.full((w.batch, w.num_q_heads, budget), -7, dtype=torch.int32, device=dev.device)
-    sel_ub = torch.empty((w.batch, w.num_q_heads, budget), dtype=torch.float32,
-                         device=dev.device)
-    out, tau, sup = dev._outs()
-    E.entmaxkv_decode_topk(dev.shape, dev.q, dev.meta, dev.k, dev.v, dev.bt, dev.lens, budget,
-                           alpha, sel, out, sel_ub=sel_ub, tau=tau, support=sup)
-    return sel, sel_ub, out, tau, sup
 
 
 def compare(inp, budget, alpha, heads=None, dev=None):
@@ -46,7 +34,7 @@ def compare(inp, budget, alpha, heads=None, dev=None):
     if dev.meta is None:
         dev.build_meta()
     announce(f"{w.name}: decode_topk budget={budget} alpha={alpha}")
-    sel, sel_ub, out, tau, sup = topk(dev, budget, alpha)
+    sel, sel_ub, out, tau, sup = dev.topk(budget, alpha)
     sel2, ub2 = dev.select(budget)
     out2, tau2, sup2 = dev.sparse(sel2, budget, alpha)
     torch.cuda.synchronize()
