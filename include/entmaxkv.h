@@ -205,7 +205,7 @@ int entmaxkv_append_page_moments(const entmaxkv_shape* shape, const void* k_pool
  * num_q_heads]) receives tau_hat (NaN for an empty sequence). The selection
  * feeds entmaxkv_decode_sparse with budget_pages = cap_pages.
  * Workspace: entmaxkv_workspace_bytes(..., ENTMAXKV_WS_GAUSS).
- * Kernels launched: 3 (page statistics, tau_hat and keys, select).
+ * Kernels launched: 2 (page statistics; tau_hat, keys and the capped select).
  */
 int entmaxkv_gauss_select(const entmaxkv_shape* shape, const float* q, const void* moments,
                           const int32_t* block_table, const int32_t* seq_lens, float alpha,

@@ -436,14 +436,10 @@ int entmaxkv_gauss_select(const entmaxkv_shape* shape, const float* q, const voi
   if (launch_gauss_stats(s, q, moments, block_table, seq_lens, am1, stats, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
-  if (launch_gauss_solve(s, stats, seq_lens, m, (double)delta, keys, tau_hat, stream) !=
-      hipSuccess)
+  if (launch_gauss_solve(s, stats, seq_lens, m, (double)delta, keys, tau_hat, cap_pages, sel,
+                         stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
-  if (!ev.after(1) || !ev.before(2)) return ENTMAXKV_ERR_HIP;
-  if (launch_select(s, SelectPlan(), keys, seq_lens, cap_pages, sel, nullptr, true, stream) !=
-      hipSuccess)
-    return ENTMAXKV_ERR_HIP;
-  if (!ev.after(2)) return ENTMAXKV_ERR_HIP;
+  if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
   return ENTMAXKV_OK;
 }
 
@@ -485,7 +481,7 @@ int entmaxkv_score_select(const entmaxkv_shape* shape, const float* q, const voi
   if (launch_bounds(s, sp, q, meta, block_table, seq_lens, ub, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
-  if (launch_select(s, sp, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
+  if (launch_select(s, sp, ub, seq_lens, budget_pages, sel, sel_ub, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
   return ENTMAXKV_OK;
@@ -513,7 +509,7 @@ int entmaxkv_score_select_noalloc(const entmaxkv_shape* shape, const float* q, c
   if (launch_bounds(s, sp, q, meta, block_table, seq_lens, ub, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(0) || !ev.before(1)) return ENTMAXKV_ERR_HIP;
-  if (launch_select(s, sp, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
+  if (launch_select(s, sp, ub, seq_lens, budget_pages, sel, sel_ub, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
   return ENTMAXKV_OK;
@@ -571,7 +567,7 @@ int entmaxkv_decode_topk(const entmaxkv_shape* shape, const float* q, const void
     if (!ev.after(2) || !ev.before(3) || !ev.after(3)) return ENTMAXKV_ERR_HIP;
     return ENTMAXKV_OK;
   }
-  if (launch_select(s, sp, ub, seq_lens, budget_pages, sel, sel_ub, false, stream) != hipSuccess)
+  if (launch_select(s, sp, ub, seq_lens, budget_pages, sel, sel_ub, stream) != hipSuccess)
     return ENTMAXKV_ERR_HIP;
   if (!ev.after(1)) return ENTMAXKV_ERR_HIP;
   return decode_common(shape, q, k_pool, v_pool, block_table, seq_lens, sel, budget_pages, alpha,

@@ -15,21 +15,24 @@
 //   a page's moment record [mean | var] is split over D/4 lanes, the G
 //   heads' two dot products are formed in float64 and finished by a
 //   multi-value butterfly; (mu_a, s_a) per (b, h, page) go to the workspace.
-// gauss_solve_kernel: one workgroup of 1024 threads per (b, h), the head's
-//   page statistics staged in LDS: tau_hat by Newton steps on the logarithm
+// gauss_solve_kernel: one workgroup of 512 threads per (b, h), the head's
+//   page statistics staged in LDS: tau_hat by Halley steps on the logarithm
 //   of the equation's left side (nearly quadratic in t for Gaussian tails),
 //   safeguarded by a bracket that bisects when a step would leave it; then
 //   one key per page (its estimated maximum as float32, or -inf when it fails
-//   the rule) for the top-cap select kernel.
+//   the rule), and the top-cap select over those keys by the same workgroup
+//   (the radix select of the top-k path, -inf keys not candidates).
 #include <cfloat>
 #include <type_traits>
 
+#include "erfc_fit.hpp"
 #include "launch.hpp"
+#include "select_impl.hpp"
 
 namespace ekv {
 
 constexpr int kGaussPages = 32;    // pages per workgroup of the statistics kernel
-constexpr int kGaussNT = 1024;     // threads of a solve workgroup (one per (b, h))
+constexpr int kGaussNT = 512;      // threads of a solve workgroup (one per (b, h))
 constexpr int kGaussLds = 4096;    // pages of a head a solve workgroup holds in LDS
 constexpr int kGaussIters = 100;   // most solve steps
 constexpr double kGaussReach = 9.0;  // pages with mu_a + 9 s_a <= the bracket's left end
@@ -131,78 +134,122 @@ gauss_stats_kernel(const float* __restrict__ q, const KV* __restrict__ moments,
   }
 }
 
-// E[(Y - c)_+^k] for Y ~ N(0, 1), k = M and M - 1 (M in 1..4), from the
-// truncated moments J_k = E[Y^k; Y > c]: J_0 = Q(c), J_1 = phi(c),
-// J_k = c^(k-1) phi(c) + (k-1) J_(k-2), and the binomial expansion of
-// (Y - c)^k. Clamped at 0 (the expansion cancels to rounding noise where
-// phi underflows).
-template <int M>
-__device__ __forceinline__ void normal_partial_moments(double c, double& pm, double& pm1) {
-  const double phi = 0.3989422804014327 * exp(-0.5 * c * c);  // 1/sqrt(2 pi)
-  double J[M + 1];
-  J[0] = 0.5 * erfc(c * 0.7071067811865476);  // Q(c) = erfc(c / sqrt 2) / 2
-  if constexpr (M >= 1) J[1] = phi;
+// Clenshaw's recurrence for sum_k coef[k] T_k(x).
+template <typename T, int N>
+__device__ __forceinline__ T cheb_series(const T (&coef)[N], T x) {
+  T b1 = 0, b2 = 0;
+  const T x2 = x + x;
 #pragma unroll
-  for (int k = 2; k <= M; ++k) {
-    double ck = 1.0;
-#pragma unroll
-    for (int i = 0; i < k - 1; ++i) ck *= c;
-    J[k] = ck * phi + (double)(k - 1) * J[k - 2];
+  for (int k = N - 1; k >= 1; --k) {
+    const T b0 = fma(x2, b1, -b2) + coef[k];
+    b2 = b1;
+    b1 = b0;
   }
-  auto expand = [&](int m) {
-    // sum_k binom(m, k) (-c)^(m-k) J_k
-    double s = 0.0, binom = 1.0;
-    for (int k = m; k >= 0; --k) {
-      double p = 1.0;
-      for (int i = 0; i < m - k; ++i) p *= -c;
-      s += binom * p * J[k];
-      binom = binom * (double)k / (double)(m - k + 1);
-    }
-    return fmax(s, 0.0);
-  };
-  pm = expand(M);
-  pm1 = expand(M - 1);
+  return fma(x, b1, -b2) + coef[0];
 }
 
-// The same in float32 (a cheaper first approximation of tau_hat; the
-// expansion's cancellation in the far tail only touches pages whose share
-// of the sum is negligible there).
-template <int M>
-__device__ __forceinline__ void normal_partial_moments_f(float c, float& pm, float& pm1) {
-  const float phi = 0.39894228f * __expf(-0.5f * c * c);
-  float J[M + 1];
-  J[0] = 0.5f * erfcf(c * 0.70710678f);
-  if constexpr (M >= 1) J[1] = phi;
+// Q(c) = P(Y > c) for Y ~ N(0, 1), given e = exp(-c^2 / 2) (the normal
+// density's exponential, which the caller needs too): for z = |c| / sqrt 2,
+// erfc(z) = t h(t) e with t = 1 / (1 + z / K) and h the fitted Chebyshev
+// series of erfc_fit.hpp (no branches; one reciprocal), and Q(c) = erfc(z)
+// / 2 for c >= 0, 1 - erfc(z) / 2 below.
+__device__ __forceinline__ double normal_tail(double c, double e) {
+  const double t = 1.0 / (1.0 + fabs(c) * (0.7071067811865476 / kErfcK));
+  const double q = 0.5 * t * cheb_series(kErfcC64, 2.0 * t - 1.0) * e;
+  return c >= 0.0 ? q : 1.0 - q;
+}
+__device__ __forceinline__ float normal_tail_f(float c, float e) {
+  const float t = __builtin_amdgcn_rcpf(1.0f + fabsf(c) * (float)(0.7071067811865476 / kErfcK));
+  const float q = 0.5f * t * cheb_series(kErfcC32, 2.0f * t - 1.0f) * e;
+  return c >= 0.0f ? q : 1.0f - q;
+}
+
+constexpr int binomial(int m, int k) {
+  int r = 1;
+  for (int i = 0; i < k; ++i) r = r * (m - i) / (i + 1);
+  return r;
+}
+
+// E[(Y - c)_+^k] for Y ~ N(0, 1) and k = M, M - 1, M - 2 (M in 1..4) in
+// pm[0..2] (for M = 1, pm[2] is the density phi(c), the derivative of
+// pm[1] = Q(c) with the sign flipped), from the truncated moments
+// J_k = E[Y^k; Y > c]: J_0 = Q(c), J_1 = phi(c),
+// J_k = c^(k-1) phi(c) + (k-1) J_(k-2), and the binomial expansion of
+// (Y - c)^k. Clamped at 0 (the expansion cancels to rounding noise where
+// phi underflows). T = double, or float for a cheaper first approximation
+// of tau_hat (the expansion's cancellation in the far tail only touches
+// pages whose share of the sum is negligible there).
+template <int M, typename T>
+__device__ __forceinline__ void normal_partial_moments(T c, T (&pm)[3]) {
+  constexpr bool F64 = std::is_same<T, double>::value;
+  T e, q;
+  if constexpr (F64) {
+    e = exp(-0.5 * c * c);
+    q = normal_tail(c, e);
+  } else {
+    e = __expf(-0.5f * c * c);
+    q = normal_tail_f(c, e);
+  }
+  const T phi = (T)0.3989422804014327 * e;  // 1/sqrt(2 pi)
+  T J[M + 1];
+  J[0] = q;
+  J[1] = phi;
 #pragma unroll
   for (int k = 2; k <= M; ++k) {
-    float ck = 1.0f;
+    T ck = 1;
 #pragma unroll
     for (int i = 0; i < k - 1; ++i) ck *= c;
-    J[k] = ck * phi + (float)(k - 1) * J[k - 2];
+    J[k] = ck * phi + (T)(k - 1) * J[k - 2];
   }
-  auto expand = [&](int m) {
-    float s = 0.0f, binom = 1.0f;
+  auto expand = [&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    // sum_k binom(m, k) (-c)^(m-k) J_k
+    T s = 0;
+#pragma unroll
     for (int k = m; k >= 0; --k) {
-      float p = 1.0f;
+      T p = 1;
+#pragma unroll
       for (int i = 0; i < m - k; ++i) p *= -c;
-      s += binom * p * J[k];
-      binom = binom * (float)k / (float)(m - k + 1);
+      s += (T)binomial(m, k) * p * J[k];
     }
-    return fmaxf(s, 0.0f);
+    return s > 0 ? s : (T)0;
   };
-  pm = expand(M);
-  pm1 = expand(M - 1);
+  pm[0] = expand(std::integral_constant<int, M>{});
+  pm[1] = expand(std::integral_constant<int, M - 1>{});
+  if constexpr (M >= 2) pm[2] = expand(std::integral_constant<int, M - 2>{});
+  else pm[2] = phi;
+}
+
+// Halley's step for the root of F(x) = ln E(x) - const, where E(x) =
+// sum n (A - x)_+^M-type terms with E' = -M E1 and E'' = kH E2 (kH =
+// M (M - 1), or 1 for M = 1): F' = -M E1 / E, F'' = kH E2 / E - F'^2, and
+// the step is -2 F F' / (2 F'^2 - F F'') (Newton's -F / F' where that
+// denominator is not positive). Fv = F(x), e0..e2 = E, E1, E2 at x.
+template <int M>
+__device__ __forceinline__ double halley_step(double Fv, double e0, double e1, double e2) {
+  constexpr double kH = M >= 2 ? (double)(M * (M - 1)) : 1.0;
+  const double F1 = -(double)M * e1 / e0;
+  const double F2 = kH * e2 / e0 - F1 * F1;
+  const double den = 2.0 * F1 * F1 - Fv * F2;
+  return den > 0.0 ? -2.0 * Fv * F1 / den : -Fv / F1;
 }
 
 template <int M>
 __global__ void __launch_bounds__(kGaussNT)
 gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict__ seq_lens,
                    int H, int ps, int max_pages, int ldu, double delta, float* __restrict__ keys,
-                   float* __restrict__ tau_hat) {
+                   float* __restrict__ tau_hat, int cap, int32_t* __restrict__ sel) {
   constexpr int NT = kGaussNT, NW = NT / kWave;
-  __shared__ double red[2 * NW];
-  __shared__ double smu[kGaussLds];
-  __shared__ double ss[kGaussLds];
+  static_assert(3 * kGaussLds * sizeof(double) >= kSelLds * sizeof(uint32_t),
+                "the select's staging reuses the statistics' LDS");
+  __shared__ double red[3 * NW];
+  // (mu, s, 1/s) of the head's pages; after the keys are written, the
+  // select's key staging
+  __shared__ __align__(16) double lds_d[3 * kGaussLds];
+  __shared__ SelectScratch<NT> sel_sh;
+  double* smu = lds_d;
+  double* ss = lds_d + kGaussLds;
+  double* sinv = lds_d + 2 * kGaussLds;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int bh = blockIdx.x, b = bh / H;
@@ -210,33 +257,37 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
   const int P = (L + ps - 1) / ps;
   const double2* row = stats + (size_t)bh * ldu;
   float* krow = keys + (size_t)bh * ldu;
+  int32_t* srow = sel + (size_t)bh * cap;
   if (P == 0) {
     if (tid == 0 && tau_hat) tau_hat[bh] = __builtin_nanf("");
+    for (int i = tid; i < cap; i += NT) srow[i] = -1;
     return;
   }
   auto rows_of = [&](int j) { return (double)min(ps, L - j * ps); };
-  // two sums (or maxima) over the workgroup, the same on every thread
-  auto block2 = [&](double& x, double& y, bool is_max) {
-    if (is_max) {
-      x = wave_max(x);
-      y = wave_max(y);
-    } else {
-      x = wave_allsum(x);
-      y = wave_allsum(y);
-    }
+  // N sums (or maxima) over the workgroup, the same on every thread
+  auto block_reduce = [&](auto nc, double(&x)[decltype(nc)::value], bool is_max) {
+    constexpr int N = decltype(nc)::value;
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = is_max ? wave_max(x[i]) : wave_allsum(x[i]);
     if (lane == 0) {
-      red[2 * wid] = x;
-      red[2 * wid + 1] = y;
+#pragma unroll
+      for (int i = 0; i < N; ++i) red[N * wid + i] = x[i];
     }
     __syncthreads();
-    x = red[0];
-    y = red[1];
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = red[i];
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
-      x = is_max ? fmax(x, red[2 * w]) : x + red[2 * w];
-      y = is_max ? fmax(y, red[2 * w + 1]) : y + red[2 * w + 1];
+#pragma unroll
+      for (int i = 0; i < N; ++i) x[i] = is_max ? fmax(x[i], red[N * w + i]) : x[i] + red[N * w + i];
     }
     __syncthreads();
+  };
+  auto block2 = [&](double& x, double& y, bool is_max) {
+    double v[2] = {x, y};
+    block_reduce(std::integral_constant<int, 2>{}, v, is_max);
+    x = v[0];
+    y = v[1];
   };
 
   // (mu_a, s_a) of the head's pages: staged in LDS when the sequence has at
@@ -248,6 +299,7 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
     if (in_lds) {
       smu[j] = v.x;
       ss[j] = v.y;
+      sinv[j] = v.y > 0.0 ? 1.0 / v.y : 0.0;
     }
     mx = fmax(mx, v.x);
     hx = fmax(hx, v.x + 40.0 * v.y);
@@ -259,7 +311,7 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
 
   // Starting point: the root for one Gaussian pooled over the head's tokens
   // (mean and variance of the page mixture, taken about mx), i.e.
-  // N sbar^M E[(Y - c)_+^M] = 1 solved for c by Newton steps on the log of
+  // N sbar^M E[(Y - c)_+^M] = 1 solved for c by Halley steps on the log of
   // the left side (concave and decreasing in c), then t0 = mubar + c sbar.
   double s1 = 0.0, s2 = 0.0;
   for (int j = tid; j < P; j += NT) {
@@ -282,12 +334,10 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
       const double target = -log(N) - (double)M * log(sbar);  // ln E[(Y - c)_+^M] at the root
       double c = 0.0;
       for (int it = 0; it < 12; ++it) {
-        double pm, pm1;
-        normal_partial_moments<M>(c, pm, pm1);
-        if (!(pm > 0.0)) break;
-        const double h = log(pm) - target;
-        const double dh = -(double)M * pm1 / pm;
-        const double step = -h / dh;
+        double pm[3];
+        normal_partial_moments<M>(c, pm);
+        if (!(pm[0] > 0.0)) break;
+        const double step = halley_step<M>(log(pm[0]) - target, pm[0], pm[1], pm[2]);
         c += step;
         if (fabs(step) <= 1e-6 * fmax(1.0, fabs(c))) break;
       }
@@ -295,108 +345,100 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
     }
   }
 
-  // f(t) = sum_p n_p E[(A_p - t)_+^M] and g(t) = -f'(t) / M, over the pages
-  // that can reach t (a page with mu + 9 s below the bracket's left end adds
-  // less than 1e-19 n s^M). sums64 in float64; sums32 entirely in float32, a
-  // cheaper first approximation (its cancellation in the far tail only
-  // touches pages whose share of the sum is negligible there).
-  auto term64 = [&](double mu, double s, double n, double t, double& f, double& g) {
-    if (s > 0.0) {
-      if (mu + kGaussReach * s <= a) return;
-      double pm, pm1;
-      normal_partial_moments<M>((t - mu) / s, pm, pm1);
-      double sm1 = 1.0;
+  // f(t) = sum_p n_p E[(A_p - t)_+^M], g(t) = -f'(t) / M and h(t) =
+  // f''(t) / kH over the pages that can reach t (a page with mu + 9 s below
+  // the bracket's left end adds less than 1e-19 n s^M). In float64, or
+  // entirely in float32 for a cheaper first approximation (its cancellation
+  // in the far tail only touches pages whose share of the sum is negligible
+  // there; c is clamped so that its powers stay finite, and only the float64
+  // step that follows decides tau_hat).
+  auto term = [&](auto mu, auto s, auto inv_s, auto n, auto t, auto lo, auto (&acc)[3]) {
+    using T = decltype(mu);
+    T v0 = 0, v1 = 0, v2 = 0;  // this page's f, g and h
+    if (s > (T)0) {
+      if (mu + (T)kGaussReach * s <= lo) return;
+      T c = (t - mu) * inv_s;
+      if constexpr (!std::is_same<T, double>::value) c = fminf(fmaxf(c, -1.0e4f), 1.0e4f);
+      T pm[3];
+      normal_partial_moments<M>(c, pm);
+      T sm2 = 1;  // s^(M-2) for M >= 2
 #pragma unroll
-      for (int i = 0; i < M - 1; ++i) sm1 *= s;
-      f += n * sm1 * s * pm;
-      g += n * sm1 * pm1;
+      for (int i = 0; i < M - 2; ++i) sm2 *= s;
+      const T sm1 = M >= 2 ? sm2 * s : (T)1;  // s^(M-1)
+      v0 = n * sm1 * s * pm[0];
+      v1 = n * sm1 * pm[1];
+      v2 = n * (M >= 2 ? sm2 : inv_s) * pm[2];
     } else if (mu > t) {
-      const double d = mu - t;
-      double dm1 = 1.0;
+      const T d = mu - t;
+      T dm2 = 1;  // d^(M-2) for M >= 2
 #pragma unroll
-      for (int i = 0; i < M - 1; ++i) dm1 *= d;
-      f += n * dm1 * d;
-      g += n * dm1;
+      for (int i = 0; i < M - 2; ++i) dm2 *= d;
+      v0 = M >= 2 ? n * dm2 * d * d : n * d;
+      v1 = M >= 2 ? n * dm2 * d : n;
+      v2 = M >= 2 ? n * dm2 : (T)0;
     }
+    acc[0] += v0;
+    acc[1] += v1;
+    acc[2] += v2;
   };
-  auto term32 = [&](float mu, float s, float n, float t, float a32, float& f, float& g) {
-    if (s > 0.0f) {
-      if (mu + (float)kGaussReach * s <= a32) return;
-      float pm, pm1;
-      // (clamped so that its powers stay finite in float32; only the float64
-      // steps that follow decide tau_hat)
-      const float c = fminf(fmaxf((t - mu) * __frcp_rn(s), -1.0e4f), 1.0e4f);
-      normal_partial_moments_f<M>(c, pm, pm1);
-      float sm1 = 1.0f;
-#pragma unroll
-      for (int i = 0; i < M - 1; ++i) sm1 *= s;
-      f += n * sm1 * s * pm;
-      g += n * sm1 * pm1;
-    } else if (mu > t) {
-      const float d = mu - t;
-      float dm1 = 1.0f;
-#pragma unroll
-      for (int i = 0; i < M - 1; ++i) dm1 *= d;
-      f += n * dm1 * d;
-      g += n * dm1;
-    }
-  };
-  auto sums = [&](auto f32, double t, double& f, double& g) {
+  auto sums = [&](auto f32, double t, double (&fgh)[3]) {
     constexpr bool F32 = decltype(f32)::value;
-    f = 0.0;
-    g = 0.0;
     if constexpr (F32) {
-      float ff = 0.0f, gg = 0.0f;
+      float acc[3] = {0.0f, 0.0f, 0.0f};
       const float tf = (float)t, af = (float)a;
 #pragma unroll 1
       for (int j = tid; j < P; j += NT) {
-        double mu, sd;
+        double mu, sd, si;
         if (in_lds) {
           mu = smu[j];
           sd = ss[j];
+          si = sinv[j];
         } else {
           const double2 v = row[j];
           mu = v.x;
           sd = v.y;
+          si = sd > 0.0 ? 1.0 / sd : 0.0;
         }
-        term32((float)mu, (float)sd, (float)rows_of(j), tf, af, ff, gg);
+        term((float)mu, (float)sd, (float)si, (float)rows_of(j), tf, af, acc);
       }
-      f = ff;
-      g = gg;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) fgh[i] = acc[i];
     } else {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) fgh[i] = 0.0;
 #pragma unroll 1
       for (int j = tid; j < P; j += NT) {
         if (in_lds) {
-          term64(smu[j], ss[j], rows_of(j), t, f, g);
+          term(smu[j], ss[j], sinv[j], rows_of(j), t, a, fgh);
         } else {
           const double2 v = row[j];
-          term64(v.x, v.y, rows_of(j), t, f, g);
+          term(v.x, v.y, v.y > 0.0 ? 1.0 / v.y : 0.0, rows_of(j), t, a, fgh);
         }
       }
     }
-    block2(f, g, false);
+    block_reduce(std::integral_constant<int, 3>{}, fgh, false);
   };
-  // Newton steps on ln f (nearly quadratic for Gaussian tails, so few steps)
-  // inside a bracket [lo, hi] that every step shrinks; a step that would
-  // leave it bisects instead. First in float32 from the pooled start, to
-  // about 1e-4 of f (on a bracket of its own: float32 may misjudge which side
-  // of the root a point is on), then in float64 from there on the float64
-  // bracket: from that start Newton's quadratic convergence reaches the
-  // sum's rounding level in two steps.
+  // Halley steps on ln f (cubic convergence; ln f is nearly quadratic in t
+  // for Gaussian tails) inside a bracket [lo, hi] that every step shrinks; a
+  // step that would leave it bisects instead. First in float32 from the
+  // pooled start, to about 1e-5 of f (on a bracket of its own: float32 may
+  // misjudge which side of the root a point is on), then in float64 from
+  // there on the float64 bracket: from within 1e-5 one cubic step reaches
+  // the sum's rounding level.
   // tol: stop when |f - 1| <= tol; last: when |f - 1| <= last, take that
-  // step and stop (from there one quadratic step reaches the rounding
-  // level); rel: stop when a step or the bracket is below rel of t.
-  auto newton = [&](auto f32, double t, double lo, double hi, double tol, double last,
-                    double rel, int iters) {
+  // step and stop; rel: stop when a step or the bracket is below rel of t.
+  auto solve = [&](auto f32, double t, double lo, double hi, double tol, double last,
+                   double rel, int iters) {
     for (int it = 0; it < iters; ++it) {
-      double f, g;
-      sums(f32, t, f, g);
+      double fgh[3];
+      sums(f32, t, fgh);
+      const double f = fgh[0];
       if (f >= 1.0) lo = t;
       else hi = t;
       if (fabs(f - 1.0) <= tol) break;
       double tn = 0.5 * (lo + hi);
-      if (f > 0.0 && g > 0.0) {
-        const double tt = t + log(f) * f / ((double)M * g);
+      if (f > 0.0 && fgh[1] > 0.0) {
+        const double tt = t + halley_step<M>(log(f), f, fgh[1], fgh[2]);
         if (tt > lo && tt < hi) tn = tt;
       }
       const double scale = fmax(1.0, fabs(t));
@@ -408,8 +450,8 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
     }
     return t;
   };
-  double t = newton(std::true_type{}, t0, a, z, 1e-4, 0.0, 1e-6, kGaussIters);
-  t = newton(std::false_type{}, fmin(fmax(t, a), z), a, z, 1e-13, 1e-7, 1e-14, kGaussIters);
+  double t = solve(std::true_type{}, t0, a, z, 1e-5, 0.0, 1e-6, kGaussIters);
+  t = solve(std::false_type{}, fmin(fmax(t, a), z), a, z, 1e-13, 1e-5, 1e-14, kGaussIters);
 
   // one key per page: the estimated maximum, or -inf off the rule
   const double cut = t - delta;
@@ -428,6 +470,15 @@ gauss_solve_kernel(const double2* __restrict__ stats, const int32_t* __restrict_
     }
   }
   if (tid == 0 && tau_hat) tau_hat[bh] = (float)t;
+
+  // the capped select over the keys just written (a workgroup-scope barrier
+  // orders their stores before its loads; the statistics' LDS is dead)
+  __syncthreads();
+  const int kept = select_row<NT, true, false>(
+      krow, reinterpret_cast<const uint64_t*>(krow), P, cap, 0, 0, ldu,
+      reinterpret_cast<uint32_t*>(lds_d), sel_sh,
+      [&](int pos, int page, uint32_t) { srow[pos] = page; });
+  for (int i = kept + tid; i < cap; i += NT) srow[i] = -1;
 }
 
 template <typename KV, int D, int G>
@@ -467,26 +518,27 @@ hipError_t launch_gauss_stats(const LaunchShape& s, const float* q, const void* 
 }
 
 hipError_t launch_gauss_solve(const LaunchShape& s, const void* stats, const int32_t* lens, int m,
-                              double delta, float* keys, float* tau_hat, hipStream_t st) {
+                              double delta, float* keys, float* tau_hat, int cap, int32_t* sel,
+                              hipStream_t st) {
   const int heads = s.batch * s.num_q_heads;
   const double2* st2 = static_cast<const double2*>(stats);
   const int ldu = ub_ld(s.max_pages);
   switch (m) {
     case 1:
       hipLaunchKernelGGL(gauss_solve_kernel<1>, dim3(heads), dim3(kGaussNT), 0, st, st2, lens,
-                         s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat);
+                         s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat, cap, sel);
       break;
     case 2:
       hipLaunchKernelGGL(gauss_solve_kernel<2>, dim3(heads), dim3(kGaussNT), 0, st, st2, lens,
-                         s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat);
+                         s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat, cap, sel);
       break;
     case 3:
       hipLaunchKernelGGL(gauss_solve_kernel<3>, dim3(heads), dim3(kGaussNT), 0, st, st2, lens,
-                         s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat);
+                         s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat, cap, sel);
       break;
     default:
       hipLaunchKernelGGL(gauss_solve_kernel<4>, dim3(heads), dim3(kGaussNT), 0, st, st2, lens,
-                         s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat);
+                         s.num_q_heads, s.page_size, s.max_pages, ldu, delta, keys, tau_hat, cap, sel);
       break;
   }
   return hipGetLastError();

@@ -198,12 +198,9 @@ hipError_t launch_bounds(const LaunchShape& s, const SelectPlan& p, const float*
                          const void* meta, const int32_t* bt, const int32_t* lens, float* ub,
                          hipStream_t st);
 
-// drop_neg_inf: pages whose key is -inf are not candidates (the Gaussian
-// selection marks the pages that fail its rule that way); when no more than
-// `budget` candidates remain, all are kept and the rest of the row is -1.
 hipError_t launch_select(const LaunchShape& s, const SelectPlan& p, const float* ub,
                          const int32_t* lens, int budget, int32_t* sel, float* sel_ub,
-                         bool drop_neg_inf, hipStream_t st);
+                         hipStream_t st);
 
 // Page key moments of every page (old_lens == nullptr), or, after an append,
 // of the pages the tokens [old_lens, lens) touch (at most max_new per sequence).
@@ -219,7 +216,8 @@ hipError_t launch_gauss_stats(const LaunchShape& s, const float* q, const void* 
                               const int32_t* bt, const int32_t* lens, double am1, void* stats,
                               hipStream_t st);
 hipError_t launch_gauss_solve(const LaunchShape& s, const void* stats, const int32_t* lens, int m,
-                              double delta, float* keys, float* tau_hat, hipStream_t st);
+                              double delta, float* keys, float* tau_hat, int cap, int32_t* sel,
+                              hipStream_t st);
 size_t gauss_ws_bytes(const LaunchShape& s);
 
 // Per-head select-and-decode (bf16 caches): one workgroup per query head

@@ -471,14 +471,11 @@ bounds_mfma_kernel(const float* __restrict__ q, const bf16_t* __restrict__ meta,
 
 // --------------------------------------------------------------------------
 
-// kDrop: keys at or below the order value of -inf are not candidates (the
-// Gaussian selection marks the pages that fail its rule that way); when no
-// more than `budget` candidates remain all are kept and the row is -1 padded.
 // kCand: the keys are the chunked candidates of bounds_mfma_kernel<..., true>
 // (order key | page << 32, keepc per chunk of cp pages, nchunks per head),
 // at most kSelCand of them per head; the kept candidates' pages are written.
 constexpr long long kSelChunkedMinPages = 8192;
-template <int kSelNT, bool kDrop, bool kCand>
+template <int kSelNT, bool kCand>
 __global__ void __launch_bounds__(kSelNT)
 select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens, int H, int G,
               int Hkv, int U, int ps, int max_pages, int ldu, int budget,
@@ -494,7 +491,7 @@ select_kernel(const float* __restrict__ ub, const int32_t* __restrict__ seq_lens
   const int P = (L + ps - 1) / ps;
   int32_t* out = sel + (size_t)bh * budget;
   float* out_ub = sel_ub ? sel_ub + (size_t)bh * budget : nullptr;
-  const int kept = select_row<kSelNT, kDrop, kCand>(
+  const int kept = select_row<kSelNT, false, kCand>(
       ub + (size_t)bh * ldu, reinterpret_cast<const uint64_t*>(ub) + (size_t)bh * nchunks * keepc,
       P, budget, cp, keepc, kCand ? nchunks * keepc : ldu, sord, sh,
       [&](int pos, int page, uint32_t key) {
@@ -606,17 +603,12 @@ hipError_t launch_bounds(const LaunchShape& s, const SelectPlan& p, const float*
 
 hipError_t launch_select(const LaunchShape& s, const SelectPlan& p, const float* ub,
                          const int32_t* lens, int budget, int32_t* sel, float* sel_ub,
-                         bool drop_neg_inf, hipStream_t st) {
+                         hipStream_t st) {
   const int U = s.batch * s.num_kv_heads;
   const bool wide = U * s.group >= kSelWideFrom;
   const dim3 grid(U * s.group), block(wide ? 256 : 512);
-  const bool cand = p.chunked && !drop_neg_inf;
-  auto kern = wide ? (drop_neg_inf ? select_kernel<256, true, false>
-                                   : (cand ? select_kernel<256, false, true>
-                                           : select_kernel<256, false, false>))
-                   : (drop_neg_inf ? select_kernel<512, true, false>
-                                   : (cand ? select_kernel<512, false, true>
-                                           : select_kernel<512, false, false>));
+  auto kern = wide ? (p.chunked ? select_kernel<256, true> : select_kernel<256, false>)
+                   : (p.chunked ? select_kernel<512, true> : select_kernel<512, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, st, ub, lens, s.num_q_heads, s.group, s.num_kv_heads,
                      U, s.page_size, s.max_pages, ub_ld(s.max_pages), budget, sel, sel_ub, p.cp,
                      p.keepc, p.nchunks);

@@ -40,7 +40,7 @@ ENTMAXKV_WS_TOPK = 4
 KERNELS = {"build_page_meta": 1, "append_page_meta": 1, "score_select": 2,
            "score_select_noalloc": 2, "decode_sparse": 2, "decode_topk": 4,
            "decode_full": 2, "build_page_moments": 1, "append_page_moments": 1,
-           "gauss_select": 3}
+           "gauss_select": 2}
 
 
 class Shape(ctypes.Structure):
