@@ -11,7 +11,7 @@
 //  - a page's estimated maximum is mu_a + s_a sqrt(2 ln n_p), and the page
 //    is a candidate when that exceeds tau_hat - Delta.
 //
-// gauss_stats_kernel: one workgroup per (chunk of 32 pages, (b, KV head));
+// gauss_stats_kernel: one workgroup per (chunk of 64 pages, (b, KV head));
 //   a page's moment record [mean | var] is split over D/4 lanes, the G
 //   heads' two dot products are formed in float64 and finished by a
 //   multi-value butterfly; (mu_a, s_a) per (b, h, page) go to the workspace.
@@ -31,7 +31,7 @@
 
 namespace ekv {
 
-constexpr int kGaussPages = 32;    // pages per workgroup of the statistics kernel
+constexpr int kGaussPages = 64;    // pages per workgroup of the statistics kernel
 constexpr int kGaussNT = 512;      // threads of a solve workgroup (one per (b, h))
 constexpr int kGaussLds = 4096;    // pages of a head a solve workgroup holds in LDS
 constexpr int kGaussIters = 100;   // most solve steps
