@@ -27,8 +27,9 @@
 //   the window into a list (tightened first by a lower bound on tau when
 //   there are many), solves tau on f(tau) = sum [a_i - tau]_+^m = 1 -- by
 //   the sort-based closed form for m = 1, 2 on short lists, else by a
-//   safeguarded Newton iteration bracketed by [a_max - 1, a_max] with
-//   bisection when a step leaves the bracket -- then reads V rows only for
+//   safeguarded iteration from the left (Newton's method on f^(1/m) - 1,
+//   then on f near the root) bracketed by [a_max - 1, a_max] with bisection
+//   when a step leaves the bracket -- then reads V rows only for
 //   the tokens with p > 0 (for short lists they are requested before the
 //   solve) and writes o = sum p v / sum p. The rarely taken steps are
 //   out-of-line functions, which keeps the common path's code compact.
@@ -212,6 +213,38 @@ __device__ __forceinline__ double pow_m1(double d, double m, int mcode) {
   }
 }
 
+// The next iterate of the threshold solve from t, where f = sum [a_i - t]_+^m
+// and fp = m sum [a_i - t]_+^(m-1) > 0 (so f'(t) = -fp). Far from the root
+// (|f - 1| >= 1e-3) and for m >= 1 it is Newton's step on phi(t) =
+// f(t)^(1/m) - 1: t + m (f - f^(1 - 1/m)) / fp. phi is convex and
+// decreasing in t (the m-norm of the convex functions [a_i - t]_+), so from
+// a point left of the root the step stays left of it and the iterates rise
+// to the root, as Newton's on f does; the step is exact whenever the active
+// terms are equal and the active set does not change, where Newton's on f
+// needs many steps from a_max - 1. Near the root, and for m < 1 (where
+// f^(1/m) is not a norm), it is Newton's step on f, whose numerator f - 1 is
+// exact there.
+__device__ __forceinline__ double tau_step(double t, double f, double fp, double m, int mcode) {
+  if (m < 1.0 || fabs(f - 1.0) < 1e-3) return t + (f - 1.0) / fp;
+  double g;  // f^(1 - 1/m)
+  switch (mcode) {
+    case 1: g = 1.0; break;
+    case 2: g = sqrt(f); break;
+    case 3: {
+      const double c = cbrt(f);
+      g = c * c;
+      break;
+    }
+    case 4: {
+      const double r = sqrt(f);
+      g = r * sqrt(r);
+      break;
+    }
+    default: g = pow_general(f, 1.0 - 1.0 / m);
+  }
+  return t + m * (f - g) / fp;
+}
+
 template <int SNT>
 __device__ __forceinline__ void scope_sum2(double& a, double& c, double* red) {
   a = wave_allsum(a);
@@ -234,7 +267,8 @@ __device__ __forceinline__ void scope_sum2(double& a, double& c, double* red) {
   }
 }
 
-// Safeguarded Newton for sum_i [a_i - t]_+^m = 1 with a_i = am1 * z_i. The
+// Safeguarded iteration (tau_step) for sum_i [a_i - t]_+^m = 1 with
+// a_i = am1 * z_i. The
 // root lies in [a_max - 1, a_max): f(a_max - 1) >= 1 (top term is 1) and
 // f(a_max) = 0. tlo, when given, is a known lower bound on the root (the
 // threshold of a subset of the tokens, less a margin): the bracket and the
@@ -260,7 +294,7 @@ __device__ double solve_tau(const ZT* z, int n, double am1, double m, int mcode,
     else hi = t;
     if (f == 1.0) break;
     const double scale = fmax(1.0, fabs(t));
-    double tn = fp > 0.0 ? t + (f - 1.0) / fp : 0.5 * (lo + hi);
+    double tn = fp > 0.0 ? tau_step(t, f, fp, m, mcode) : 0.5 * (lo + hi);
     if (fp > 0.0 && fabs(tn - t) <= 2.0 * DBL_EPSILON * scale) {
       t = fmin(fmax(tn, lo), hi);
       break;
@@ -353,7 +387,7 @@ __device__ double solve_tau_block(const double (&a)[K], int used, double m, int 
     else hi = t;
     if (f == 1.0) break;
     const double scale = fmax(1.0, fabs(t));
-    double tn = fp > 0.0 ? t + (f - 1.0) / fp : 0.5 * (lo + hi);
+    double tn = fp > 0.0 ? tau_step(t, f, fp, m, mcode) : 0.5 * (lo + hi);
     if (fp > 0.0 && fabs(tn - t) <= 2.0 * DBL_EPSILON * scale) {
       t = fmin(fmax(tn, lo), hi);
       break;
@@ -389,7 +423,7 @@ __device__ double solve_tau_regs(const double (&a)[K], int n, double am1, double
     else hi = t;
     if (f == 1.0) break;
     const double scale = fmax(1.0, fabs(t));
-    double tn = fp > 0.0 ? t + (f - 1.0) / fp : 0.5 * (lo + hi);
+    double tn = fp > 0.0 ? tau_step(t, f, fp, m, mcode) : 0.5 * (lo + hi);
     if (fp > 0.0 && fabs(tn - t) <= 2.0 * DBL_EPSILON * scale) {
       t = fmin(fmax(tn, lo), hi);
       break;
@@ -1406,7 +1440,7 @@ __device__ __attribute__((noinline)) int tau_prune_list(ZT* lz, int* li, int n_l
         if (!(f >= 1.0) || !(fp > 0.0)) break;  // (not left of the root)
         lo = t;
         if (f == 1.0) break;
-        t = t + (f - 1.0) / fp;
+        t = tau_step(t, f, fp, m, mcode);
         if (!(t < amax)) break;
       }
 #pragma unroll
@@ -1573,7 +1607,7 @@ __device__ __forceinline__ void tau_solve_pv(
   double tau;
   int n_sup;
   double psum = 0.0;
-  if (list_lds && mcode != 0 && n_list > kWave * kRegListLong)
+  if (list_lds && mcode != 0 && n_list > kWave * 2 * kRegListLong)
     n_list = tau_prune_list<ZT, KB, NT>(lz, li, n_list, am1, m, mcode, amax, sh.red, sh.tmp, &tlo);
 
   if (list_lds && n_list <= kWave * kRegList) {
@@ -1600,15 +1634,20 @@ __device__ __forceinline__ void tau_solve_pv(
     tau = sh.tau_b;
     n_sup = sh.nb[1];
     psum = sh.red[0];
-  } else if (list_lds && n_list <= kWave * kRegListLong && mcode != 0) {
-    // Up to 1024 entries at integer m: the same by wave 0 with 16 entries
-    // per lane (no call to the general power).
+  } else if (list_lds && n_list <= kWave * 2 * kRegListLong && mcode != 0) {
+    // Up to 2048 entries at integer m: the same by wave 0 with 16 entries
+    // per lane, or 32 beyond 1024 (no barrier per iteration, no call to the
+    // general power).
     if (wave == 0) {
       int o;
       double t;
       with_mcode<true>(mcode, [&](auto mc) {
-        wave_solve_list<kRegListLong, decltype(mc)::value>(lz, li, sp, n_list, am1, m, mcode,
-                                                           amax, lane, ltm, true, o, psum, t, tlo);
+        if (n_list <= kWave * kRegListLong)
+          wave_solve_list<kRegListLong, decltype(mc)::value>(
+              lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm, true, o, psum, t, tlo);
+        else
+          wave_solve_list<2 * kRegListLong, decltype(mc)::value>(
+              lz, li, sp, n_list, am1, m, mcode, amax, lane, ltm, true, o, psum, t, tlo);
       });
       if (lane == 0) {
         sh.nb[1] = o;
@@ -1805,7 +1844,7 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
   // takes a contiguous run of the batch (all of its loads in flight
   // together), keeps those with z >= thr, and one block scan places them in
   // order; members beyond the LDS capacity go to the head's global list. The
-  // run length is a compile-time 2, 8 or KB, picked from the batch size.
+  // run length is a compile-time 2, 8, 16 or KB, picked from the batch size.
   ZT* gz = list_z + (size_t)bh * list_cap;
   int* gi = list_i + (size_t)bh * list_cap;
   int n_list = 0;
@@ -1815,6 +1854,9 @@ __device__ __forceinline__ void tau_head(const TauArgs<KV>& args, int u, int hh,
     const GatherArgs<ZT> ga{roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp};
     if (per <= 2) n_list = gather_batch<2>(ga, bbase, nb_, n_list);
     else if (per <= 8) n_list = gather_batch<8>(ga, bbase, nb_, n_list);
+    else if (per <= 16)
+      n_list = gather_batch_wide<16>(roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp,
+                                     bbase, nb_, n_list);
     else
       n_list = gather_batch_wide<KB>(roff, creg, splits, cap, thr, lz, li, gz, gi, lcap, tmp,
                                           bbase, nb_, n_list);
