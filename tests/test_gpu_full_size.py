@@ -128,7 +128,19 @@ def test_full_size_alpha_sweep():
                              f"sweep topk a{alpha} B{budget} b{b} h{h}")
             if fu is not None:
                 fo, ft, fs = (x.cpu().numpy() for x in fu)
-                for b, h in heads:
+                checked = list(heads)
+                if alpha == min(w.alphas):
+                    # the heads with the largest supports are those with the
+                    # longest window lists (over 1024 members, over 2048
+                    # candidates at alpha 1.25): the threshold step's long-list
+                    # solve and wide gathers
+                    order = np.argsort(-fs.reshape(-1), kind="stable")[:16]
+                    longest = [(int(i) // w.num_q_heads, int(i) % w.num_q_heads) for i in order]
+                    assert fs.reshape(-1)[order[-1]] >= 250, fs.reshape(-1)[order[-1]]
+                    checked += [bh for bh in longest if bh not in checked]
+                    announce(f"full size {name}: full decode alpha={alpha}, the 16 largest "
+                             f"supports {sorted(int(x) for x in fs.reshape(-1)[order])} checked")
+                for b, h in checked:
                     check_decode(O.decode_full(inp, b, h, alpha), fo[b, h], ft[b, h], fs[b, h],
                                  w.kv_dtype, alpha, f"sweep full a{alpha} b{b} h{h}")
 
