@@ -120,7 +120,17 @@ def test_full_size_alpha_sweep():
             whole_batch_properties(w, sel, sel_ub, *tk, budget, inp["seq_lens"])
             so, st, ss = (x.cpu().numpy() for x in sp)
             to, tt, ts = (x.cpu().numpy() for x in tk)
-            for b, h in heads:
+            sparse_checked = list(heads)
+            if alpha == min(w.alphas) and budget == max(w.budgets):
+                # the sparse heads with the largest supports (the longest
+                # window lists of the sparse threshold step)
+                order = np.argsort(-ss.reshape(-1), kind="stable")[:8]
+                sparse_checked += [(int(i) // w.num_q_heads, int(i) % w.num_q_heads)
+                                   for i in order]
+                announce(f"full size {name}: sparse decode alpha={alpha} budget={budget}, "
+                         f"the 8 largest supports "
+                         f"{sorted(int(x) for x in ss.reshape(-1)[order])} checked")
+            for b, h in dict.fromkeys(sparse_checked):
                 ref = O.decode_sparse(inp, b, h, alpha, sel_np[b, h])
                 check_decode(ref, so[b, h], st[b, h], ss[b, h], w.kv_dtype, alpha,
                              f"sweep sparse a{alpha} B{budget} b{b} h{h}")
