@@ -13,8 +13,9 @@
 //
 // gauss_stats_kernel: one workgroup per (chunk of 64 pages, (b, KV head));
 //   a page's moment record [mean | var] is split over D/4 lanes, the G
-//   heads' two dot products are formed in float64 and finished by a
-//   multi-value butterfly; (mu_a, s_a) per (b, h, page) go to the workspace.
+//   heads' two dot products are formed in float64, and each wave's partials
+//   are transposed through LDS so that a lane adds up 2G of one sum before a
+//   short DPP butterfly; (mu_a, s_a) per (b, h, page) go to the workspace.
 // gauss_solve_kernel: one workgroup of 512 threads per (b, h), the head's
 //   page statistics staged in LDS: tau_hat by Halley steps on the logarithm
 //   of the equation's left side (nearly quadratic in t for Gaussian tails),
@@ -38,6 +39,14 @@ constexpr int kGaussIters = 100;   // most solve steps
 constexpr double kGaussReach = 9.0;  // pages with mu_a + 9 s_a <= the bracket's left end
                                      // contribute below 1e-19 n_p s_a^m: left out of the sums
 
+// Orders a wave's LDS writes before its later LDS reads (a wave's LDS
+// instructions execute in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <typename KV, int D, int G>
 __global__ void __launch_bounds__(256)
 gauss_stats_kernel(const float* __restrict__ q, const KV* __restrict__ moments,
@@ -51,10 +60,19 @@ gauss_stats_kernel(const float* __restrict__ q, const KV* __restrict__ moments,
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   using Chunk = typename std::conditional<sizeof(KV) == 2, u32x2, u32x4>::type;
-  using BF = Butterfly<G, LP>;
-  static_assert(BF::CNT == 1, "group size must not exceed lanes per page");
+  // a wave's partial sums are transposed through LDS: each lane writes its
+  // NV partials (mu and s^2 of every head) of its page, then adds up NV
+  // partials of one sum, and the R lanes that share a sum combine theirs
+  // by DPP lane swaps
+  constexpr int NW = 256 / kWave;
+  constexpr int PPW = kWave / LP;        // pages per wave and step
+  constexpr int NV = 2 * G;              // sums per page: rows 2h (mu), 2h + 1 (s^2)
+  constexpr int R = LP / NV;             // lanes per sum
+  constexpr int ROW = LP * 8 + 16;       // bytes per row of LP partials, padded
+  static_assert(R >= 1 && R * NV == LP && R * PPW * NV == kWave, "group size must not exceed lanes per page");
   static_assert(kGaussPages % PPB == 0, "whole block steps");
   __shared__ int sphys[kGaussPages];
+  __shared__ __align__(16) unsigned char red[NW][PPW * NV * ROW];
 
   const int u = blockIdx.x % U;
   const int chunk = blockIdx.x / U;
@@ -78,8 +96,10 @@ gauss_stats_kernel(const float* __restrict__ q, const KV* __restrict__ moments,
     const float4 v = *reinterpret_cast<const float4*>(q + (size_t)(h0 + h) * D + c * VPC);
     qf[h][0] = v.x; qf[h][1] = v.y; qf[h][2] = v.z; qf[h][3] = v.w;
   }
-  const int my_head = BF::first_index(lane);
-  const bool owner = BF::owner(lane);
+  const int wv = (int)threadIdx.x / kWave;
+  unsigned char* wred = red[wv];
+  const int o = lane / R, k = lane % R;  // the sum this lane adds up, its part
+  const int po = o / NV, ro = o % NV;     // its page in the wave, its row
   __syncthreads();
 
   // every record load of the workgroup in flight before the first is used
@@ -121,16 +141,38 @@ gauss_stats_kernel(const float* __restrict__ q, const KV* __restrict__ moments,
       mu[h] = a;
       s2[h] = v;
     }
-    BF::reduce(mu, lane);
-    BF::reduce(s2, lane);
-    const int jj = t * PPB + threadIdx.x / LP;
+    const int pw = lane / LP;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      *reinterpret_cast<double*>(wred + (pw * NV + 2 * h) * ROW + c * 8) = mu[h];
+      *reinterpret_cast<double*>(wred + (pw * NV + 2 * h + 1) * ROW + c * 8) = s2[h];
+    }
+    wave_lds_sync();
+    const double2* part = reinterpret_cast<const double2*>(wred + o * ROW + k * NV * 8);
+    double sum = 0.0;
+#pragma unroll
+    for (int i = 0; i < NV / 2; ++i) {
+      const double2 d = part[i];
+      sum += d.x;
+      sum += d.y;
+    }
+    wave_lds_sync();  // the next step's partials go to the same rows
+    if constexpr (R >= 2) sum += partner<1>(sum);
+    if constexpr (R >= 4) sum += partner<2>(sum);
+    if constexpr (R >= 8) sum += partner<4>(sum);
+    if constexpr (R >= 16) sum += partner<8>(sum);
+    if constexpr (R >= 32) sum += partner<16>(sum);
+    const double s2sum = partner<R>(sum);  // row 2h + 1 (every lane of it holds the sum)
+    const int jj = t * PPB + wv * PPW + po;
     // a page past the block table's valid range (an input outside the
     // contract) gets a neutral entry: it adds nothing to tau_hat's sum and
     // its key is -inf
-    if (jj < n && owner)
-      stats[(size_t)(h0 + my_head) * ldu + j0 + jj] =
-          ok[t] ? make_double2(am1 * mu[0], am1 * sqrt(fmax(s2[0], 0.0)))
-                : make_double2(-DBL_MAX, 0.0);
+    if (jj < n && k == 0 && (ro & 1) == 0) {
+      const int phys = sphys[jj];
+      stats[(size_t)(h0 + ro / 2) * ldu + j0 + jj] =
+          phys >= 0 && phys < num_phys ? make_double2(am1 * sum, am1 * sqrt(fmax(s2sum, 0.0)))
+                                       : make_double2(-DBL_MAX, 0.0);
+    }
   }
 }
 
